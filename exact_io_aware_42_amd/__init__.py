@@ -1,0 +1,13 @@
+"""FlashAttention-2 exact attention for MI355X (gfx950): HIP kernels behind a C ABI
+(include/fa2.h, libfa2.so) and a thin ctypes binding.
+
+    from exact_io_aware_42_amd import fwd, bwd
+    o, lse = fwd(q, k, v, causal=True)            # bf16 [B, H, N, d] on the GPU
+    dq, dk, dv = bwd(q, k, v, o, do, lse, causal=True)
+
+The library is loaded on first use; if it has not been built the call raises (there is no
+fallback path).
+"""
+from .ops import FA2Error, bwd, bwd_workspace_bytes, fwd, load_library
+
+__all__ = ["fwd", "bwd", "bwd_workspace_bytes", "load_library", "FA2Error"]

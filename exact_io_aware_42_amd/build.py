@@ -1,0 +1,67 @@
+"""Build libfa2.so in-tree with hipcc for gfx950.
+
+    python -m exact_io_aware_42_amd.build
+
+Compiles the HIP kernels and the C ABI into exact_io_aware_42_amd/libfa2.so. Packed-fp32
+VALU instructions are disabled for all device code.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG_DIR)
+CSRC = os.path.join(PKG_DIR, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+LIB_PATH = os.path.join(PKG_DIR, "libfa2.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+SOURCES = ["fa2_api.cpp", "fa2_fwd.hip", "fa2_bwd.hip"]
+ARCH = "gfx950"
+
+COMMON_FLAGS = [
+    f"--offload-arch={ARCH}",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-Wall",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    f"-I{INCLUDE}",
+    f"-I{CSRC}",
+]
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    """Compile every source and link libfa2.so; returns its path. Raises on failure."""
+    objs = []
+    tmp_dir = os.path.join(PKG_DIR, "_build")
+    os.makedirs(tmp_dir, exist_ok=True)
+    for src in SOURCES:
+        obj = os.path.join(tmp_dir, src + ".o")
+        cmd = [HIPCC, *COMMON_FLAGS, *(extra_flags or []), "-c", os.path.join(CSRC, src), "-o", obj]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        # hipcc's host pass does not know the packed-fp32 feature and says so: harmless
+        noise = "not a recognized feature for this target"
+        msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln]
+        if res.returncode != 0:
+            raise RuntimeError(f"hipcc failed on {src}:\n" + "\n".join(msgs))
+        if verbose and msgs:
+            print("\n".join(msgs))
+        objs.append(obj)
+    tmp_lib = LIB_PATH + ".tmp"
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("link failed:\n" + res.stdout + res.stderr)
+    os.replace(tmp_lib, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,120 @@
+// C ABI of libfa2.so (declared in include/fa2.h): host-side validation, then the kernel
+// launches on the caller's stream. No device memory is allocated here.
+#include "fa2.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "fa2_launch.hpp"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+constexpr double kLog2e = 1.4426950408889634074;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Shared size checks. Returns FA2_OK or the status to report.
+fa2_status check_sizes(int B, int H, int N, int d, float scale) {
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return FA2_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return FA2_ERR_INVALID_ARGUMENT;
+  const unsigned long long elems =
+      (unsigned long long)B * (unsigned long long)H * (unsigned long long)N * (unsigned long long)d;
+  if (elems > (1ull << 46)) return FA2_ERR_INVALID_ARGUMENT;
+  // the workgroup grid (B*H*ceil(N/64)) must fit a 32-bit dimension
+  if ((unsigned long long)B * H * ((unsigned long long)(N + 63) / 64) > 0x7fffffffull)
+    return FA2_ERR_INVALID_ARGUMENT;
+  if (d != 64 && d != 128) return FA2_ERR_UNSUPPORTED;
+  return FA2_OK;
+}
+
+fa2_status from_hip(hipError_t e) {
+  if (e == hipSuccess) return FA2_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return FA2_ERR_HIP;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+extern "C" {
+
+fa2_status fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                   int H, int N, int d, int causal, float softmax_scale, hipStream_t stream) {
+  const fa2_status st = check_sizes(B, H, N, d, softmax_scale);
+  if (st != FA2_OK) return st;
+  const void* ptrs[] = {q, k, v, o, lse};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned16(p)) return FA2_ERR_INVALID_ARGUMENT;
+  fa2::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.d = d;
+  a.causal = causal != 0;
+  a.scale_log2 = static_cast<float>(static_cast<double>(softmax_scale) * kLog2e);
+  a.stream = stream;
+  return from_hip(fa2::launch_fwd(a));
+}
+
+size_t fa2_bwd_workspace_bytes(int B, int H, int N, int d) {
+  if (check_sizes(B, H, N, d, 1.0f) != FA2_OK) return 0;
+  return round256((size_t)B * H * N * sizeof(float));
+}
+
+fa2_status fa2_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                   size_t workspace_bytes, int B, int H, int N, int d, int causal,
+                   float softmax_scale, hipStream_t stream) {
+  const fa2_status st = check_sizes(B, H, N, d, softmax_scale);
+  if (st != FA2_OK) return st;
+  const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv, workspace};
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned16(p)) return FA2_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < fa2_bwd_workspace_bytes(B, H, N, d)) return FA2_ERR_INVALID_ARGUMENT;
+  fa2::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.dout = dout;
+  a.lse = lse;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.delta = static_cast<float*>(workspace);
+  a.B = B;
+  a.H = H;
+  a.N = N;
+  a.d = d;
+  a.causal = causal != 0;
+  a.scale = softmax_scale;
+  a.scale_log2 = static_cast<float>(static_cast<double>(softmax_scale) * kLog2e);
+  a.stream = stream;
+  return from_hip(fa2::launch_bwd(a));
+}
+
+const char* fa2_status_string(fa2_status s) {
+  switch (s) {
+    case FA2_OK:
+      return "FA2_OK";
+    case FA2_ERR_INVALID_ARGUMENT:
+      return "FA2_ERR_INVALID_ARGUMENT";
+    case FA2_ERR_UNSUPPORTED:
+      return "FA2_ERR_UNSUPPORTED";
+    case FA2_ERR_HIP:
+      return "FA2_ERR_HIP";
+  }
+  return "FA2_UNKNOWN_STATUS";
+}
+
+int fa2_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

@@ -1,0 +1,106 @@
+// Device-side building blocks shared by the gfx950 attention kernels: vector types, the
+// bf16 MFMA wrapper, bf16 packing, cross-half lane exchange, LDS swizzles and the
+// workgroup -> (query block, batch*head) schedule.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa2 {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr float kLn2 = 0.69314718055994530942f;
+
+// D(32x32) += A(32x16) * B(16x32), bf16 inputs, fp32 accumulate (v_mfma_f32_32x32x16_bf16).
+// Lane l holds A[l%32][8*(l/32) + i] and B[8*(l/32) + i][l%32] for i = 0..7; the result
+// register i of lane l is D[8*(i/4) + 4*(l/32) + (i%4)][l%32].
+__device__ __forceinline__ f32x16_t mfma32(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// Two fp32 values -> one dword of two bf16 (round to nearest even, v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// acc + lo(w) + hi(w), the two bf16 halves of w widened exactly (v_dot2c_f32_bf16 with 1.0).
+__device__ __forceinline__ float add_bf16_pair(float acc, uint32_t w) {
+  const bf16x2_t one = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), one, acc, false);
+}
+
+// max / sum of x over lanes l and l^32 (the two halves of a wave hold the two halves of
+// one query's key set). v_permlane32_swap exchanges the upper half of its first operand
+// with the lower half of its second; applied to (x, x) the two results hold x[l] and
+// x[l^32] in some order in every lane, so a commutative combine needs no lane select.
+__device__ __forceinline__ float max_xor32(float x) {
+  int xi = __float_as_int(x);
+  auto r = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+  return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  int xi = __float_as_int(x);
+  auto r = __builtin_amdgcn_permlane32_swap(xi, xi, false, false);
+  return __int_as_float(r[0]) + __int_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// Key order inside a 32-key MFMA block: M-row m of the score MFMA reads key kmap(m), which
+// swaps bits 2 and 3 of m. With this order lane l's 16 score registers hold keys
+// 8*(l/32) + 0..7 (registers 0..7) and 16 + 8*(l/32) + 0..7 (registers 8..15), exactly
+// the B-operand layout the P*V MFMA needs, so P never leaves registers.
+__device__ __forceinline__ int kmap(int m) {
+  return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
+}
+
+// XOR swizzle of 16-byte chunks in a K tile row (row-major [keys][d]). The 8 lanes of one
+// ds_read_b128 phase read rows kmap(0..7) (or kmap(8..15)) of the same logical chunk; the
+// swizzle sends them to 8 distinct bank groups.
+__device__ __forceinline__ int kswz(int row) { return (row & 3) | ((row >> 1) & 4); }
+
+// XOR swizzle of 16-byte chunks in a transposed V tile row (V^T, [d][keys], 8 chunks of 8
+// keys per row). Readers take 8 consecutive rows of one chunk; writers take one chunk
+// position across rows c = 8*cc + const, so both c and c/8 enter the swizzle.
+__device__ __forceinline__ int vswz(int c) { return (c ^ (c >> 3)) & 7; }
+
+// Workgroup id -> (query block, batch*head) order. Workgroups are dealt to the 8 XCDs in
+// turn (id % 8), each XCD with its own L2. When the heads divide evenly, XCD x gets whole
+// heads x, x+8, ... and runs one head's query blocks back to back, so K/V tiles of a head are
+// re-read from that XCD's L2. With `heavy_first` (causal) the longest query blocks start first.
+struct TileCoord {
+  int qb;
+  int bh;
+};
+__device__ __forceinline__ TileCoord schedule_tile(int wg, int n_qblocks, int bh_count,
+                                                   bool heavy_first) {
+  int qr, bh;
+  if ((bh_count & 7) == 0) {
+    const int xcd = wg & 7;
+    const int j = wg >> 3;
+    bh = (j / n_qblocks) * 8 + xcd;
+    qr = j % n_qblocks;
+  } else {
+    bh = wg % bh_count;
+    qr = wg / bh_count;
+  }
+  TileCoord t;
+  t.qb = heavy_first ? (n_qblocks - 1 - qr) : qr;
+  t.bh = bh;
+  return t;
+}
+
+}  // namespace fa2

@@ -1,0 +1,145 @@
+"""Thin Python binding of libfa2.so (ctypes): argument marshalling only.
+
+Every step of the attention computation runs in the HIP kernels behind the C ABI declared in
+include/fa2.h. PyTorch supplies device memory and the current stream; nothing here computes
+attention, and there is no fallback: if the library is missing or a call fails, an exception
+is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa2.so")
+
+FA2_OK = 0
+FA2_ERR_INVALID_ARGUMENT = 1
+FA2_ERR_UNSUPPORTED = 2
+FA2_ERR_HIP = 3
+
+EXPORTED = ("fa2_fwd", "fa2_bwd", "fa2_bwd_workspace_bytes", "fa2_status_string",
+            "fa2_last_hip_error")
+
+_lib = None
+_lock = threading.Lock()
+
+
+class FA2Error(RuntimeError):
+    pass
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libfa2.so once and declare its signatures. Raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise FA2Error(f"{path} is missing: build it with "
+                           "`python -m exact_io_aware_42_amd.build` (no fallback exists)")
+        lib = ctypes.CDLL(path)
+        vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        lib.fa2_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+        lib.fa2_fwd.restype = i
+        lib.fa2_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                i, i, i, i, i, f, vp]
+        lib.fa2_bwd.restype = i
+        lib.fa2_bwd_workspace_bytes.argtypes = [i, i, i, i]
+        lib.fa2_bwd_workspace_bytes.restype = sz
+        lib.fa2_status_string.argtypes = [i]
+        lib.fa2_status_string.restype = ctypes.c_char_p
+        lib.fa2_last_hip_error.argtypes = []
+        lib.fa2_last_hip_error.restype = i
+        _lib = lib
+        return lib
+
+
+def _check(status: int, what: str):
+    if status != FA2_OK:
+        lib = load_library()
+        name = lib.fa2_status_string(status).decode()
+        extra = f" (HIP error {lib.fa2_last_hip_error()})" if status == FA2_ERR_HIP else ""
+        raise FA2Error(f"{what} failed: {name}{extra}")
+
+
+def _check_tensor(t: torch.Tensor, name: str, shape, dtype=torch.bfloat16, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device, got {t.device}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream_ptr(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+        scale: float | None = None, out: torch.Tensor | None = None,
+        lse: torch.Tensor | None = None):
+    """Attention forward on bf16 [B, H, N, d] tensors. Returns (o bf16, lse fp32 [B, H, N])."""
+    lib = load_library()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    dev = q.device
+    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
+        _check_tensor(t, nm, (B, H, N, d), device=dev)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    _check_tensor(out, "out", (B, H, N, d), device=dev)
+    _check_tensor(lse, "lse", (B, H, N), dtype=torch.float32, device=dev)
+    s = default_scale(d) if scale is None else float(scale)
+    st = lib.fa2_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                     B, H, N, d, int(bool(causal)), s, _stream_ptr(dev))
+    _check(st, "fa2_fwd")
+    return out, lse
+
+
+def bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(load_library().fa2_bwd_workspace_bytes(B, H, N, d))
+
+
+def bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None,
+        dq=None, dk=None, dv=None, workspace=None):
+    """Attention backward. Returns (dq, dk, dv) bf16 [B, H, N, d]."""
+    lib = load_library()
+    B, H, N, d = q.shape
+    dev = q.device
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _check_tensor(t, nm, (B, H, N, d), device=dev)
+    _check_tensor(lse, "lse", (B, H, N), dtype=torch.float32, device=dev)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, nm in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
+        _check_tensor(t, nm, (B, H, N, d), device=dev)
+    ws_bytes = bwd_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+    if workspace.device != dev or workspace.numel() * workspace.element_size() < ws_bytes:
+        raise ValueError("workspace too small or on another device")
+    s = default_scale(d) if scale is None else float(scale)
+    st = lib.fa2_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                     lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                     workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                     B, H, N, d, int(bool(causal)), s, _stream_ptr(dev))
+    _check(st, "fa2_bwd")
+    return dq, dk, dv

@@ -1,0 +1,92 @@
+/*
+ * fa2.h - C ABI of libfa2.so: exact attention forward and backward on one MI355X (gfx950).
+ *
+ * What is computed
+ *   Forward: O = softmax(scale * Q K^T [+ causal mask]) V, row by row, and the per-row
+ *   log-sum-exp LSE_i = log sum_j exp(scale * q_i . k_j) over the visible keys j. This is the
+ *   standard attention of page "Flash Attention v2", section "Flash Attention v1: Recap /
+ *   What v1 Solved", computed with the tiled online softmax of the same page's "Detailed
+ *   Algorithm Comparison / Forward Pass Comparison" and the seven steps of page
+ *   "flashattention-2", "How FlashAttention-2 Works (Tiled Algorithm)": the N x N score
+ *   matrix never reaches device memory. The causal mask keeps keys j <= i (top-left
+ *   aligned; queries and keys share the sequence length N); fully masked tiles are skipped
+ *   (page "flashattention-2", "FlashAttention-2 Improvements Over v1", causal masking row).
+ *   Backward: dQ, dK, dV of that map for a cotangent dO, recomputing the scores block by
+ *   block from Q, K and the saved LSE instead of storing P (page "Flash Attention v2",
+ *   sections "2. Backward Pass Computation" and "5. Gradient Accumulation"; a separate
+ *   backward kernel as on page "FlashAttention-2: Faster Attention with Better Parallelism
+ *   and Work Partitioning"). The gradient is the exact softmax gradient:
+ *     D_i = sum_c dO_ic O_ic,  dS = P * (dO V^T - D),  dV = P^T dO,
+ *     dQ = scale dS K,  dK = scale dS^T Q.
+ *
+ * Layout and types
+ *   q, k, v, o, dout, dq, dk, dv: bfloat16 (raw 16-bit patterns), contiguous row-major
+ *   [B, H, N, d] with d fastest. lse: float32 [B, H, N], natural log. All pointers are
+ *   device pointers and must be 16-byte aligned. B*H*N*d may exceed 2^31 (64-bit offsets).
+ *   Supported head dimensions: d = 64 and d = 128. N >= 1 (any N; ragged tails are masked).
+ *
+ * Ownership
+ *   The caller allocates and owns every buffer. The library never allocates or frees
+ *   device memory and keeps no state between calls except a thread-local error code, so
+ *   calls are re-entrant and thread-safe. Outputs must not alias inputs or each other.
+ *
+ * Asynchrony and errors
+ *   Arguments are validated on the host before any HIP call. Invalid arguments return
+ *   FA2_ERR_INVALID_ARGUMENT (null or misaligned pointers, sizes <= 0, a non-finite scale,
+ *   a workspace that is too small, sizes whose product overflows); an unsupported head
+ *   dimension returns FA2_ERR_UNSUPPORTED. Otherwise the kernels are enqueued on `stream`
+ *   (0 = the default stream) and the call returns FA2_OK, or FA2_ERR_HIP when the launch
+ *   fails (the HIP error code is then available from fa2_last_hip_error()). Results are
+ *   valid once the stream has been synchronised. No C++ exception crosses this interface.
+ */
+#ifndef FA2_H_
+#define FA2_H_
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum fa2_status {
+  FA2_OK = 0,
+  FA2_ERR_INVALID_ARGUMENT = 1,
+  FA2_ERR_UNSUPPORTED = 2,
+  FA2_ERR_HIP = 3
+} fa2_status;
+
+/* Forward pass. Writes o [B,H,N,d] (bf16) and lse [B,H,N] (fp32).
+ * softmax_scale multiplies the scores before the softmax (1/sqrt(d) is the usual choice;
+ * page "Flash Attention v2", "Detailed Algorithm Comparison", scores divided by sqrt(d)).
+ * causal != 0 applies the causal mask. Deterministic: identical inputs give identical bits. */
+fa2_status fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, int causal, float softmax_scale,
+                   hipStream_t stream);
+
+/* Bytes of device workspace fa2_bwd needs for these sizes (the row statistic D = rowsum(dO*O)
+ * as fp32 [B,H,N], rounded up to 256 bytes). Returns 0 for invalid sizes. */
+size_t fa2_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/* Backward pass. Inputs: q, k, v, the forward output o and its lse (from fa2_fwd with the
+ * same causal flag and scale), and the cotangent dout. Writes dq, dk, dv [B,H,N,d] (bf16,
+ * accumulated in fp32). workspace: device buffer of at least fa2_bwd_workspace_bytes(...)
+ * bytes, owned by the caller; its contents on entry do not matter and are clobbered.
+ * Deterministic (no atomics). */
+fa2_status fa2_bwd(const void* q, const void* k, const void* v, const void* o,
+                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                   void* workspace, size_t workspace_bytes,
+                   int B, int H, int N, int d, int causal, float softmax_scale,
+                   hipStream_t stream);
+
+/* Static, human-readable name of a status code. */
+const char* fa2_status_string(fa2_status s);
+
+/* HIP error code of the last FA2_ERR_HIP returned on this thread (0 if none). */
+int fa2_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA2_H_ */
