@@ -1,0 +1,263 @@
+"""Benchmark: FlashAttention-2 forward + backward on one MI355X through the fa2 C ABI.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5] [--direction both]
+
+One step is one pass of the whole hot path over one batch of synthetic seeded inputs
+(i.i.d. N(0, 1) bf16, already resident in device memory): the forward kernel (O and LSE)
+and the backward (D = rowsum(dO * O), the dK/dV kernel, the dQ kernel). The default workload
+is the fwd+bwd attention workload B=4, H=16, N=2048, d=128, causal. FLOP counts: forward
+4*B*H*N^2*d (halved when causal), backward 2.5x forward. `value` is the step's total FLOP
+over its wall time, in TFLOP/s.
+
+Each kernel launch in the timed region is bracketed by HIP events on the stream it runs on;
+the `roofline` object describes the kernel with the largest share of the step time:
+achieved = its algorithmic FLOP per launch / its mean event-measured duration, against the
+dense bf16 MFMA peak of MI355X (2.5 PFLOP/s). `traffic` comes from committed rocprofv3
+FETCH_SIZE / WRITE_SIZE counter summaries under profiles/ (null if the kernel source changed
+since they were taken). `cpu_baseline` times the CPU float64 oracle on a bounded sample of
+the same workload (whole heads) on the host cores.
+
+Prints ONE JSON line (rank 0).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0
+METRIC = "attention fwd/bwd TFLOP/s (bf16, causal+non-causal) and % of MFMA peak, 1 GPU"
+
+
+def parse_args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=5)
+    ap.add_argument("--causal", choices=("default", "causal", "full"), default="default")
+    ap.add_argument("--direction", choices=("both", "fwd"), default="both")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time budget for the oracle baseline sample")
+    return ap.parse_args()
+
+
+def fwd_flop(B, H, N, d, causal):
+    f = 4.0 * B * H * N * N * d
+    return f / 2 if causal else f
+
+
+def kernel_source_digest(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "exact_io_aware_42_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "fa2_fwd_kernel": ["fa2_device.hpp", "fa2_fwd.hip"],
+    "fa2_bwd_dkdv_kernel": ["fa2_device.hpp", "fa2_bwd.hip"],
+    "fa2_bwd_dq_kernel": ["fa2_device.hpp", "fa2_bwd.hip"],
+    "fa2_bwd_pre_kernel": ["fa2_device.hpp", "fa2_bwd.hip"],
+}
+
+
+def load_traffic(kernel, workload_tag):
+    """HBM bytes per launch from a committed counter summary, if it matches the source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload_tag}.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, _, v = line.partition(":")
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_digest") != kernel_source_digest(KERNEL_SOURCES[kernel]):
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, causal, with_bwd, budget_s):
+    """Time the CPU float64 oracle on whole (batch, head) slices of the same inputs until the
+    budget is spent; scale to TFLOP/s with the same FLOP formula."""
+    import numpy as np
+
+    from exact_io_aware_42_amd.inputs import bf16_bits_to_f64, default_scale, workload_tensors
+    from oracle import attention_backward, attention_forward
+
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    t = workload_tensors(w, with_dout=with_bwd)
+    scale = default_scale(w.d)
+    per_head = fwd_flop(1, 1, w.N, w.d, causal) * (3.5 if with_bwd else 1.0)
+    heads = 0
+    start = time.perf_counter()
+    for b in range(w.B):
+        for h in range(w.H):
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            q, k, v = (bf16_bits_to_f64(t[x][sl]) for x in ("q", "k", "v"))
+            attention_forward(q, k, v, causal=causal, scale=scale)
+            if with_bwd:
+                attention_backward(q, k, v, bf16_bits_to_f64(t["dout"][sl]), causal=causal,
+                                   scale=scale)
+            heads += 1
+            if time.perf_counter() - start >= budget_s:
+                break
+        if time.perf_counter() - start >= budget_s:
+            break
+    el = time.perf_counter() - start
+    return {
+        "value": per_head * heads / el / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": (f"{heads} of {w.B * w.H} (batch, head) slices, "
+                   f"{'forward+backward' if with_bwd else 'forward'}, float64 numpy, "
+                   f"{el:.1f} s"),
+    }
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
+                          "(the per-head work is independent, so more GPUs would shard "
+                          "batch x heads without any exchange)"}))
+        sys.exit(2)
+
+    import torch
+
+    import exact_io_aware_42_amd as fa2
+    from exact_io_aware_42_amd.inputs import WORKLOADS, default_scale, workload_tensors
+
+    w = WORKLOADS[args.workload]
+    causal = w.causal_modes[0] if args.causal == "default" else args.causal == "causal"
+    with_bwd = args.direction == "both"
+    B, H, N, d = w.shape
+    scale = default_scale(d)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    fa2.load_library()
+
+    t = workload_tensors(w, with_dout=with_bwd)
+
+    def dev_t(bits):
+        import numpy as np
+        return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = dev_t(t["q"]), dev_t(t["k"]), dev_t(t["v"])
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    if with_bwd:
+        do = dev_t(t["dout"])
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(max(1, fa2.bwd_workspace_bytes(B, H, N, d)), dtype=torch.uint8,
+                         device=dev)
+
+    stream = torch.cuda.current_stream(dev)
+    kernels = ["fa2_fwd_kernel"]
+    if with_bwd:
+        kernels += ["fa2_bwd_pre_kernel", "fa2_bwd_dkdv_kernel", "fa2_bwd_dq_kernel"]
+    f_fwd = fwd_flop(B, H, N, d, causal)
+    algo_flop = {"fa2_fwd_kernel": f_fwd, "fa2_bwd_pre_kernel": 0.0,
+                 "fa2_bwd_dkdv_kernel": 2.0 * f_fwd, "fa2_bwd_dq_kernel": 0.5 * f_fwd}
+    step_flop = f_fwd * (3.5 if with_bwd else 1.0)
+
+    def step(events=None):
+        def mark(i):
+            if events is not None:
+                events[i].record(stream)
+        mark(0)
+        fa2.fwd(q, k, v, causal=causal, scale=scale, out=o, lse=lse)
+        mark(1)
+        if with_bwd:
+            fa2.bwd_preprocess(o, do, ws)
+            mark(2)
+            fa2.bwd_dkdv(q, k, v, do, lse, ws, causal=causal, scale=scale, dk=dk, dv=dv)
+            mark(3)
+            fa2.bwd_dq(q, k, v, do, lse, ws, causal=causal, scale=scale, dq=dq)
+            mark(4)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    n_ev = len(kernels) + 1
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(ev[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    kernel_ms = {}
+    for i, kname in enumerate(kernels):
+        durs = [ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]
+        kernel_ms[kname] = sum(durs) / len(durs)
+    dominant = max(kernels, key=lambda kn: kernel_ms[kn])
+    achieved = algo_flop[dominant] / (kernel_ms[dominant] * 1e-3) / 1e12
+    wtag = f"w{w.wid}_{'causal' if causal else 'full'}"
+    traffic = load_traffic(dominant, wtag)
+
+    value = step_flop * args.steps / elapsed / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: i.i.d. N(0,1) rounded to bf16, seeded (seed = 1000*workload + t)",
+        "config": {
+            "workload": w.name,
+            "B": B, "H": H, "N": N, "d": d,
+            "causal": causal,
+            "direction": "fwd+bwd" if with_bwd else "fwd",
+            "step_flop": step_flop,
+        },
+        "pct_of_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
+        "kernel_ms": {kn: round(v_, 5) for kn, v_ in kernel_ms.items()},
+        "kernel_tflops": {kn: (round(algo_flop[kn] / (kernel_ms[kn] * 1e-3) / 1e12, 2)
+                               if algo_flop[kn] else None) for kn in kernels},
+        "roofline": {
+            "kernel": dominant,
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic,
+        },
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, causal, with_bwd, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -7,6 +7,7 @@ VALU instructions are disabled for all device code.
 """
 from __future__ import annotations
 
+import hashlib
 import os
 import subprocess
 import sys
@@ -33,10 +34,11 @@ COMMON_FLAGS = [
 ]
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    """Compile every source and link libfa2.so; returns its path. Raises on failure."""
+def build(verbose: bool = False, extra_flags=None, out_path: str = LIB_PATH) -> str:
+    """Compile every source and link libfa2.so (or `out_path`); returns its path. Raises on
+    failure."""
     objs = []
-    tmp_dir = os.path.join(PKG_DIR, "_build")
+    tmp_dir = os.path.join(PKG_DIR, "_build", hashlib.sha1(out_path.encode()).hexdigest()[:8])
     os.makedirs(tmp_dir, exist_ok=True)
     for src in SOURCES:
         obj = os.path.join(tmp_dir, src + ".o")
@@ -52,15 +54,15 @@ def build(verbose: bool = False, extra_flags=None) -> str:
         if verbose and msgs:
             print("\n".join(msgs))
         objs.append(obj)
-    tmp_lib = LIB_PATH + ".tmp"
+    tmp_lib = out_path + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp_lib]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("link failed:\n" + res.stdout + res.stderr)
-    os.replace(tmp_lib, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp_lib, out_path)
+    return out_path
 
 
 if __name__ == "__main__":

@@ -22,6 +22,9 @@ fa2_status check_sizes(int B, int H, int N, int d, float scale) {
   const unsigned long long elems =
       (unsigned long long)B * (unsigned long long)H * (unsigned long long)N * (unsigned long long)d;
   if (elems > (1ull << 46)) return FA2_ERR_INVALID_ARGUMENT;
+  // one head's Q/K/V slice is addressed with 32-bit buffer offsets
+  if ((unsigned long long)N * (unsigned long long)d * 2ull >= (1ull << 31))
+    return FA2_ERR_INVALID_ARGUMENT;
   // the workgroup grid (B*H*ceil(N/64)) must fit a 32-bit dimension
   if ((unsigned long long)B * H * ((unsigned long long)(N + 63) / 64) > 0x7fffffffull)
     return FA2_ERR_INVALID_ARGUMENT;

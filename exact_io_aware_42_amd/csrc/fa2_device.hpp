@@ -14,6 +14,43 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+
+#define FA2_LDS __attribute__((address_space(3)))
+
+// Buffer resource over [base, base + bytes): loads beyond `bytes` return zeros, which is how
+// ragged sequence tails are padded without branches. (Word 3 = 0x00020000 selects the plain
+// 32-bit data format on gfx9-family parts.)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// 16-byte buffer load into registers (zeros when out of range).
+__device__ __forceinline__ u32x4_t buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff,
+                                                 uint32_t soff) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+
+// 16 bytes per lane from global memory straight into LDS (no VGPRs): lane l's data lands at
+// lds_wave_base + 16*l; lds_wave_base must be wave-uniform. Zeros when out of range.
+__device__ __forceinline__ void buffer_load16_to_lds(__amdgpu_buffer_rsrc_t r,
+                                                     void* lds_wave_base, uint32_t voff,
+                                                     uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (FA2_LDS void*)lds_wave_base, 16, voff, soff, 0, 0);
+}
+
+// Transposing LDS read of 16-bit data (ds_read_b64_tr_b16). Within each group of 16 lanes,
+// lane i receives element (i % 4) of the 8-byte chunks addressed by lanes i/4, i/4 + 4,
+// i/4 + 8 and i/4 + 12 (in that order). If lane j of the group addresses row r0 + j/4,
+// columns c0 + 4*(j%4) .. +3 of a row-major bf16 matrix, lane i receives column c0 + i of
+// rows r0 .. r0+3: a column slice, i.e. the transposed operand an MFMA needs.
+__device__ __forceinline__ u32x2_t lds_read_tr16(const void* p) {
+  s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FA2_LDS s16x4_t*)(p));
+  return __builtin_bit_cast(u32x2_t, v);
+}
+
+// Wait until this wave's outstanding vector-memory loads (including loads into LDS) are done.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 constexpr float kLn2 = 0.69314718055994530942f;
 
@@ -72,10 +109,10 @@ __device__ __forceinline__ int kmap(int m) {
 // swizzle sends them to 8 distinct bank groups.
 __device__ __forceinline__ int kswz(int row) { return (row & 3) | ((row >> 1) & 4); }
 
-// XOR swizzle of 16-byte chunks in a transposed V tile row (V^T, [d][keys], 8 chunks of 8
-// keys per row). Readers take 8 consecutive rows of one chunk; writers take one chunk
-// position across rows c = 8*cc + const, so both c and c/8 enter the swizzle.
-__device__ __forceinline__ int vswz(int c) { return (c ^ (c >> 3)) & 7; }
+// XOR swizzle of 16-byte chunks in a V tile row (row-major [keys][d]). A transposing read
+// covers rows 4a .. 4a+3 and two adjacent chunks (32 bytes) per row; XOR with 2*(row % 4)
+// spreads those 8 chunks over all 32 banks.
+__device__ __forceinline__ int vswz(int row) { return (row & 3) << 1; }
 
 // Workgroup id -> (query block, batch*head) order. Workgroups are dealt to the 8 XCDs in
 // turn (id % 8), each XCD with its own L2. When the heads divide evenly, XCD x gets whole

@@ -15,14 +15,18 @@
 //    query l%32 of its wave, so row max and row sums are in-lane plus one exchange with lane
 //    l^32; Q^T fragments (the B operand) stay in VGPRs for the whole key loop;
 //  * O^T = V^T P^T with the same MFMA: P^T is the B operand straight from the score
-//    registers (the kmap key order makes the layouts agree) and each lane's O^T column is
-//    its own query, so the rescale and the final 1/l are per-lane scalars;
-//  * K tiles are staged row-major and V tiles transposed (V^T) in a double-buffered LDS ring
-//    with XOR-swizzled 16-byte chunks; the next tile's global loads are issued before the
-//    current tile's MFMAs and written to the other LDS buffer after them (one barrier/tile);
-//  * exp2 form: p = exp2(s * scale*log2(e) - m) is one FMA and one v_exp_f32; l is summed from
-//    the same bf16-rounded p that feeds the MFMA (consistent convex weights), while the LSE
-//    uses an fp32 sum of the unrounded p.
+//    registers (the kmap key order makes the layouts agree), V^T fragments come from the
+//    row-major V tile through the transposing LDS read, and each lane's O^T column is its own
+//    query, so the rescale and the final 1/l are per-lane scalars;
+//  * K and V tiles move HBM -> LDS by buffer loads that write LDS directly (no VGPR staging,
+//    zero fill past the sequence end), into XOR-swizzled row-major tiles, double-buffered
+//    (tile j+1 streams in while tile j is computed), one barrier per tile;
+//  * exp2 form: p = exp2(s * scale*log2(e) - m) is one FMA + one v_exp_f32. Masked tiles
+//    (causal diagonal, ragged tail) start their score accumulators at -inf instead of 0 for
+//    hidden keys. Two workgroups per CU let one wave's softmax VALU work overlap another
+//    wave's MFMAs;
+//  * l is summed from the same bf16-rounded p that feeds the MFMA (consistent convex
+//    weights, v_dot2 with ones), while the LSE uses an fp32 sum of the unrounded p.
 #include "fa2_device.hpp"
 #include "fa2_launch.hpp"
 
@@ -30,244 +34,236 @@ namespace fa2 {
 
 namespace {
 
+#ifndef FA2_FWD_OCC
+#define FA2_FWD_OCC 2  // waves per SIMD the forward kernel is compiled for
+#endif
+
 constexpr int kFwdBR = 128;
 constexpr int kFwdBC = 64;
 constexpr int kFwdThreads = 256;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: exponentials stay <= 2^8
-constexpr float kMinusBig = -1.0e30f;      // finite start value of the running max
 
 template <int D>
 struct FwdShape {
-  static constexpr int DCH = D / 8;                        // 16-byte chunks per K row
-  static constexpr int KK = D / 16;                        // MFMA k-steps of the score GEMM
-  static constexpr int CB = D / 32;                        // 32-row blocks of O^T
-  static constexpr int K_LOADS = kFwdBC * DCH / kFwdThreads;   // 16-byte K loads per thread
-  static constexpr int KPT = kFwdBC * D / 8 / kFwdThreads;     // keys per thread, V transpose
-  static constexpr int KGROUPS = kFwdBC / KPT;                 // key groups per tile
-  static constexpr int K_TILE_BYTES = kFwdBC * D * 2;
-  static constexpr int V_TILE_BYTES = D * kFwdBC * 2;
-  static constexpr int STAGE_BYTES = K_TILE_BYTES + V_TILE_BYTES;
-  static_assert(K_LOADS >= 1 && KPT >= 2 && (KPT % 2) == 0, "tile shape");
-  static_assert(KGROUPS * DCH == kFwdThreads, "V transpose covers the tile");
+  static constexpr int DCH = D / 8;            // 16-byte chunks per K/V row
+  static constexpr int KK = D / 16;            // MFMA k-steps of the score GEMM
+  static constexpr int CB = D / 32;            // 32-row blocks of O^T
+  static constexpr int TILE_BYTES = kFwdBC * D * 2;
+  static constexpr int LOADS = TILE_BYTES / (kFwdThreads * 16);  // 16-byte loads per lane per tile
+  static constexpr int K_SLOT0 = 0;
+  static constexpr int V_SLOT0 = 2 * TILE_BYTES;
+  static constexpr int SMEM = 4 * TILE_BYTES;
+  static_assert(LOADS >= 1 && DCH >= 8, "tile shape");
 };
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kFwdThreads, 2) void fa2_fwd_kernel(
+__global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
     int N, int n_qblocks, int bh_count, float scale_log2) {
   using S = FwdShape<D>;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * S::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[S::SMEM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31;
   const int g = lane >> 5;
 
   const TileCoord tc = schedule_tile(blockIdx.x, n_qblocks, bh_count, CAUSAL);
   const size_t head_off = (size_t)tc.bh * (size_t)N * D;
-  const uint16_t* qh = q + head_off;
-  const uint16_t* kh = k + head_off;
-  const uint16_t* vh = v + head_off;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + head_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + head_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + head_off, head_bytes);
 
   const int q_block0 = tc.qb * kFwdBR;
   const int q_wave0 = q_block0 + wave * 32;
   const int my_q = q_wave0 + l32;
 
-  // ---- Q^T fragments (B operand of S^T = K Q^T): lane holds q[my_q][16kk + 8g .. +7]
-  u32x4_t qf[S::KK];
+  // ---- key tiles this workgroup visits, and the last one not fully masked for this wave
+  int n_tiles = (N + kFwdBC - 1) / kFwdBC;
+  if (CAUSAL) n_tiles = min(N - 1, q_block0 + kFwdBR - 1) / kFwdBC + 1;
+  const int wave_last = CAUSAL ? min(n_tiles - 1, (q_wave0 + 31) / kFwdBC) : n_tiles - 1;
+
+  // ---- HBM -> LDS tile loads. Load r of wave w writes the 1 KiB block i = 4r + w of the tile
+  // (lane l -> chunk p = 64i + l: row p / DCH, physical chunk p % DCH) and fetches the logical
+  // chunk the row's XOR swizzle maps there. With i = 4r + w the swizzle bits of the row do not
+  // depend on r, so one per-lane offset serves every load (r adds a constant).
+  constexpr int kRowsPerBlock = 64 / S::DCH;
+  uint32_t koff0, voff0;
   {
-    const bool ok = my_q < N;
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(qh + (size_t)(ok ? my_q : 0) * D);
-#pragma unroll
-    for (int kk = 0; kk < S::KK; ++kk) {
-      u32x4_t t = src[2 * kk + g];
-      qf[kk] = ok ? t : u32x4_t{0u, 0u, 0u, 0u};
-    }
+    const int p = wave * 64 + lane;
+    const int row = p / S::DCH;
+    const int pc = p % S::DCH;
+    koff0 = (uint32_t)(row * D * 2 + (pc ^ kswz(row)) * 16);
+    voff0 = (uint32_t)(row * D * 2 + (pc ^ vswz(row)) * 16);
   }
-
-  // ---- number of key tiles this workgroup visits
-  const int n_ktiles_all = (N + kFwdBC - 1) / kFwdBC;
-  int n_ktiles = n_ktiles_all;
-  if (CAUSAL) {
-    const int last_key = min(N - 1, q_block0 + kFwdBR - 1);
-    n_ktiles = last_key / kFwdBC + 1;
-  }
-  // last tile index that is not fully masked for this wave's rows
-  const int wave_last_tile = CAUSAL ? min(n_ktiles - 1, (q_wave0 + 31) / kFwdBC) : n_ktiles - 1;
-
-  // ---- global -> register staging of one K/V tile
-  u32x4_t kreg[S::K_LOADS];
-  u32x4_t vreg[S::KPT];
-  const int vkg = tid % S::KGROUPS;  // key group (KPT keys) of this thread's V block
-  const int vcc = tid / S::KGROUPS;  // 8-wide d chunk of this thread's V block
-
-  auto load_tile = [&](int j) {
-    const int key0 = j * kFwdBC;
+  auto load_k = [&](int j, int slot) {
 #pragma unroll
-    for (int r = 0; r < S::K_LOADS; ++r) {
-      const int cid = tid + r * kFwdThreads;
-      const int row = cid / S::DCH;
-      const int cc = cid % S::DCH;
-      const int key = key0 + row;
-      u32x4_t t = {0u, 0u, 0u, 0u};
-      if (key < N) t = *reinterpret_cast<const u32x4_t*>(kh + (size_t)key * D + cc * 8);
-      kreg[r] = t;
-    }
+    for (int r = 0; r < S::LOADS; ++r)
+      buffer_load16_to_lds(rk, smem + S::K_SLOT0 + slot * S::TILE_BYTES + (4 * r + wave) * 1024,
+                           koff0 + r * 4 * kRowsPerBlock * D * 2, (uint32_t)j * kFwdBC * D * 2);
+  };
+  auto load_v = [&](int j, int slot) {
 #pragma unroll
-    for (int r = 0; r < S::KPT; ++r) {
-      const int key = key0 + vkg * S::KPT + r;
-      u32x4_t t = {0u, 0u, 0u, 0u};
-      if (key < N) t = *reinterpret_cast<const u32x4_t*>(vh + (size_t)key * D + vcc * 8);
-      vreg[r] = t;
-    }
+    for (int r = 0; r < S::LOADS; ++r)
+      buffer_load16_to_lds(rv, smem + S::V_SLOT0 + slot * S::TILE_BYTES + (4 * r + wave) * 1024,
+                           voff0 + r * 4 * kRowsPerBlock * D * 2, (uint32_t)j * kFwdBC * D * 2);
   };
 
-  auto store_tile = [&](int stage) {
-    unsigned char* sk = smem + stage * S::STAGE_BYTES;
-    unsigned char* sv = sk + S::K_TILE_BYTES;
-#pragma unroll
-    for (int r = 0; r < S::K_LOADS; ++r) {
-      const int cid = tid + r * kFwdThreads;
-      const int row = cid / S::DCH;
-      const int cc = cid % S::DCH;
-      *reinterpret_cast<u32x4_t*>(sk + (row * S::DCH + (cc ^ kswz(row))) * 16) = kreg[r];
-    }
-    // transpose KPT keys x 8 d-values into 8 rows of V^T, KPT keys each
-    const int chunk = (vkg * S::KPT) / 8;
-    const int sub = ((vkg * S::KPT) % 8) * 2;  // byte offset inside the 16-byte chunk
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {      // dword e of the 8-wide chunk: d = 8*vcc + 2e, +1
-#pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int c = vcc * 8 + 2 * e + half;
-        uint32_t w[S::KPT / 2];
-#pragma unroll
-        for (int p = 0; p < S::KPT / 2; ++p) {
-          const uint32_t a = vreg[2 * p][e], b = vreg[2 * p + 1][e];
-          w[p] = half ? __builtin_amdgcn_perm(b, a, 0x07060302u)
-                      : __builtin_amdgcn_perm(b, a, 0x05040100u);
-        }
-        unsigned char* dst = sv + (c * 8 + (chunk ^ vswz(c))) * 16 + sub;
-        if constexpr (S::KPT == 4) {
-          *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{w[0], w[1]};
-        } else {
-          *reinterpret_cast<uint32_t*>(dst) = w[0];
-        }
-      }
-    }
-  };
-
-  // ---- per-lane LDS read offsets (bytes, within a stage). The swizzle only touches the low 3
-  // bits of the chunk index and does not depend on row bits >= 4, so block kb, k-step group
-  // kk/4 and d-block pair cb/2 become immediate offsets on a few base registers.
+  // ---- per-lane LDS read offsets (bytes within a tile)
+  // K (A operand of S^T): row 32kb + kmap(l32), logical chunk 2kk + g. The swizzle acts on the
+  // low 3 chunk bits only and ignores row bits >= 4, so kb and kk/4 become immediates.
   const int krow = kmap(l32);
-  int koff[4];
+  int kbase[4];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) koff[kk] = (krow * S::DCH + ((2 * kk + g) ^ kswz(krow))) * 16;
-  auto k_off = [&](int kb, int kk) {
-    return koff[kk & 3] + (kk >> 2) * 128 + kb * 32 * S::DCH * 16;
-  };
-  int voff[2][4];
+  for (int kk = 0; kk < 4; ++kk) kbase[kk] = krow * D * 2 + ((2 * kk + g) ^ kswz(krow)) * 16;
+  auto k_off = [&](int kb, int kk) { return kbase[kk & 3] + (kk >> 2) * 128 + kb * 32 * D * 2; };
+  // V^T fragments (A operand of O^T) via the transposing read: 16-lane group G = lane/16 covers
+  // d rows c0 = 32cb + 16(G%2) .. +15 and k-slots 8g .. 8g+7 = keys 16u + 8g + 4h + (0..3).
+  // Lane j of the group addresses key row 16u + 8g + 4h + j/4, columns c0 + 4(j%4) .. +3.
+  const int jl = lane & 15;
+  const int grp = lane >> 4;
+  int vbase[2];
 #pragma unroll
-  for (int cb = 0; cb < 2; ++cb) {
-    const int c = cb * 32 + l32;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      voff[cb][u] = S::K_TILE_BYTES + (c * 8 + ((2 * u + g) ^ vswz(c))) * 16;
+  for (int par = 0; par < 2; ++par) {
+    const int row = 8 * g + jl / 4;                 // + 16u + 4h (multiples of 4) added below
+    const int col = 32 * par + 16 * (grp & 1) + 4 * (jl & 3);
+    vbase[par] = row * D * 2 + (((col >> 3) ^ vswz(row)) * 16) + (col & 7) * 2;
   }
-  auto v_off = [&](int cb, int u) { return voff[cb & 1][u] + (cb >> 1) * 64 * 8 * 16; };
+  auto v_off = [&](int cb, int u, int h) {
+    return vbase[cb & 1] + (cb >> 1) * 128 + (16 * u + 4 * h) * D * 2;
+  };
 
-  // ---- accumulators and row statistics (per lane: query my_q, half g of the keys)
+  // ---- Q^T fragments (B operand of S^T): lane holds q[my_q][16kk + 8g .. +7]; zeros past N
+  u32x4_t qf[S::KK];
+#pragma unroll
+  for (int kk = 0; kk < S::KK; ++kk) qf[kk] = buffer_load16(rq, (uint32_t)my_q * D * 2 + (2 * kk + g) * 16, 0);
+
+  // ---- accumulators and row statistics (per lane: query my_q, key half g)
   f32x16_t oacc[S::CB];
 #pragma unroll
   for (int cb = 0; cb < S::CB; ++cb) oacc[cb] = f32x16_t{};
-  float m_run = kMinusBig;  // running max of scale*log2(e)*s (possibly stale by < threshold)
-  float l_f32 = 0.f;        // partial sum of p over this lane's keys (fp32, for LSE)
-  float l_bf = 0.f;         // partial sum of bf16(p) (normaliser of O)
+  float m_run;        // running max of scale*log2(e)*s (stale by < threshold)
+  float l_f32 = 0.f;  // partial sum of p over this lane's keys (fp32, for LSE)
+  float l_bf = 0.f;   // partial sum of bf16(p) (normaliser of O)
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int j = 0; j < n_ktiles; ++j) {
-    const int stage = j & 1;
-    if (j + 1 < n_ktiles) load_tile(j + 1);
-
-    if (j <= wave_last_tile) {
-      const unsigned char* sbase = smem + stage * S::STAGE_BYTES;
-      // S^T tile: two 32-key blocks x 32 queries
-      f32x16_t s[2] = {f32x16_t{}, f32x16_t{}};
+  // hidden-key bias for tile j: -inf where key >= N or (causal) key > query
+  auto tile_needs_mask = [&](int j) {
+    const int key0 = j * kFwdBC;
+    return (key0 + kFwdBC > N) || (CAUSAL && key0 + kFwdBC - 1 > q_wave0);
+  };
+  auto mask_bias = [&](int j, f32x16_t* s) {
+    const int key0 = j * kFwdBC;
 #pragma unroll
-      for (int kk = 0; kk < S::KK; ++kk) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(sbase + k_off(kb, kk));
-          s[kb] = mfma32(a, qf[kk], s[kb]);
-        }
+      for (int i = 0; i < 16; ++i) {
+        const int key = key0 + kb * 32 + (i / 8) * 16 + g * 8 + (i % 8);
+        const bool hidden = (key >= N) || (CAUSAL && key > my_q);
+        s[kb][i] = hidden ? -INFINITY : 0.f;
       }
-
-      // masking: key index of register i of block kb is key0 + 32kb + 16(i/8) + 8g + i%8
-      const int key0 = j * kFwdBC;
-      const bool need_mask = (key0 + kFwdBC > N) || (CAUSAL && key0 + kFwdBC - 1 > q_wave0);
-      if (need_mask) {
+  };
+  // S^T tile j from K slot `slot`: two 32-key blocks x 32 queries
+  auto scores = [&](int slot, bool masked, int j, f32x16_t* s) {
+    const unsigned char* kt = smem + S::K_SLOT0 + slot * S::TILE_BYTES;
+    if (masked) mask_bias(j, s);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+    for (int kk = 0; kk < S::KK; ++kk)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = key0 + kb * 32 + (i / 8) * 16 + g * 8 + (i % 8);
-            const bool masked = (key >= N) || (CAUSAL && key > my_q);
-            s[kb][i] = masked ? -INFINITY : s[kb][i];
-          }
+      for (int kb = 0; kb < 2; ++kb) {
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(kt + k_off(kb, kk));
+        s[kb] = (kk == 0 && !masked) ? mfma32(a, qf[kk], f32x16_t{}) : mfma32(a, qf[kk], s[kb]);
       }
-
-      // online softmax, exp2 form, deferred rescale
-      float mx = s[0][0];
+  };
+  auto row_max = [&](const f32x16_t* s) {
+    float a = fmaxf(s[0][0], s[0][1]), b = fmaxf(s[1][0], s[1][1]);
 #pragma unroll
-      for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[0][i]);
+    for (int i = 2; i < 16; i += 2) {
+      a = __builtin_fmaxf(a, __builtin_fmaxf(s[0][i], s[0][i + 1]));
+      b = __builtin_fmaxf(b, __builtin_fmaxf(s[1][i], s[1][i + 1]));
+    }
+    return max_xor32(fmaxf(a, b)) * scale_log2;
+  };
+  // p = exp2(s*c - m) -> packed bf16 (the PV B operand); partial sums of p and bf16(p)
+  auto probs = [&](const f32x16_t* s, uint32_t (*pk)[8]) {
+    const float neg_m = -m_run;
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[1][i]);
-      mx = max_xor32(mx);
-      const float m_tile = mx * scale_log2;
-      const bool raise = m_tile > m_run + kRescaleThreshold;
-      if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-        const float m_new = fmaxf(m_run, m_tile);
-        const float alpha = fast_exp2(m_run - m_new);
-        m_run = m_new;
-        l_f32 *= alpha;
-        l_bf *= alpha;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int cb = 0; cb < S::CB; ++cb) oacc[cb] *= alpha;
+      for (int i = 0; i < 8; ++i) {
+        const float p0 = fast_exp2(__builtin_fmaf(s[kb][2 * i], scale_log2, neg_m));
+        const float p1 = fast_exp2(__builtin_fmaf(s[kb][2 * i + 1], scale_log2, neg_m));
+        acc[(i & 1) * 2 + kb] += p0 + p1;
+        const uint32_t w = pack_bf16(p0, p1);
+        pk[kb][i] = w;
+        l_bf = add_bf16_pair(l_bf, w);
       }
-      const float neg_m = -m_run;
-      uint32_t pk[2][8];
+    l_f32 += (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  };
+  // O^T += V^T P^T from V slot `slot`; MFMA u covers keys 16u .. 16u+15 = score block u/2,
+  // registers 8(u%2) .. 8(u%2)+7
+  auto pv = [&](int slot, uint32_t (*pk)[8]) {
+    const unsigned char* vt = smem + S::V_SLOT0 + slot * S::TILE_BYTES;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+    for (int u = 0; u < 4; ++u) {
+      const u32x4_t b = {pk[u / 2][4 * (u % 2) + 0], pk[u / 2][4 * (u % 2) + 1],
+                         pk[u / 2][4 * (u % 2) + 2], pk[u / 2][4 * (u % 2) + 3]};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float p0 = fast_exp2(__builtin_fmaf(s[kb][2 * i], scale_log2, neg_m));
-          const float p1 = fast_exp2(__builtin_fmaf(s[kb][2 * i + 1], scale_log2, neg_m));
-          l_f32 += p0 + p1;
-          const uint32_t w = pack_bf16(p0, p1);
-          pk[kb][i] = w;
-          l_bf = add_bf16_pair(l_bf, w);
-        }
-
-      // O^T += V^T P^T: MFMA u covers keys 16u .. 16u+15, i.e. score block u/2, regs 8(u%2)..
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const u32x4_t b = {pk[u / 2][4 * (u % 2) + 0], pk[u / 2][4 * (u % 2) + 1],
-                           pk[u / 2][4 * (u % 2) + 2], pk[u / 2][4 * (u % 2) + 3]};
-#pragma unroll
-        for (int cb = 0; cb < S::CB; ++cb) {
-          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(sbase + v_off(cb, u));
-          oacc[cb] = mfma32(a, b, oacc[cb]);
-        }
+      for (int cb = 0; cb < S::CB; ++cb) {
+        const u32x2_t lo = lds_read_tr16(vt + v_off(cb, u, 0));
+        const u32x2_t hi = lds_read_tr16(vt + v_off(cb, u, 1));
+        const u32x4_t a = {lo[0], lo[1], hi[0], hi[1]};
+        oacc[cb] = mfma32(a, b, oacc[cb]);
       }
     }
+  };
+  // deferred rescale: raise the running max only when a tile's max exceeds it by > threshold
+  auto maybe_rescale = [&](float m_tile) {
+    const bool raise = m_tile > m_run + kRescaleThreshold;
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+      const float m_new = fmaxf(m_run, m_tile);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_f32 *= alpha;
+      l_bf *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < S::CB; ++cb) oacc[cb] *= alpha;
+    }
+  };
 
-    if (j + 1 < n_ktiles) store_tile(stage ^ 1);
+  // ---- main loop: tile j+1 streams into the other LDS slot while tile j is computed
+  load_k(0, 0);
+  load_v(0, 0);
+  wait_vmem();
+  __syncthreads();
+  m_run = -INFINITY;
+  bool first = true;
+  for (int j = 0; j < n_tiles; ++j) {
+    const int slot = j & 1;
+    // slot (j+1)&1 held tile j-1, whose readers all passed the barrier that ended step j-1
+    if (j + 1 < n_tiles) {
+      load_k(j + 1, slot ^ 1);
+      load_v(j + 1, slot ^ 1);
+    }
+    if (j <= wave_last) {
+      f32x16_t s[2];
+      if (tile_needs_mask(j)) scores(slot, true, j, s);
+      else scores(slot, false, j, s);
+      const float m_tile = row_max(s);
+      if (first) {
+        m_run = m_tile;  // tile 0 holds key 0, visible to every row: finite
+        first = false;
+      } else {
+        maybe_rescale(m_tile);
+      }
+      uint32_t pk[2][8];
+      probs(s, pk);
+      pv(slot, pk);
+    }
+    wait_vmem();
     __syncthreads();
   }
 

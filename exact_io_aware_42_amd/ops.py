@@ -14,7 +14,9 @@ import threading
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa2.so")
+# The in-tree library; FA2_LIBRARY may name another build of the same sources.
+LIB_PATH = os.environ.get("FA2_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libfa2.so")
 
 FA2_OK = 0
 FA2_ERR_INVALID_ARGUMENT = 1

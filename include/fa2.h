@@ -22,7 +22,8 @@
  * Layout and types
  *   q, k, v, o, dout, dq, dk, dv: bfloat16 (raw 16-bit patterns), contiguous row-major
  *   [B, H, N, d] with d fastest. lse: float32 [B, H, N], natural log. All pointers are
- *   device pointers and must be 16-byte aligned. B*H*N*d may exceed 2^31 (64-bit offsets).
+ *   device pointers and must be 16-byte aligned. B*H*N*d may exceed 2^31 (64-bit offsets);
+ *   one head's slice must stay below 2 GiB (N*d*2 < 2^31 bytes, i.e. N < 8M at d = 128).
  *   Supported head dimensions: d = 64 and d = 128. N >= 1 (any N; ragged tails are masked).
  *
  * Ownership
@@ -33,7 +34,8 @@
  * Asynchrony and errors
  *   Arguments are validated on the host before any HIP call. Invalid arguments return
  *   FA2_ERR_INVALID_ARGUMENT (null or misaligned pointers, sizes <= 0, a non-finite scale,
- *   a workspace that is too small, sizes whose product overflows); an unsupported head
+ *   a scale that is not > 0, a workspace that is too small, sizes beyond the limits above);
+ *   an unsupported head
  *   dimension returns FA2_ERR_UNSUPPORTED. Otherwise the kernels are enqueued on `stream`
  *   (0 = the default stream) and the call returns FA2_OK, or FA2_ERR_HIP when the launch
  *   fails (the HIP error code is then available from fa2_last_hip_error()). Results are
