@@ -8,6 +8,8 @@
 The library is loaded on first use; if it has not been built the call raises (there is no
 fallback path).
 """
-from .ops import FA2Error, bwd, bwd_workspace_bytes, fwd, load_library
+from .ops import (FA2Error, bwd, bwd_dkdv, bwd_dq, bwd_preprocess, bwd_workspace_bytes, fwd,
+                  load_library)
 
-__all__ = ["fwd", "bwd", "bwd_workspace_bytes", "load_library", "FA2Error"]
+__all__ = ["fwd", "bwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "bwd_workspace_bytes",
+           "load_library", "FA2Error"]

@@ -4,6 +4,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <initializer_list>
 
 #include "fa2_launch.hpp"
 
@@ -72,36 +73,86 @@ size_t fa2_bwd_workspace_bytes(int B, int H, int N, int d) {
   return round256((size_t)B * H * N * sizeof(float));
 }
 
+namespace {
+
+fa2_status bwd_args(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, float* delta, void* dq, void* dk, void* dv, int B, int H,
+                    int N, int d, int causal, float softmax_scale, hipStream_t stream,
+                    fa2::BwdArgs* a) {
+  const fa2_status st = check_sizes(B, H, N, d, softmax_scale);
+  if (st != FA2_OK) return st;
+  a->q = q;
+  a->k = k;
+  a->v = v;
+  a->o = o;
+  a->dout = dout;
+  a->lse = lse;
+  a->dq = dq;
+  a->dk = dk;
+  a->dv = dv;
+  a->delta = delta;
+  a->B = B;
+  a->H = H;
+  a->N = N;
+  a->d = d;
+  a->causal = causal != 0;
+  a->scale = softmax_scale;
+  a->scale_log2 = static_cast<float>(static_cast<double>(softmax_scale) * kLog2e);
+  a->stream = stream;
+  return FA2_OK;
+}
+
+bool all_ok(std::initializer_list<const void*> ptrs) {
+  for (const void* p : ptrs)
+    if (p == nullptr || !aligned16(p)) return false;
+  return true;
+}
+
+}  // namespace
+
 fa2_status fa2_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
                    const float* lse, void* dq, void* dk, void* dv, void* workspace,
                    size_t workspace_bytes, int B, int H, int N, int d, int causal,
                    float softmax_scale, hipStream_t stream) {
-  const fa2_status st = check_sizes(B, H, N, d, softmax_scale);
-  if (st != FA2_OK) return st;
-  const void* ptrs[] = {q, k, v, o, dout, lse, dq, dk, dv, workspace};
-  for (const void* p : ptrs)
-    if (p == nullptr || !aligned16(p)) return FA2_ERR_INVALID_ARGUMENT;
-  if (workspace_bytes < fa2_bwd_workspace_bytes(B, H, N, d)) return FA2_ERR_INVALID_ARGUMENT;
   fa2::BwdArgs a;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.o = o;
-  a.dout = dout;
-  a.lse = lse;
-  a.dq = dq;
-  a.dk = dk;
-  a.dv = dv;
-  a.delta = static_cast<float*>(workspace);
-  a.B = B;
-  a.H = H;
-  a.N = N;
-  a.d = d;
-  a.causal = causal != 0;
-  a.scale = softmax_scale;
-  a.scale_log2 = static_cast<float>(static_cast<double>(softmax_scale) * kLog2e);
-  a.stream = stream;
+  const fa2_status st = bwd_args(q, k, v, o, dout, lse, static_cast<float*>(workspace), dq, dk,
+                                 dv, B, H, N, d, causal, softmax_scale, stream, &a);
+  if (st != FA2_OK) return st;
+  if (!all_ok({q, k, v, o, dout, lse, dq, dk, dv, workspace})) return FA2_ERR_INVALID_ARGUMENT;
+  if (workspace_bytes < fa2_bwd_workspace_bytes(B, H, N, d)) return FA2_ERR_INVALID_ARGUMENT;
   return from_hip(fa2::launch_bwd(a));
+}
+
+fa2_status fa2_bwd_preprocess(const void* o, const void* dout, float* delta, int B, int H, int N,
+                              int d, hipStream_t stream) {
+  fa2::BwdArgs a;
+  const fa2_status st = bwd_args(nullptr, nullptr, nullptr, o, dout, nullptr, delta, nullptr,
+                                 nullptr, nullptr, B, H, N, d, 0, 1.0f, stream, &a);
+  if (st != FA2_OK) return st;
+  if (!all_ok({o, dout, delta})) return FA2_ERR_INVALID_ARGUMENT;
+  return from_hip(fa2::launch_bwd_pre(a));
+}
+
+fa2_status fa2_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
+                        const float* lse, const float* delta, void* dk, void* dv, int B, int H,
+                        int N, int d, int causal, float softmax_scale, hipStream_t stream) {
+  fa2::BwdArgs a;
+  const fa2_status st = bwd_args(q, k, v, nullptr, dout, lse, const_cast<float*>(delta), nullptr,
+                                 dk, dv, B, H, N, d, causal, softmax_scale, stream, &a);
+  if (st != FA2_OK) return st;
+  if (!all_ok({q, k, v, dout, lse, delta, dk, dv})) return FA2_ERR_INVALID_ARGUMENT;
+  return from_hip(fa2::launch_bwd_dkdv(a));
+}
+
+fa2_status fa2_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
+                      const float* lse, const float* delta, void* dq, int B, int H, int N, int d,
+                      int causal, float softmax_scale, hipStream_t stream) {
+  fa2::BwdArgs a;
+  const fa2_status st = bwd_args(q, k, v, nullptr, dout, lse, const_cast<float*>(delta), dq,
+                                 nullptr, nullptr, B, H, N, d, causal, softmax_scale, stream, &a);
+  if (st != FA2_OK) return st;
+  if (!all_ok({q, k, v, dout, lse, delta, dq})) return FA2_ERR_INVALID_ARGUMENT;
+  return from_hip(fa2::launch_bwd_dq(a));
 }
 
 const char* fa2_status_string(fa2_status s) {

@@ -1,4 +1,500 @@
+// FlashAttention-2 backward for gfx950: dQ, dK, dV of O = softmax(scale Q K^T [+ causal]) V.
+//
+// The pages describe the backward as block-wise recomputation: recompute S and P for each
+// block pair from Q, K and the saved softmax statistic, never store the N x N P or dP, and
+// accumulate the gradients block by block (page "Flash Attention v2", sections "2. Backward
+// Pass Computation" and "5. Gradient Accumulation"; a separate backward kernel, page
+// "FlashAttention-2: Faster Attention with Better Parallelism and Work Partitioning"). The
+// per-block arithmetic is the exact softmax gradient (the listing on the first page keeps only
+// the diagonal of the softmax Jacobian; the full form is used):
+//
+//   P = exp(scale S - LSE),  D_i = sum_c dO_ic O_ic,  dS = P * (dO V^T - D),
+//   dV = P^T dO,  dK = scale dS^T Q,  dQ = scale dS K.
+//
+// Three kernels, deterministic (no atomics):
+//   fa2_bwd_pre_kernel   D = rowsum(dO * O), fp32 [B, H, N] (HBM-bound, one pass).
+//   fa2_bwd_dkdv_kernel  grid over (key block of 128, head, batch): each wave keeps its 32 keys'
+//                        K and V fragments in VGPRs and its dK, dV accumulators in registers,
+//                        and streams 64-query tiles of Q, dO, LSE and D through LDS.
+//   fa2_bwd_dq_kernel    grid over (query block of 128, head, batch): the forward's layout
+//                        (lane = query), recomputing S^T and dP^T per key tile and
+//                        accumulating dQ^T = K^T dS^T.
+// dK/dV and dQ each recompute S and dP; dQ's two recompute GEMMs are the price of avoiding
+// atomic dQ accumulation.
+#include "fa2_device.hpp"
 #include "fa2_launch.hpp"
+
 namespace fa2 {
-hipError_t launch_bwd(const BwdArgs&) { return hipErrorNotSupported; }
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// XOR swizzle of 16-byte chunks for tiles read both ways: row-wise by 32-lane MFMA operand
+// reads (8 lanes of one phase take rows kmap(0..7) = {0,1,2,3,8,9,10,11}, one chunk) and by
+// transposing reads (16 lanes take rows 4a..4a+3, two adjacent chunks). ((row & 3) << 1) |
+// bit 3 of row is injective on both row sets, so neither pattern conflicts.
+__device__ __forceinline__ int bswz(int row) { return ((row & 3) << 1) | ((row >> 3) & 1); }
+
+// HBM -> LDS copy of a 64-row bf16 tile [64][D] starting at byte `soff` of buffer `r`, into
+// `dst` (row-major, bswz-swizzled 16-byte chunks). Load r of wave w writes the 1 KiB block
+// 4r + w; the swizzle bits of a row do not depend on r.
+template <int D>
+struct TileLoader {
+  static constexpr int DCH = D / 8;
+  static constexpr int LOADS = 64 * D * 2 / (kThreads * 16);
+  static constexpr int ROWS_PER_BLOCK = 64 / DCH;
+  uint32_t off0;
+  int wave;
+  __device__ __forceinline__ TileLoader(int wave_, int lane) : wave(wave_) {
+    const int p = wave * 64 + lane;
+    const int row = p / DCH;
+    off0 = (uint32_t)(row * D * 2 + ((p % DCH) ^ bswz(row)) * 16);
+  }
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, unsigned char* dst,
+                                       uint32_t soff) const {
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i)
+      buffer_load16_to_lds(r, dst + (4 * i + wave) * 1024, off0 + i * 4 * ROWS_PER_BLOCK * D * 2,
+                           soff);
+  }
+};
+
+// Per-lane byte offsets into a bswz tile for the two read patterns.
+template <int D>
+struct TileReads {
+  int rbase[4];  // row-wise operand reads: row 32*blk + kmap(l32), logical chunk 2kk + g
+  int tbase[2];  // transposing reads: row 16u + 8g + 4h + j/4, column 32cb + 16(G%2) + 4(j%4)
+  __device__ __forceinline__ TileReads(int lane) {
+    const int l32 = lane & 31, g = lane >> 5, jl = lane & 15, grp = lane >> 4;
+    const int krow = kmap(l32);
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) rbase[kk] = krow * D * 2 + ((2 * kk + g) ^ bswz(krow)) * 16;
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int row = 8 * g + jl / 4;
+      const int col = 32 * par + 16 * (grp & 1) + 4 * (jl & 3);
+      tbase[par] = row * D * 2 + (((col >> 3) ^ bswz(row)) * 16) + (col & 7) * 2;
+    }
+  }
+  __device__ __forceinline__ int row_off(int blk, int kk) const {
+    return rbase[kk & 3] + (kk >> 2) * 128 + blk * 32 * D * 2;
+  }
+  __device__ __forceinline__ int tr_off(int cb, int u, int h) const {
+    return tbase[cb & 1] + (cb >> 1) * 128 + (16 * u + 4 * h) * D * 2;
+  }
+};
+
+// 8 bf16 of a 32x32x16 MFMA operand as two transposing reads (k-slots 0..3 and 4..7).
+__device__ __forceinline__ u32x4_t tr_operand(const unsigned char* tile, int off_h0, int off_h1) {
+  const u32x2_t lo = lds_read_tr16(tile + off_h0);
+  const u32x2_t hi = lds_read_tr16(tile + off_h1);
+  return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
 }
+
+// ---------------------------------------------------------------------------------------
+// D = rowsum(dO * O): D/8 lanes per row, 16 bytes each, reduced across the row's lanes.
+template <int D>
+__global__ __launch_bounds__(kThreads) void fa2_bwd_pre_kernel(const uint16_t* __restrict__ o,
+                                                               const uint16_t* __restrict__ dout,
+                                                               float* __restrict__ delta,
+                                                               long long rows) {
+  constexpr int TPR = D / 8;
+  const long long t = (long long)blockIdx.x * kThreads + threadIdx.x;
+  const long long row = t / TPR;
+  const int c = (int)(t % TPR);
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4_t a = *reinterpret_cast<const u32x4_t*>(o + row * D + c * 8);
+    const u32x4_t b = *reinterpret_cast<const u32x4_t*>(dout + row * D + c * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      acc += bf16_lo(a[e]) * bf16_lo(b[e]) + bf16_hi(a[e]) * bf16_hi(b[e]);
+  }
+#pragma unroll
+  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (row < rows && c == 0) delta[row] = acc;
+}
+
+// ---------------------------------------------------------------------------------------
+// dK, dV. Workgroup = 4 waves x 32 keys; query tiles of 64 (two 32-row MFMA blocks).
+// S = Q K^T and dP = dO V^T come out with lane = key and registers = queries (kmap order), so
+// P and dS are directly the B operands of dV^T = dO^T P and dK^T = Q^T dS; dO^T and Q^T
+// fragments come from the row-major LDS tiles through transposing reads.
+constexpr int kKvBK = 128;
+constexpr int kKvBQ = 64;
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 1) void fa2_bwd_dkdv_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+    const float* __restrict__ lse, const float* __restrict__ delta, uint16_t* __restrict__ dk,
+    uint16_t* __restrict__ dv, int N, int n_kblocks, int bh_count, float scale_log2,
+    float scale) {
+  constexpr int KK = D / 16, CB = D / 32;
+  constexpr int TILE = kKvBQ * D * 2;
+  constexpr int STAGE = 2 * TILE + 2 * kKvBQ * 4;  // Q, dO, LSE*log2(e), D
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+
+  // causal: key block 0 sees every query tile, so ascending order is heaviest first
+  const TileCoord tc = schedule_tile(blockIdx.x, n_kblocks, bh_count, false);
+  const size_t head_off = (size_t)tc.bh * (size_t)N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + head_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + head_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + head_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dout + head_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(lse + (size_t)tc.bh * N, (uint32_t)N * 4);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(delta + (size_t)tc.bh * N, (uint32_t)N * 4);
+
+  const int key_w0 = tc.qb * kKvBK + wave * 32;
+  const int my_key = key_w0 + l32;
+
+  // K^T and V^T fragments (B operands of S and dP): lane holds row my_key, chunk 2kk + g
+  u32x4_t kf[KK], vf[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    kf[kk] = buffer_load16(rk, (uint32_t)my_key * D * 2 + (2 * kk + g) * 16, 0);
+    vf[kk] = buffer_load16(rv, (uint32_t)my_key * D * 2 + (2 * kk + g) * 16, 0);
+  }
+
+  const int n_qt = (N + kKvBQ - 1) / kKvBQ;
+  const int qt_begin = CAUSAL ? (tc.qb * kKvBK) / kKvBQ : 0;
+  const TileLoader<D> ld(wave, lane);
+  const TileReads<D> rd_off(lane);
+
+  auto load_stage = [&](int it, int stage) {
+    unsigned char* st = smem + stage * STAGE;
+    const uint32_t soff = (uint32_t)it * kKvBQ * D * 2;
+    ld.load(rq, st, soff);
+    ld.load(rdo, st + TILE, soff);
+    // LSE and D of the tile's 64 queries (256 bytes each): 16 lanes of waves 0 and 1
+    if (wave == 0) {
+      if (lane < 16) {
+        buffer_load16_to_lds(rl, st + 2 * TILE, (uint32_t)lane * 16, (uint32_t)it * kKvBQ * 4);
+      }
+    } else if (wave == 1) {
+      if (lane < 16) {
+        buffer_load16_to_lds(rd, st + 2 * TILE + kKvBQ * 4, (uint32_t)lane * 16,
+                             (uint32_t)it * kKvBQ * 4);
+      }
+    }
+  };
+
+  f32x16_t dkacc[CB], dvacc[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) {
+    dkacc[cb] = f32x16_t{};
+    dvacc[cb] = f32x16_t{};
+  }
+
+  if (qt_begin < n_qt) load_stage(qt_begin, 0);
+  wait_vmem();
+  __syncthreads();
+
+  for (int it = qt_begin; it < n_qt; ++it) {
+    const int stage = (it - qt_begin) & 1;
+    if (it + 1 < n_qt) load_stage(it + 1, stage ^ 1);
+    const int q0 = it * kKvBQ;
+    // every query of the tile precedes every key of the wave: fully masked
+    const bool skip = CAUSAL && (q0 + kKvBQ - 1 < key_w0);
+    if (!skip) {
+      const unsigned char* st = smem + stage * STAGE;
+      const unsigned char* tq = st;
+      const unsigned char* tdo = st + TILE;
+      const float* tl = reinterpret_cast<const float*>(st + 2 * TILE);
+      const float* tdl = tl + kKvBQ;
+      const bool masked = (q0 + kKvBQ > N) || (CAUSAL && q0 < key_w0 + 31);
+
+      // one 32-query MFMA block at a time: scores, probabilities, then its dV/dK MFMAs
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        f32x16_t s, dp;
+        if (masked) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int qi = q0 + 32 * mb + 16 * (i / 8) + 8 * g + (i % 8);
+            s[i] = (qi >= N || (CAUSAL && my_key > qi)) ? -INFINITY : 0.f;
+          }
+        } else {
+          s = f32x16_t{};
+        }
+        dp = f32x16_t{};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const u32x4_t aq = *reinterpret_cast<const u32x4_t*>(tq + rd_off.row_off(mb, kk));
+          s = mfma32(aq, kf[kk], s);
+          const u32x4_t ad = *reinterpret_cast<const u32x4_t*>(tdo + rd_off.row_off(mb, kk));
+          dp = mfma32(ad, vf[kk], dp);
+        }
+        // P = exp2(s*c - LSE*log2e), dS = P * (dP - D); register i is query
+        // 32mb + 16(i/8) + 8g + i%8
+        uint32_t pk[8], dsk[8];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int qo = 32 * mb + 16 * hf + 8 * g;
+          const f32x4_t l0 = *reinterpret_cast<const f32x4_t*>(tl + qo);
+          const f32x4_t l1 = *reinterpret_cast<const f32x4_t*>(tl + qo + 4);
+          const f32x4_t d0 = *reinterpret_cast<const f32x4_t*>(tdl + qo);
+          const f32x4_t d1 = *reinterpret_cast<const f32x4_t*>(tdl + qo + 4);
+          float p[8], ds[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float lv = (e < 4 ? l0[e] : l1[e - 4]) * 1.4426950408889634f;
+            const float dv_ = e < 4 ? d0[e] : d1[e - 4];
+            p[e] = fast_exp2(__builtin_fmaf(s[8 * hf + e], scale_log2, -lv));
+            ds[e] = p[e] * (dp[8 * hf + e] - dv_);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pk[4 * hf + e] = pack_bf16(p[2 * e], p[2 * e + 1]);
+            dsk[4 * hf + e] = pack_bf16(ds[2 * e], ds[2 * e + 1]);
+          }
+        }
+        // dV^T += dO^T P and dK^T += Q^T dS over this block's 32 queries (k-steps t = 2mb + hf)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int t = 2 * mb + hf;
+          const u32x4_t bp = {pk[4 * hf + 0], pk[4 * hf + 1], pk[4 * hf + 2], pk[4 * hf + 3]};
+          const u32x4_t bs = {dsk[4 * hf + 0], dsk[4 * hf + 1], dsk[4 * hf + 2], dsk[4 * hf + 3]};
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) {
+            const u32x4_t ao = tr_operand(tdo, rd_off.tr_off(cb, t, 0), rd_off.tr_off(cb, t, 1));
+            dvacc[cb] = mfma32(ao, bp, dvacc[cb]);
+            const u32x4_t aq = tr_operand(tq, rd_off.tr_off(cb, t, 0), rd_off.tr_off(cb, t, 1));
+            dkacc[cb] = mfma32(aq, bs, dkacc[cb]);
+          }
+        }
+      }
+    }
+    wait_vmem();
+    __syncthreads();
+  }
+
+  // dK = scale * dK_acc, dV = dV_acc. Lane holds key my_key, columns 32cb + 8t + 4g + 0..3.
+  if (my_key < N) {
+    uint16_t* dkrow = dk + head_off + (size_t)my_key * D;
+    uint16_t* dvrow = dv + head_off + (size_t)my_key * D;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int c = cb * 32 + 8 * t + 4 * g;
+        *reinterpret_cast<u32x2_t*>(dkrow + c) =
+            u32x2_t{pack_bf16(dkacc[cb][4 * t] * scale, dkacc[cb][4 * t + 1] * scale),
+                    pack_bf16(dkacc[cb][4 * t + 2] * scale, dkacc[cb][4 * t + 3] * scale)};
+        *reinterpret_cast<u32x2_t*>(dvrow + c) =
+            u32x2_t{pack_bf16(dvacc[cb][4 * t], dvacc[cb][4 * t + 1]),
+                    pack_bf16(dvacc[cb][4 * t + 2], dvacc[cb][4 * t + 3])};
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// dQ. Workgroup = 4 waves x 32 queries (lane = query, as in the forward); key tiles of 64.
+// S^T = K Q^T and dP^T = V dO^T from row-wise K/V tile reads with Q^T/dO^T fragments held in
+// VGPRs; dQ^T += K^T dS^T with K^T fragments from transposing reads of the same K tile.
+constexpr int kDqBR = 128;
+constexpr int kDqBC = 64;
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dq_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+    const float* __restrict__ lse, const float* __restrict__ delta, uint16_t* __restrict__ dq,
+    int N, int n_qblocks, int bh_count, float scale_log2, float scale) {
+  constexpr int KK = D / 16, CB = D / 32;
+  constexpr int TILE = kDqBC * D * 2;
+  constexpr int STAGE = 2 * TILE;  // K, V
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+
+  const TileCoord tc = schedule_tile(blockIdx.x, n_qblocks, bh_count, CAUSAL);
+  const size_t head_off = (size_t)tc.bh * (size_t)N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + head_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + head_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + head_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dout + head_off, head_bytes);
+
+  const int q_block0 = tc.qb * kDqBR;
+  const int q_wave0 = q_block0 + wave * 32;
+  const int my_q = q_wave0 + l32;
+  const bool valid_q = my_q < N;
+
+  u32x4_t qf[KK], dof[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) {
+    qf[kk] = buffer_load16(rq, (uint32_t)my_q * D * 2 + (2 * kk + g) * 16, 0);
+    dof[kk] = buffer_load16(rdo, (uint32_t)my_q * D * 2 + (2 * kk + g) * 16, 0);
+  }
+  // padded queries get LSE = +inf, hence P = 0
+  const float lse2 = valid_q ? lse[(size_t)tc.bh * N + my_q] * 1.4426950408889634f : INFINITY;
+  const float dlt = valid_q ? delta[(size_t)tc.bh * N + my_q] : 0.f;
+
+  int n_tiles = (N + kDqBC - 1) / kDqBC;
+  if (CAUSAL) n_tiles = min(N - 1, q_block0 + kDqBR - 1) / kDqBC + 1;
+  const int wave_last = CAUSAL ? min(n_tiles - 1, (q_wave0 + 31) / kDqBC) : n_tiles - 1;
+
+  const TileLoader<D> ld(wave, lane);
+  const TileReads<D> rd_off(lane);
+  auto load_stage = [&](int j, int stage) {
+    unsigned char* st = smem + stage * STAGE;
+    const uint32_t soff = (uint32_t)j * kDqBC * D * 2;
+    ld.load(rk, st, soff);
+    ld.load(rv, st + TILE, soff);
+  };
+
+  f32x16_t dqacc[CB];
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) dqacc[cb] = f32x16_t{};
+
+  load_stage(0, 0);
+  wait_vmem();
+  __syncthreads();
+
+  for (int j = 0; j < n_tiles; ++j) {
+    const int stage = j & 1;
+    if (j + 1 < n_tiles) load_stage(j + 1, stage ^ 1);
+    if (j <= wave_last) {
+      const unsigned char* tk = smem + stage * STAGE;
+      const unsigned char* tv = tk + TILE;
+      const int key0 = j * kDqBC;
+      const bool masked = (key0 + kDqBC > N) || (CAUSAL && key0 + kDqBC - 1 > q_wave0);
+      f32x16_t s[2], dp[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        if (masked) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = key0 + kb * 32 + (i / 8) * 16 + g * 8 + (i % 8);
+            s[kb][i] = (key >= N || (CAUSAL && key > my_q)) ? -INFINITY : 0.f;
+          }
+        } else {
+          s[kb] = f32x16_t{};
+        }
+        dp[kb] = f32x16_t{};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const u32x4_t ak = *reinterpret_cast<const u32x4_t*>(tk + rd_off.row_off(kb, kk));
+          s[kb] = mfma32(ak, qf[kk], s[kb]);
+          const u32x4_t av = *reinterpret_cast<const u32x4_t*>(tv + rd_off.row_off(kb, kk));
+          dp[kb] = mfma32(av, dof[kk], dp[kb]);
+        }
+      }
+      uint32_t dsk[2][8];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float p0 = fast_exp2(__builtin_fmaf(s[kb][2 * i], scale_log2, -lse2));
+          const float p1 = fast_exp2(__builtin_fmaf(s[kb][2 * i + 1], scale_log2, -lse2));
+          dsk[kb][i] = pack_bf16(p0 * (dp[kb][2 * i] - dlt), p1 * (dp[kb][2 * i + 1] - dlt));
+        }
+      // dQ^T += K^T dS^T; MFMA u covers keys 16u .. 16u+15
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const u32x4_t b = {dsk[u / 2][4 * (u % 2) + 0], dsk[u / 2][4 * (u % 2) + 1],
+                           dsk[u / 2][4 * (u % 2) + 2], dsk[u / 2][4 * (u % 2) + 3]};
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          const u32x4_t a = tr_operand(tk, rd_off.tr_off(cb, u, 0), rd_off.tr_off(cb, u, 1));
+          dqacc[cb] = mfma32(a, b, dqacc[cb]);
+        }
+      }
+    }
+    wait_vmem();
+    __syncthreads();
+  }
+
+  if (valid_q) {
+    uint16_t* row = dq + head_off + (size_t)my_q * D;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int c = cb * 32 + 8 * t + 4 * g;
+        *reinterpret_cast<u32x2_t*>(row + c) =
+            u32x2_t{pack_bf16(dqacc[cb][4 * t] * scale, dqacc[cb][4 * t + 1] * scale),
+                    pack_bf16(dqacc[cb][4 * t + 2] * scale, dqacc[cb][4 * t + 3] * scale)};
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+template <int D>
+hipError_t launch_pre_t(const BwdArgs& a) {
+  const long long rows = (long long)a.B * a.H * a.N;
+  const long long threads = rows * (D / 8);
+  const long long grid = (threads + kThreads - 1) / kThreads;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((fa2_bwd_pre_kernel<D>), dim3((unsigned)grid), dim3(kThreads), 0, a.stream,
+                     static_cast<const uint16_t*>(a.o), static_cast<const uint16_t*>(a.dout),
+                     a.delta, rows);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_dkdv_t(const BwdArgs& a) {
+  const int n_kblocks = (a.N + kKvBK - 1) / kKvBK;
+  const long long grid = (long long)n_kblocks * a.B * a.H;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0,
+                     a.stream, static_cast<const uint16_t*>(a.q),
+                     static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
+                     static_cast<const uint16_t*>(a.dout), a.lse, a.delta,
+                     static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), a.N, n_kblocks,
+                     a.B * a.H, a.scale_log2, a.scale);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t launch_dq_t(const BwdArgs& a) {
+  const int n_qblocks = (a.N + kDqBR - 1) / kDqBR;
+  const long long grid = (long long)n_qblocks * a.B * a.H;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((fa2_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0,
+                     a.stream, static_cast<const uint16_t*>(a.q),
+                     static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
+                     static_cast<const uint16_t*>(a.dout), a.lse, a.delta,
+                     static_cast<uint16_t*>(a.dq), a.N, n_qblocks, a.B * a.H, a.scale_log2,
+                     a.scale);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd_pre(const BwdArgs& a) {
+  return a.d == 64 ? launch_pre_t<64>(a) : launch_pre_t<128>(a);
+}
+
+hipError_t launch_bwd_dkdv(const BwdArgs& a) {
+  if (a.d == 64) return a.causal ? launch_dkdv_t<64, true>(a) : launch_dkdv_t<64, false>(a);
+  return a.causal ? launch_dkdv_t<128, true>(a) : launch_dkdv_t<128, false>(a);
+}
+
+hipError_t launch_bwd_dq(const BwdArgs& a) {
+  if (a.d == 64) return a.causal ? launch_dq_t<64, true>(a) : launch_dq_t<64, false>(a);
+  return a.causal ? launch_dq_t<128, true>(a) : launch_dq_t<128, false>(a);
+}
+
+hipError_t launch_bwd(const BwdArgs& a) {
+  hipError_t e = launch_bwd_pre(a);
+  if (e != hipSuccess) return e;
+  e = launch_bwd_dkdv(a);
+  if (e != hipSuccess) return e;
+  return launch_bwd_dq(a);
+}
+
+}  // namespace fa2

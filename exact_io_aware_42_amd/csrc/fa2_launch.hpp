@@ -38,6 +38,9 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs& a);
-hipError_t launch_bwd(const BwdArgs& a);
+hipError_t launch_bwd(const BwdArgs& a);  // pre, then dK/dV, then dQ
+hipError_t launch_bwd_pre(const BwdArgs& a);
+hipError_t launch_bwd_dkdv(const BwdArgs& a);
+hipError_t launch_bwd_dq(const BwdArgs& a);
 
 }  // namespace fa2

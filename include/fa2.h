@@ -81,6 +81,29 @@ fa2_status fa2_bwd(const void* q, const void* k, const void* v, const void* o,
                    int B, int H, int N, int d, int causal, float softmax_scale,
                    hipStream_t stream);
 
+/* The three stages of fa2_bwd, for callers that schedule them separately (fa2_bwd runs them
+ * in this order on one stream; the results are identical).
+ *
+ * fa2_bwd_preprocess: delta [B,H,N] fp32 = rowsum(dout * o), the softmax-gradient row term
+ *   D_i = sum_c dO_ic O_ic (it equals sum_j P_ij dP_ij). o and dout as in fa2_bwd; delta is a
+ *   caller-owned device buffer of B*H*N floats. */
+fa2_status fa2_bwd_preprocess(const void* o, const void* dout, float* delta,
+                              int B, int H, int N, int d, hipStream_t stream);
+
+/* fa2_bwd_dkdv: dk and dv [B,H,N,d] (bf16) from q, k, v, dout, the forward lse and the delta
+ *   of fa2_bwd_preprocess. Parallel over blocks of 128 keys; recomputes P block by block. */
+fa2_status fa2_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
+                        const float* lse, const float* delta, void* dk, void* dv,
+                        int B, int H, int N, int d, int causal, float softmax_scale,
+                        hipStream_t stream);
+
+/* fa2_bwd_dq: dq [B,H,N,d] (bf16) from the same inputs. Parallel over blocks of 128 queries;
+ *   recomputes P and dP block by block, so no atomics are needed. */
+fa2_status fa2_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
+                      const float* lse, const float* delta, void* dq,
+                      int B, int H, int N, int d, int causal, float softmax_scale,
+                      hipStream_t stream);
+
 /* Static, human-readable name of a status code. */
 const char* fa2_status_string(fa2_status s);
 
