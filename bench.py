@@ -22,7 +22,6 @@ Prints ONE JSON line (rank 0).
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import math
 import os
@@ -54,41 +53,6 @@ def parse_args():
 def fwd_flop(B, H, N, d, causal):
     f = 4.0 * B * H * N * N * d
     return f / 2 if causal else f
-
-
-def kernel_source_digest(names):
-    h = hashlib.sha256()
-    for n in names:
-        with open(os.path.join(ROOT, "exact_io_aware_42_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
-
-
-KERNEL_SOURCES = {
-    "fa2_fwd_kernel": ["fa2_device.hpp", "fa2_fwd.hip"],
-    "fa2_bwd_dkdv_kernel": ["fa2_device.hpp", "fa2_bwd.hip"],
-    "fa2_bwd_dq_kernel": ["fa2_device.hpp", "fa2_bwd.hip"],
-    "fa2_bwd_pre_kernel": ["fa2_device.hpp", "fa2_bwd.hip"],
-}
-
-
-def load_traffic(kernel, workload_tag):
-    """HBM bytes per launch from a committed counter summary, if it matches the source."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload_tag}.txt")
-    if not os.path.exists(path):
-        return None
-    vals = {}
-    with open(path) as f:
-        for line in f:
-            if ":" in line and not line.startswith("#"):
-                k, _, v = line.partition(":")
-                vals[k.strip()] = v.strip()
-    if vals.get("kernel_source_digest") != kernel_source_digest(KERNEL_SOURCES[kernel]):
-        return None
-    try:
-        return float(vals["traffic_bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
 
 
 def cpu_baseline(w, causal, with_bwd, budget_s):
@@ -217,6 +181,7 @@ def main():
     dominant = max(kernels, key=lambda kn: kernel_ms[kn])
     achieved = algo_flop[dominant] / (kernel_ms[dominant] * 1e-3) / 1e12
     wtag = f"w{w.wid}_{'causal' if causal else 'full'}"
+    from exact_io_aware_42_amd.profiling import load_traffic
     traffic = load_traffic(dominant, wtag)
 
     value = step_flop * args.steps / elapsed / 1e12

@@ -1,0 +1,140 @@
+"""HBM-traffic accounting from rocprofv3 counter runs (FETCH_SIZE, WRITE_SIZE).
+
+    # a plain device copy of known size, to calibrate the counters
+    python -m exact_io_aware_42_amd.profiling copy --mib 256
+    # turn counter CSVs into profiles/traffic_<kernel>_<workload>.txt
+    python -m exact_io_aware_42_amd.profiling traffic --kernel fa2_fwd_kernel \\
+        --workload w4_full --fetch run_fetch.csv --write run_write.csv \\
+        --copy-fetch copy_fetch.csv --copy-write copy_write.csv --copy-mib 256
+
+The counters report KiB per dispatch; the copy of known size gives the factor between what a
+counter reads and the bytes that actually moved (fetch: bytes read, write: bytes written).
+The summary records a digest of the kernel's sources so that a stale summary is not used.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import os
+import statistics
+import sys
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG_DIR)
+
+KERNEL_SOURCES = {
+    "fa2_fwd_kernel": ["fa2_device.hpp", "fa2_fwd.hip"],
+    "fa2_bwd_dkdv_kernel": ["fa2_device.hpp", "fa2_bwd.hip"],
+    "fa2_bwd_dq_kernel": ["fa2_device.hpp", "fa2_bwd.hip"],
+    "fa2_bwd_pre_kernel": ["fa2_device.hpp", "fa2_bwd.hip"],
+}
+
+
+def kernel_source_digest(kernel: str) -> str:
+    h = hashlib.sha256()
+    for n in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(PKG_DIR, "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_path(kernel: str, workload_tag: str) -> str:
+    return os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload_tag}.txt")
+
+
+def load_traffic(kernel: str, workload_tag: str):
+    """HBM bytes per launch from a committed summary, or None if absent or stale."""
+    path = traffic_path(kernel, workload_tag)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, _, v = line.partition(":")
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_digest") != kernel_source_digest(kernel):
+        return None
+    try:
+        return float(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def counter_values(path: str, counter: str, name_substr: str):
+    vals = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter and name_substr in r["Kernel_Name"]:
+                vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"no {counter} rows for kernels matching {name_substr!r} in {path}")
+    return vals
+
+
+def copy_main(mib: int):
+    import torch
+
+    n = mib << 20
+    x = torch.empty(n, dtype=torch.uint8, device="cuda")
+    x.fill_(1)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(f"copied {mib} MiB three times", flush=True)
+
+
+def traffic_main(a):
+    fetch = statistics.median(counter_values(a.fetch, "FETCH_SIZE", a.kernel))
+    write = statistics.median(counter_values(a.write, "WRITE_SIZE", a.kernel))
+    # the copy kernel is the only kernel in the calibration runs besides the fill
+    copy_bytes = a.copy_mib * 1024 * 1024
+    cf = counter_values(a.copy_fetch, "FETCH_SIZE", a.copy_kernel)
+    cw = counter_values(a.copy_write, "WRITE_SIZE", a.copy_kernel)
+    f_fetch = copy_bytes / (statistics.median(cf) * 1024)
+    f_write = copy_bytes / (statistics.median(cw) * 1024)
+    traffic = fetch * 1024 * f_fetch + write * 1024 * f_write
+    out = traffic_path(a.kernel, a.workload)
+    with open(out, "w") as f:
+        f.write(f"# HBM traffic of {a.kernel} on workload {a.workload}, from rocprofv3 counters\n")
+        f.write(f"# command (fetch pass): {a.cmd_fetch}\n")
+        f.write(f"# command (write pass): {a.cmd_write}\n")
+        f.write(f"# calibration: {a.copy_mib} MiB device copy (torch copy_), "
+                f"kernel matching {a.copy_kernel!r}\n")
+        f.write(f"kernel_source_digest: {kernel_source_digest(a.kernel)}\n")
+        f.write(f"fetch_kib_per_dispatch: {fetch:.1f}\n")
+        f.write(f"write_kib_per_dispatch: {write:.1f}\n")
+        f.write(f"copy_fetch_factor: {f_fetch:.4f}\n")
+        f.write(f"copy_write_factor: {f_write:.4f}\n")
+        f.write(f"traffic_bytes_per_launch: {traffic:.0f}\n")
+    print(open(out).read())
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    c = sub.add_parser("copy")
+    c.add_argument("--mib", type=int, default=256)
+    t = sub.add_parser("traffic")
+    t.add_argument("--kernel", required=True, choices=sorted(KERNEL_SOURCES))
+    t.add_argument("--workload", required=True)
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--copy-fetch", required=True)
+    t.add_argument("--copy-write", required=True)
+    t.add_argument("--copy-mib", type=int, default=256)
+    t.add_argument("--copy-kernel", default="copy")
+    t.add_argument("--cmd-fetch", default="")
+    t.add_argument("--cmd-write", default="")
+    a = ap.parse_args(argv)
+    if a.cmd == "copy":
+        copy_main(a.mib)
+    else:
+        traffic_main(a)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])
