@@ -152,11 +152,11 @@ def main():
         fa2.fwd(q, k, v, causal=causal, scale=scale, out=o, lse=lse)
         mark(1)
         if with_bwd:
-            fa2.bwd_preprocess(o, do, ws)
+            fa2.bwd_preprocess(o, do, lse, ws)
             mark(2)
-            fa2.bwd_dkdv(q, k, v, do, lse, ws, causal=causal, scale=scale, dk=dk, dv=dv)
+            fa2.bwd_dkdv(q, k, v, do, ws, causal=causal, scale=scale, dk=dk, dv=dv)
             mark(3)
-            fa2.bwd_dq(q, k, v, do, lse, ws, causal=causal, scale=scale, dq=dq)
+            fa2.bwd_dq(q, k, v, do, ws, causal=causal, scale=scale, dq=dq)
             mark(4)
 
     for _ in range(args.warmup):

@@ -29,6 +29,12 @@ COMMON_FLAGS = [
     "-fPIC",
     "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: softmax reads the score accumulators with plain VALU ops, so
+    # AGPR-form MFMAs would need a v_accvgpr_read per element
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
+    # the ILP-oriented machine scheduler issues LDS operand reads well ahead of the MFMAs that
+    # consume them (the default occupancy-oriented one waits on each read right before its MFMA)
+    "-mllvm", "-amdgpu-sched-strategy=iterative-ilp",
     f"-I{INCLUDE}",
     f"-I{CSRC}",
 ]

@@ -68,19 +68,26 @@ fa2_status fa2_fwd(const void* q, const void* k, const void* v, void* o, float* 
   return from_hip(fa2::launch_fwd(a));
 }
 
+// Workspace layout: D = rowsum(dO * O) [B*H*N floats], then LSE * log2(e) [B*H*N floats],
+// the second part starting at a 256-byte boundary.
+static size_t ws_part_bytes(int B, int H, int N) { return round256((size_t)B * H * N * sizeof(float)); }
+
 size_t fa2_bwd_workspace_bytes(int B, int H, int N, int d) {
   if (check_sizes(B, H, N, d, 1.0f) != FA2_OK) return 0;
-  return round256((size_t)B * H * N * sizeof(float));
+  return 2 * ws_part_bytes(B, H, N);
 }
 
 namespace {
 
 fa2_status bwd_args(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                    const float* lse, float* delta, void* dq, void* dk, void* dv, int B, int H,
-                    int N, int d, int causal, float softmax_scale, hipStream_t stream,
-                    fa2::BwdArgs* a) {
+                    const float* lse, void* workspace, size_t workspace_bytes, void* dq, void* dk,
+                    void* dv, int B, int H, int N, int d, int causal, float softmax_scale,
+                    hipStream_t stream, fa2::BwdArgs* a) {
   const fa2_status st = check_sizes(B, H, N, d, softmax_scale);
   if (st != FA2_OK) return st;
+  if (workspace == nullptr || !aligned16(workspace) ||
+      workspace_bytes < fa2_bwd_workspace_bytes(B, H, N, d))
+    return FA2_ERR_INVALID_ARGUMENT;
   a->q = q;
   a->k = k;
   a->v = v;
@@ -90,7 +97,8 @@ fa2_status bwd_args(const void* q, const void* k, const void* v, const void* o, 
   a->dq = dq;
   a->dk = dk;
   a->dv = dv;
-  a->delta = delta;
+  a->delta = static_cast<float*>(workspace);
+  a->lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws_part_bytes(B, H, N));
   a->B = B;
   a->H = H;
   a->N = N;
@@ -115,43 +123,46 @@ fa2_status fa2_bwd(const void* q, const void* k, const void* v, const void* o, c
                    size_t workspace_bytes, int B, int H, int N, int d, int causal,
                    float softmax_scale, hipStream_t stream) {
   fa2::BwdArgs a;
-  const fa2_status st = bwd_args(q, k, v, o, dout, lse, static_cast<float*>(workspace), dq, dk,
-                                 dv, B, H, N, d, causal, softmax_scale, stream, &a);
+  const fa2_status st = bwd_args(q, k, v, o, dout, lse, workspace, workspace_bytes, dq, dk, dv,
+                                 B, H, N, d, causal, softmax_scale, stream, &a);
   if (st != FA2_OK) return st;
-  if (!all_ok({q, k, v, o, dout, lse, dq, dk, dv, workspace})) return FA2_ERR_INVALID_ARGUMENT;
-  if (workspace_bytes < fa2_bwd_workspace_bytes(B, H, N, d)) return FA2_ERR_INVALID_ARGUMENT;
+  if (!all_ok({q, k, v, o, dout, lse, dq, dk, dv})) return FA2_ERR_INVALID_ARGUMENT;
   return from_hip(fa2::launch_bwd(a));
 }
 
-fa2_status fa2_bwd_preprocess(const void* o, const void* dout, float* delta, int B, int H, int N,
-                              int d, hipStream_t stream) {
+fa2_status fa2_bwd_preprocess(const void* o, const void* dout, const float* lse, void* workspace,
+                              size_t workspace_bytes, int B, int H, int N, int d,
+                              hipStream_t stream) {
   fa2::BwdArgs a;
-  const fa2_status st = bwd_args(nullptr, nullptr, nullptr, o, dout, nullptr, delta, nullptr,
-                                 nullptr, nullptr, B, H, N, d, 0, 1.0f, stream, &a);
+  const fa2_status st = bwd_args(nullptr, nullptr, nullptr, o, dout, lse, workspace,
+                                 workspace_bytes, nullptr, nullptr, nullptr, B, H, N, d, 0, 1.0f,
+                                 stream, &a);
   if (st != FA2_OK) return st;
-  if (!all_ok({o, dout, delta})) return FA2_ERR_INVALID_ARGUMENT;
+  if (!all_ok({o, dout, lse})) return FA2_ERR_INVALID_ARGUMENT;
   return from_hip(fa2::launch_bwd_pre(a));
 }
 
 fa2_status fa2_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
-                        const float* lse, const float* delta, void* dk, void* dv, int B, int H,
-                        int N, int d, int causal, float softmax_scale, hipStream_t stream) {
+                        const void* workspace, size_t workspace_bytes, void* dk, void* dv, int B,
+                        int H, int N, int d, int causal, float softmax_scale, hipStream_t stream) {
   fa2::BwdArgs a;
-  const fa2_status st = bwd_args(q, k, v, nullptr, dout, lse, const_cast<float*>(delta), nullptr,
-                                 dk, dv, B, H, N, d, causal, softmax_scale, stream, &a);
+  const fa2_status st = bwd_args(q, k, v, nullptr, dout, nullptr, const_cast<void*>(workspace),
+                                 workspace_bytes, nullptr, dk, dv, B, H, N, d, causal,
+                                 softmax_scale, stream, &a);
   if (st != FA2_OK) return st;
-  if (!all_ok({q, k, v, dout, lse, delta, dk, dv})) return FA2_ERR_INVALID_ARGUMENT;
+  if (!all_ok({q, k, v, dout, dk, dv})) return FA2_ERR_INVALID_ARGUMENT;
   return from_hip(fa2::launch_bwd_dkdv(a));
 }
 
 fa2_status fa2_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
-                      const float* lse, const float* delta, void* dq, int B, int H, int N, int d,
-                      int causal, float softmax_scale, hipStream_t stream) {
+                      const void* workspace, size_t workspace_bytes, void* dq, int B, int H, int N,
+                      int d, int causal, float softmax_scale, hipStream_t stream) {
   fa2::BwdArgs a;
-  const fa2_status st = bwd_args(q, k, v, nullptr, dout, lse, const_cast<float*>(delta), dq,
-                                 nullptr, nullptr, B, H, N, d, causal, softmax_scale, stream, &a);
+  const fa2_status st = bwd_args(q, k, v, nullptr, dout, nullptr, const_cast<void*>(workspace),
+                                 workspace_bytes, dq, nullptr, nullptr, B, H, N, d, causal,
+                                 softmax_scale, stream, &a);
   if (st != FA2_OK) return st;
-  if (!all_ok({q, k, v, dout, lse, delta, dq})) return FA2_ERR_INVALID_ARGUMENT;
+  if (!all_ok({q, k, v, dout, dq})) return FA2_ERR_INVALID_ARGUMENT;
   return from_hip(fa2::launch_bwd_dq(a));
 }
 

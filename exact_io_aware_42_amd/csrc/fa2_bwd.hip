@@ -12,10 +12,10 @@
 //   dV = P^T dO,  dK = scale dS^T Q,  dQ = scale dS K.
 //
 // Three kernels, deterministic (no atomics):
-//   fa2_bwd_pre_kernel   D = rowsum(dO * O), fp32 [B, H, N] (HBM-bound, one pass).
-//   fa2_bwd_dkdv_kernel  grid over (key block of 128, head, batch): each wave keeps its 32 keys'
-//                        K and V fragments in VGPRs and its dK, dV accumulators in registers,
-//                        and streams 64-query tiles of Q, dO, LSE and D through LDS.
+//   fa2_bwd_pre_kernel   D = rowsum(dO * O) and LSE*log2(e), fp32 [B, H, N] (HBM-bound).
+//   fa2_bwd_dkdv_kernel  grid over (key block of 128, head, batch): the block's K and V rows
+//                        stay in LDS, each wave accumulates dK, dV for its 32 keys in registers,
+//                        and 64-query tiles of Q, dO, LSE and D stream through LDS.
 //   fa2_bwd_dq_kernel    grid over (query block of 128, head, batch): the forward's layout
 //                        (lane = query), recomputing S^T and dP^T per key tile and
 //                        accumulating dQ^T = K^T dS^T.
@@ -29,6 +29,7 @@ namespace fa2 {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr float kLog2e = 1.4426950408889634f;
 
 // XOR swizzle of 16-byte chunks for tiles read both ways: row-wise by 32-lane MFMA operand
 // reads (8 lanes of one phase take rows kmap(0..7) = {0,1,2,3,8,9,10,11}, one chunk) and by
@@ -93,11 +94,14 @@ __device__ __forceinline__ u32x4_t tr_operand(const unsigned char* tile, int off
 }
 
 // ---------------------------------------------------------------------------------------
-// D = rowsum(dO * O): D/8 lanes per row, 16 bytes each, reduced across the row's lanes.
+// D = rowsum(dO * O): D/8 lanes per row, 16 bytes each, reduced across the row's lanes. The
+// same pass stores LSE * log2(e), the form the other two kernels subtract inside exp2.
 template <int D>
 __global__ __launch_bounds__(kThreads) void fa2_bwd_pre_kernel(const uint16_t* __restrict__ o,
                                                                const uint16_t* __restrict__ dout,
+                                                               const float* __restrict__ lse,
                                                                float* __restrict__ delta,
+                                                               float* __restrict__ lse2,
                                                                long long rows) {
   constexpr int TPR = D / 8;
   const long long t = (long long)blockIdx.x * kThreads + threadIdx.x;
@@ -113,28 +117,38 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_pre_kernel(const uint16_t* _
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (row < rows && c == 0) delta[row] = acc;
+  if (row < rows && c == 0) {
+    delta[row] = acc;
+    lse2[row] = lse[row] * kLog2e;
+  }
 }
 
 // ---------------------------------------------------------------------------------------
-// dK, dV. Workgroup = 4 waves x 32 keys; query tiles of 64 (two 32-row MFMA blocks).
+// dK, dV. Workgroup = 4 waves x 32 keys = 128 keys, whose K and V rows stay in LDS for the
+// whole kernel; query tiles of 64 (two 32-row MFMA blocks) stream through a second LDS ring.
 // S = Q K^T and dP = dO V^T come out with lane = key and registers = queries (kmap order), so
 // P and dS are directly the B operands of dV^T = dO^T P and dK^T = Q^T dS; dO^T and Q^T
-// fragments come from the row-major LDS tiles through transposing reads.
+// fragments come from the row-major tiles through transposing reads. Each K/V fragment read
+// from LDS feeds both 32-query blocks.
 constexpr int kKvBK = 128;
 constexpr int kKvBQ = 64;
+
+// swizzle of the resident K/V rows: read row-wise with lane = row, 8 consecutive rows per phase
+__device__ __forceinline__ int kvswz(int row) { return row & 7; }
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void fa2_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-    const float* __restrict__ lse, const float* __restrict__ delta, uint16_t* __restrict__ dk,
+    const float* __restrict__ lse2, const float* __restrict__ delta, uint16_t* __restrict__ dk,
     uint16_t* __restrict__ dv, int N, int n_kblocks, int bh_count, float scale_log2,
     float scale) {
-  constexpr int KK = D / 16, CB = D / 32;
+  constexpr int KK = D / 16, CB = D / 32, DCH = D / 8;
   constexpr int TILE = kKvBQ * D * 2;
+  constexpr int KV_BYTES = kKvBK * D * 2;
   constexpr int STAGE = 2 * TILE + 2 * kKvBQ * 4;  // Q, dO, LSE*log2(e), D
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+  constexpr int RING0 = 2 * KV_BYTES;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[RING0 + 2 * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -150,40 +164,52 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_bwd_dkdv_kernel(
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + head_off, head_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + head_off, head_bytes);
   const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dout + head_off, head_bytes);
-  const __amdgpu_buffer_rsrc_t rl = make_rsrc(lse + (size_t)tc.bh * N, (uint32_t)N * 4);
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(lse2 + (size_t)tc.bh * N, (uint32_t)N * 4);
   const __amdgpu_buffer_rsrc_t rd = make_rsrc(delta + (size_t)tc.bh * N, (uint32_t)N * 4);
 
-  const int key_w0 = tc.qb * kKvBK + wave * 32;
+  const int key_b0 = tc.qb * kKvBK;
+  const int key_w0 = key_b0 + wave * 32;
   const int my_key = key_w0 + l32;
 
-  // K^T and V^T fragments (B operands of S and dP): lane holds row my_key, chunk 2kk + g
-  u32x4_t kf[KK], vf[KK];
+  // resident K and V rows of the block: 128 rows each, kvswz-swizzled; block i of 1 KiB holds
+  // rows (64/DCH)*i .. ; 2*DCH/4 loads per wave per tensor
+  {
+    constexpr int LOADS = KV_BYTES / (kThreads * 16);
+    constexpr int RPB = 64 / DCH;
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
-    kf[kk] = buffer_load16(rk, (uint32_t)my_key * D * 2 + (2 * kk + g) * 16, 0);
-    vf[kk] = buffer_load16(rv, (uint32_t)my_key * D * 2 + (2 * kk + g) * 16, 0);
+    for (int r = 0; r < LOADS; ++r) {
+      const int blk = 4 * r + wave;
+      const int row = blk * RPB + lane / DCH;
+      const uint32_t off = (uint32_t)(row * D * 2 + ((lane % DCH) ^ kvswz(row)) * 16);
+      buffer_load16_to_lds(rk, smem + blk * 1024, off, (uint32_t)key_b0 * D * 2);
+      buffer_load16_to_lds(rv, smem + KV_BYTES + blk * 1024, off, (uint32_t)key_b0 * D * 2);
+    }
   }
+  // per-lane offset of this wave's K/V fragment: row 32*wave + l32, logical chunk 2kk + g
+  const int kvrow = wave * 32 + l32;
+  int kvbase[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) kvbase[kk] = kvrow * D * 2 + ((2 * kk + g) ^ kvswz(kvrow)) * 16;
+  auto kv_off = [&](int kk) { return kvbase[kk & 3] + (kk >> 2) * 128; };
 
   const int n_qt = (N + kKvBQ - 1) / kKvBQ;
-  const int qt_begin = CAUSAL ? (tc.qb * kKvBK) / kKvBQ : 0;
+  const int qt_begin = CAUSAL ? key_b0 / kKvBQ : 0;
   const TileLoader<D> ld(wave, lane);
   const TileReads<D> rd_off(lane);
 
   auto load_stage = [&](int it, int stage) {
-    unsigned char* st = smem + stage * STAGE;
+    unsigned char* st = smem + RING0 + stage * STAGE;
     const uint32_t soff = (uint32_t)it * kKvBQ * D * 2;
     ld.load(rq, st, soff);
     ld.load(rdo, st + TILE, soff);
-    // LSE and D of the tile's 64 queries (256 bytes each): 16 lanes of waves 0 and 1
+    // LSE*log2(e) and D of the tile's 64 queries (256 bytes each): 16 lanes of waves 0 and 1
     if (wave == 0) {
-      if (lane < 16) {
+      if (lane < 16)
         buffer_load16_to_lds(rl, st + 2 * TILE, (uint32_t)lane * 16, (uint32_t)it * kKvBQ * 4);
-      }
     } else if (wave == 1) {
-      if (lane < 16) {
+      if (lane < 16)
         buffer_load16_to_lds(rd, st + 2 * TILE + kKvBQ * 4, (uint32_t)lane * 16,
                              (uint32_t)it * kKvBQ * 4);
-      }
     }
   };
 
@@ -205,36 +231,43 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_bwd_dkdv_kernel(
     // every query of the tile precedes every key of the wave: fully masked
     const bool skip = CAUSAL && (q0 + kKvBQ - 1 < key_w0);
     if (!skip) {
-      const unsigned char* st = smem + stage * STAGE;
+      const unsigned char* st = smem + RING0 + stage * STAGE;
       const unsigned char* tq = st;
       const unsigned char* tdo = st + TILE;
       const float* tl = reinterpret_cast<const float*>(st + 2 * TILE);
       const float* tdl = tl + kKvBQ;
       const bool masked = (q0 + kKvBQ > N) || (CAUSAL && q0 < key_w0 + 31);
 
-      // one 32-query MFMA block at a time: scores, probabilities, then its dV/dK MFMAs
+      f32x16_t s[2], dp[2];
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        f32x16_t s, dp;
         if (masked) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int qi = q0 + 32 * mb + 16 * (i / 8) + 8 * g + (i % 8);
-            s[i] = (qi >= N || (CAUSAL && my_key > qi)) ? -INFINITY : 0.f;
+            s[mb][i] = (qi >= N || (CAUSAL && my_key > qi)) ? -INFINITY : 0.f;
           }
         } else {
-          s = f32x16_t{};
+          s[mb] = f32x16_t{};
         }
-        dp = f32x16_t{};
+        dp[mb] = f32x16_t{};
+      }
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
+      for (int kk = 0; kk < KK; ++kk) {
+        const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(smem + kv_off(kk));
+        const u32x4_t vf = *reinterpret_cast<const u32x4_t*>(smem + KV_BYTES + kv_off(kk));
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
           const u32x4_t aq = *reinterpret_cast<const u32x4_t*>(tq + rd_off.row_off(mb, kk));
-          s = mfma32(aq, kf[kk], s);
+          s[mb] = mfma32(aq, kf, s[mb]);
           const u32x4_t ad = *reinterpret_cast<const u32x4_t*>(tdo + rd_off.row_off(mb, kk));
-          dp = mfma32(ad, vf[kk], dp);
+          dp[mb] = mfma32(ad, vf, dp[mb]);
         }
-        // P = exp2(s*c - LSE*log2e), dS = P * (dP - D); register i is query
-        // 32mb + 16(i/8) + 8g + i%8
+      }
+      // P = exp2(s*c - LSE*log2e), dS = P * (dP - D); register i of block mb is query
+      // 32mb + 16(i/8) + 8g + i%8
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
         uint32_t pk[8], dsk[8];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
@@ -246,10 +279,10 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_bwd_dkdv_kernel(
           float p[8], ds[8];
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float lv = (e < 4 ? l0[e] : l1[e - 4]) * 1.4426950408889634f;
+            const float lv = e < 4 ? l0[e] : l1[e - 4];
             const float dv_ = e < 4 ? d0[e] : d1[e - 4];
-            p[e] = fast_exp2(__builtin_fmaf(s[8 * hf + e], scale_log2, -lv));
-            ds[e] = p[e] * (dp[8 * hf + e] - dv_);
+            p[e] = fast_exp2(__builtin_fmaf(s[mb][8 * hf + e], scale_log2, -lv));
+            ds[e] = p[e] * (dp[mb][8 * hf + e] - dv_);
           }
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -307,7 +340,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-    const float* __restrict__ lse, const float* __restrict__ delta, uint16_t* __restrict__ dq,
+    const float* __restrict__ lse2, const float* __restrict__ delta, uint16_t* __restrict__ dq,
     int N, int n_qblocks, int bh_count, float scale_log2, float scale) {
   constexpr int KK = D / 16, CB = D / 32;
   constexpr int TILE = kDqBC * D * 2;
@@ -340,7 +373,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dq_kernel(
     dof[kk] = buffer_load16(rdo, (uint32_t)my_q * D * 2 + (2 * kk + g) * 16, 0);
   }
   // padded queries get LSE = +inf, hence P = 0
-  const float lse2 = valid_q ? lse[(size_t)tc.bh * N + my_q] * 1.4426950408889634f : INFINITY;
+  const float lse_q = valid_q ? lse2[(size_t)tc.bh * N + my_q] : INFINITY;
   const float dlt = valid_q ? delta[(size_t)tc.bh * N + my_q] : 0.f;
 
   int n_tiles = (N + kDqBC - 1) / kDqBC;
@@ -398,8 +431,8 @@ __global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dq_kernel(
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-          const float p0 = fast_exp2(__builtin_fmaf(s[kb][2 * i], scale_log2, -lse2));
-          const float p1 = fast_exp2(__builtin_fmaf(s[kb][2 * i + 1], scale_log2, -lse2));
+          const float p0 = fast_exp2(__builtin_fmaf(s[kb][2 * i], scale_log2, -lse_q));
+          const float p1 = fast_exp2(__builtin_fmaf(s[kb][2 * i + 1], scale_log2, -lse_q));
           dsk[kb][i] = pack_bf16(p0 * (dp[kb][2 * i] - dlt), p1 * (dp[kb][2 * i + 1] - dlt));
         }
       // dQ^T += K^T dS^T; MFMA u covers keys 16u .. 16u+15
@@ -441,7 +474,7 @@ hipError_t launch_pre_t(const BwdArgs& a) {
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((fa2_bwd_pre_kernel<D>), dim3((unsigned)grid), dim3(kThreads), 0, a.stream,
                      static_cast<const uint16_t*>(a.o), static_cast<const uint16_t*>(a.dout),
-                     a.delta, rows);
+                     a.lse, a.delta, a.lse2, rows);
   return hipGetLastError();
 }
 
@@ -453,7 +486,7 @@ hipError_t launch_dkdv_t(const BwdArgs& a) {
   hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0,
                      a.stream, static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
-                     static_cast<const uint16_t*>(a.dout), a.lse, a.delta,
+                     static_cast<const uint16_t*>(a.dout), a.lse2, a.delta,
                      static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), a.N, n_kblocks,
                      a.B * a.H, a.scale_log2, a.scale);
   return hipGetLastError();
@@ -467,7 +500,7 @@ hipError_t launch_dq_t(const BwdArgs& a) {
   hipLaunchKernelGGL((fa2_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0,
                      a.stream, static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
-                     static_cast<const uint16_t*>(a.dout), a.lse, a.delta,
+                     static_cast<const uint16_t*>(a.dout), a.lse2, a.delta,
                      static_cast<uint16_t*>(a.dq), a.N, n_qblocks, a.B * a.H, a.scale_log2,
                      a.scale);
   return hipGetLastError();

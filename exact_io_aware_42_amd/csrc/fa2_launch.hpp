@@ -30,6 +30,7 @@ struct BwdArgs {
   void* dk;
   void* dv;
   float* delta;  // workspace: D = rowsum(dO * O), fp32 [B, H, N]
+  float* lse2;   // workspace: LSE * log2(e), fp32 [B, H, N]
   int B, H, N, d;
   bool causal;
   float scale;       // softmax_scale

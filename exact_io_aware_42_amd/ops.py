@@ -50,11 +50,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.fa2_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                 i, i, i, i, i, f, vp]
         lib.fa2_bwd.restype = i
-        lib.fa2_bwd_preprocess.argtypes = [vp, vp, vp, i, i, i, i, vp]
+        lib.fa2_bwd_preprocess.argtypes = [vp, vp, vp, vp, sz, i, i, i, i, vp]
         lib.fa2_bwd_preprocess.restype = i
-        lib.fa2_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+        lib.fa2_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, sz, vp, vp, i, i, i, i, i, f, vp]
         lib.fa2_bwd_dkdv.restype = i
-        lib.fa2_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+        lib.fa2_bwd_dq.argtypes = [vp, vp, vp, vp, vp, sz, vp, i, i, i, i, i, f, vp]
         lib.fa2_bwd_dq.restype = i
         lib.fa2_bwd_workspace_bytes.argtypes = [i, i, i, i]
         lib.fa2_bwd_workspace_bytes.restype = sz
@@ -153,56 +153,56 @@ def bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None,
     return dq, dk, dv
 
 
-def _delta_view(workspace: torch.Tensor, B: int, H: int, N: int) -> int:
-    need = B * H * N * 4
-    if workspace.device.type != "cuda" or workspace.numel() * workspace.element_size() < need:
-        raise ValueError("workspace too small for delta [B, H, N] fp32")
-    return workspace.data_ptr()
+def _ws(workspace: torch.Tensor, B: int, H: int, N: int, d: int):
+    need = bwd_workspace_bytes(B, H, N, d)
+    nbytes = workspace.numel() * workspace.element_size()
+    if workspace.device.type != "cuda" or nbytes < need:
+        raise ValueError(f"workspace must be a GPU buffer of at least {need} bytes")
+    return workspace.data_ptr(), nbytes
 
 
-def bwd_preprocess(o, dout, workspace):
-    """delta = rowsum(dout * o) into `workspace` (fp32 [B, H, N] at its start)."""
+def bwd_preprocess(o, dout, lse, workspace):
+    """Fill `workspace` with D = rowsum(dout * o) and LSE * log2(e)."""
     lib = load_library()
     B, H, N, d = o.shape
     _check_tensor(o, "o", (B, H, N, d))
     _check_tensor(dout, "dout", (B, H, N, d), device=o.device)
-    st = lib.fa2_bwd_preprocess(o.data_ptr(), dout.data_ptr(), _delta_view(workspace, B, H, N),
-                                B, H, N, d, _stream_ptr(o.device))
+    _check_tensor(lse, "lse", (B, H, N), dtype=torch.float32, device=o.device)
+    st = lib.fa2_bwd_preprocess(o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
+                                *_ws(workspace, B, H, N, d), B, H, N, d, _stream_ptr(o.device))
     _check(st, "fa2_bwd_preprocess")
     return workspace
 
 
-def bwd_dkdv(q, k, v, dout, lse, workspace, causal=False, scale=None, dk=None, dv=None):
-    """dK, dV from q, k, v, dout, lse and the delta held in `workspace`."""
+def bwd_dkdv(q, k, v, dout, workspace, causal=False, scale=None, dk=None, dv=None):
+    """dK, dV from q, k, v, dout and a workspace filled by bwd_preprocess."""
     lib = load_library()
     B, H, N, d = q.shape
     for t, nm in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
         _check_tensor(t, nm, (B, H, N, d), device=q.device)
-    _check_tensor(lse, "lse", (B, H, N), dtype=torch.float32, device=q.device)
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     _check_tensor(dk, "dk", (B, H, N, d), device=q.device)
     _check_tensor(dv, "dv", (B, H, N, d), device=q.device)
     s = default_scale(d) if scale is None else float(scale)
     st = lib.fa2_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
-                          lse.data_ptr(), _delta_view(workspace, B, H, N), dk.data_ptr(),
-                          dv.data_ptr(), B, H, N, d, int(bool(causal)), s, _stream_ptr(q.device))
+                          *_ws(workspace, B, H, N, d), dk.data_ptr(), dv.data_ptr(),
+                          B, H, N, d, int(bool(causal)), s, _stream_ptr(q.device))
     _check(st, "fa2_bwd_dkdv")
     return dk, dv
 
 
-def bwd_dq(q, k, v, dout, lse, workspace, causal=False, scale=None, dq=None):
-    """dQ from q, k, v, dout, lse and the delta held in `workspace`."""
+def bwd_dq(q, k, v, dout, workspace, causal=False, scale=None, dq=None):
+    """dQ from q, k, v, dout and a workspace filled by bwd_preprocess."""
     lib = load_library()
     B, H, N, d = q.shape
     for t, nm in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
         _check_tensor(t, nm, (B, H, N, d), device=q.device)
-    _check_tensor(lse, "lse", (B, H, N), dtype=torch.float32, device=q.device)
     dq = torch.empty_like(q) if dq is None else dq
     _check_tensor(dq, "dq", (B, H, N, d), device=q.device)
     s = default_scale(d) if scale is None else float(scale)
-    st = lib.fa2_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(), lse.data_ptr(),
-                        _delta_view(workspace, B, H, N), dq.data_ptr(), B, H, N, d,
+    st = lib.fa2_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
+                        *_ws(workspace, B, H, N, d), dq.data_ptr(), B, H, N, d,
                         int(bool(causal)), s, _stream_ptr(q.device))
     _check(st, "fa2_bwd_dq")
     return dq

@@ -66,41 +66,43 @@ fa2_status fa2_fwd(const void* q, const void* k, const void* v, void* o, float* 
                    int B, int H, int N, int d, int causal, float softmax_scale,
                    hipStream_t stream);
 
-/* Bytes of device workspace fa2_bwd needs for these sizes (the row statistic D = rowsum(dO*O)
- * as fp32 [B,H,N], rounded up to 256 bytes). Returns 0 for invalid sizes. */
+/* Bytes of device workspace the backward needs for these sizes: two fp32 [B,H,N] arrays (the
+ * row term D = rowsum(dO*O) and LSE*log2(e)), each rounded up to 256 bytes. Returns 0 for
+ * invalid sizes. */
 size_t fa2_bwd_workspace_bytes(int B, int H, int N, int d);
 
 /* Backward pass. Inputs: q, k, v, the forward output o and its lse (from fa2_fwd with the
  * same causal flag and scale), and the cotangent dout. Writes dq, dk, dv [B,H,N,d] (bf16,
  * accumulated in fp32). workspace: device buffer of at least fa2_bwd_workspace_bytes(...)
  * bytes, owned by the caller; its contents on entry do not matter and are clobbered.
- * Deterministic (no atomics). */
+ * Deterministic (no atomics). Runs fa2_bwd_preprocess, fa2_bwd_dkdv and fa2_bwd_dq below, in
+ * that order, on `stream`. */
 fa2_status fa2_bwd(const void* q, const void* k, const void* v, const void* o,
                    const void* dout, const float* lse, void* dq, void* dk, void* dv,
                    void* workspace, size_t workspace_bytes,
                    int B, int H, int N, int d, int causal, float softmax_scale,
                    hipStream_t stream);
 
-/* The three stages of fa2_bwd, for callers that schedule them separately (fa2_bwd runs them
- * in this order on one stream; the results are identical).
+/* The three stages of fa2_bwd, for callers that schedule or time them separately (the
+ * results are identical to fa2_bwd's). All take the same workspace.
  *
- * fa2_bwd_preprocess: delta [B,H,N] fp32 = rowsum(dout * o), the softmax-gradient row term
- *   D_i = sum_c dO_ic O_ic (it equals sum_j P_ij dP_ij). o and dout as in fa2_bwd; delta is a
- *   caller-owned device buffer of B*H*N floats. */
-fa2_status fa2_bwd_preprocess(const void* o, const void* dout, float* delta,
+ * fa2_bwd_preprocess: fills the workspace with D_i = sum_c dO_ic O_ic (it equals
+ *   sum_j P_ij dP_ij, the row term of the softmax gradient) and LSE_i * log2(e). */
+fa2_status fa2_bwd_preprocess(const void* o, const void* dout, const float* lse,
+                              void* workspace, size_t workspace_bytes,
                               int B, int H, int N, int d, hipStream_t stream);
 
-/* fa2_bwd_dkdv: dk and dv [B,H,N,d] (bf16) from q, k, v, dout, the forward lse and the delta
- *   of fa2_bwd_preprocess. Parallel over blocks of 128 keys; recomputes P block by block. */
+/* fa2_bwd_dkdv: dk and dv [B,H,N,d] (bf16) from q, k, v, dout and a workspace filled by
+ *   fa2_bwd_preprocess. Parallel over blocks of 128 keys; recomputes P block by block. */
 fa2_status fa2_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
-                        const float* lse, const float* delta, void* dk, void* dv,
+                        const void* workspace, size_t workspace_bytes, void* dk, void* dv,
                         int B, int H, int N, int d, int causal, float softmax_scale,
                         hipStream_t stream);
 
 /* fa2_bwd_dq: dq [B,H,N,d] (bf16) from the same inputs. Parallel over blocks of 128 queries;
  *   recomputes P and dP block by block, so no atomics are needed. */
 fa2_status fa2_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
-                      const float* lse, const float* delta, void* dq,
+                      const void* workspace, size_t workspace_bytes, void* dq,
                       int B, int H, int N, int d, int causal, float softmax_scale,
                       hipStream_t stream);
 

@@ -74,7 +74,7 @@ def test_fwd_validation(args, expect):
 def test_bwd_validation_and_workspace():
     lib = _lib()
     ws = lib.fa2_bwd_workspace_bytes(2, 3, 100, 64)
-    assert ws >= 2 * 3 * 100 * 4 and ws % 256 == 0
+    assert ws >= 2 * (2 * 3 * 100 * 4) and ws % 256 == 0
     assert lib.fa2_bwd_workspace_bytes(0, 3, 100, 64) == 0
     assert lib.fa2_bwd_workspace_bytes(1, 1, 100, 80) == 0
     base = [P] * 10
@@ -90,6 +90,17 @@ def test_bwd_validation_and_workspace():
     args[9] = P + 8
     assert lib.fa2_bwd(*args, ws, *ok_sizes, None) == ops.FA2_ERR_INVALID_ARGUMENT
     assert lib.fa2_bwd(*base, ws, 2, 3, 100, 48, 1, 0.125, None) == ops.FA2_ERR_UNSUPPORTED
+    # stage entry points validate the same way
+    assert lib.fa2_bwd_preprocess(P, P, P, P, ws - 1, 2, 3, 100, 64, None) == \
+        ops.FA2_ERR_INVALID_ARGUMENT
+    assert lib.fa2_bwd_preprocess(P, None, P, P, ws, 2, 3, 100, 64, None) == \
+        ops.FA2_ERR_INVALID_ARGUMENT
+    assert lib.fa2_bwd_dkdv(P, P, P, P, P, ws, P, P, 2, 3, 100, 96, 1, 0.1, None) == \
+        ops.FA2_ERR_UNSUPPORTED
+    assert lib.fa2_bwd_dq(P, P, P, P, P, ws, None, 2, 3, 100, 64, 1, 0.1, None) == \
+        ops.FA2_ERR_INVALID_ARGUMENT
+    assert lib.fa2_bwd_dq(P, P, P, P, P, ws, P, 2, 3, 100, 64, 1, -1.0, None) == \
+        ops.FA2_ERR_INVALID_ARGUMENT
 
 
 def schedule_tile_model(wg, n_qblocks, bh_count, heavy_first):

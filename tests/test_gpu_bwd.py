@@ -103,9 +103,9 @@ def test_deterministic_coverage_and_stages(causal):
     g1 = fa2.bwd(q, k, v, o, do, lse, causal=causal, dq=nan(), dk=nan(), dv=nan())
     g2 = fa2.bwd(q, k, v, o, do, lse, causal=causal)
     ws = torch.empty(fa2.bwd_workspace_bytes(*shape), dtype=torch.uint8, device=q.device)
-    fa2.bwd_preprocess(o, do, ws)
-    dk3, dv3 = fa2.bwd_dkdv(q, k, v, do, lse, ws, causal=causal)
-    dq3 = fa2.bwd_dq(q, k, v, do, lse, ws, causal=causal)
+    fa2.bwd_preprocess(o, do, lse, ws)
+    dk3, dv3 = fa2.bwd_dkdv(q, k, v, do, ws, causal=causal)
+    dq3 = fa2.bwd_dq(q, k, v, do, ws, causal=causal)
     torch.cuda.synchronize()
     for a, b, c in zip(g1, g2, (dq3, dk3, dv3)):
         assert torch.isfinite(a.float()).all()
@@ -114,13 +114,21 @@ def test_deterministic_coverage_and_stages(causal):
 
 
 def test_preprocess_matches_rowsum():
+    """The workspace holds D = rowsum(dO * O) and then (at the next 256-byte boundary)
+    LSE * log2(e)."""
     fa2 = _fa2()
     shape = (2, 2, 130, 128)
     bo, bdo = normal_bf16(shape, 8800), normal_bf16(shape, 8801)
     o, do = to_dev(bo), to_dev(bdo)
+    lse = torch.from_numpy(np.random.default_rng(8802).standard_normal((2, 2, 130))
+                           .astype(np.float32)).to(o.device)
     ws = torch.empty(fa2.bwd_workspace_bytes(*shape), dtype=torch.uint8, device=o.device)
-    fa2.bwd_preprocess(o, do, ws)
+    fa2.bwd_preprocess(o, do, lse, ws)
     torch.cuda.synchronize()
-    got = ws[: 2 * 2 * 130 * 4].view(torch.float32).cpu().double().numpy().reshape(2, 2, 130)
+    n = 2 * 2 * 130
+    part = ws.numel() // 2
+    got = ws[: n * 4].view(torch.float32).cpu().double().numpy().reshape(2, 2, 130)
     want = np.sum(bf16_bits_to_f64(bo) * bf16_bits_to_f64(bdo), axis=-1)
     np.testing.assert_allclose(got, want, rtol=1e-5, atol=1e-4)
+    got2 = ws[part: part + n * 4].view(torch.float32).cpu().double().numpy().reshape(2, 2, 130)
+    np.testing.assert_allclose(got2, lse.cpu().double().numpy() * np.log2(np.e), rtol=1e-6)
