@@ -28,6 +28,9 @@ COMMON_FLAGS = [
     "-std=c++17",
     "-fPIC",
     "-Wall",
+    # NaNs are not produced on purpose anywhere in the kernels; without this flag every fmaxf on
+    # an MFMA result is preceded by a canonicalising v_max_f32
+    "-fno-honor-nans",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # MFMA results in VGPRs: softmax reads the score accumulators with plain VALU ops, so
     # AGPR-form MFMAs would need a v_accvgpr_read per element

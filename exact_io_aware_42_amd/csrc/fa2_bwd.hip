@@ -31,15 +31,10 @@ namespace {
 constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 
-// XOR swizzle of 16-byte chunks for tiles read both ways: row-wise by 32-lane MFMA operand
-// reads (8 lanes of one phase take rows kmap(0..7) = {0,1,2,3,8,9,10,11}, one chunk) and by
-// transposing reads (16 lanes take rows 4a..4a+3, two adjacent chunks). ((row & 3) << 1) |
-// bit 3 of row is injective on both row sets, so neither pattern conflicts.
-__device__ __forceinline__ int bswz(int row) { return ((row & 3) << 1) | ((row >> 3) & 1); }
-
 // HBM -> LDS copy of a 64-row bf16 tile [64][D] starting at byte `soff` of buffer `r`, into
-// `dst` (row-major, bswz-swizzled 16-byte chunks). Load r of wave w writes the 1 KiB block
-// 4r + w; the swizzle bits of a row do not depend on r.
+// `dst` (row-major, swz<D>-swizzled 16-byte chunks, conflict-free for both the row-wise MFMA
+// operand reads and the transposing reads). Load r of wave w writes the 1 KiB block 4r + w; the
+// swizzle bits of a row do not depend on r.
 template <int D>
 struct TileLoader {
   static constexpr int DCH = D / 8;
@@ -50,7 +45,7 @@ struct TileLoader {
   __device__ __forceinline__ TileLoader(int wave_, int lane) : wave(wave_) {
     const int p = wave * 64 + lane;
     const int row = p / DCH;
-    off0 = (uint32_t)(row * D * 2 + ((p % DCH) ^ bswz(row)) * 16);
+    off0 = (uint32_t)(row * D * 2 + ((p % DCH) ^ swz<D>(row)) * 16);
   }
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, unsigned char* dst,
                                        uint32_t soff) const {
@@ -61,28 +56,31 @@ struct TileLoader {
   }
 };
 
-// Per-lane byte offsets into a bswz tile for the two read patterns.
+// Per-lane byte offsets into a swizzled tile for the two read patterns.
 template <int D>
 struct TileReads {
-  int rbase[4];  // row-wise operand reads: row 32*blk + kmap(l32), logical chunk 2kk + g
-  int tbase[2];  // transposing reads: row 16u + 8g + 4h + j/4, column 32cb + 16(G%2) + 4(j%4)
+  static constexpr int KK = D / 16, CB = D / 32;
+  int rbase[KK];     // row-wise operand reads: row 32*blk + kmap(l32), logical chunk 2kk + g
+  int tbase[CB][2];  // transposing reads: row 16u + 8g + 4h + j/4, column 32cb + 16(G%2) + 4(j%4)
   __device__ __forceinline__ TileReads(int lane) {
     const int l32 = lane & 31, g = lane >> 5, jl = lane & 15, grp = lane >> 4;
     const int krow = kmap(l32);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) rbase[kk] = krow * D * 2 + ((2 * kk + g) ^ bswz(krow)) * 16;
+    for (int kk = 0; kk < KK; ++kk) rbase[kk] = krow * D * 2 + ((2 * kk + g) ^ swz<D>(krow)) * 16;
 #pragma unroll
-    for (int par = 0; par < 2; ++par) {
-      const int row = 8 * g + jl / 4;
-      const int col = 32 * par + 16 * (grp & 1) + 4 * (jl & 3);
-      tbase[par] = row * D * 2 + (((col >> 3) ^ bswz(row)) * 16) + (col & 7) * 2;
-    }
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int row = 8 * g + 4 * h + jl / 4;
+        const int col = 32 * cb + 16 * (grp & 1) + 4 * (jl & 3);
+        tbase[cb][h] = row * D * 2 + (((col >> 3) ^ swz<D>(row)) * 16) + (col & 7) * 2;
+      }
   }
   __device__ __forceinline__ int row_off(int blk, int kk) const {
-    return rbase[kk & 3] + (kk >> 2) * 128 + blk * 32 * D * 2;
+    return rbase[kk] + blk * 32 * D * 2;
   }
   __device__ __forceinline__ int tr_off(int cb, int u, int h) const {
-    return tbase[cb & 1] + (cb >> 1) * 128 + (16 * u + 4 * h) * D * 2;
+    return tbase[cb][h] + 16 * u * D * 2;
   }
 };
 
@@ -133,9 +131,6 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_pre_kernel(const uint16_t* _
 constexpr int kKvBK = 128;
 constexpr int kKvBQ = 64;
 
-// swizzle of the resident K/V rows: read row-wise with lane = row, 8 consecutive rows per phase
-__device__ __forceinline__ int kvswz(int row) { return row & 7; }
-
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void fa2_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -171,7 +166,7 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_bwd_dkdv_kernel(
   const int key_w0 = key_b0 + wave * 32;
   const int my_key = key_w0 + l32;
 
-  // resident K and V rows of the block: 128 rows each, kvswz-swizzled; block i of 1 KiB holds
+  // resident K and V rows of the block: 128 rows each, swz-swizzled; block i of 1 KiB holds
   // rows (64/DCH)*i .. ; 2*DCH/4 loads per wave per tensor
   {
     constexpr int LOADS = KV_BYTES / (kThreads * 16);
@@ -180,17 +175,17 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_bwd_dkdv_kernel(
     for (int r = 0; r < LOADS; ++r) {
       const int blk = 4 * r + wave;
       const int row = blk * RPB + lane / DCH;
-      const uint32_t off = (uint32_t)(row * D * 2 + ((lane % DCH) ^ kvswz(row)) * 16);
+      const uint32_t off = (uint32_t)(row * D * 2 + ((lane % DCH) ^ swz<D>(row)) * 16);
       buffer_load16_to_lds(rk, smem + blk * 1024, off, (uint32_t)key_b0 * D * 2);
       buffer_load16_to_lds(rv, smem + KV_BYTES + blk * 1024, off, (uint32_t)key_b0 * D * 2);
     }
   }
   // per-lane offset of this wave's K/V fragment: row 32*wave + l32, logical chunk 2kk + g
   const int kvrow = wave * 32 + l32;
-  int kvbase[4];
+  int kvbase[KK];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) kvbase[kk] = kvrow * D * 2 + ((2 * kk + g) ^ kvswz(kvrow)) * 16;
-  auto kv_off = [&](int kk) { return kvbase[kk & 3] + (kk >> 2) * 128; };
+  for (int kk = 0; kk < KK; ++kk) kvbase[kk] = kvrow * D * 2 + ((2 * kk + g) ^ swz<D>(kvrow)) * 16;
+  auto kv_off = [&](int kk) { return kvbase[kk]; };
 
   const int n_qt = (N + kKvBQ - 1) / kKvBQ;
   const int qt_begin = CAUSAL ? key_b0 / kKvBQ : 0;

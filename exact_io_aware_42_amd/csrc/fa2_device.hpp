@@ -104,15 +104,24 @@ __device__ __forceinline__ int kmap(int m) {
   return (m & ~12) | ((m & 4) << 1) | ((m & 8) >> 1);
 }
 
-// XOR swizzle of 16-byte chunks in a K tile row (row-major [keys][d]). The 8 lanes of one
-// ds_read_b128 phase read rows kmap(0..7) (or kmap(8..15)) of the same logical chunk; the
-// swizzle sends them to 8 distinct bank groups.
-__device__ __forceinline__ int kswz(int row) { return (row & 3) | ((row >> 1) & 4); }
-
-// XOR swizzle of 16-byte chunks in a V tile row (row-major [keys][d]). A transposing read
-// covers rows 4a .. 4a+3 and two adjacent chunks (32 bytes) per row; XOR with 2*(row % 4)
-// spreads those 8 chunks over all 32 banks.
-__device__ __forceinline__ int vswz(int row) { return (row & 3) << 1; }
+// XOR swizzle of the 16-byte chunks of a row-major bf16 tile with D columns: physical chunk =
+// logical chunk ^ swz<D>(row). gfx950's LDS has 64 banks of 4 bytes (256 bytes per cycle); a
+// ds_read_b128 serves 16 lanes per cycle and a ds_read_b64_tr_b16 32 lanes. The two read
+// patterns of the kernels are
+//   (a) MFMA operand rows: 16 lanes read one logical chunk of 16 different rows (any 16
+//       consecutive rows, possibly permuted by kmap);
+//   (b) transposing reads: 32 lanes read rows 4a .. 4a+3, four adjacent chunks per row.
+// For D = 128 a row is the whole 256-byte bank window: (a) needs swz injective on 16 rows, (b)
+// needs bits 2-3 of swz to differ across rows 4a .. 4a+3; ((row & 3) << 2) | ((row >> 2) & 3)
+// does both. For D = 64 two rows share the window (row parity picks the half), so swz must be
+// injective on rows of one parity for (a) and differ in bit 2 between rows 4a and 4a+2 (and
+// 4a+1, 4a+3) for (b): (bit 1 of row) << 2 | ((row >> 2) & 3).
+template <int D>
+__device__ __forceinline__ int swz(int row) {
+  static_assert(D == 64 || D == 128, "head dimension");
+  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+}
 
 // Workgroup id -> (query block, batch*head) order. Workgroups are dealt to the 8 XCDs in
 // turn (id % 8), each XCD with its own L2. When the heads divide evenly, XCD x gets whole

@@ -19,7 +19,8 @@
 //    row-major V tile through the transposing LDS read, and each lane's O^T column is its own
 //    query, so the rescale and the final 1/l are per-lane scalars;
 //  * K and V tiles move HBM -> LDS by buffer loads that write LDS directly (no VGPR staging,
-//    zero fill past the sequence end), into XOR-swizzled row-major tiles, double-buffered
+//    zero fill past the sequence end), into row-major tiles whose 16-byte chunks are XOR-
+//    swizzled so both LDS read patterns are free of bank conflicts, double-buffered
 //    (tile j+1 streams in while tile j is computed), one barrier per tile;
 //  * exp2 form: p = exp2(s * scale*log2(e) - m) is one FMA + one v_exp_f32. Masked tiles
 //    (causal diagonal, ragged tail) start their score accumulators at -inf instead of 0 for
@@ -88,16 +89,17 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
 
   // ---- HBM -> LDS tile loads. Load r of wave w writes the 1 KiB block i = 4r + w of the tile
   // (lane l -> chunk p = 64i + l: row p / DCH, physical chunk p % DCH) and fetches the logical
-  // chunk the row's XOR swizzle maps there. With i = 4r + w the swizzle bits of the row do not
-  // depend on r, so one per-lane offset serves every load (r adds a constant).
+  // chunk the row's XOR swizzle maps there. Block 4r + w starts at row 4*(64/DCH)*r + ..., a
+  // multiple of 16, so the swizzle (row bits 0-3) does not depend on r and one per-lane offset
+  // serves every load (r adds a constant).
   constexpr int kRowsPerBlock = 64 / S::DCH;
   uint32_t koff0, voff0;
   {
     const int p = wave * 64 + lane;
     const int row = p / S::DCH;
     const int pc = p % S::DCH;
-    koff0 = (uint32_t)(row * D * 2 + (pc ^ kswz(row)) * 16);
-    voff0 = (uint32_t)(row * D * 2 + (pc ^ vswz(row)) * 16);
+    koff0 = (uint32_t)(row * D * 2 + (pc ^ swz<D>(row)) * 16);
+    voff0 = koff0;
   }
   auto load_k = [&](int j, int slot) {
 #pragma unroll
@@ -112,29 +114,29 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
                            voff0 + r * 4 * kRowsPerBlock * D * 2, (uint32_t)j * kFwdBC * D * 2);
   };
 
-  // ---- per-lane LDS read offsets (bytes within a tile)
-  // K (A operand of S^T): row 32kb + kmap(l32), logical chunk 2kk + g. The swizzle acts on the
-  // low 3 chunk bits only and ignores row bits >= 4, so kb and kk/4 become immediates.
+  // ---- per-lane LDS read offsets (bytes within a tile). The swizzle depends on row bits 0-3
+  // only, so 32-row block kb and 16-row step u become immediates.
+  // K (A operand of S^T): row 32kb + kmap(l32), logical chunk 2kk + g.
   const int krow = kmap(l32);
-  int kbase[4];
+  int kbase[S::KK];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) kbase[kk] = krow * D * 2 + ((2 * kk + g) ^ kswz(krow)) * 16;
-  auto k_off = [&](int kb, int kk) { return kbase[kk & 3] + (kk >> 2) * 128 + kb * 32 * D * 2; };
+  for (int kk = 0; kk < S::KK; ++kk) kbase[kk] = krow * D * 2 + ((2 * kk + g) ^ swz<D>(krow)) * 16;
+  auto k_off = [&](int kb, int kk) { return kbase[kk] + kb * 32 * D * 2; };
   // V^T fragments (A operand of O^T) via the transposing read: 16-lane group G = lane/16 covers
   // d rows c0 = 32cb + 16(G%2) .. +15 and k-slots 8g .. 8g+7 = keys 16u + 8g + 4h + (0..3).
   // Lane j of the group addresses key row 16u + 8g + 4h + j/4, columns c0 + 4(j%4) .. +3.
   const int jl = lane & 15;
   const int grp = lane >> 4;
-  int vbase[2];
+  int vbase[S::CB][2];
 #pragma unroll
-  for (int par = 0; par < 2; ++par) {
-    const int row = 8 * g + jl / 4;                 // + 16u + 4h (multiples of 4) added below
-    const int col = 32 * par + 16 * (grp & 1) + 4 * (jl & 3);
-    vbase[par] = row * D * 2 + (((col >> 3) ^ vswz(row)) * 16) + (col & 7) * 2;
-  }
-  auto v_off = [&](int cb, int u, int h) {
-    return vbase[cb & 1] + (cb >> 1) * 128 + (16 * u + 4 * h) * D * 2;
-  };
+  for (int cb = 0; cb < S::CB; ++cb)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int row = 8 * g + 4 * h + jl / 4;
+      const int col = 32 * cb + 16 * (grp & 1) + 4 * (jl & 3);
+      vbase[cb][h] = row * D * 2 + (((col >> 3) ^ swz<D>(row)) * 16) + (col & 7) * 2;
+    }
+  auto v_off = [&](int cb, int u, int h) { return vbase[cb][h] + 16 * u * D * 2; };
 
   // ---- Q^T fragments (B operand of S^T): lane holds q[my_q][16kk + 8g .. +7]; zeros past N
   u32x4_t qf[S::KK];
