@@ -15,7 +15,8 @@ achieved = its algorithmic FLOP per launch / its mean event-measured duration, a
 dense bf16 MFMA peak of MI355X (2.5 PFLOP/s). `traffic` comes from committed rocprofv3
 FETCH_SIZE / WRITE_SIZE counter summaries under profiles/ (null if the kernel source changed
 since they were taken). `cpu_baseline` times the CPU float64 oracle on a bounded sample of
-the same workload (whole heads) on the host cores.
+the same workload (whole heads) on the host cores. `forward_workloads` adds the forward
+kernel's TFLOP/s on the forward-only workloads (not part of `value`).
 
 Prints ONE JSON line (rank 0).
 """
@@ -45,6 +46,8 @@ def parse_args():
     ap.add_argument("--causal", choices=("default", "causal", "full"), default="default")
     ap.add_argument("--direction", choices=("both", "fwd"), default="both")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-fwd-sweep", action="store_true",
+                    help="skip the forward-only timing of the other workloads")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time budget for the oracle baseline sample")
     return ap.parse_args()
@@ -96,6 +99,46 @@ def cpu_baseline(w, causal, with_bwd, budget_s):
                    f"{'forward+backward' if with_bwd else 'forward'}, float64 numpy, "
                    f"{el:.1f} s"),
     }
+
+
+FWD_SWEEP = ((2, False), (2, True), (3, True), (4, True), (4, False))
+
+
+def forward_sweep(fa2, torch, dev, reps=5):
+    """Forward-only TFLOP/s of the forward workloads (B=8 H=32 N=2048 d=64 both masks,
+    B=4 H=16 N=4096 d=128 causal, B=1 H=16 N=16384 d=128 both masks), timed with HIP events
+    on the launch stream after two warm-up calls."""
+    import numpy as np
+
+    from exact_io_aware_42_amd.inputs import WORKLOADS, default_scale, workload_tensors
+
+    res = {}
+    stream = torch.cuda.current_stream(dev)
+    cache = {}
+    for wid, causal in FWD_SWEEP:
+        w = WORKLOADS[wid]
+        if wid not in cache:
+            cache.clear()
+            t = workload_tensors(w)
+            cache[wid] = [torch.from_numpy(t[x].view(np.int16)).view(torch.bfloat16).to(dev)
+                          for x in ("q", "k", "v")]
+        q, k, v = cache[wid]
+        o = torch.empty_like(q)
+        lse = torch.empty(w.shape[:3], dtype=torch.float32, device=dev)
+        for _ in range(2):
+            fa2.fwd(q, k, v, causal=causal, scale=default_scale(w.d), out=o, lse=lse)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record(stream)
+        for r in range(reps):
+            fa2.fwd(q, k, v, causal=causal, scale=default_scale(w.d), out=o, lse=lse)
+            ev[r + 1].record(stream)
+        torch.cuda.synchronize()
+        ms = sum(ev[r].elapsed_time(ev[r + 1]) for r in range(reps)) / reps
+        tf = fwd_flop(*w.shape, causal) / (ms * 1e-3) / 1e12
+        res[f"{w.name} {'causal' if causal else 'non-causal'}"] = {
+            "ms": round(ms, 4), "tflops": round(tf, 1),
+            "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+    return res
 
 
 def main():
@@ -219,6 +262,8 @@ def main():
             "traffic": traffic,
         },
     }
+    if not args.no_fwd_sweep:
+        out["forward_workloads"] = forward_sweep(fa2, torch, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, causal, with_bwd, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -2,6 +2,9 @@
 
     # a plain device copy of known size, to calibrate the counters
     python -m exact_io_aware_42_amd.profiling copy --mib 256
+    # turn a rocprofv3 --stats kernel_stats.csv into a short text summary
+    python -m exact_io_aware_42_amd.profiling stats --csv run_kernel_stats.csv \
+        --out profiles/kernels_<workload>.txt --title "..." --cmd "rocprofv3 ..."
     # turn counter CSVs into profiles/traffic_<kernel>_<workload>.txt
     python -m exact_io_aware_42_amd.profiling traffic --kernel fa2_fwd_kernel \\
         --workload w4_full --fetch run_fetch.csv --write run_write.csv \\
@@ -87,6 +90,38 @@ def copy_main(mib: int):
     print(f"copied {mib} MiB three times", flush=True)
 
 
+def short_name(name: str) -> str:
+    """'void fa2::(anonymous namespace)::fa2_fwd_kernel<128, true>(...)' -> 'fa2_fwd_kernel<128,
+    true>'."""
+    head = name.split("(", 1)[0] if "(anonymous" not in name else name
+    head = head.replace("void ", "").replace("fa2::(anonymous namespace)::", "")
+    depth, out = 0, []
+    for ch in head:
+        if ch == "(" and depth == 0:
+            break
+        depth += ch == "<"
+        depth -= ch == ">"
+        out.append(ch)
+    return "".join(out).strip()
+
+
+def stats_main(a):
+    rows = []
+    with open(a.csv) as f:
+        for r in csv.DictReader(f):
+            rows.append((short_name(r["Name"]), int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                         float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3,
+                         float(r["Percentage"])))
+    rows.sort(key=lambda x: -x[5])
+    with open(a.out, "w") as f:
+        f.write(f"# rocprofv3 kernel statistics: {a.title}\n")
+        f.write(f"# command: {a.cmd}\n")
+        f.write("# kernel | calls | average us | min us | max us | share of GPU time\n")
+        for n, c, avg, mn, mx, pct in rows:
+            f.write(f"{n} | {c} | {avg:.1f} | {mn:.1f} | {mx:.1f} | {pct:.1f}%\n")
+    print(open(a.out).read())
+
+
 def traffic_main(a):
     fetch = statistics.median(counter_values(a.fetch, "FETCH_SIZE", a.kernel))
     write = statistics.median(counter_values(a.write, "WRITE_SIZE", a.kernel))
@@ -115,9 +150,14 @@ def traffic_main(a):
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
-    sub = ap.add_subparsers(dest="cmd", required=True)
+    sub = ap.add_subparsers(dest="sub", required=True)
     c = sub.add_parser("copy")
     c.add_argument("--mib", type=int, default=256)
+    st = sub.add_parser("stats")
+    st.add_argument("--csv", required=True)
+    st.add_argument("--out", required=True)
+    st.add_argument("--title", required=True)
+    st.add_argument("--cmd", required=True)
     t = sub.add_parser("traffic")
     t.add_argument("--kernel", required=True, choices=sorted(KERNEL_SOURCES))
     t.add_argument("--workload", required=True)
@@ -130,8 +170,10 @@ def main(argv=None):
     t.add_argument("--cmd-fetch", default="")
     t.add_argument("--cmd-write", default="")
     a = ap.parse_args(argv)
-    if a.cmd == "copy":
+    if a.sub == "copy":
         copy_main(a.mib)
+    elif a.sub == "stats":
+        stats_main(a)
     else:
         traffic_main(a)
 
