@@ -14,8 +14,9 @@
 // Three kernels, deterministic (no atomics):
 //   fa2_bwd_pre_kernel   D = rowsum(dO * O) and LSE*log2(e), fp32 [B, H, N] (HBM-bound).
 //   fa2_bwd_dkdv_kernel  grid over (key block of 128, head, batch): the block's K and V rows
-//                        stay in LDS, each wave accumulates dK, dV for its 32 keys in registers,
-//                        and 64-query tiles of Q, dO, LSE and D stream through LDS.
+//                        stay in LDS, 64-query tiles of Q, dO, LSE and D stream through LDS, and
+//                        two waves per 32 keys (one per half of each query tile) accumulate
+//                        dK, dV in registers; the pair's sums meet in LDS at the end.
 //   fa2_bwd_dq_kernel    grid over (query block of 128, head, batch): the forward's layout
 //                        (lane = query), recomputing S^T and dP^T per key tile and
 //                        accumulating dQ^T = K^T dS^T.
@@ -33,13 +34,16 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 // HBM -> LDS copy of a 64-row bf16 tile [64][D] starting at byte `soff` of buffer `r`, into
 // `dst` (row-major, swz<D>-swizzled 16-byte chunks, conflict-free for both the row-wise MFMA
-// operand reads and the transposing reads). Load r of wave w writes the 1 KiB block 4r + w; the
-// swizzle bits of a row do not depend on r.
-template <int D>
+// operand reads and the transposing reads), by a workgroup of NT threads. Load i of wave w writes
+// the 1 KiB block (NT/64)i + w; block starts advance by a multiple of 16 rows per i, so the
+// swizzle bits of a row do not depend on i.
+template <int D, int NT = kThreads>
 struct TileLoader {
   static constexpr int DCH = D / 8;
-  static constexpr int LOADS = 64 * D * 2 / (kThreads * 16);
+  static constexpr int WAVES = NT / 64;
+  static constexpr int LOADS = 64 * D * 2 / (NT * 16);
   static constexpr int ROWS_PER_BLOCK = 64 / DCH;
+  static_assert(LOADS >= 1 && (WAVES * ROWS_PER_BLOCK) % 16 == 0, "tile loader shape");
   uint32_t off0;
   int wave;
   __device__ __forceinline__ TileLoader(int wave_, int lane) : wave(wave_) {
@@ -51,8 +55,8 @@ struct TileLoader {
                                        uint32_t soff) const {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i)
-      buffer_load16_to_lds(r, dst + (4 * i + wave) * 1024, off0 + i * 4 * ROWS_PER_BLOCK * D * 2,
-                           soff);
+      buffer_load16_to_lds(r, dst + (WAVES * i + wave) * 1024,
+                           off0 + i * WAVES * ROWS_PER_BLOCK * D * 2, soff);
   }
 };
 
@@ -122,17 +126,20 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_pre_kernel(const uint16_t* _
 }
 
 // ---------------------------------------------------------------------------------------
-// dK, dV. Workgroup = 4 waves x 32 keys = 128 keys, whose K and V rows stay in LDS for the
-// whole kernel; query tiles of 64 (two 32-row MFMA blocks) stream through a second LDS ring.
-// S = Q K^T and dP = dO V^T come out with lane = key and registers = queries (kmap order), so
-// P and dS are directly the B operands of dV^T = dO^T P and dK^T = Q^T dS; dO^T and Q^T
-// fragments come from the row-major tiles through transposing reads. Each K/V fragment read
-// from LDS feeds both 32-query blocks.
+// dK, dV. Workgroup = 8 waves over 128 keys, whose K and V rows stay in LDS for the whole
+// kernel; query tiles of 64 stream through a second LDS ring. Waves w and w+4 share the 32 keys
+// 32(w%4) .. +31 and split each query tile: wave w takes queries 0..31, wave w+4 queries 32..63
+// (two waves per SIMD, each with one 32x32 S and dP block). S = Q K^T and dP = dO V^T come out
+// with lane = key and registers = queries (kmap order), so P and dS are directly the B operands
+// of dV^T = dO^T P and dK^T = Q^T dS; the dO^T and Q^T fragments come from the row-major tiles
+// through transposing reads. The two partial dK, dV of a key group are summed through LDS at the
+// end (each wave of the pair finishes one of the two).
 constexpr int kKvBK = 128;
 constexpr int kKvBQ = 64;
+constexpr int kKvThreads = 512;
 
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 1) void fa2_bwd_dkdv_kernel(
+__global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse2, const float* __restrict__ delta, uint16_t* __restrict__ dk,
@@ -143,11 +150,17 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_bwd_dkdv_kernel(
   constexpr int KV_BYTES = kKvBK * D * 2;
   constexpr int STAGE = 2 * TILE + 2 * kKvBQ * 4;  // Q, dO, LSE*log2(e), D
   constexpr int RING0 = 2 * KV_BYTES;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[RING0 + 2 * STAGE];
+  constexpr int MAIN_BYTES = RING0 + 2 * STAGE;
+  constexpr int ACC_BYTES = CB * 16 * 64 * 4;   // one wave's dK (or dV) accumulator
+  constexpr int XCH_BYTES = 8 * ACC_BYTES;      // combine area, reuses the main area
+  constexpr int SMEM = MAIN_BYTES > XCH_BYTES ? MAIN_BYTES : XCH_BYTES;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kw = wave & 3;   // key group
+  const int hq = wave >> 2;  // query half of each tile
   const int l32 = lane & 31;
   const int g = lane >> 5;
 
@@ -163,33 +176,32 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_bwd_dkdv_kernel(
   const __amdgpu_buffer_rsrc_t rd = make_rsrc(delta + (size_t)tc.bh * N, (uint32_t)N * 4);
 
   const int key_b0 = tc.qb * kKvBK;
-  const int key_w0 = key_b0 + wave * 32;
+  const int key_w0 = key_b0 + kw * 32;
   const int my_key = key_w0 + l32;
 
-  // resident K and V rows of the block: 128 rows each, swz-swizzled; block i of 1 KiB holds
-  // rows (64/DCH)*i .. ; 2*DCH/4 loads per wave per tensor
+  // resident K and V rows of the block: 128 rows each, swz-swizzled; 1 KiB block i holds rows
+  // (64/DCH)*i ..
   {
-    constexpr int LOADS = KV_BYTES / (kThreads * 16);
+    constexpr int LOADS = KV_BYTES / (kKvThreads * 16);
     constexpr int RPB = 64 / DCH;
 #pragma unroll
     for (int r = 0; r < LOADS; ++r) {
-      const int blk = 4 * r + wave;
+      const int blk = 8 * r + wave;
       const int row = blk * RPB + lane / DCH;
       const uint32_t off = (uint32_t)(row * D * 2 + ((lane % DCH) ^ swz<D>(row)) * 16);
       buffer_load16_to_lds(rk, smem + blk * 1024, off, (uint32_t)key_b0 * D * 2);
       buffer_load16_to_lds(rv, smem + KV_BYTES + blk * 1024, off, (uint32_t)key_b0 * D * 2);
     }
   }
-  // per-lane offset of this wave's K/V fragment: row 32*wave + l32, logical chunk 2kk + g
-  const int kvrow = wave * 32 + l32;
+  // per-lane offset of this wave's K/V fragment: row 32*kw + l32, logical chunk 2kk + g
+  const int kvrow = kw * 32 + l32;
   int kvbase[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk) kvbase[kk] = kvrow * D * 2 + ((2 * kk + g) ^ swz<D>(kvrow)) * 16;
-  auto kv_off = [&](int kk) { return kvbase[kk]; };
 
   const int n_qt = (N + kKvBQ - 1) / kKvBQ;
   const int qt_begin = CAUSAL ? key_b0 / kKvBQ : 0;
-  const TileLoader<D> ld(wave, lane);
+  const TileLoader<D, kKvThreads> ld(wave, lane);
   const TileReads<D> rd_off(lane);
 
   auto load_stage = [&](int it, int stage) {
@@ -222,82 +234,72 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_bwd_dkdv_kernel(
   for (int it = qt_begin; it < n_qt; ++it) {
     const int stage = (it - qt_begin) & 1;
     if (it + 1 < n_qt) load_stage(it + 1, stage ^ 1);
-    const int q0 = it * kKvBQ;
-    // every query of the tile precedes every key of the wave: fully masked
-    const bool skip = CAUSAL && (q0 + kKvBQ - 1 < key_w0);
+    const int q0 = it * kKvBQ + 32 * hq;  // this wave's 32 queries
+    // every query of the half precedes every key of the wave: fully masked
+    const bool skip = CAUSAL && (q0 + 31 < key_w0);
     if (!skip) {
       const unsigned char* st = smem + RING0 + stage * STAGE;
       const unsigned char* tq = st;
       const unsigned char* tdo = st + TILE;
       const float* tl = reinterpret_cast<const float*>(st + 2 * TILE);
       const float* tdl = tl + kKvBQ;
-      const bool masked = (q0 + kKvBQ > N) || (CAUSAL && q0 < key_w0 + 31);
+      const bool masked = (q0 + 32 > N) || (CAUSAL && q0 < key_w0 + 31);
 
-      f32x16_t s[2], dp[2];
+      f32x16_t s, dp = f32x16_t{};
+      if (masked) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        if (masked) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int qi = q0 + 32 * mb + 16 * (i / 8) + 8 * g + (i % 8);
-            s[mb][i] = (qi >= N || (CAUSAL && my_key > qi)) ? -INFINITY : 0.f;
-          }
-        } else {
-          s[mb] = f32x16_t{};
+        for (int i = 0; i < 16; ++i) {
+          const int qi = q0 + 16 * (i / 8) + 8 * g + (i % 8);
+          s[i] = (qi >= N || (CAUSAL && my_key > qi)) ? -INFINITY : 0.f;
         }
-        dp[mb] = f32x16_t{};
+      } else {
+        s = f32x16_t{};
       }
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(smem + kv_off(kk));
-        const u32x4_t vf = *reinterpret_cast<const u32x4_t*>(smem + KV_BYTES + kv_off(kk));
+        const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(smem + kvbase[kk]);
+        const u32x4_t vf = *reinterpret_cast<const u32x4_t*>(smem + KV_BYTES + kvbase[kk]);
+        const u32x4_t aq = *reinterpret_cast<const u32x4_t*>(tq + rd_off.row_off(hq, kk));
+        const u32x4_t ad = *reinterpret_cast<const u32x4_t*>(tdo + rd_off.row_off(hq, kk));
+        s = mfma32(aq, kf, s);
+        dp = mfma32(ad, vf, dp);
+      }
+      // P = exp2(s*c - LSE*log2e), dS = P * (dP - D); register i is query
+      // q0 + 16(i/8) + 8g + i%8
+      uint32_t pk[8], dsk[8];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          const u32x4_t aq = *reinterpret_cast<const u32x4_t*>(tq + rd_off.row_off(mb, kk));
-          s[mb] = mfma32(aq, kf, s[mb]);
-          const u32x4_t ad = *reinterpret_cast<const u32x4_t*>(tdo + rd_off.row_off(mb, kk));
-          dp[mb] = mfma32(ad, vf, dp[mb]);
+      for (int hf = 0; hf < 2; ++hf) {
+        const int qo = 32 * hq + 16 * hf + 8 * g;
+        const f32x4_t l0 = *reinterpret_cast<const f32x4_t*>(tl + qo);
+        const f32x4_t l1 = *reinterpret_cast<const f32x4_t*>(tl + qo + 4);
+        const f32x4_t d0 = *reinterpret_cast<const f32x4_t*>(tdl + qo);
+        const f32x4_t d1 = *reinterpret_cast<const f32x4_t*>(tdl + qo + 4);
+        float p[8], ds[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float lv = e < 4 ? l0[e] : l1[e - 4];
+          const float dv_ = e < 4 ? d0[e] : d1[e - 4];
+          p[e] = fast_exp2(__builtin_fmaf(s[8 * hf + e], scale_log2, -lv));
+          ds[e] = p[e] * (dp[8 * hf + e] - dv_);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pk[4 * hf + e] = pack_bf16(p[2 * e], p[2 * e + 1]);
+          dsk[4 * hf + e] = pack_bf16(ds[2 * e], ds[2 * e + 1]);
         }
       }
-      // P = exp2(s*c - LSE*log2e), dS = P * (dP - D); register i of block mb is query
-      // 32mb + 16(i/8) + 8g + i%8
+      // dV^T += dO^T P and dK^T += Q^T dS over the wave's 32 queries (k-steps t = 2hq + hf)
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        uint32_t pk[8], dsk[8];
+      for (int hf = 0; hf < 2; ++hf) {
+        const int t = 2 * hq + hf;
+        const u32x4_t bp = {pk[4 * hf + 0], pk[4 * hf + 1], pk[4 * hf + 2], pk[4 * hf + 3]};
+        const u32x4_t bs = {dsk[4 * hf + 0], dsk[4 * hf + 1], dsk[4 * hf + 2], dsk[4 * hf + 3]};
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const int qo = 32 * mb + 16 * hf + 8 * g;
-          const f32x4_t l0 = *reinterpret_cast<const f32x4_t*>(tl + qo);
-          const f32x4_t l1 = *reinterpret_cast<const f32x4_t*>(tl + qo + 4);
-          const f32x4_t d0 = *reinterpret_cast<const f32x4_t*>(tdl + qo);
-          const f32x4_t d1 = *reinterpret_cast<const f32x4_t*>(tdl + qo + 4);
-          float p[8], ds[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float lv = e < 4 ? l0[e] : l1[e - 4];
-            const float dv_ = e < 4 ? d0[e] : d1[e - 4];
-            p[e] = fast_exp2(__builtin_fmaf(s[mb][8 * hf + e], scale_log2, -lv));
-            ds[e] = p[e] * (dp[mb][8 * hf + e] - dv_);
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            pk[4 * hf + e] = pack_bf16(p[2 * e], p[2 * e + 1]);
-            dsk[4 * hf + e] = pack_bf16(ds[2 * e], ds[2 * e + 1]);
-          }
-        }
-        // dV^T += dO^T P and dK^T += Q^T dS over this block's 32 queries (k-steps t = 2mb + hf)
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const int t = 2 * mb + hf;
-          const u32x4_t bp = {pk[4 * hf + 0], pk[4 * hf + 1], pk[4 * hf + 2], pk[4 * hf + 3]};
-          const u32x4_t bs = {dsk[4 * hf + 0], dsk[4 * hf + 1], dsk[4 * hf + 2], dsk[4 * hf + 3]};
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb) {
-            const u32x4_t ao = tr_operand(tdo, rd_off.tr_off(cb, t, 0), rd_off.tr_off(cb, t, 1));
-            dvacc[cb] = mfma32(ao, bp, dvacc[cb]);
-            const u32x4_t aq = tr_operand(tq, rd_off.tr_off(cb, t, 0), rd_off.tr_off(cb, t, 1));
-            dkacc[cb] = mfma32(aq, bs, dkacc[cb]);
-          }
+        for (int cb = 0; cb < CB; ++cb) {
+          const u32x4_t ao = tr_operand(tdo, rd_off.tr_off(cb, t, 0), rd_off.tr_off(cb, t, 1));
+          dvacc[cb] = mfma32(ao, bp, dvacc[cb]);
+          const u32x4_t aq = tr_operand(tq, rd_off.tr_off(cb, t, 0), rd_off.tr_off(cb, t, 1));
+          dkacc[cb] = mfma32(aq, bs, dkacc[cb]);
         }
       }
     }
@@ -305,21 +307,46 @@ __global__ __launch_bounds__(kThreads, 1) void fa2_bwd_dkdv_kernel(
     __syncthreads();
   }
 
-  // dK = scale * dK_acc, dV = dV_acc. Lane holds key my_key, columns 32cb + 8t + 4g + 0..3.
+  // Combine the pair's partial sums through LDS (the loop ended with a barrier, so the tiles are
+  // dead): wave (kw, 0) hands over dV and finishes dK, wave (kw, 1) hands over dK and finishes
+  // dV. Slot of wave w: ACC_BYTES at w * ACC_BYTES, register 4r..4r+3 of lane l at 16(64r + l).
+  {
+    f32x16_t* give = hq == 0 ? dvacc : dkacc;
+    unsigned char* mine = smem + wave * ACC_BYTES;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        *reinterpret_cast<f32x4_t*>(mine + 16 * (64 * (4 * cb + r) + lane)) =
+            f32x4_t{give[cb][4 * r], give[cb][4 * r + 1], give[cb][4 * r + 2], give[cb][4 * r + 3]};
+  }
+  __syncthreads();
+  f32x16_t* keep = hq == 0 ? dkacc : dvacc;
+  {
+    const unsigned char* other = smem + (wave ^ 4) * ACC_BYTES;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const f32x4_t x = *reinterpret_cast<const f32x4_t*>(other + 16 * (64 * (4 * cb + r) + lane));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) keep[cb][4 * r + e] += x[e];
+      }
+  }
+
+  // dK = scale * dK_acc (wave kw, 0), dV = dV_acc (wave kw, 1). Lane holds key my_key, columns
+  // 32cb + 8t + 4g + 0..3.
   if (my_key < N) {
-    uint16_t* dkrow = dk + head_off + (size_t)my_key * D;
-    uint16_t* dvrow = dv + head_off + (size_t)my_key * D;
+    const float mul = hq == 0 ? scale : 1.f;
+    uint16_t* row = (hq == 0 ? dk : dv) + head_off + (size_t)my_key * D;
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         const int c = cb * 32 + 8 * t + 4 * g;
-        *reinterpret_cast<u32x2_t*>(dkrow + c) =
-            u32x2_t{pack_bf16(dkacc[cb][4 * t] * scale, dkacc[cb][4 * t + 1] * scale),
-                    pack_bf16(dkacc[cb][4 * t + 2] * scale, dkacc[cb][4 * t + 3] * scale)};
-        *reinterpret_cast<u32x2_t*>(dvrow + c) =
-            u32x2_t{pack_bf16(dvacc[cb][4 * t], dvacc[cb][4 * t + 1]),
-                    pack_bf16(dvacc[cb][4 * t + 2], dvacc[cb][4 * t + 3])};
+        *reinterpret_cast<u32x2_t*>(row + c) =
+            u32x2_t{pack_bf16(keep[cb][4 * t] * mul, keep[cb][4 * t + 1] * mul),
+                    pack_bf16(keep[cb][4 * t + 2] * mul, keep[cb][4 * t + 3] * mul)};
       }
   }
 }
@@ -478,7 +505,7 @@ hipError_t launch_dkdv_t(const BwdArgs& a) {
   const int n_kblocks = (a.N + kKvBK - 1) / kKvBK;
   const long long grid = (long long)n_kblocks * a.B * a.H;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kKvThreads), 0,
                      a.stream, static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                      static_cast<const uint16_t*>(a.dout), a.lse2, a.delta,
