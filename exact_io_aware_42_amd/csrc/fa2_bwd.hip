@@ -164,8 +164,9 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
   const int l32 = lane & 31;
   const int g = lane >> 5;
 
-  // causal: key block 0 sees every query tile, so ascending order is heaviest first
-  const TileCoord tc = schedule_tile(blockIdx.x, n_kblocks, bh_count, false);
+  // causal: key block 0 sees every query tile, so ascending order is longest first
+  const TileCoord tc = schedule_tile<CAUSAL ? Order::kLongAscending : Order::kHeadMajor>(
+      blockIdx.x, n_kblocks, bh_count);
   const size_t head_off = (size_t)tc.bh * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + head_off, head_bytes);
@@ -375,7 +376,8 @@ __global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dq_kernel(
   const int l32 = lane & 31;
   const int g = lane >> 5;
 
-  const TileCoord tc = schedule_tile(blockIdx.x, n_qblocks, bh_count, CAUSAL);
+  const TileCoord tc = schedule_tile<CAUSAL ? Order::kLongDescending : Order::kHeadMajor>(
+      blockIdx.x, n_qblocks, bh_count);
   const size_t head_off = (size_t)tc.bh * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + head_off, head_bytes);

@@ -123,28 +123,42 @@ __device__ __forceinline__ int swz(int row) {
   return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
 
-// Workgroup id -> (query block, batch*head) order. Workgroups are dealt to the 8 XCDs in
-// turn (id % 8), each XCD with its own L2. When the heads divide evenly, XCD x gets whole
-// heads x, x+8, ... and runs one head's query blocks back to back, so K/V tiles of a head are
-// re-read from that XCD's L2. With `heavy_first` (causal) the longest query blocks start first.
+// Workgroup id -> (block, batch*head) order. Workgroups are dealt to the 8 XCDs in turn
+// (id % 8), each XCD with its own L2; when the heads divide evenly, XCD x gets the heads
+// x, x+8, ... only.
+//  * kHeadMajor (equal-length blocks, no mask): an XCD runs one head's blocks back to back,
+//    so that head's K/V tiles are re-read from its L2.
+//  * kLongDescending / kLongAscending (causal: block lengths differ): an XCD deals the blocks
+//    of all its heads longest first (rank-major over its heads: a list schedule in
+//    longest-processing-time order, so no long block starts near the end). Descending: the
+//    highest block index is the longest (query blocks of the forward and dQ); ascending: the
+//    lowest is (key blocks of dK/dV). Blocks of one head that run together walk the same K/V
+//    (or Q/dO) tiles in step, which keeps the L2 working set small.
+enum class Order { kHeadMajor, kLongDescending, kLongAscending };
 struct TileCoord {
   int qb;
   int bh;
 };
-__device__ __forceinline__ TileCoord schedule_tile(int wg, int n_qblocks, int bh_count,
-                                                   bool heavy_first) {
-  int qr, bh;
+template <Order O>
+__device__ __forceinline__ TileCoord schedule_tile(int wg, int n_blocks, int bh_count) {
+  int r, bh;
   if ((bh_count & 7) == 0) {
     const int xcd = wg & 7;
     const int j = wg >> 3;
-    bh = (j / n_qblocks) * 8 + xcd;
-    qr = j % n_qblocks;
+    if constexpr (O == Order::kHeadMajor) {
+      bh = (j / n_blocks) * 8 + xcd;
+      r = j % n_blocks;
+    } else {
+      const int hpx = bh_count >> 3;
+      bh = (j % hpx) * 8 + xcd;
+      r = j / hpx;
+    }
   } else {
     bh = wg % bh_count;
-    qr = wg / bh_count;
+    r = wg / bh_count;
   }
   TileCoord t;
-  t.qb = heavy_first ? (n_qblocks - 1 - qr) : qr;
+  t.qb = O == Order::kLongDescending ? (n_blocks - 1 - r) : r;
   t.bh = bh;
   return t;
 }

@@ -71,7 +71,8 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
   const int l32 = lane & 31;
   const int g = lane >> 5;
 
-  const TileCoord tc = schedule_tile(blockIdx.x, n_qblocks, bh_count, CAUSAL);
+  const TileCoord tc = schedule_tile<CAUSAL ? Order::kLongDescending : Order::kHeadMajor>(
+      blockIdx.x, n_qblocks, bh_count);
   const size_t head_off = (size_t)tc.bh * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + head_off, head_bytes);

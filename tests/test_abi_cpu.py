@@ -103,35 +103,66 @@ def test_bwd_validation_and_workspace():
         ops.FA2_ERR_INVALID_ARGUMENT
 
 
-def schedule_tile_model(wg, n_qblocks, bh_count, heavy_first):
-    """Python model of the kernels' workgroup -> (query block, batch*head) mapping."""
+HEAD_MAJOR, LONG_DESC, LONG_ASC = "head_major", "long_desc", "long_asc"
+
+
+def schedule_tile_model(wg, n_blocks, bh_count, order):
+    """Python model of the kernels' workgroup -> (block, batch*head) mapping."""
     if bh_count % 8 == 0:
         xcd, j = wg % 8, wg // 8
-        bh = (j // n_qblocks) * 8 + xcd
-        qr = j % n_qblocks
+        if order == HEAD_MAJOR:
+            bh, r = (j // n_blocks) * 8 + xcd, j % n_blocks
+        else:
+            hpx = bh_count // 8
+            bh, r = (j % hpx) * 8 + xcd, j // hpx
     else:
-        bh, qr = wg % bh_count, wg // bh_count
-    return (n_qblocks - 1 - qr if heavy_first else qr), bh
+        bh, r = wg % bh_count, wg // bh_count
+    return (n_blocks - 1 - r if order == LONG_DESC else r), bh
+
+
+def causal_work(qb, order):
+    """Relative length of block qb (16 blocks): the forward/dQ block qb sees qb+1 key blocks,
+    the dK/dV key block qb sees 16-qb query blocks."""
+    return qb + 1 if order == LONG_DESC else 16 - qb
 
 
 @pytest.mark.parametrize("nq,bh", [(2, 2), (16, 256), (32, 64), (128, 16), (16, 64), (3, 5),
                                    (1, 8), (7, 24)])
-@pytest.mark.parametrize("heavy", [False, True])
-def test_schedule_covers_every_tile_once(nq, bh, heavy):
+@pytest.mark.parametrize("order", [HEAD_MAJOR, LONG_DESC, LONG_ASC])
+def test_schedule_covers_every_tile_once(nq, bh, order):
     seen = set()
     for wg in range(nq * bh):
-        qb, h = schedule_tile_model(wg, nq, bh, heavy)
+        qb, h = schedule_tile_model(wg, nq, bh, order)
         assert 0 <= qb < nq and 0 <= h < bh
         seen.add((qb, h))
     assert len(seen) == nq * bh
     if bh % 8 == 0:
-        # every head's query blocks run on one XCD (workgroup id mod 8)
+        # every head's blocks run on one XCD (workgroup id mod 8)
         for wg in range(nq * bh):
-            assert schedule_tile_model(wg, nq, bh, heavy)[1] % 8 == wg % 8
-    if heavy:
-        # per XCD, a head's blocks start with the longest (highest index) one
-        firsts = {}
-        for wg in range(nq * bh):
-            qb, h = schedule_tile_model(wg, nq, bh, heavy)
-            firsts.setdefault(h, qb)
-        assert all(v == nq - 1 for v in firsts.values())
+            assert schedule_tile_model(wg, nq, bh, order)[1] % 8 == wg % 8
+    if order != HEAD_MAJOR:
+        # per XCD, blocks come in non-increasing length order across all of its heads
+        for x in range(8):
+            lens = [causal_work(schedule_tile_model(wg, nq, bh, order)[0] * 16 // nq, order)
+                    for wg in range(x, nq * bh, 8)]
+            assert lens == sorted(lens, reverse=True)
+
+
+def _makespan(order, nq=16, bh=64, slots=64):
+    """Greedy list schedule of one XCD's blocks on `slots` workgroup slots."""
+    import heapq
+    free = [0.0] * slots
+    for wg in range(0, nq * bh, 8):
+        qb, _ = schedule_tile_model(wg, nq, bh, order)
+        t = heapq.heappop(free)
+        heapq.heappush(free, t + causal_work(qb, LONG_DESC))
+    return max(free)
+
+
+def test_longest_first_shortens_the_causal_tail():
+    """For the causal forward with 8 heads per XCD, dealing all heads' blocks longest first
+    ends within a few percent of the ideal (total work / slots); head by head it does not."""
+    total = 8 * sum(range(1, 17))
+    ideal = total / 64
+    assert _makespan(LONG_DESC) <= 1.15 * ideal
+    assert _makespan(LONG_DESC) < _makespan(HEAD_MAJOR)
