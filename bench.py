@@ -40,8 +40,8 @@ METRIC = "attention fwd/bwd TFLOP/s (bf16, causal+non-causal) and % of MFMA peak
 def parse_args():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", type=int, default=5)
     ap.add_argument("--causal", choices=("default", "causal", "full"), default="default")
     ap.add_argument("--direction", choices=("both", "fwd"), default="both")
@@ -104,33 +104,40 @@ def cpu_baseline(w, causal, with_bwd, budget_s):
 FWD_SWEEP = ((2, False), (2, True), (3, True), (4, True), (4, False))
 
 
-def forward_sweep(fa2, torch, dev, reps=5):
+def forward_sweep(fa2, torch, dev, reps=10, warm_ms=60.0):
     """Forward-only TFLOP/s of the forward workloads (B=8 H=32 N=2048 d=64 both masks,
-    B=4 H=16 N=4096 d=128 causal, B=1 H=16 N=16384 d=128 both masks), timed with HIP events
-    on the launch stream after two warm-up calls."""
+    B=4 H=16 N=4096 d=128 causal, B=1 H=16 N=16384 d=128 both masks). All inputs are made
+    and copied to the device first; each case then runs back to back for at least `warm_ms`
+    of GPU time before `reps` calls are timed with HIP events on the launch stream."""
     import numpy as np
 
     from exact_io_aware_42_amd.inputs import WORKLOADS, default_scale, workload_tensors
 
-    res = {}
     stream = torch.cuda.current_stream(dev)
-    cache = {}
+    dev_inputs = {}
+    for wid in sorted({wid for wid, _ in FWD_SWEEP}):
+        t = workload_tensors(WORKLOADS[wid])
+        dev_inputs[wid] = [torch.from_numpy(t[x].view(np.int16)).view(torch.bfloat16).to(dev)
+                           for x in ("q", "k", "v")]
+    torch.cuda.synchronize()
+    res = {}
     for wid, causal in FWD_SWEEP:
         w = WORKLOADS[wid]
-        if wid not in cache:
-            cache.clear()
-            t = workload_tensors(w)
-            cache[wid] = [torch.from_numpy(t[x].view(np.int16)).view(torch.bfloat16).to(dev)
-                          for x in ("q", "k", "v")]
-        q, k, v = cache[wid]
+        q, k, v = dev_inputs[wid]
         o = torch.empty_like(q)
         lse = torch.empty(w.shape[:3], dtype=torch.float32, device=dev)
-        for _ in range(2):
-            fa2.fwd(q, k, v, causal=causal, scale=default_scale(w.d), out=o, lse=lse)
+        run = lambda: fa2.fwd(q, k, v, causal=causal, scale=default_scale(w.d), out=o, lse=lse)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        for _ in range(max(2, int(warm_ms / max(e0.elapsed_time(e1), 1e-3)))):
+            run()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
         ev[0].record(stream)
         for r in range(reps):
-            fa2.fwd(q, k, v, causal=causal, scale=default_scale(w.d), out=o, lse=lse)
+            run()
             ev[r + 1].record(stream)
         torch.cuda.synchronize()
         ms = sum(ev[r].elapsed_time(ev[r + 1]) for r in range(reps)) / reps
