@@ -25,9 +25,11 @@
 //  * exp2 form: p = exp2(s * scale*log2(e) - m) is one FMA + one v_exp_f32. Masked tiles
 //    (causal diagonal, ragged tail) start their score accumulators at -inf instead of 0 for
 //    hidden keys. Two workgroups per CU let one wave's softmax VALU work overlap another
-//    wave's MFMAs;
-//  * l is summed from the same bf16-rounded p that feeds the MFMA (consistent convex
-//    weights, v_dot2 with ones), while the LSE uses an fp32 sum of the unrounded p.
+//    wave's MFMAs. The key loop is unrolled by two so the LDS slot of a tile is a
+//    compile-time constant and every LDS address is a base register plus an immediate;
+//  * l is one fp32 sum of the unrounded p; it normalises O and gives the LSE.
+#include <type_traits>
+
 #include "fa2_device.hpp"
 #include "fa2_launch.hpp"
 
@@ -149,8 +151,7 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
 #pragma unroll
   for (int cb = 0; cb < S::CB; ++cb) oacc[cb] = f32x16_t{};
   float m_run;        // running max of scale*log2(e)*s (stale by < threshold)
-  float l_f32 = 0.f;  // partial sum of p over this lane's keys (fp32, for LSE)
-  float l_bf = 0.f;   // partial sum of bf16(p) (normaliser of O)
+  float l_f32 = 0.f;  // partial sum of p over this lane's keys
 
   // hidden-key bias for tile j: -inf where key >= N or (causal) key > query
   auto tile_needs_mask = [&](int j) {
@@ -180,16 +181,19 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
         s[kb] = (kk == 0 && !masked) ? mfma32(a, qf[kk], f32x16_t{}) : mfma32(a, qf[kk], s[kb]);
       }
   };
+  // four independent chains of 3-input maxima over the 32 scores of the lane
   auto row_max = [&](const f32x16_t* s) {
-    float a = fmaxf(s[0][0], s[0][1]), b = fmaxf(s[1][0], s[1][1]);
+    float a[4];
 #pragma unroll
-    for (int i = 2; i < 16; i += 2) {
-      a = __builtin_fmaxf(a, __builtin_fmaxf(s[0][i], s[0][i + 1]));
-      b = __builtin_fmaxf(b, __builtin_fmaxf(s[1][i], s[1][i + 1]));
-    }
-    return max_xor32(fmaxf(a, b)) * scale_log2;
+    for (int c = 0; c < 4; ++c) a[c] = fmaxf(s[c / 2][8 * (c % 2)], s[c / 2][8 * (c % 2) + 1]);
+#pragma unroll
+    for (int i = 2; i < 8; i += 2)
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        a[c] = fmaxf(a[c], fmaxf(s[c / 2][8 * (c % 2) + i], s[c / 2][8 * (c % 2) + i + 1]));
+    return max_xor32(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]))) * scale_log2;
   };
-  // p = exp2(s*c - m) -> packed bf16 (the PV B operand); partial sums of p and bf16(p)
+  // p = exp2(s*c - m) -> packed bf16 (the PV B operand); partial sum of p
   auto probs = [&](const f32x16_t* s, uint32_t (*pk)[8]) {
     const float neg_m = -m_run;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -200,9 +204,7 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
         const float p0 = fast_exp2(__builtin_fmaf(s[kb][2 * i], scale_log2, neg_m));
         const float p1 = fast_exp2(__builtin_fmaf(s[kb][2 * i + 1], scale_log2, neg_m));
         acc[(i & 1) * 2 + kb] += p0 + p1;
-        const uint32_t w = pack_bf16(p0, p1);
-        pk[kb][i] = w;
-        l_bf = add_bf16_pair(l_bf, w);
+        pk[kb][i] = pack_bf16(p0, p1);
       }
     l_f32 += (acc[0] + acc[1]) + (acc[2] + acc[3]);
   };
@@ -231,7 +233,6 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
       const float alpha = fast_exp2(m_run - m_new);
       m_run = m_new;
       l_f32 *= alpha;
-      l_bf *= alpha;
 #pragma unroll
       for (int cb = 0; cb < S::CB; ++cb) oacc[cb] *= alpha;
     }
@@ -244,9 +245,9 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
   __syncthreads();
   m_run = -INFINITY;
   bool first = true;
-  for (int j = 0; j < n_tiles; ++j) {
-    const int slot = j & 1;
-    // slot (j+1)&1 held tile j-1, whose readers all passed the barrier that ended step j-1
+  auto step = [&](auto slot_c, int j) {
+    constexpr int slot = decltype(slot_c)::value;
+    // slot ^ 1 held tile j-1, whose readers all passed the barrier that ended step j-1
     if (j + 1 < n_tiles) {
       load_k(j + 1, slot ^ 1);
       load_v(j + 1, slot ^ 1);
@@ -268,13 +269,16 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
     }
     wait_vmem();
     __syncthreads();
+  };
+  for (int j = 0; j < n_tiles; j += 2) {
+    step(std::integral_constant<int, 0>{}, j);
+    if (j + 1 < n_tiles) step(std::integral_constant<int, 1>{}, j + 1);
   }
 
   // ---- epilogue: deferred normalisation, bf16 output, LSE
   const float l_tot = sum_xor32(l_f32);
-  const float lb_tot = sum_xor32(l_bf);
   if (my_q < N) {
-    const float inv = fast_rcp(lb_tot);
+    const float inv = fast_rcp(l_tot);
     uint16_t* orow = o + head_off + (size_t)my_q * D;
 #pragma unroll
     for (int cb = 0; cb < S::CB; ++cb)
