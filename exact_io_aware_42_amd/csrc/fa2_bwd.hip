@@ -22,6 +22,8 @@
 //                        accumulating dQ^T = K^T dS^T.
 // dK/dV and dQ each recompute S and dP; dQ's two recompute GEMMs are the price of avoiding
 // atomic dQ accumulation.
+#include <type_traits>
+
 #include "fa2_device.hpp"
 #include "fa2_launch.hpp"
 
@@ -146,11 +148,16 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
     uint16_t* __restrict__ dv, int N, int n_kblocks, int bh_count, float scale_log2,
     float scale) {
   constexpr int KK = D / 16, CB = D / 32, DCH = D / 8;
+  // LDS: the two ring stages of Q and dO tiles at the bottom (every ds_read of them is a
+  // per-lane base plus a 16-bit immediate), then LSE*log2(e) and D of both stages, then the
+  // resident K and V rows (their per-lane bases carry the offset).
   constexpr int TILE = kKvBQ * D * 2;
   constexpr int KV_BYTES = kKvBK * D * 2;
-  constexpr int STAGE = 2 * TILE + 2 * kKvBQ * 4;  // Q, dO, LSE*log2(e), D
-  constexpr int RING0 = 2 * KV_BYTES;
-  constexpr int MAIN_BYTES = RING0 + 2 * STAGE;
+  constexpr int STAGE = 2 * TILE;               // Q, dO
+  constexpr int STATS0 = 2 * STAGE;             // per stage: LSE*log2(e), then D (256 B each)
+  constexpr int STATS_STAGE = 2 * kKvBQ * 4;
+  constexpr int KV0 = STATS0 + 2 * STATS_STAGE;
+  constexpr int MAIN_BYTES = KV0 + 2 * KV_BYTES;
   constexpr int ACC_BYTES = CB * 16 * 64 * 4;   // one wave's dK (or dV) accumulator
   constexpr int XCH_BYTES = 8 * ACC_BYTES;      // combine area, reuses the main area
   constexpr int SMEM = MAIN_BYTES > XCH_BYTES ? MAIN_BYTES : XCH_BYTES;
@@ -190,34 +197,49 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
       const int blk = 8 * r + wave;
       const int row = blk * RPB + lane / DCH;
       const uint32_t off = (uint32_t)(row * D * 2 + ((lane % DCH) ^ swz<D>(row)) * 16);
-      buffer_load16_to_lds(rk, smem + blk * 1024, off, (uint32_t)key_b0 * D * 2);
-      buffer_load16_to_lds(rv, smem + KV_BYTES + blk * 1024, off, (uint32_t)key_b0 * D * 2);
+      buffer_load16_to_lds(rk, smem + KV0 + blk * 1024, off, (uint32_t)key_b0 * D * 2);
+      buffer_load16_to_lds(rv, smem + KV0 + KV_BYTES + blk * 1024, off,
+                           (uint32_t)key_b0 * D * 2);
     }
   }
   // per-lane offset of this wave's K/V fragment: row 32*kw + l32, logical chunk 2kk + g
   const int kvrow = kw * 32 + l32;
   int kvbase[KK];
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) kvbase[kk] = kvrow * D * 2 + ((2 * kk + g) ^ swz<D>(kvrow)) * 16;
+  for (int kk = 0; kk < KK; ++kk)
+    kvbase[kk] = KV0 + kvrow * D * 2 + ((2 * kk + g) ^ swz<D>(kvrow)) * 16;
+  // LSE*log2(e) / D of this lane's queries 32hq + 16hf + 8g + (0..7) within a stage
+  const int statbase = STATS0 + (32 * hq + 8 * g) * 4;
 
   const int n_qt = (N + kKvBQ - 1) / kKvBQ;
   const int qt_begin = CAUSAL ? key_b0 / kKvBQ : 0;
   const TileLoader<D, kKvThreads> ld(wave, lane);
-  const TileReads<D> rd_off(lane);
+  // per-lane read offsets within a stage for this wave's query half: row-wise Q/dO fragments
+  // (rows 32hq + kmap(l32)) and transposing reads (k-steps t = 2hq + hf)
+  int qrow[KK], qtr[CB][2];
+  {
+    const TileReads<D> rd_off(lane);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) qrow[kk] = rd_off.row_off(hq, kk);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) qtr[cb][h] = rd_off.tr_off(cb, 2 * hq, h);
+  }
 
   auto load_stage = [&](int it, int stage) {
-    unsigned char* st = smem + RING0 + stage * STAGE;
+    unsigned char* st = smem + stage * STAGE;
     const uint32_t soff = (uint32_t)it * kKvBQ * D * 2;
     ld.load(rq, st, soff);
     ld.load(rdo, st + TILE, soff);
     // LSE*log2(e) and D of the tile's 64 queries (256 bytes each): 16 lanes of waves 0 and 1
+    unsigned char* sst = smem + STATS0 + stage * STATS_STAGE;
     if (wave == 0) {
       if (lane < 16)
-        buffer_load16_to_lds(rl, st + 2 * TILE, (uint32_t)lane * 16, (uint32_t)it * kKvBQ * 4);
+        buffer_load16_to_lds(rl, sst, (uint32_t)lane * 16, (uint32_t)it * kKvBQ * 4);
     } else if (wave == 1) {
       if (lane < 16)
-        buffer_load16_to_lds(rd, st + 2 * TILE + kKvBQ * 4, (uint32_t)lane * 16,
-                             (uint32_t)it * kKvBQ * 4);
+        buffer_load16_to_lds(rd, sst + kKvBQ * 4, (uint32_t)lane * 16, (uint32_t)it * kKvBQ * 4);
     }
   };
 
@@ -232,18 +254,18 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
   wait_vmem();
   __syncthreads();
 
-  for (int it = qt_begin; it < n_qt; ++it) {
-    const int stage = (it - qt_begin) & 1;
+  // unrolled by two below, so the ring stage is a compile-time constant (LDS addresses are a
+  // base register plus an immediate)
+  auto step = [&](auto stage_c, int it) {
+    constexpr int stage = decltype(stage_c)::value;
     if (it + 1 < n_qt) load_stage(it + 1, stage ^ 1);
     const int q0 = it * kKvBQ + 32 * hq;  // this wave's 32 queries
     // every query of the half precedes every key of the wave: fully masked
     const bool skip = CAUSAL && (q0 + 31 < key_w0);
     if (!skip) {
-      const unsigned char* st = smem + RING0 + stage * STAGE;
-      const unsigned char* tq = st;
-      const unsigned char* tdo = st + TILE;
-      const float* tl = reinterpret_cast<const float*>(st + 2 * TILE);
-      const float* tdl = tl + kKvBQ;
+      const unsigned char* tq = smem + stage * STAGE;
+      const unsigned char* tdo = tq + TILE;
+      const unsigned char* ts = smem + statbase + stage * STATS_STAGE;
       const bool masked = (q0 + 32 > N) || (CAUSAL && q0 < key_w0 + 31);
 
       f32x16_t s, dp = f32x16_t{};
@@ -259,9 +281,9 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(smem + kvbase[kk]);
-        const u32x4_t vf = *reinterpret_cast<const u32x4_t*>(smem + KV_BYTES + kvbase[kk]);
-        const u32x4_t aq = *reinterpret_cast<const u32x4_t*>(tq + rd_off.row_off(hq, kk));
-        const u32x4_t ad = *reinterpret_cast<const u32x4_t*>(tdo + rd_off.row_off(hq, kk));
+        const u32x4_t vf = *reinterpret_cast<const u32x4_t*>(smem + kvbase[kk] + KV_BYTES);
+        const u32x4_t aq = *reinterpret_cast<const u32x4_t*>(tq + qrow[kk]);
+        const u32x4_t ad = *reinterpret_cast<const u32x4_t*>(tdo + qrow[kk]);
         s = mfma32(aq, kf, s);
         dp = mfma32(ad, vf, dp);
       }
@@ -270,11 +292,11 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
       uint32_t pk[8], dsk[8];
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        const int qo = 32 * hq + 16 * hf + 8 * g;
-        const f32x4_t l0 = *reinterpret_cast<const f32x4_t*>(tl + qo);
-        const f32x4_t l1 = *reinterpret_cast<const f32x4_t*>(tl + qo + 4);
-        const f32x4_t d0 = *reinterpret_cast<const f32x4_t*>(tdl + qo);
-        const f32x4_t d1 = *reinterpret_cast<const f32x4_t*>(tdl + qo + 4);
+        const unsigned char* sl = ts + 16 * hf * 4;  // queries 32hq + 16hf + 8g + (0..7)
+        const f32x4_t l0 = *reinterpret_cast<const f32x4_t*>(sl);
+        const f32x4_t l1 = *reinterpret_cast<const f32x4_t*>(sl + 16);
+        const f32x4_t d0 = *reinterpret_cast<const f32x4_t*>(sl + kKvBQ * 4);
+        const f32x4_t d1 = *reinterpret_cast<const f32x4_t*>(sl + kKvBQ * 4 + 16);
         float p[8], ds[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -289,23 +311,28 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
           dsk[4 * hf + e] = pack_bf16(ds[2 * e], ds[2 * e + 1]);
         }
       }
-      // dV^T += dO^T P and dK^T += Q^T dS over the wave's 32 queries (k-steps t = 2hq + hf)
+      // dV^T += dO^T P and dK^T += Q^T dS over the wave's 32 queries (k-steps t = 2hq + hf,
+      // 16 rows = 16 * D * 2 bytes apart)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        const int t = 2 * hq + hf;
+        const int hoff = hf * 16 * D * 2;
         const u32x4_t bp = {pk[4 * hf + 0], pk[4 * hf + 1], pk[4 * hf + 2], pk[4 * hf + 3]};
         const u32x4_t bs = {dsk[4 * hf + 0], dsk[4 * hf + 1], dsk[4 * hf + 2], dsk[4 * hf + 3]};
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
-          const u32x4_t ao = tr_operand(tdo, rd_off.tr_off(cb, t, 0), rd_off.tr_off(cb, t, 1));
+          const u32x4_t ao = tr_operand(tdo + hoff, qtr[cb][0], qtr[cb][1]);
           dvacc[cb] = mfma32(ao, bp, dvacc[cb]);
-          const u32x4_t aq = tr_operand(tq, rd_off.tr_off(cb, t, 0), rd_off.tr_off(cb, t, 1));
+          const u32x4_t aq = tr_operand(tq + hoff, qtr[cb][0], qtr[cb][1]);
           dkacc[cb] = mfma32(aq, bs, dkacc[cb]);
         }
       }
     }
     wait_vmem();
     __syncthreads();
+  };
+  for (int it = qt_begin; it < n_qt; it += 2) {
+    step(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < n_qt) step(std::integral_constant<int, 1>{}, it + 1);
   }
 
   // Combine the pair's partial sums through LDS (the loop ended with a barrier, so the tiles are
@@ -421,8 +448,9 @@ __global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dq_kernel(
   wait_vmem();
   __syncthreads();
 
-  for (int j = 0; j < n_tiles; ++j) {
-    const int stage = j & 1;
+  // unrolled by two below: the stage is a compile-time constant
+  auto step = [&](auto stage_c, int j) {
+    constexpr int stage = decltype(stage_c)::value;
     if (j + 1 < n_tiles) load_stage(j + 1, stage ^ 1);
     if (j <= wave_last) {
       const unsigned char* tk = smem + stage * STAGE;
@@ -473,6 +501,10 @@ __global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dq_kernel(
     }
     wait_vmem();
     __syncthreads();
+  };
+  for (int j = 0; j < n_tiles; j += 2) {
+    step(std::integral_constant<int, 0>{}, j);
+    if (j + 1 < n_tiles) step(std::integral_constant<int, 1>{}, j + 1);
   }
 
   if (valid_q) {
