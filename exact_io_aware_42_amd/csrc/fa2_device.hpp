@@ -71,6 +71,12 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
+// acc + lo(w) + hi(w), the two bf16 halves of w widened exactly (v_dot2c_f32_bf16 with 1.0).
+__device__ __forceinline__ float add_bf16_pair(float acc, uint32_t w) {
+  const bf16x2_t one = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w), one, acc, false);
+}
+
 // max / sum of x over lanes l and l^32 (the two halves of a wave hold the two halves of
 // one query's key set). v_permlane32_swap exchanges the upper half of its first operand
 // with the lower half of its second; applied to (x, x) the two results hold x[l] and

@@ -27,7 +27,12 @@
 //    hidden keys. Two workgroups per CU let one wave's softmax VALU work overlap another
 //    wave's MFMAs. The key loop is unrolled by two so the LDS slot of a tile is a
 //    compile-time constant and every LDS address is a base register plus an immediate;
-//  * l is one fp32 sum of the unrounded p; it normalises O and gives the LSE.
+//  * the LSE uses the fp32 sum of the unrounded p. O is normalised by the sum of the weights
+//    the PV MFMA actually used: on masked tiles (causal diagonal, ragged tail) a correction
+//    sum(bf16(p)) - sum(p) is added, so a row whose visible keys all lie in masked tiles (every
+//    causal row with fewer than 64 keys, where O mixes only a few V rows) gets exactly
+//    convex bf16 weights; on unmasked tiles the fp32 sum stands in (rows with >= 64 keys, where
+//    the difference averages out).
 #include <type_traits>
 
 #include "fa2_device.hpp"
@@ -152,6 +157,7 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
   for (int cb = 0; cb < S::CB; ++cb) oacc[cb] = f32x16_t{};
   float m_run;        // running max of scale*log2(e)*s (stale by < threshold)
   float l_f32 = 0.f;  // partial sum of p over this lane's keys
+  float l_corr = 0.f; // masked tiles: sum of bf16(p) - p
 
   // hidden-key bias for tile j: -inf where key >= N or (causal) key > query
   auto tile_needs_mask = [&](int j) {
@@ -206,7 +212,18 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
         acc[(i & 1) * 2 + kb] += p0 + p1;
         pk[kb][i] = pack_bf16(p0, p1);
       }
-    l_f32 += (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    const float tile_sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+    l_f32 += tile_sum;
+    return tile_sum;
+  };
+  // masked tiles: l_corr += sum of bf16(p) - sum of p (after the PV MFMAs, off their path)
+  auto bf16_correction = [&](uint32_t (*pk)[8], float tile_sum) {
+    float b[2] = {0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) b[kb] = add_bf16_pair(b[kb], pk[kb][i]);
+    l_corr += (b[0] + b[1]) - tile_sum;
   };
   // O^T += V^T P^T from V slot `slot`; MFMA u covers keys 16u .. 16u+15 = score block u/2,
   // registers 8(u%2) .. 8(u%2)+7
@@ -233,6 +250,7 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
       const float alpha = fast_exp2(m_run - m_new);
       m_run = m_new;
       l_f32 *= alpha;
+      l_corr *= alpha;
 #pragma unroll
       for (int cb = 0; cb < S::CB; ++cb) oacc[cb] *= alpha;
     }
@@ -254,7 +272,8 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
     }
     if (j <= wave_last) {
       f32x16_t s[2];
-      if (tile_needs_mask(j)) scores(slot, true, j, s);
+      const bool masked = tile_needs_mask(j);
+      if (masked) scores(slot, true, j, s);
       else scores(slot, false, j, s);
       const float m_tile = row_max(s);
       if (first) {
@@ -264,12 +283,13 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
         maybe_rescale(m_tile);
       }
       uint32_t pk[2][8];
-      probs(s, pk);
+      const float tile_sum = probs(s, pk);
       // raised priority while this wave issues its PV MFMAs: the other wave on the SIMD then
       // tends to run its softmax VALU work in between (measured +2-6%)
       __builtin_amdgcn_s_setprio(1);
       pv(slot, pk);
       __builtin_amdgcn_s_setprio(0);
+      if (masked) bf16_correction(pk, tile_sum);
     }
     wait_vmem();
     __syncthreads();
@@ -281,8 +301,9 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
 
   // ---- epilogue: deferred normalisation, bf16 output, LSE
   const float l_tot = sum_xor32(l_f32);
+  const float l_o = sum_xor32(l_f32 + l_corr);
   if (my_q < N) {
-    const float inv = fast_rcp(l_tot);
+    const float inv = fast_rcp(l_o);
     uint16_t* orow = o + head_off + (size_t)my_q * D;
 #pragma unroll
     for (int cb = 0; cb < S::CB; ++cb)
