@@ -4,7 +4,7 @@
 
 One step is one pass of the whole hot path over one batch of synthetic seeded inputs
 (i.i.d. N(0, 1) bf16, already resident in device memory): the forward kernel (O and LSE)
-and the backward (D = rowsum(dO * O), the dK/dV kernel, the dQ kernel). The default workload
+and the backward (the dQ kernel, which also forms D = rowsum(dO * O), then the dK/dV kernel). The default workload
 is the fwd+bwd attention workload B=4, H=16, N=2048, d=128, causal. FLOP counts: forward
 4*B*H*N^2*d (halved when causal), backward 2.5x forward. `value` is the step's total FLOP
 over its wall time, in TFLOP/s.
@@ -188,10 +188,10 @@ def main():
     stream = torch.cuda.current_stream(dev)
     kernels = ["fa2_fwd_kernel"]
     if with_bwd:
-        kernels += ["fa2_bwd_pre_kernel", "fa2_bwd_dkdv_kernel", "fa2_bwd_dq_kernel"]
+        kernels += ["fa2_bwd_dq_kernel", "fa2_bwd_dkdv_kernel"]
     f_fwd = fwd_flop(B, H, N, d, causal)
-    algo_flop = {"fa2_fwd_kernel": f_fwd, "fa2_bwd_pre_kernel": 0.0,
-                 "fa2_bwd_dkdv_kernel": 2.0 * f_fwd, "fa2_bwd_dq_kernel": 0.5 * f_fwd}
+    algo_flop = {"fa2_fwd_kernel": f_fwd, "fa2_bwd_dkdv_kernel": 2.0 * f_fwd,
+                 "fa2_bwd_dq_kernel": 0.5 * f_fwd}
     step_flop = f_fwd * (3.5 if with_bwd else 1.0)
 
     def step(events=None):
@@ -202,12 +202,11 @@ def main():
         fa2.fwd(q, k, v, causal=causal, scale=scale, out=o, lse=lse)
         mark(1)
         if with_bwd:
-            fa2.bwd_preprocess(o, do, lse, ws)
+            # dQ first: it also stores D = rowsum(dO * O) and LSE*log2(e) for dK/dV
+            fa2.bwd_dq(q, k, v, o, do, lse, ws, causal=causal, scale=scale, dq=dq)
             mark(2)
             fa2.bwd_dkdv(q, k, v, do, ws, causal=causal, scale=scale, dk=dk, dv=dv)
             mark(3)
-            fa2.bwd_dq(q, k, v, do, ws, causal=causal, scale=scale, dq=dq)
-            mark(4)
 
     for _ in range(args.warmup):
         step()

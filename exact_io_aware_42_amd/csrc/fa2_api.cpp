@@ -154,15 +154,15 @@ fa2_status fa2_bwd_dkdv(const void* q, const void* k, const void* v, const void*
   return from_hip(fa2::launch_bwd_dkdv(a));
 }
 
-fa2_status fa2_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
-                      const void* workspace, size_t workspace_bytes, void* dq, int B, int H, int N,
-                      int d, int causal, float softmax_scale, hipStream_t stream) {
+fa2_status fa2_bwd_dq(const void* q, const void* k, const void* v, const void* o,
+                      const void* dout, const float* lse, void* workspace,
+                      size_t workspace_bytes, void* dq, int B, int H, int N, int d, int causal,
+                      float softmax_scale, hipStream_t stream) {
   fa2::BwdArgs a;
-  const fa2_status st = bwd_args(q, k, v, nullptr, dout, nullptr, const_cast<void*>(workspace),
-                                 workspace_bytes, dq, nullptr, nullptr, B, H, N, d, causal,
-                                 softmax_scale, stream, &a);
+  const fa2_status st = bwd_args(q, k, v, o, dout, lse, workspace, workspace_bytes, dq, nullptr,
+                                 nullptr, B, H, N, d, causal, softmax_scale, stream, &a);
   if (st != FA2_OK) return st;
-  if (!all_ok({q, k, v, dout, dq})) return FA2_ERR_INVALID_ARGUMENT;
+  if (!all_ok({q, k, v, o, dout, lse, dq})) return FA2_ERR_INVALID_ARGUMENT;
   return from_hip(fa2::launch_bwd_dq(a));
 }
 

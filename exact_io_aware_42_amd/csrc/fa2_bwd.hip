@@ -11,15 +11,18 @@
 //   P = exp(scale S - LSE),  D_i = sum_c dO_ic O_ic,  dS = P * (dO V^T - D),
 //   dV = P^T dO,  dK = scale dS^T Q,  dQ = scale dS K.
 //
-// Three kernels, deterministic (no atomics):
-//   fa2_bwd_pre_kernel   D = rowsum(dO * O) and LSE*log2(e), fp32 [B, H, N] (HBM-bound).
-//   fa2_bwd_dkdv_kernel  grid over (key block of 128, head, batch): the block's K and V rows
-//                        stay in LDS, 64-query tiles of Q, dO, LSE and D stream through LDS, and
-//                        two waves per 32 keys (one per half of each query tile) accumulate
-//                        dK, dV in registers; the pair's sums meet in LDS at the end.
+// Deterministic (no atomics); the backward runs two kernels, dQ first:
 //   fa2_bwd_dq_kernel    grid over (query block of 128, head, batch): the forward's layout
-//                        (lane = query), recomputing S^T and dP^T per key tile and
-//                        accumulating dQ^T = K^T dS^T.
+//                        (lane = query). It first forms D_i = rowsum(dO_i * O_i) from the
+//                        dO and O rows it loads and stores D and LSE*log2(e) of its queries
+//                        in the workspace; then it recomputes S^T and dP^T per key tile and
+//                        accumulates dQ^T = K^T dS^T.
+//   fa2_bwd_dkdv_kernel  grid over (key block of 128, head, batch): the block's K and V rows
+//                        stay in LDS, 64-query tiles of Q, dO, LSE*log2(e) and D stream
+//                        through LDS, and two waves per 32 keys (one per half of each query
+//                        tile) accumulate dK, dV in registers; the pair's sums meet in LDS.
+//   fa2_bwd_pre_kernel   D and LSE*log2(e) alone (HBM-bound), for callers that want dK/dV
+//                        without dQ.
 // dK/dV and dQ each recompute S and dP; dQ's two recompute GEMMs are the price of avoiding
 // atomic dQ accumulation.
 #include <type_traits>
@@ -393,9 +396,10 @@ constexpr int kDqBC = 64;
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-    const float* __restrict__ lse2, const float* __restrict__ delta, uint16_t* __restrict__ dq,
-    int N, int n_qblocks, int bh_count, float scale_log2, float scale) {
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ o,
+    const uint16_t* __restrict__ dout, const float* __restrict__ lse, float* __restrict__ lse2,
+    float* __restrict__ delta, uint16_t* __restrict__ dq, int N, int n_qblocks, int bh_count,
+    float scale_log2, float scale) {
   constexpr int KK = D / 16, CB = D / 32;
   constexpr int TILE = kDqBC * D * 2;
   constexpr int STAGE = 2 * TILE;  // K, V
@@ -421,15 +425,35 @@ __global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dq_kernel(
   const int my_q = q_wave0 + l32;
   const bool valid_q = my_q < N;
 
+  // Q and dO fragments (B operands of S^T and dP^T): lane holds row my_q, columns
+  // 16kk + 8g .. +7; the O fragments of the same columns give this lane's half of
+  // D = rowsum(dO * O), the other half is in lane l^32.
   u32x4_t qf[KK], dof[KK];
+  float dpart = 0.f;
+  {
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(o + head_off, head_bytes);
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) {
-    qf[kk] = buffer_load16(rq, (uint32_t)my_q * D * 2 + (2 * kk + g) * 16, 0);
-    dof[kk] = buffer_load16(rdo, (uint32_t)my_q * D * 2 + (2 * kk + g) * 16, 0);
+    for (int kk = 0; kk < KK; ++kk) {
+      qf[kk] = buffer_load16(rq, (uint32_t)my_q * D * 2 + (2 * kk + g) * 16, 0);
+      dof[kk] = buffer_load16(rdo, (uint32_t)my_q * D * 2 + (2 * kk + g) * 16, 0);
+    }
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const u32x4_t of = buffer_load16(ro, (uint32_t)my_q * D * 2 + (2 * kk + g) * 16, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        dpart += bf16_lo(dof[kk][e]) * bf16_lo(of[e]) + bf16_hi(dof[kk][e]) * bf16_hi(of[e]);
+    }
   }
+  const float dsum = sum_xor32(dpart);
   // padded queries get LSE = +inf, hence P = 0
-  const float lse_q = valid_q ? lse2[(size_t)tc.bh * N + my_q] : INFINITY;
-  const float dlt = valid_q ? delta[(size_t)tc.bh * N + my_q] : 0.f;
+  const float lse_q = valid_q ? lse[(size_t)tc.bh * N + my_q] * kLog2e : INFINITY;
+  const float dlt = valid_q ? dsum : 0.f;
+  // D and LSE*log2(e) of this block's queries go to the workspace for the dK/dV kernel
+  if (valid_q && g == 0) {
+    delta[(size_t)tc.bh * N + my_q] = dlt;
+    lse2[(size_t)tc.bh * N + my_q] = lse_q;
+  }
 
   int n_tiles = (N + kDqBC - 1) / kDqBC;
   if (CAUSAL) n_tiles = min(N - 1, q_block0 + kDqBR - 1) / kDqBC + 1;
@@ -562,9 +586,9 @@ hipError_t launch_dq_t(const BwdArgs& a) {
   hipLaunchKernelGGL((fa2_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0,
                      a.stream, static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
-                     static_cast<const uint16_t*>(a.dout), a.lse2, a.delta,
-                     static_cast<uint16_t*>(a.dq), a.N, n_qblocks, a.B * a.H, a.scale_log2,
-                     a.scale);
+                     static_cast<const uint16_t*>(a.o), static_cast<const uint16_t*>(a.dout),
+                     a.lse, a.lse2, a.delta, static_cast<uint16_t*>(a.dq), a.N, n_qblocks,
+                     a.B * a.H, a.scale_log2, a.scale);
   return hipGetLastError();
 }
 
@@ -585,11 +609,9 @@ hipError_t launch_bwd_dq(const BwdArgs& a) {
 }
 
 hipError_t launch_bwd(const BwdArgs& a) {
-  hipError_t e = launch_bwd_pre(a);
+  const hipError_t e = launch_bwd_dq(a);  // also fills the workspace (D, LSE*log2(e))
   if (e != hipSuccess) return e;
-  e = launch_bwd_dkdv(a);
-  if (e != hipSuccess) return e;
-  return launch_bwd_dq(a);
+  return launch_bwd_dkdv(a);
 }
 
 }  // namespace fa2

@@ -54,7 +54,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.fa2_bwd_preprocess.restype = i
         lib.fa2_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, sz, vp, vp, i, i, i, i, i, f, vp]
         lib.fa2_bwd_dkdv.restype = i
-        lib.fa2_bwd_dq.argtypes = [vp, vp, vp, vp, vp, sz, vp, i, i, i, i, i, f, vp]
+        lib.fa2_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, vp, i, i, i, i, i, f, vp]
         lib.fa2_bwd_dq.restype = i
         lib.fa2_bwd_workspace_bytes.argtypes = [i, i, i, i]
         lib.fa2_bwd_workspace_bytes.restype = sz
@@ -162,7 +162,8 @@ def _ws(workspace: torch.Tensor, B: int, H: int, N: int, d: int):
 
 
 def bwd_preprocess(o, dout, lse, workspace):
-    """Fill `workspace` with D = rowsum(dout * o) and LSE * log2(e)."""
+    """Fill `workspace` with D = rowsum(dout * o) and LSE * log2(e) (bwd_dq does this too;
+    this stage is for callers that need dK/dV only)."""
     lib = load_library()
     B, H, N, d = o.shape
     _check_tensor(o, "o", (B, H, N, d))
@@ -175,7 +176,7 @@ def bwd_preprocess(o, dout, lse, workspace):
 
 
 def bwd_dkdv(q, k, v, dout, workspace, causal=False, scale=None, dk=None, dv=None):
-    """dK, dV from q, k, v, dout and a workspace filled by bwd_preprocess."""
+    """dK, dV from q, k, v, dout and a workspace filled by bwd_dq (or bwd_preprocess)."""
     lib = load_library()
     B, H, N, d = q.shape
     for t, nm in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
@@ -192,17 +193,19 @@ def bwd_dkdv(q, k, v, dout, workspace, causal=False, scale=None, dk=None, dv=Non
     return dk, dv
 
 
-def bwd_dq(q, k, v, dout, workspace, causal=False, scale=None, dq=None):
-    """dQ from q, k, v, dout and a workspace filled by bwd_preprocess."""
+def bwd_dq(q, k, v, o, dout, lse, workspace, causal=False, scale=None, dq=None):
+    """dQ from q, k, v, o, dout and lse; also fills `workspace` (D, LSE * log2(e)) for
+    bwd_dkdv."""
     lib = load_library()
     B, H, N, d = q.shape
-    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (dout, "dout")):
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
         _check_tensor(t, nm, (B, H, N, d), device=q.device)
+    _check_tensor(lse, "lse", (B, H, N), dtype=torch.float32, device=q.device)
     dq = torch.empty_like(q) if dq is None else dq
     _check_tensor(dq, "dq", (B, H, N, d), device=q.device)
     s = default_scale(d) if scale is None else float(scale)
-    st = lib.fa2_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
-                        *_ws(workspace, B, H, N, d), dq.data_ptr(), B, H, N, d,
-                        int(bool(causal)), s, _stream_ptr(q.device))
+    st = lib.fa2_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                        dout.data_ptr(), lse.data_ptr(), *_ws(workspace, B, H, N, d),
+                        dq.data_ptr(), B, H, N, d, int(bool(causal)), s, _stream_ptr(q.device))
     _check(st, "fa2_bwd_dq")
     return dq

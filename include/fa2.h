@@ -75,36 +75,38 @@ size_t fa2_bwd_workspace_bytes(int B, int H, int N, int d);
  * same causal flag and scale), and the cotangent dout. Writes dq, dk, dv [B,H,N,d] (bf16,
  * accumulated in fp32). workspace: device buffer of at least fa2_bwd_workspace_bytes(...)
  * bytes, owned by the caller; its contents on entry do not matter and are clobbered.
- * Deterministic (no atomics). Runs fa2_bwd_preprocess, fa2_bwd_dkdv and fa2_bwd_dq below, in
- * that order, on `stream`. */
+ * Deterministic (no atomics). Runs fa2_bwd_dq and then fa2_bwd_dkdv below on `stream`. */
 fa2_status fa2_bwd(const void* q, const void* k, const void* v, const void* o,
                    const void* dout, const float* lse, void* dq, void* dk, void* dv,
                    void* workspace, size_t workspace_bytes,
                    int B, int H, int N, int d, int causal, float softmax_scale,
                    hipStream_t stream);
 
-/* The three stages of fa2_bwd, for callers that schedule or time them separately (the
- * results are identical to fa2_bwd's). All take the same workspace.
+/* The stages of fa2_bwd, for callers that schedule or time them separately (fa2_bwd_dq
+ * followed by fa2_bwd_dkdv gives fa2_bwd's results bit for bit). All take the same workspace.
  *
- * fa2_bwd_preprocess: fills the workspace with D_i = sum_c dO_ic O_ic (it equals
- *   sum_j P_ij dP_ij, the row term of the softmax gradient) and LSE_i * log2(e). */
-fa2_status fa2_bwd_preprocess(const void* o, const void* dout, const float* lse,
-                              void* workspace, size_t workspace_bytes,
-                              int B, int H, int N, int d, hipStream_t stream);
+ * fa2_bwd_dq: dq [B,H,N,d] (bf16) from q, k, v, o, dout and lse. Parallel over blocks of 128
+ *   queries; recomputes P and dP block by block, so no atomics are needed. It also fills the
+ *   workspace with D_i = sum_c dO_ic O_ic (equal to sum_j P_ij dP_ij, the row term of the
+ *   softmax gradient) and LSE_i * log2(e) for fa2_bwd_dkdv. */
+fa2_status fa2_bwd_dq(const void* q, const void* k, const void* v, const void* o,
+                      const void* dout, const float* lse, void* workspace,
+                      size_t workspace_bytes, void* dq, int B, int H, int N, int d, int causal,
+                      float softmax_scale, hipStream_t stream);
 
 /* fa2_bwd_dkdv: dk and dv [B,H,N,d] (bf16) from q, k, v, dout and a workspace filled by
- *   fa2_bwd_preprocess. Parallel over blocks of 128 keys; recomputes P block by block. */
+ *   fa2_bwd_dq or fa2_bwd_preprocess (earlier on the same stream). Parallel over blocks of 128
+ *   keys; recomputes P block by block. */
 fa2_status fa2_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
                         const void* workspace, size_t workspace_bytes, void* dk, void* dv,
                         int B, int H, int N, int d, int causal, float softmax_scale,
                         hipStream_t stream);
 
-/* fa2_bwd_dq: dq [B,H,N,d] (bf16) from the same inputs. Parallel over blocks of 128 queries;
- *   recomputes P and dP block by block, so no atomics are needed. */
-fa2_status fa2_bwd_dq(const void* q, const void* k, const void* v, const void* dout,
-                      const void* workspace, size_t workspace_bytes, void* dq,
-                      int B, int H, int N, int d, int causal, float softmax_scale,
-                      hipStream_t stream);
+/* fa2_bwd_preprocess: fills the workspace with D and LSE * log2(e) (the same values
+ *   fa2_bwd_dq stores, summed in a different order), for callers that need dK/dV only. */
+fa2_status fa2_bwd_preprocess(const void* o, const void* dout, const float* lse,
+                              void* workspace, size_t workspace_bytes,
+                              int B, int H, int N, int d, hipStream_t stream);
 
 /* Static, human-readable name of a status code. */
 const char* fa2_status_string(fa2_status s);

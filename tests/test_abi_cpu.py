@@ -97,10 +97,14 @@ def test_bwd_validation_and_workspace():
         ops.FA2_ERR_INVALID_ARGUMENT
     assert lib.fa2_bwd_dkdv(P, P, P, P, P, ws, P, P, 2, 3, 100, 96, 1, 0.1, None) == \
         ops.FA2_ERR_UNSUPPORTED
-    assert lib.fa2_bwd_dq(P, P, P, P, P, ws, None, 2, 3, 100, 64, 1, 0.1, None) == \
+    assert lib.fa2_bwd_dq(P, P, P, P, P, P, P, ws, None, 2, 3, 100, 64, 1, 0.1, None) == \
         ops.FA2_ERR_INVALID_ARGUMENT
-    assert lib.fa2_bwd_dq(P, P, P, P, P, ws, P, 2, 3, 100, 64, 1, -1.0, None) == \
+    assert lib.fa2_bwd_dq(P, P, P, P, P, P, P, ws, P, 2, 3, 100, 64, 1, -1.0, None) == \
         ops.FA2_ERR_INVALID_ARGUMENT
+    assert lib.fa2_bwd_dq(P, P, P, None, P, P, P, ws, P, 2, 3, 100, 64, 1, 0.1, None) == \
+        ops.FA2_ERR_INVALID_ARGUMENT  # null o
+    assert lib.fa2_bwd_dq(P, P, P, P, P, P + 4, P, ws, P, 2, 3, 100, 64, 1, 0.1, None) == \
+        ops.FA2_ERR_INVALID_ARGUMENT  # misaligned lse
 
 
 HEAD_MAJOR, LONG_DESC, LONG_ASC = "head_major", "long_desc", "long_asc"

@@ -94,7 +94,8 @@ def test_gradient_invariants(causal):
 @pytest.mark.parametrize("causal", [False, True])
 def test_deterministic_coverage_and_stages(causal):
     """Gradients pre-filled with NaN are fully overwritten; two runs give identical bits; the
-    three stage entry points reproduce fa2_bwd bit for bit."""
+    stage entry points (dQ, which fills the workspace, then dK/dV) reproduce fa2_bwd bit for
+    bit, and dK/dV after the separate preprocess stage agrees to fp32 rounding of D."""
     fa2 = _fa2()
     shape = (2, 3, 421, 64)
     q, k, v, do = (to_dev(normal_bf16(shape, 8700 + t)) for t in range(4))
@@ -102,15 +103,25 @@ def test_deterministic_coverage_and_stages(causal):
     nan = lambda: torch.full(shape, float("nan"), dtype=torch.bfloat16, device=q.device)
     g1 = fa2.bwd(q, k, v, o, do, lse, causal=causal, dq=nan(), dk=nan(), dv=nan())
     g2 = fa2.bwd(q, k, v, o, do, lse, causal=causal)
-    ws = torch.empty(fa2.bwd_workspace_bytes(*shape), dtype=torch.uint8, device=q.device)
-    fa2.bwd_preprocess(o, do, lse, ws)
+    ws = torch.full((fa2.bwd_workspace_bytes(*shape),), 255, dtype=torch.uint8, device=q.device)
+    dq3 = fa2.bwd_dq(q, k, v, o, do, lse, ws, causal=causal)
     dk3, dv3 = fa2.bwd_dkdv(q, k, v, do, ws, causal=causal)
-    dq3 = fa2.bwd_dq(q, k, v, do, ws, causal=causal)
+    ws2 = torch.full_like(ws, 255)
+    fa2.bwd_preprocess(o, do, lse, ws2)
+    dk4, dv4 = fa2.bwd_dkdv(q, k, v, do, ws2, causal=causal)
     torch.cuda.synchronize()
     for a, b, c in zip(g1, g2, (dq3, dk3, dv3)):
         assert torch.isfinite(a.float()).all()
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
         assert torch.equal(a.view(torch.int16), c.view(torch.int16))
+    n = shape[0] * shape[1] * shape[2]
+    part = ws.numel() // 2
+    for lo in (0, part):  # D, then LSE * log2(e)
+        x = ws[lo: lo + 4 * n].view(torch.float32)
+        y = ws2[lo: lo + 4 * n].view(torch.float32)
+        torch.testing.assert_close(x, y, rtol=1e-5, atol=1e-5)
+    for a, b in ((dk3, dk4), (dv3, dv4)):
+        torch.testing.assert_close(a.float(), b.float(), rtol=0, atol=2e-2 * a.float().abs().max().item())
 
 
 def test_preprocess_matches_rowsum():
