@@ -5,6 +5,11 @@
     # turn a rocprofv3 --stats kernel_stats.csv into a short text summary
     python -m exact_io_aware_42_amd.profiling stats --csv run_kernel_stats.csv \
         --out profiles/kernels_<workload>.txt --title "..." --cmd "rocprofv3 ..."
+    # the same from run_kernel_trace.csv, one line per (kernel, grid size); --last N keeps
+    # the last N dispatches of each line (the timed steps after the warm-up); --workgroups
+    # keeps only launches of the given grid sizes
+    python -m exact_io_aware_42_amd.profiling trace --csv run_kernel_trace.csv \
+        --out profiles/kernels_<workload>.txt --title "..." --cmd "rocprofv3 ..." [--last N]
     # turn counter CSVs into profiles/traffic_<kernel>_<workload>.txt
     python -m exact_io_aware_42_amd.profiling traffic --kernel fa2_fwd_kernel \\
         --workload w4_full --fetch run_fetch.csv --write run_write.csv \\
@@ -122,6 +127,33 @@ def stats_main(a):
     print(open(a.out).read())
 
 
+def trace_main(a):
+    groups = {}
+    with open(a.csv) as f:
+        for r in csv.DictReader(f):
+            key = (short_name(r["Kernel_Name"]), int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"]))
+            if a.workgroups and key[1] not in a.workgroups:
+                continue
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            groups.setdefault(key, []).append((int(r["Start_Timestamp"]), dur))
+    total = sum(d for v in groups.values() for _, d in v)
+    rows = []
+    for (name, wgs), v in groups.items():
+        v.sort()
+        sel = [d for _, d in v][-a.last:] if a.last else [d for _, d in v]
+        rows.append((name, wgs, len(v), len(sel), statistics.mean(sel), min(sel), max(sel),
+                     100.0 * sum(d for _, d in v) / total))
+    rows.sort(key=lambda x: -x[7])
+    with open(a.out, "w") as f:
+        f.write(f"# rocprofv3 kernel trace: {a.title}\n")
+        f.write(f"# command: {a.cmd}\n")
+        f.write("# kernel | workgroups | dispatches | dispatches averaged (last) | average us | "
+                "min us | max us | share of GPU time\n")
+        for n, w, c, k, avg, mn, mx, pct in rows:
+            f.write(f"{n} | {w} | {c} | {k} | {avg:.1f} | {mn:.1f} | {mx:.1f} | {pct:.1f}%\n")
+    print(open(a.out).read())
+
+
 def traffic_main(a):
     fetch = statistics.median(counter_values(a.fetch, "FETCH_SIZE", a.kernel))
     write = statistics.median(counter_values(a.write, "WRITE_SIZE", a.kernel))
@@ -158,6 +190,14 @@ def main(argv=None):
     st.add_argument("--out", required=True)
     st.add_argument("--title", required=True)
     st.add_argument("--cmd", required=True)
+    tr = sub.add_parser("trace")
+    tr.add_argument("--csv", required=True)
+    tr.add_argument("--out", required=True)
+    tr.add_argument("--title", required=True)
+    tr.add_argument("--cmd", required=True)
+    tr.add_argument("--last", type=int, default=0)
+    tr.add_argument("--workgroups", type=lambda x: [int(v) for v in x.split(",")], default=None,
+                    help="keep only launches with these workgroup counts")
     t = sub.add_parser("traffic")
     t.add_argument("--kernel", required=True, choices=sorted(KERNEL_SOURCES))
     t.add_argument("--workload", required=True)
@@ -174,6 +214,8 @@ def main(argv=None):
         copy_main(a.mib)
     elif a.sub == "stats":
         stats_main(a)
+    elif a.sub == "trace":
+        trace_main(a)
     else:
         traffic_main(a)
 
