@@ -16,9 +16,17 @@ constexpr double kLog2e = 1.4426950408889634074;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Shared size checks. Returns FA2_OK or the status to report.
-fa2_status check_sizes(int B, int H, int N, int d, float scale) {
-  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return FA2_ERR_INVALID_ARGUMENT;
+// Shared size checks. Returns FA2_OK or the status to report; *empty is set when B, H or N is 0
+// (a valid call with nothing to compute).
+fa2_status check_sizes(int B, int H, int N, int d, float scale, bool* empty) {
+  *empty = false;
+  if (B < 0 || H < 0 || N < 0 || d <= 0) return FA2_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(scale) || !(scale > 0.0f)) return FA2_ERR_INVALID_ARGUMENT;
+  if (d != 64 && d != 128) return FA2_ERR_UNSUPPORTED;
+  if (B == 0 || H == 0 || N == 0) {
+    *empty = true;
+    return FA2_OK;
+  }
   if (!std::isfinite(scale) || !(scale > 0.0f)) return FA2_ERR_INVALID_ARGUMENT;
   const unsigned long long elems =
       (unsigned long long)B * (unsigned long long)H * (unsigned long long)N * (unsigned long long)d;
@@ -29,7 +37,6 @@ fa2_status check_sizes(int B, int H, int N, int d, float scale) {
   // the workgroup grid (B*H*ceil(N/64)) must fit a 32-bit dimension
   if ((unsigned long long)B * H * ((unsigned long long)(N + 63) / 64) > 0x7fffffffull)
     return FA2_ERR_INVALID_ARGUMENT;
-  if (d != 64 && d != 128) return FA2_ERR_UNSUPPORTED;
   return FA2_OK;
 }
 
@@ -47,8 +54,9 @@ extern "C" {
 
 fa2_status fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                    int H, int N, int d, int causal, float softmax_scale, hipStream_t stream) {
-  const fa2_status st = check_sizes(B, H, N, d, softmax_scale);
-  if (st != FA2_OK) return st;
+  bool empty;
+  const fa2_status st = check_sizes(B, H, N, d, softmax_scale, &empty);
+  if (st != FA2_OK || empty) return st;
   const void* ptrs[] = {q, k, v, o, lse};
   for (const void* p : ptrs)
     if (p == nullptr || !aligned16(p)) return FA2_ERR_INVALID_ARGUMENT;
@@ -73,7 +81,8 @@ fa2_status fa2_fwd(const void* q, const void* k, const void* v, void* o, float* 
 static size_t ws_part_bytes(int B, int H, int N) { return round256((size_t)B * H * N * sizeof(float)); }
 
 size_t fa2_bwd_workspace_bytes(int B, int H, int N, int d) {
-  if (check_sizes(B, H, N, d, 1.0f) != FA2_OK) return 0;
+  bool empty;
+  if (check_sizes(B, H, N, d, 1.0f, &empty) != FA2_OK || empty) return 0;
   return 2 * ws_part_bytes(B, H, N);
 }
 
@@ -82,9 +91,9 @@ namespace {
 fa2_status bwd_args(const void* q, const void* k, const void* v, const void* o, const void* dout,
                     const float* lse, void* workspace, size_t workspace_bytes, void* dq, void* dk,
                     void* dv, int B, int H, int N, int d, int causal, float softmax_scale,
-                    hipStream_t stream, fa2::BwdArgs* a) {
-  const fa2_status st = check_sizes(B, H, N, d, softmax_scale);
-  if (st != FA2_OK) return st;
+                    hipStream_t stream, fa2::BwdArgs* a, bool* empty) {
+  const fa2_status st = check_sizes(B, H, N, d, softmax_scale, empty);
+  if (st != FA2_OK || *empty) return st;
   if (workspace == nullptr || !aligned16(workspace) ||
       workspace_bytes < fa2_bwd_workspace_bytes(B, H, N, d))
     return FA2_ERR_INVALID_ARGUMENT;
@@ -123,9 +132,10 @@ fa2_status fa2_bwd(const void* q, const void* k, const void* v, const void* o, c
                    size_t workspace_bytes, int B, int H, int N, int d, int causal,
                    float softmax_scale, hipStream_t stream) {
   fa2::BwdArgs a;
+  bool empty;
   const fa2_status st = bwd_args(q, k, v, o, dout, lse, workspace, workspace_bytes, dq, dk, dv,
-                                 B, H, N, d, causal, softmax_scale, stream, &a);
-  if (st != FA2_OK) return st;
+                                 B, H, N, d, causal, softmax_scale, stream, &a, &empty);
+  if (st != FA2_OK || empty) return st;
   if (!all_ok({q, k, v, o, dout, lse, dq, dk, dv})) return FA2_ERR_INVALID_ARGUMENT;
   return from_hip(fa2::launch_bwd(a));
 }
@@ -134,10 +144,11 @@ fa2_status fa2_bwd_preprocess(const void* o, const void* dout, const float* lse,
                               size_t workspace_bytes, int B, int H, int N, int d,
                               hipStream_t stream) {
   fa2::BwdArgs a;
+  bool empty;
   const fa2_status st = bwd_args(nullptr, nullptr, nullptr, o, dout, lse, workspace,
                                  workspace_bytes, nullptr, nullptr, nullptr, B, H, N, d, 0, 1.0f,
-                                 stream, &a);
-  if (st != FA2_OK) return st;
+                                 stream, &a, &empty);
+  if (st != FA2_OK || empty) return st;
   if (!all_ok({o, dout, lse})) return FA2_ERR_INVALID_ARGUMENT;
   return from_hip(fa2::launch_bwd_pre(a));
 }
@@ -146,10 +157,11 @@ fa2_status fa2_bwd_dkdv(const void* q, const void* k, const void* v, const void*
                         const void* workspace, size_t workspace_bytes, void* dk, void* dv, int B,
                         int H, int N, int d, int causal, float softmax_scale, hipStream_t stream) {
   fa2::BwdArgs a;
+  bool empty;
   const fa2_status st = bwd_args(q, k, v, nullptr, dout, nullptr, const_cast<void*>(workspace),
                                  workspace_bytes, nullptr, dk, dv, B, H, N, d, causal,
-                                 softmax_scale, stream, &a);
-  if (st != FA2_OK) return st;
+                                 softmax_scale, stream, &a, &empty);
+  if (st != FA2_OK || empty) return st;
   if (!all_ok({q, k, v, dout, dk, dv})) return FA2_ERR_INVALID_ARGUMENT;
   return from_hip(fa2::launch_bwd_dkdv(a));
 }
@@ -159,9 +171,10 @@ fa2_status fa2_bwd_dq(const void* q, const void* k, const void* v, const void* o
                       size_t workspace_bytes, void* dq, int B, int H, int N, int d, int causal,
                       float softmax_scale, hipStream_t stream) {
   fa2::BwdArgs a;
+  bool empty;
   const fa2_status st = bwd_args(q, k, v, o, dout, lse, workspace, workspace_bytes, dq, nullptr,
-                                 nullptr, B, H, N, d, causal, softmax_scale, stream, &a);
-  if (st != FA2_OK) return st;
+                                 nullptr, B, H, N, d, causal, softmax_scale, stream, &a, &empty);
+  if (st != FA2_OK || empty) return st;
   if (!all_ok({q, k, v, o, dout, lse, dq})) return FA2_ERR_INVALID_ARGUMENT;
   return from_hip(fa2::launch_bwd_dq(a));
 }

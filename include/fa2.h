@@ -24,7 +24,10 @@
  *   [B, H, N, d] with d fastest. lse: float32 [B, H, N], natural log. All pointers are
  *   device pointers and must be 16-byte aligned. B*H*N*d may exceed 2^31 (64-bit offsets);
  *   one head's slice must stay below 2 GiB (N*d*2 < 2^31 bytes, i.e. N < 8M at d = 128).
- *   Supported head dimensions: d = 64 and d = 128. N >= 1 (any N; ragged tails are masked).
+ *   Supported head dimensions: d = 64 and d = 128. Any N >= 1 (ragged tails are masked).
+ *   Empty problems (B, H or N equal to 0, the others >= 0) are valid: the call checks d and
+ *   the scale, does nothing else (pointers are not examined, no HIP call) and returns FA2_OK;
+ *   fa2_bwd_workspace_bytes is then 0.
  *
  * Ownership
  *   The caller allocates and owns every buffer. The library never allocates or frees
@@ -33,10 +36,9 @@
  *
  * Asynchrony and errors
  *   Arguments are validated on the host before any HIP call. Invalid arguments return
- *   FA2_ERR_INVALID_ARGUMENT (null or misaligned pointers, sizes <= 0, a non-finite scale,
- *   a scale that is not > 0, a workspace that is too small, sizes beyond the limits above);
- *   an unsupported head
- *   dimension returns FA2_ERR_UNSUPPORTED. Otherwise the kernels are enqueued on `stream`
+ *   FA2_ERR_INVALID_ARGUMENT (null or misaligned pointers, negative sizes or d <= 0, a
+ *   non-finite scale, a scale that is not > 0, a workspace that is too small, sizes beyond the
+ *   limits above); an unsupported head dimension returns FA2_ERR_UNSUPPORTED. Otherwise the kernels are enqueued on `stream`
  *   (0 = the default stream) and the call returns FA2_OK, or FA2_ERR_HIP when the launch
  *   fails (the HIP error code is then available from fa2_last_hip_error()). Results are
  *   valid once the stream has been synchronised. No C++ exception crosses this interface.
@@ -68,7 +70,7 @@ fa2_status fa2_fwd(const void* q, const void* k, const void* v, void* o, float* 
 
 /* Bytes of device workspace the backward needs for these sizes: two fp32 [B,H,N] arrays (the
  * row term D = rowsum(dO*O) and LSE*log2(e)), each rounded up to 256 bytes. Returns 0 for
- * invalid sizes. */
+ * invalid or empty sizes. */
 size_t fa2_bwd_workspace_bytes(int B, int H, int N, int d);
 
 /* Backward pass. Inputs: q, k, v, the forward output o and its lse (from fa2_fwd with the

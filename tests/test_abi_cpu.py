@@ -55,9 +55,16 @@ P = 0x10000
 @pytest.mark.parametrize("args,expect", [
     ((None, P, P, P, P, 1, 1, 16, 64, 0, 0.125), ops.FA2_ERR_INVALID_ARGUMENT),   # null q
     ((P, P, P, P, P + 4, 1, 1, 16, 64, 0, 0.125), ops.FA2_ERR_INVALID_ARGUMENT),  # misaligned lse
-    ((P, P, P, P, P, 0, 1, 16, 64, 0, 0.125), ops.FA2_ERR_INVALID_ARGUMENT),      # B = 0
+    ((P, P, P, P, P, -1, 1, 16, 64, 0, 0.125), ops.FA2_ERR_INVALID_ARGUMENT),     # B < 0
     ((P, P, P, P, P, 1, -1, 16, 64, 0, 0.125), ops.FA2_ERR_INVALID_ARGUMENT),     # H < 0
-    ((P, P, P, P, P, 1, 1, 0, 64, 0, 0.125), ops.FA2_ERR_INVALID_ARGUMENT),       # N = 0
+    ((P, P, P, P, P, 1, 1, -5, 64, 0, 0.125), ops.FA2_ERR_INVALID_ARGUMENT),      # N < 0
+    ((P, P, P, P, P, 1, 1, 16, 0, 0, 0.125), ops.FA2_ERR_INVALID_ARGUMENT),       # d = 0
+    # empty problems are valid no-ops, even with null pointers (never examined)
+    ((None, None, None, None, None, 0, 1, 16, 64, 0, 0.125), ops.FA2_OK),         # B = 0
+    ((None, None, None, None, None, 2, 0, 16, 128, 1, 0.125), ops.FA2_OK),        # H = 0
+    ((None, None, None, None, None, 1, 1, 0, 64, 1, 0.125), ops.FA2_OK),          # N = 0
+    ((None, None, None, None, None, 1, 1, 0, 96, 0, 0.125), ops.FA2_ERR_UNSUPPORTED),
+    ((None, None, None, None, None, 1, 1, 0, 64, 0, float("nan")), ops.FA2_ERR_INVALID_ARGUMENT),
     ((P, P, P, P, P, 1, 1, 16, 64, 0, float("nan")), ops.FA2_ERR_INVALID_ARGUMENT),
     ((P, P, P, P, P, 1, 1, 16, 64, 0, float("inf")), ops.FA2_ERR_INVALID_ARGUMENT),
     ((P, P, P, P, P, 1, 1, 16, 64, 0, 0.0), ops.FA2_ERR_INVALID_ARGUMENT),
@@ -76,6 +83,14 @@ def test_bwd_validation_and_workspace():
     ws = lib.fa2_bwd_workspace_bytes(2, 3, 100, 64)
     assert ws >= 2 * (2 * 3 * 100 * 4) and ws % 256 == 0
     assert lib.fa2_bwd_workspace_bytes(0, 3, 100, 64) == 0
+    assert lib.fa2_bwd_workspace_bytes(2, 3, 0, 64) == 0
+    assert lib.fa2_bwd_workspace_bytes(-1, 3, 10, 64) == 0
+    # empty backward problems: no-ops that never look at the (null) pointers
+    nul = [None] * 10
+    assert lib.fa2_bwd(*nul, 0, 2, 3, 0, 64, 1, 0.125, None) == ops.FA2_OK
+    assert lib.fa2_bwd_dq(*nul[:7], 0, None, 0, 3, 5, 128, 0, 0.125, None) == ops.FA2_OK
+    assert lib.fa2_bwd_dkdv(*nul[:5], 0, None, None, 1, 0, 5, 64, 1, 0.125, None) == ops.FA2_OK
+    assert lib.fa2_bwd_preprocess(*nul[:4], 0, 1, 1, 0, 64, None) == ops.FA2_OK
     assert lib.fa2_bwd_workspace_bytes(1, 1, 100, 80) == 0
     base = [P] * 10
     ok_sizes = (2, 3, 100, 64, 1, 0.125)

@@ -143,3 +143,20 @@ def test_preprocess_matches_rowsum():
     np.testing.assert_allclose(got, want, rtol=1e-5, atol=1e-4)
     got2 = ws[part: part + n * 4].view(torch.float32).cpu().double().numpy().reshape(2, 2, 130)
     np.testing.assert_allclose(got2, lse.cpu().double().numpy() * np.log2(np.e), rtol=1e-6)
+
+
+@pytest.mark.parametrize("shape", [(0, 2, 16, 64), (1, 0, 16, 128), (1, 2, 0, 64), (2, 3, 0, 128)])
+def test_empty_problems_are_no_ops(shape):
+    """B, H or N equal to 0: forward and backward return empty outputs without a launch
+    (the library returns FA2_OK without examining the pointers)."""
+    fa2 = _fa2()
+    dev = torch.device("cuda:0")
+    q, k, v, do = (torch.empty(shape, dtype=torch.bfloat16, device=dev) for _ in range(4))
+    for causal in (False, True):
+        o, lse = fa2.fwd(q, k, v, causal=causal)
+        assert o.shape == shape and lse.shape == shape[:3]
+        dq, dk, dv = fa2.bwd(q, k, v, o, do, lse, causal=causal)
+        for g in (dq, dk, dv):
+            assert g.shape == shape
+    assert fa2.bwd_workspace_bytes(*shape) == 0
+    torch.cuda.synchronize()
