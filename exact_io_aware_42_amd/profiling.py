@@ -10,6 +10,10 @@
     # keeps only launches of the given grid sizes
     python -m exact_io_aware_42_amd.profiling trace --csv run_kernel_trace.csv \
         --out profiles/kernels_<workload>.txt --title "..." --cmd "rocprofv3 ..." [--last N]
+    # effective clock per kernel: GRBM_GUI_ACTIVE (summed over the 8 XCDs) of each dispatch
+    # over its kernel-trace duration, from one rocprofv3 --kernel-trace --pmc GRBM_GUI_ACTIVE run
+    python -m exact_io_aware_42_amd.profiling clock --dir <rocprofv3 output dir> \
+        --out profiles/clock_<workload>.txt --title "..." --cmd "rocprofv3 ..."
     # turn counter CSVs into profiles/traffic_<kernel>_<workload>.txt
     python -m exact_io_aware_42_amd.profiling traffic --kernel fa2_fwd_kernel \\
         --workload w4_full --fetch run_fetch.csv --write run_write.csv \\
@@ -154,6 +158,36 @@ def trace_main(a):
     print(open(a.out).read())
 
 
+def clock_main(a):
+    counters, names, durs = {}, {}, {}
+    with open(os.path.join(a.dir, "run_counter_collection.csv")) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                did = int(r["Dispatch_Id"])
+                counters[did] = float(r["Counter_Value"])
+                names[did] = short_name(r["Kernel_Name"])
+    with open(os.path.join(a.dir, "run_kernel_trace.csv")) as f:
+        for r in csv.DictReader(f):
+            durs[int(r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e9
+    groups = {}
+    for did, c in counters.items():
+        if did in durs:
+            groups.setdefault(names[did], []).append((did, c, durs[did]))
+    with open(a.out, "w") as f:
+        f.write(f"# effective shader clock: {a.title}\n")
+        f.write(f"# command: {a.cmd}\n")
+        f.write("# GRBM_GUI_ACTIVE per dispatch is summed over the 8 XCDs; clock = value / 8 / "
+                "duration. Second half of the dispatches (after warm-up).\n")
+        f.write("# kernel | dispatches used | average us | GRBM_GUI_ACTIVE / 8 | clock GHz\n")
+        for n, v in sorted(groups.items()):
+            v.sort()
+            v = v[len(v) // 2:]
+            c = statistics.mean(x[1] for x in v) / 8
+            t = statistics.mean(x[2] for x in v)
+            f.write(f"{n} | {len(v)} | {t * 1e6:.1f} | {c:.4g} | {c / t / 1e9:.3f}\n")
+    print(open(a.out).read())
+
+
 def traffic_main(a):
     fetch = statistics.median(counter_values(a.fetch, "FETCH_SIZE", a.kernel))
     write = statistics.median(counter_values(a.write, "WRITE_SIZE", a.kernel))
@@ -198,6 +232,11 @@ def main(argv=None):
     tr.add_argument("--last", type=int, default=0)
     tr.add_argument("--workgroups", type=lambda x: [int(v) for v in x.split(",")], default=None,
                     help="keep only launches with these workgroup counts")
+    ck = sub.add_parser("clock")
+    ck.add_argument("--dir", required=True)
+    ck.add_argument("--out", required=True)
+    ck.add_argument("--title", required=True)
+    ck.add_argument("--cmd", required=True)
     t = sub.add_parser("traffic")
     t.add_argument("--kernel", required=True, choices=sorted(KERNEL_SOURCES))
     t.add_argument("--workload", required=True)
@@ -216,6 +255,8 @@ def main(argv=None):
         stats_main(a)
     elif a.sub == "trace":
         trace_main(a)
+    elif a.sub == "clock":
+        clock_main(a)
     else:
         traffic_main(a)
 
