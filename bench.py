@@ -101,12 +101,13 @@ def cpu_baseline(w, causal, with_bwd, budget_s):
     }
 
 
-FWD_SWEEP = ((2, False), (2, True), (3, True), (4, True), (4, False))
+FWD_SWEEP = ((2, False), (2, True), (3, True), (4, True), (4, False), (6, True), (6, False))
 
 
 def forward_sweep(fa2, torch, dev, reps=10, warm_ms=60.0):
     """Forward-only TFLOP/s of the forward workloads (B=8 H=32 N=2048 d=64 both masks,
-    B=4 H=16 N=4096 d=128 causal, B=1 H=16 N=16384 d=128 both masks). All inputs are made
+    B=4 H=16 N=4096 d=128 causal, B=1 H=16 N=16384 d=128 both masks, B=2 H=16 N=4096 d=256
+    both masks). All inputs are made
     and copied to the device first; each case then runs back to back for at least `warm_ms`
     of GPU time before `reps` calls are timed with HIP events on the launch stream."""
     import numpy as np

@@ -113,13 +113,15 @@ __device__ __forceinline__ int kmap(int m) {
 //   (b) transposing reads: 32 lanes read rows 4a .. 4a+3, four adjacent chunks per row.
 // For D = 128 a row is the whole 256-byte bank window: (a) needs swz injective on 16 rows, (b)
 // needs bits 2-3 of swz to differ across rows 4a .. 4a+3; ((row & 3) << 2) | ((row >> 2) & 3)
-// does both. For D = 64 two rows share the window (row parity picks the half), so swz must be
-// injective on rows of one parity for (a) and differ in bit 2 between rows 4a and 4a+2 (and
-// 4a+1, 4a+3) for (b): (bit 1 of row) << 2 | ((row >> 2) & 3).
+// does both. For D = 256 a row spans two windows and every row starts on a window boundary,
+// so the bank of a chunk depends on its index mod 16 only: the D = 128 swizzle applies to chunk
+// bits 0-3 (chunk bit 4 is unchanged). For D = 64 two rows share the window (row parity picks
+// the half), so swz must be injective on rows of one parity for (a) and differ in bit 2
+// between rows 4a and 4a+2 (and 4a+1, 4a+3) for (b): (bit 1 of row) << 2 | ((row >> 2) & 3).
 template <int D>
 __device__ __forceinline__ int swz(int row) {
-  static_assert(D == 64 || D == 128, "head dimension");
-  if constexpr (D == 128) return ((row & 3) << 2) | ((row >> 2) & 3);
+  static_assert(D == 64 || D == 128 || D == 256, "head dimension");
+  if constexpr (D >= 128) return ((row & 3) << 2) | ((row >> 2) & 3);
   return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
 

@@ -47,16 +47,20 @@ namespace {
 #endif
 
 constexpr int kFwdBR = 128;
-constexpr int kFwdBC = 64;
 constexpr int kFwdThreads = 256;
 constexpr float kRescaleThreshold = 8.0f;  // log2 units: exponentials stay <= 2^8
 
+// Key tiles of 64 for d <= 128; of 32 at d = 256, where O^T (128 registers) and the resident
+// Q^T fragments (64) leave room for one 32-key score block only. A K or V tile is 16 KiB
+// (8 KiB at d = 64) either way.
 template <int D>
 struct FwdShape {
+  static constexpr int BC = D == 256 ? 32 : 64;  // keys per tile
+  static constexpr int KB = BC / 32;             // 32-key MFMA blocks per tile
   static constexpr int DCH = D / 8;            // 16-byte chunks per K/V row
   static constexpr int KK = D / 16;            // MFMA k-steps of the score GEMM
   static constexpr int CB = D / 32;            // 32-row blocks of O^T
-  static constexpr int TILE_BYTES = kFwdBC * D * 2;
+  static constexpr int TILE_BYTES = BC * D * 2;
   static constexpr int LOADS = TILE_BYTES / (kFwdThreads * 16);  // 16-byte loads per lane per tile
   static constexpr int K_SLOT0 = 0;
   static constexpr int V_SLOT0 = 2 * TILE_BYTES;
@@ -91,60 +95,65 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
   const int my_q = q_wave0 + l32;
 
   // ---- key tiles this workgroup visits, and the last one not fully masked for this wave
-  int n_tiles = (N + kFwdBC - 1) / kFwdBC;
-  if (CAUSAL) n_tiles = min(N - 1, q_block0 + kFwdBR - 1) / kFwdBC + 1;
-  const int wave_last = CAUSAL ? min(n_tiles - 1, (q_wave0 + 31) / kFwdBC) : n_tiles - 1;
+  constexpr int BC = S::BC;
+  int n_tiles = (N + BC - 1) / BC;
+  if (CAUSAL) n_tiles = min(N - 1, q_block0 + kFwdBR - 1) / BC + 1;
+  const int wave_last = CAUSAL ? min(n_tiles - 1, (q_wave0 + 31) / BC) : n_tiles - 1;
 
   // ---- HBM -> LDS tile loads. Load r of wave w writes the 1 KiB block i = 4r + w of the tile
   // (lane l -> chunk p = 64i + l: row p / DCH, physical chunk p % DCH) and fetches the logical
-  // chunk the row's XOR swizzle maps there. Block 4r + w starts at row 4*(64/DCH)*r + ..., a
-  // multiple of 16, so the swizzle (row bits 0-3) does not depend on r and one per-lane offset
-  // serves every load (r adds a constant).
-  constexpr int kRowsPerBlock = 64 / S::DCH;
-  uint32_t koff0, voff0;
-  {
-    const int p = wave * 64 + lane;
+  // chunk the row's XOR swizzle maps there. For d <= 128, block 4r + w starts 4*(64/DCH)*r
+  // rows (a multiple of 16) after block w, so the swizzle (row bits 0-3) does not depend on r
+  // and r only adds a constant; at d = 256 (2 rows per block) each load has its own offset.
+  uint32_t koff[S::LOADS];
+#pragma unroll
+  for (int r = 0; r < S::LOADS; ++r) {
+    const int p = (4 * r + wave) * 64 + lane;
     const int row = p / S::DCH;
     const int pc = p % S::DCH;
-    koff0 = (uint32_t)(row * D * 2 + (pc ^ swz<D>(row)) * 16);
-    voff0 = koff0;
+    koff[r] = (uint32_t)(row * D * 2 + (pc ^ swz<D>(row)) * 16);
   }
   auto load_k = [&](int j, int slot) {
 #pragma unroll
     for (int r = 0; r < S::LOADS; ++r)
       buffer_load16_to_lds(rk, smem + S::K_SLOT0 + slot * S::TILE_BYTES + (4 * r + wave) * 1024,
-                           koff0 + r * 4 * kRowsPerBlock * D * 2, (uint32_t)j * kFwdBC * D * 2);
+                           koff[r], (uint32_t)j * BC * D * 2);
   };
   auto load_v = [&](int j, int slot) {
 #pragma unroll
     for (int r = 0; r < S::LOADS; ++r)
       buffer_load16_to_lds(rv, smem + S::V_SLOT0 + slot * S::TILE_BYTES + (4 * r + wave) * 1024,
-                           voff0 + r * 4 * kRowsPerBlock * D * 2, (uint32_t)j * kFwdBC * D * 2);
+                           koff[r], (uint32_t)j * BC * D * 2);
   };
 
   // ---- per-lane LDS read offsets (bytes within a tile). The swizzle depends on row bits 0-3
-  // only, so 32-row block kb and 16-row step u become immediates.
+  // and permutes chunk bits 0-3 only, so 32-row block kb, 16-row step u and chunk bit 4
+  // (+256 bytes, d = 256) become immediates.
   // K (A operand of S^T): row 32kb + kmap(l32), logical chunk 2kk + g.
+  constexpr int KB8 = S::KK < 8 ? S::KK : 8;
   const int krow = kmap(l32);
-  int kbase[S::KK];
+  int kbase[KB8];
 #pragma unroll
-  for (int kk = 0; kk < S::KK; ++kk) kbase[kk] = krow * D * 2 + ((2 * kk + g) ^ swz<D>(krow)) * 16;
-  auto k_off = [&](int kb, int kk) { return kbase[kk] + kb * 32 * D * 2; };
+  for (int kk = 0; kk < KB8; ++kk) kbase[kk] = krow * D * 2 + ((2 * kk + g) ^ swz<D>(krow)) * 16;
+  auto k_off = [&](int kb, int kk) { return kbase[kk % 8] + (kk / 8) * 256 + kb * 32 * D * 2; };
   // V^T fragments (A operand of O^T) via the transposing read: 16-lane group G = lane/16 covers
   // d rows c0 = 32cb + 16(G%2) .. +15 and k-slots 8g .. 8g+7 = keys 16u + 8g + 4h + (0..3).
   // Lane j of the group addresses key row 16u + 8g + 4h + j/4, columns c0 + 4(j%4) .. +3.
+  constexpr int CB4 = S::CB < 4 ? S::CB : 4;
   const int jl = lane & 15;
   const int grp = lane >> 4;
-  int vbase[S::CB][2];
+  int vbase[CB4][2];
 #pragma unroll
-  for (int cb = 0; cb < S::CB; ++cb)
+  for (int cb = 0; cb < CB4; ++cb)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int row = 8 * g + 4 * h + jl / 4;
       const int col = 32 * cb + 16 * (grp & 1) + 4 * (jl & 3);
       vbase[cb][h] = row * D * 2 + (((col >> 3) ^ swz<D>(row)) * 16) + (col & 7) * 2;
     }
-  auto v_off = [&](int cb, int u, int h) { return vbase[cb][h] + 16 * u * D * 2; };
+  auto v_off = [&](int cb, int u, int h) {
+    return vbase[cb % 4][h] + (cb / 4) * 256 + 16 * u * D * 2;
+  };
 
   // ---- Q^T fragments (B operand of S^T): lane holds q[my_q][16kk + 8g .. +7]; zeros past N
   u32x4_t qf[S::KK];
@@ -161,13 +170,13 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
 
   // hidden-key bias for tile j: -inf where key >= N or (causal) key > query
   auto tile_needs_mask = [&](int j) {
-    const int key0 = j * kFwdBC;
-    return (key0 + kFwdBC > N) || (CAUSAL && key0 + kFwdBC - 1 > q_wave0);
+    const int key0 = j * BC;
+    return (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > q_wave0);
   };
   auto mask_bias = [&](int j, f32x16_t* s) {
-    const int key0 = j * kFwdBC;
+    const int key0 = j * BC;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < S::KB; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = key0 + kb * 32 + (i / 8) * 16 + g * 8 + (i % 8);
@@ -175,36 +184,40 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
         s[kb][i] = hidden ? -INFINITY : 0.f;
       }
   };
-  // S^T tile j from K slot `slot`: two 32-key blocks x 32 queries
+  // S^T tile j from K slot `slot`: KB 32-key blocks x 32 queries
   auto scores = [&](int slot, bool masked, int j, f32x16_t* s) {
     const unsigned char* kt = smem + S::K_SLOT0 + slot * S::TILE_BYTES;
     if (masked) mask_bias(j, s);
 #pragma unroll
     for (int kk = 0; kk < S::KK; ++kk)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < S::KB; ++kb) {
         const u32x4_t a = *reinterpret_cast<const u32x4_t*>(kt + k_off(kb, kk));
         s[kb] = (kk == 0 && !masked) ? mfma32(a, qf[kk], f32x16_t{}) : mfma32(a, qf[kk], s[kb]);
       }
   };
-  // four independent chains of 3-input maxima over the 32 scores of the lane
+  // 2*KB independent chains of 3-input maxima over the 16*KB scores of the lane
   auto row_max = [&](const f32x16_t* s) {
-    float a[4];
+    constexpr int NC = 2 * S::KB;
+    float a[NC];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) a[c] = fmaxf(s[c / 2][8 * (c % 2)], s[c / 2][8 * (c % 2) + 1]);
+    for (int c = 0; c < NC; ++c) a[c] = fmaxf(s[c / 2][8 * (c % 2)], s[c / 2][8 * (c % 2) + 1]);
 #pragma unroll
     for (int i = 2; i < 8; i += 2)
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
+      for (int c = 0; c < NC; ++c)
         a[c] = fmaxf(a[c], fmaxf(s[c / 2][8 * (c % 2) + i], s[c / 2][8 * (c % 2) + i + 1]));
-    return max_xor32(fmaxf(fmaxf(a[0], a[1]), fmaxf(a[2], a[3]))) * scale_log2;
+    float m = fmaxf(a[0], a[1]);
+#pragma unroll
+    for (int c = 2; c < NC; c += 2) m = fmaxf(m, fmaxf(a[c], a[c + 1]));
+    return max_xor32(m) * scale_log2;
   };
   // p = exp2(s*c - m) -> packed bf16 (the PV B operand); partial sum of p
   auto probs = [&](const f32x16_t* s, uint32_t (*pk)[8]) {
     const float neg_m = -m_run;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < S::KB; ++kb)
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const float p0 = fast_exp2(__builtin_fmaf(s[kb][2 * i], scale_log2, neg_m));
@@ -220,7 +233,7 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
   auto bf16_correction = [&](uint32_t (*pk)[8], float tile_sum) {
     float b[2] = {0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < S::KB; ++kb)
 #pragma unroll
       for (int i = 0; i < 8; ++i) b[kb] = add_bf16_pair(b[kb], pk[kb][i]);
     l_corr += (b[0] + b[1]) - tile_sum;
@@ -230,7 +243,7 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
   auto pv = [&](int slot, uint32_t (*pk)[8]) {
     const unsigned char* vt = smem + S::V_SLOT0 + slot * S::TILE_BYTES;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 2 * S::KB; ++u) {
       const u32x4_t b = {pk[u / 2][4 * (u % 2) + 0], pk[u / 2][4 * (u % 2) + 1],
                          pk[u / 2][4 * (u % 2) + 2], pk[u / 2][4 * (u % 2) + 3]};
 #pragma unroll
@@ -271,7 +284,7 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
       load_v(j + 1, slot ^ 1);
     }
     if (j <= wave_last) {
-      f32x16_t s[2];
+      f32x16_t s[S::KB];
       const bool masked = tile_needs_mask(j);
       if (masked) scores(slot, true, j, s);
       else scores(slot, false, j, s);
@@ -282,7 +295,7 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
       } else {
         maybe_rescale(m_tile);
       }
-      uint32_t pk[2][8];
+      uint32_t pk[S::KB][8];
       const float tile_sum = probs(s, pk);
       // raised priority while this wave issues its PV MFMAs: the other wave on the SIMD then
       // tends to run its softmax VALU work in between (measured +2-6%)
@@ -335,6 +348,7 @@ hipError_t launch_fwd_t(const FwdArgs& a) {
 
 hipError_t launch_fwd(const FwdArgs& a) {
   if (a.d == 64) return a.causal ? launch_fwd_t<64, true>(a) : launch_fwd_t<64, false>(a);
+  if (a.d == 256) return a.causal ? launch_fwd_t<256, true>(a) : launch_fwd_t<256, false>(a);
   return a.causal ? launch_fwd_t<128, true>(a) : launch_fwd_t<128, false>(a);
 }
 

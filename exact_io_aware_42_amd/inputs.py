@@ -100,6 +100,8 @@ WORKLOADS = {
     3: Workload(3, "GPT-style B4 H16 N4096 d128", 4, 16, 4096, 128, (True,)),
     4: Workload(4, "long sequence B1 H16 N16384 d128", 1, 16, 16384, 128, (True, False)),
     5: Workload(5, "fwd+bwd B4 H16 N2048 d128", 4, 16, 2048, 128, (True,), backward=True),
+    # head dimension 256 (forward), the largest the pages give for FlashAttention-2
+    6: Workload(6, "head dim 256 B2 H16 N4096 d256", 2, 16, 4096, 256, (True, False)),
 }
 
 

@@ -36,7 +36,8 @@ def run_fwd(bits_q, bits_k, bits_v, causal, scale):
 
 
 SMALL = [(1, 1, 1, 64), (1, 1, 1, 128), (1, 1, 5, 64), (2, 3, 77, 64), (1, 2, 200, 128),
-         (1, 1, 129, 128), (2, 1, 383, 64), (1, 2, 1000, 128), (1, 1, 2049, 64)]
+         (1, 1, 129, 128), (2, 1, 383, 64), (1, 2, 1000, 128), (1, 1, 2049, 64),
+         (1, 1, 1, 256), (1, 2, 31, 256), (2, 1, 161, 256), (1, 2, 700, 256)]
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -84,7 +85,7 @@ def test_workload_parity(wid, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_zero_queries_give_mean_of_values(d, causal):
     """Q = 0: uniform weights, O_i = mean of V (prefix mean under the causal mask),
     LSE_i = ln N (ln(i+1) causal)."""
@@ -102,7 +103,7 @@ def test_zero_queries_give_mean_of_values(d, causal):
     assert_fwd_close(bf16_to_f64(o), lse.cpu().double().numpy(), o_ref, lse_ref, "Q=0")
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_causal_row_zero_is_bitwise_first_value_row(d):
     shape = (2, 3, 257, d)
     bq, bk, bv = (normal_bf16(shape, 90 + t) for t in range(3))
@@ -113,10 +114,11 @@ def test_causal_row_zero_is_bitwise_first_value_row(d):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_single_key_gives_values(causal):
-    shape = (3, 5, 1, 128)
+@pytest.mark.parametrize("d", [128, 256])
+def test_single_key_gives_values(causal, d):
+    shape = (3, 5, 1, d)
     bq, bk, bv = (normal_bf16(shape, 95 + t) for t in range(3))
-    o, _ = run_fwd(bq, bk, bv, causal, default_scale(128))
+    o, _ = run_fwd(bq, bk, bv, causal, default_scale(d))
     np.testing.assert_array_equal(bits_of(o), bv)
 
 
