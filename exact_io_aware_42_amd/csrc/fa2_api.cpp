@@ -18,8 +18,8 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // Shared size checks. Returns FA2_OK or the status to report; *empty is set when B, H or N is 0
 // (a valid call with nothing to compute).
-// Head dimensions: 64 and 128 everywhere, 256 in the forward only (max_d).
-fa2_status check_sizes(int B, int H, int N, int d, float scale, bool* empty, int max_d) {
+// Head dimensions 64, 128 and 256.
+fa2_status check_sizes(int B, int H, int N, int d, float scale, bool* empty, int max_d = 256) {
   *empty = false;
   if (B < 0 || H < 0 || N < 0 || d <= 0) return FA2_ERR_INVALID_ARGUMENT;
   if (!std::isfinite(scale) || !(scale > 0.0f)) return FA2_ERR_INVALID_ARGUMENT;
@@ -56,7 +56,7 @@ extern "C" {
 fa2_status fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                    int H, int N, int d, int causal, float softmax_scale, hipStream_t stream) {
   bool empty;
-  const fa2_status st = check_sizes(B, H, N, d, softmax_scale, &empty, 256);
+  const fa2_status st = check_sizes(B, H, N, d, softmax_scale, &empty);
   if (st != FA2_OK || empty) return st;
   const void* ptrs[] = {q, k, v, o, lse};
   for (const void* p : ptrs)
@@ -83,7 +83,7 @@ static size_t ws_part_bytes(int B, int H, int N) { return round256((size_t)B * H
 
 size_t fa2_bwd_workspace_bytes(int B, int H, int N, int d) {
   bool empty;
-  if (check_sizes(B, H, N, d, 1.0f, &empty, 128) != FA2_OK || empty) return 0;
+  if (check_sizes(B, H, N, d, 1.0f, &empty) != FA2_OK || empty) return 0;
   return 2 * ws_part_bytes(B, H, N);
 }
 
@@ -93,7 +93,7 @@ fa2_status bwd_args(const void* q, const void* k, const void* v, const void* o, 
                     const float* lse, void* workspace, size_t workspace_bytes, void* dq, void* dk,
                     void* dv, int B, int H, int N, int d, int causal, float softmax_scale,
                     hipStream_t stream, fa2::BwdArgs* a, bool* empty) {
-  const fa2_status st = check_sizes(B, H, N, d, softmax_scale, empty, 128);
+  const fa2_status st = check_sizes(B, H, N, d, softmax_scale, empty);
   if (st != FA2_OK || *empty) return st;
   if (workspace == nullptr || !aligned16(workspace) ||
       workspace_bytes < fa2_bwd_workspace_bytes(B, H, N, d))

@@ -37,47 +37,51 @@ namespace {
 constexpr int kThreads = 256;
 constexpr float kLog2e = 1.4426950408889634f;
 
-// HBM -> LDS copy of a 64-row bf16 tile [64][D] starting at byte `soff` of buffer `r`, into
-// `dst` (row-major, swz<D>-swizzled 16-byte chunks, conflict-free for both the row-wise MFMA
-// operand reads and the transposing reads), by a workgroup of NT threads. Load i of wave w writes
-// the 1 KiB block (NT/64)i + w; block starts advance by a multiple of 16 rows per i, so the
-// swizzle bits of a row do not depend on i.
-template <int D, int NT = kThreads>
+// HBM -> LDS copy of a ROWS-row bf16 tile [ROWS][D] starting at byte `soff` of buffer `r`,
+// into `dst` (row-major, swz<D>-swizzled 16-byte chunks, conflict-free for both the row-wise
+// MFMA operand reads and the transposing reads), by a workgroup of NT threads. Load i of wave w
+// writes the 1 KiB block (NT/64)i + w, lane l its 16 bytes at 16l: the physical chunk
+// p = 64*block + l of the tile, which holds the logical chunk (p % DCH) ^ swz(row).
+template <int D, int NT = kThreads, int ROWS = 64>
 struct TileLoader {
   static constexpr int DCH = D / 8;
   static constexpr int WAVES = NT / 64;
-  static constexpr int LOADS = 64 * D * 2 / (NT * 16);
-  static constexpr int ROWS_PER_BLOCK = 64 / DCH;
-  static_assert(LOADS >= 1 && (WAVES * ROWS_PER_BLOCK) % 16 == 0, "tile loader shape");
-  uint32_t off0;
+  static constexpr int LOADS = ROWS * D * 2 / (NT * 16);
+  static_assert(LOADS >= 1 && LOADS * NT * 16 == ROWS * D * 2, "tile loader shape");
+  uint32_t off[LOADS];
   int wave;
   __device__ __forceinline__ TileLoader(int wave_, int lane) : wave(wave_) {
-    const int p = wave * 64 + lane;
-    const int row = p / DCH;
-    off0 = (uint32_t)(row * D * 2 + ((p % DCH) ^ swz<D>(row)) * 16);
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+      const int p = (WAVES * i + wave) * 64 + lane;
+      const int row = p / DCH;
+      off[i] = (uint32_t)(row * D * 2 + ((p % DCH) ^ swz<D>(row)) * 16);
+    }
   }
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, unsigned char* dst,
                                        uint32_t soff) const {
 #pragma unroll
     for (int i = 0; i < LOADS; ++i)
-      buffer_load16_to_lds(r, dst + (WAVES * i + wave) * 1024,
-                           off0 + i * WAVES * ROWS_PER_BLOCK * D * 2, soff);
+      buffer_load16_to_lds(r, dst + (WAVES * i + wave) * 1024, off[i], soff);
   }
 };
 
-// Per-lane byte offsets into a swizzled tile for the two read patterns.
+// Per-lane byte offsets into a swizzled tile for the two read patterns. The swizzle permutes
+// chunk bits 0-3 only, so at D = 256 chunk bit 4 (+256 bytes) is an immediate and 8 row and
+// 4 x 2 transposing bases cover every read.
 template <int D>
 struct TileReads {
   static constexpr int KK = D / 16, CB = D / 32;
-  int rbase[KK];     // row-wise operand reads: row 32*blk + kmap(l32), logical chunk 2kk + g
-  int tbase[CB][2];  // transposing reads: row 16u + 8g + 4h + j/4, column 32cb + 16(G%2) + 4(j%4)
+  static constexpr int KR = KK < 8 ? KK : 8, CR = CB < 4 ? CB : 4;
+  int rbase[KR];     // row-wise operand reads: row 32*blk + kmap(l32), logical chunk 2kk + g
+  int tbase[CR][2];  // transposing reads: row 16u + 8g + 4h + j/4, column 32cb + 16(G%2) + 4(j%4)
   __device__ __forceinline__ TileReads(int lane) {
     const int l32 = lane & 31, g = lane >> 5, jl = lane & 15, grp = lane >> 4;
     const int krow = kmap(l32);
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) rbase[kk] = krow * D * 2 + ((2 * kk + g) ^ swz<D>(krow)) * 16;
+    for (int kk = 0; kk < KR; ++kk) rbase[kk] = krow * D * 2 + ((2 * kk + g) ^ swz<D>(krow)) * 16;
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
+    for (int cb = 0; cb < CR; ++cb)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int row = 8 * g + 4 * h + jl / 4;
@@ -86,10 +90,10 @@ struct TileReads {
       }
   }
   __device__ __forceinline__ int row_off(int blk, int kk) const {
-    return rbase[kk] + blk * 32 * D * 2;
+    return rbase[kk % 8] + (kk / 8) * 256 + blk * 32 * D * 2;
   }
   __device__ __forceinline__ int tr_off(int cb, int u, int h) const {
-    return tbase[cb][h] + 16 * u * D * 2;
+    return tbase[cb % 4][h] + (cb / 4) * 256 + 16 * u * D * 2;
   }
 };
 
@@ -387,13 +391,218 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
 }
 
 // ---------------------------------------------------------------------------------------
-// dQ. Workgroup = 4 waves x 32 queries (lane = query, as in the forward); key tiles of 64.
-// S^T = K Q^T and dP^T = V dO^T from row-wise K/V tile reads with Q^T/dO^T fragments held in
-// VGPRs; dQ^T += K^T dS^T with K^T fragments from transposing reads of the same K tile.
-constexpr int kDqBR = 128;
-constexpr int kDqBC = 64;
+// dK, dV at d = 256. The fused form above would need 256 accumulator registers per wave, so here
+// a wave accumulates one of them: workgroup = 4 waves over 64 keys, wave w serves the 32 keys
+// 32(w%2) .. +31; waves 0-1 accumulate dV (S, P, dV^T += dO^T P) and waves 2-3 dK (S, dP, dS,
+// dK^T += Q^T dS), 128 accumulator registers each (S is formed by both waves of a key group:
+// 1.25x the MFMAs of the fused form). The block's K and V rows stay in LDS (64 KiB); 32-query
+// tiles of Q, dO, LSE*log2(e) and D stream through a 2-stage ring at the bottom of LDS.
+constexpr int kKv256BK = 64;
+constexpr int kKv256BQ = 32;
 
-template <int D, bool CAUSAL>
+template <bool CAUSAL>
+__global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+    const float* __restrict__ lse2, const float* __restrict__ delta, uint16_t* __restrict__ dk,
+    uint16_t* __restrict__ dv, int N, int n_kblocks, int bh_count, float scale_log2,
+    float scale) {
+  constexpr int D = 256, KK = D / 16, CB = D / 32, DCH = D / 8;
+  constexpr int TILE = kKv256BQ * D * 2;          // 16 KiB
+  constexpr int KV_BYTES = kKv256BK * D * 2;      // 32 KiB
+  constexpr int STAGE = 2 * TILE;                 // Q, dO
+  constexpr int STATS0 = 2 * STAGE;               // per stage: LSE*log2(e), then D (128 B each)
+  constexpr int STATS_STAGE = 2 * kKv256BQ * 4;
+  constexpr int KV0 = STATS0 + 2 * STATS_STAGE;
+  constexpr int SMEM = KV0 + 2 * KV_BYTES;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kw = wave & 1;      // key group
+  const bool dk_wave = wave >= 2;
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+
+  const TileCoord tc = schedule_tile<CAUSAL ? Order::kLongAscending : Order::kHeadMajor>(
+      blockIdx.x, n_kblocks, bh_count);
+  const size_t head_off = (size_t)tc.bh * (size_t)N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + head_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + head_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + head_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dout + head_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t rl = make_rsrc(lse2 + (size_t)tc.bh * N, (uint32_t)N * 4);
+  const __amdgpu_buffer_rsrc_t rd = make_rsrc(delta + (size_t)tc.bh * N, (uint32_t)N * 4);
+
+  const int key_b0 = tc.qb * kKv256BK;
+  const int key_w0 = key_b0 + kw * 32;
+  const int my_key = key_w0 + l32;
+
+  // resident K and V rows of the block (64 rows each, 2 rows per 1 KiB block)
+  {
+    constexpr int LOADS = KV_BYTES / (kThreads * 16);
+    constexpr int RPB = 64 / DCH;
+#pragma unroll
+    for (int r = 0; r < LOADS; ++r) {
+      const int blk = 4 * r + wave;
+      const int row = blk * RPB + lane / DCH;
+      const uint32_t off = (uint32_t)(row * D * 2 + ((lane % DCH) ^ swz<D>(row)) * 16);
+      buffer_load16_to_lds(rk, smem + KV0 + blk * 1024, off, (uint32_t)key_b0 * D * 2);
+      buffer_load16_to_lds(rv, smem + KV0 + KV_BYTES + blk * 1024, off,
+                           (uint32_t)key_b0 * D * 2);
+    }
+  }
+  // this wave's K/V fragment: row 32kw + l32, logical chunk 2kk + g (kk >= 8: +256 bytes)
+  const int kvrow = kw * 32 + l32;
+  int kvbase[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk)
+    kvbase[kk] = KV0 + kvrow * D * 2 + ((2 * kk + g) ^ swz<D>(kvrow)) * 16;
+  auto kv_off = [&](int kk) { return kvbase[kk % 8] + (kk / 8) * 256; };
+  // LSE*log2(e) / D of this lane's queries 16hf + 8g + (0..7) within a stage
+  const int statbase = STATS0 + 8 * g * 4;
+
+  const int n_qt = (N + kKv256BQ - 1) / kKv256BQ;
+  const int qt_begin = CAUSAL ? key_b0 / kKv256BQ : 0;
+  const TileLoader<D, kThreads, kKv256BQ> ld(wave, lane);
+  const TileReads<D> rd_off(lane);
+
+  auto load_stage = [&](int it, int stage) {
+    unsigned char* st = smem + stage * STAGE;
+    const uint32_t soff = (uint32_t)it * kKv256BQ * D * 2;
+    ld.load(rq, st, soff);
+    ld.load(rdo, st + TILE, soff);
+    // LSE*log2(e) and D of the tile's 32 queries (128 bytes each): 8 lanes of waves 0 and 1
+    unsigned char* sst = smem + STATS0 + stage * STATS_STAGE;
+    if (wave == 0) {
+      if (lane < 8)
+        buffer_load16_to_lds(rl, sst, (uint32_t)lane * 16, (uint32_t)it * kKv256BQ * 4);
+    } else if (wave == 1) {
+      if (lane < 8)
+        buffer_load16_to_lds(rd, sst + kKv256BQ * 4, (uint32_t)lane * 16,
+                             (uint32_t)it * kKv256BQ * 4);
+    }
+  };
+
+  f32x16_t acc[CB];  // dV^T (waves 0-1) or dK^T (waves 2-3) of the wave's 32 keys
+#pragma unroll
+  for (int cb = 0; cb < CB; ++cb) acc[cb] = f32x16_t{};
+
+  if (qt_begin < n_qt) load_stage(qt_begin, 0);
+  wait_vmem();
+  __syncthreads();
+
+  auto step = [&](auto stage_c, int it) {
+    constexpr int stage = decltype(stage_c)::value;
+    if (it + 1 < n_qt) load_stage(it + 1, stage ^ 1);
+    const int q0 = it * kKv256BQ;
+    // every query of the tile precedes every key of the wave: fully masked
+    const bool skip = CAUSAL && (q0 + kKv256BQ - 1 < key_w0);
+    if (!skip) {
+      const unsigned char* tq = smem + stage * STAGE;
+      const unsigned char* tdo = tq + TILE;
+      const unsigned char* ts = smem + statbase + stage * STATS_STAGE;
+      const bool masked = (q0 + kKv256BQ > N) || (CAUSAL && q0 < key_w0 + 31);
+      f32x16_t s, dp = f32x16_t{};
+      if (masked) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int qi = q0 + 16 * (i / 8) + 8 * g + (i % 8);
+          s[i] = (qi >= N || (CAUSAL && my_key > qi)) ? -INFINITY : 0.f;
+        }
+      } else {
+        s = f32x16_t{};
+      }
+      // S = Q K^T (both roles) and dP = dO V^T (dK waves), lane = key, registers = queries
+      if (dk_wave) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(smem + kv_off(kk));
+          const u32x4_t vf = *reinterpret_cast<const u32x4_t*>(smem + kv_off(kk) + KV_BYTES);
+          const u32x4_t aq = *reinterpret_cast<const u32x4_t*>(tq + rd_off.row_off(0, kk));
+          const u32x4_t ad = *reinterpret_cast<const u32x4_t*>(tdo + rd_off.row_off(0, kk));
+          s = mfma32(aq, kf, s);
+          dp = mfma32(ad, vf, dp);
+        }
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(smem + kv_off(kk));
+          const u32x4_t aq = *reinterpret_cast<const u32x4_t*>(tq + rd_off.row_off(0, kk));
+          s = mfma32(aq, kf, s);
+        }
+      }
+      // P = exp2(s*c - LSE*log2e); dK waves: dS = P * (dP - D). Register i is query
+      // q0 + 16(i/8) + 8g + i%8.
+      uint32_t bk[8];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const unsigned char* sl = ts + 16 * hf * 4;
+        const f32x4_t l0 = *reinterpret_cast<const f32x4_t*>(sl);
+        const f32x4_t l1 = *reinterpret_cast<const f32x4_t*>(sl + 16);
+        const f32x4_t d0 = *reinterpret_cast<const f32x4_t*>(sl + kKv256BQ * 4);
+        const f32x4_t d1 = *reinterpret_cast<const f32x4_t*>(sl + kKv256BQ * 4 + 16);
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float lv = e < 4 ? l0[e] : l1[e - 4];
+          const float dv_ = e < 4 ? d0[e] : d1[e - 4];
+          const float p = fast_exp2(__builtin_fmaf(s[8 * hf + e], scale_log2, -lv));
+          x[e] = dk_wave ? p * (dp[8 * hf + e] - dv_) : p;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) bk[4 * hf + e] = pack_bf16(x[2 * e], x[2 * e + 1]);
+      }
+      // dV^T += dO^T P or dK^T += Q^T dS over the tile's 32 queries (k-steps hf = 0, 1)
+      const unsigned char* ta = dk_wave ? tq : tdo;
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const u32x4_t b = {bk[4 * hf + 0], bk[4 * hf + 1], bk[4 * hf + 2], bk[4 * hf + 3]};
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          const u32x4_t a = tr_operand(ta, rd_off.tr_off(cb, hf, 0), rd_off.tr_off(cb, hf, 1));
+          acc[cb] = mfma32(a, b, acc[cb]);
+        }
+      }
+      __builtin_amdgcn_s_setprio(0);
+    }
+    wait_vmem();
+    __syncthreads();
+  };
+  for (int it = qt_begin; it < n_qt; it += 2) {
+    step(std::integral_constant<int, 0>{}, it);
+    if (it + 1 < n_qt) step(std::integral_constant<int, 1>{}, it + 1);
+  }
+
+  // dK = scale * dK_acc, dV = dV_acc. Lane holds key my_key, columns 32cb + 8t + 4g + 0..3.
+  if (my_key < N) {
+    const float mul = dk_wave ? scale : 1.f;
+    uint16_t* row = (dk_wave ? dk : dv) + head_off + (size_t)my_key * D;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int c = cb * 32 + 8 * t + 4 * g;
+        *reinterpret_cast<u32x2_t*>(row + c) =
+            u32x2_t{pack_bf16(acc[cb][4 * t] * mul, acc[cb][4 * t + 1] * mul),
+                    pack_bf16(acc[cb][4 * t + 2] * mul, acc[cb][4 * t + 3] * mul)};
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// dQ. Workgroup = 4 waves x 32 queries (lane = query, as in the forward); key tiles of 64
+// (32 at d = 256). S^T = K Q^T and dP^T = V dO^T from row-wise K/V tile reads with Q^T/dO^T
+// fragments held in VGPRs; dQ^T += K^T dS^T with K^T fragments from transposing reads of the
+// same K tile. At d = 256 the resident Q^T and dO^T fragments take 128 registers, so a launch
+// accumulates one half of dQ's columns (DH = 0 or 1; two launches recompute S and dP); DH = -1
+// is the whole row.
+constexpr int kDqBR = 128;
+
+template <int D, bool CAUSAL, int DH>
 __global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ o,
@@ -401,7 +610,11 @@ __global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dq_kernel(
     float* __restrict__ delta, uint16_t* __restrict__ dq, int N, int n_qblocks, int bh_count,
     float scale_log2, float scale) {
   constexpr int KK = D / 16, CB = D / 32;
-  constexpr int TILE = kDqBC * D * 2;
+  constexpr int BC = D == 256 ? 32 : 64;   // keys per tile
+  constexpr int KB = BC / 32;              // 32-key MFMA blocks per tile
+  constexpr int CBO = DH < 0 ? CB : CB / 2;  // 32-column dQ blocks this launch accumulates
+  constexpr int CB0 = DH < 0 ? 0 : DH * CBO;
+  constexpr int TILE = BC * D * 2;
   constexpr int STAGE = 2 * TILE;  // K, V
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
 
@@ -450,27 +663,27 @@ __global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dq_kernel(
   const float lse_q = valid_q ? lse[(size_t)tc.bh * N + my_q] * kLog2e : INFINITY;
   const float dlt = valid_q ? dsum : 0.f;
   // D and LSE*log2(e) of this block's queries go to the workspace for the dK/dV kernel
-  if (valid_q && g == 0) {
+  if (DH <= 0 && valid_q && g == 0) {
     delta[(size_t)tc.bh * N + my_q] = dlt;
     lse2[(size_t)tc.bh * N + my_q] = lse_q;
   }
 
-  int n_tiles = (N + kDqBC - 1) / kDqBC;
-  if (CAUSAL) n_tiles = min(N - 1, q_block0 + kDqBR - 1) / kDqBC + 1;
-  const int wave_last = CAUSAL ? min(n_tiles - 1, (q_wave0 + 31) / kDqBC) : n_tiles - 1;
+  int n_tiles = (N + BC - 1) / BC;
+  if (CAUSAL) n_tiles = min(N - 1, q_block0 + kDqBR - 1) / BC + 1;
+  const int wave_last = CAUSAL ? min(n_tiles - 1, (q_wave0 + 31) / BC) : n_tiles - 1;
 
-  const TileLoader<D> ld(wave, lane);
+  const TileLoader<D, kThreads, BC> ld(wave, lane);
   const TileReads<D> rd_off(lane);
   auto load_stage = [&](int j, int stage) {
     unsigned char* st = smem + stage * STAGE;
-    const uint32_t soff = (uint32_t)j * kDqBC * D * 2;
+    const uint32_t soff = (uint32_t)j * BC * D * 2;
     ld.load(rk, st, soff);
     ld.load(rv, st + TILE, soff);
   };
 
-  f32x16_t dqacc[CB];
+  f32x16_t dqacc[CBO];
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) dqacc[cb] = f32x16_t{};
+  for (int cb = 0; cb < CBO; ++cb) dqacc[cb] = f32x16_t{};
 
   load_stage(0, 0);
   wait_vmem();
@@ -483,11 +696,11 @@ __global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dq_kernel(
     if (j <= wave_last) {
       const unsigned char* tk = smem + stage * STAGE;
       const unsigned char* tv = tk + TILE;
-      const int key0 = j * kDqBC;
-      const bool masked = (key0 + kDqBC > N) || (CAUSAL && key0 + kDqBC - 1 > q_wave0);
-      f32x16_t s[2], dp[2];
+      const int key0 = j * BC;
+      const bool masked = (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > q_wave0);
+      f32x16_t s[KB], dp[KB];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < KB; ++kb) {
         if (masked) {
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
@@ -506,9 +719,9 @@ __global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dq_kernel(
           dp[kb] = mfma32(av, dof[kk], dp[kb]);
         }
       }
-      uint32_t dsk[2][8];
+      uint32_t dsk[KB][8];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const float p0 = fast_exp2(__builtin_fmaf(s[kb][2 * i], scale_log2, -lse_q));
@@ -518,12 +731,13 @@ __global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dq_kernel(
       __builtin_amdgcn_s_setprio(1);  // as in the dK/dV kernel
       // dQ^T += K^T dS^T; MFMA u covers keys 16u .. 16u+15
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 2 * KB; ++u) {
         const u32x4_t b = {dsk[u / 2][4 * (u % 2) + 0], dsk[u / 2][4 * (u % 2) + 1],
                            dsk[u / 2][4 * (u % 2) + 2], dsk[u / 2][4 * (u % 2) + 3]};
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          const u32x4_t a = tr_operand(tk, rd_off.tr_off(cb, u, 0), rd_off.tr_off(cb, u, 1));
+        for (int cb = 0; cb < CBO; ++cb) {
+          const u32x4_t a = tr_operand(tk, rd_off.tr_off(CB0 + cb, u, 0),
+                                       rd_off.tr_off(CB0 + cb, u, 1));
           dqacc[cb] = mfma32(a, b, dqacc[cb]);
         }
       }
@@ -540,10 +754,10 @@ __global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dq_kernel(
   if (valid_q) {
     uint16_t* row = dq + head_off + (size_t)my_q * D;
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
+    for (int cb = 0; cb < CBO; ++cb)
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        const int c = cb * 32 + 8 * t + 4 * g;
+        const int c = (CB0 + cb) * 32 + 8 * t + 4 * g;
         *reinterpret_cast<u32x2_t*>(row + c) =
             u32x2_t{pack_bf16(dqacc[cb][4 * t] * scale, dqacc[cb][4 * t + 1] * scale),
                     pack_bf16(dqacc[cb][4 * t + 2] * scale, dqacc[cb][4 * t + 3] * scale)};
@@ -578,12 +792,9 @@ hipError_t launch_dkdv_t(const BwdArgs& a) {
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
-hipError_t launch_dq_t(const BwdArgs& a) {
-  const int n_qblocks = (a.N + kDqBR - 1) / kDqBR;
-  const long long grid = (long long)n_qblocks * a.B * a.H;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fa2_bwd_dq_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0,
+template <int D, bool CAUSAL, int DH>
+hipError_t launch_dq_one(const BwdArgs& a, unsigned grid, int n_qblocks) {
+  hipLaunchKernelGGL((fa2_bwd_dq_kernel<D, CAUSAL, DH>), dim3(grid), dim3(kThreads), 0,
                      a.stream, static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                      static_cast<const uint16_t*>(a.o), static_cast<const uint16_t*>(a.dout),
@@ -592,18 +803,49 @@ hipError_t launch_dq_t(const BwdArgs& a) {
   return hipGetLastError();
 }
 
+template <int D, bool CAUSAL>
+hipError_t launch_dq_t(const BwdArgs& a) {
+  const int n_qblocks = (a.N + kDqBR - 1) / kDqBR;
+  const long long grid = (long long)n_qblocks * a.B * a.H;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if constexpr (D == 256) {
+    const hipError_t e = launch_dq_one<D, CAUSAL, 0>(a, (unsigned)grid, n_qblocks);
+    if (e != hipSuccess) return e;
+    return launch_dq_one<D, CAUSAL, 1>(a, (unsigned)grid, n_qblocks);
+  } else {
+    return launch_dq_one<D, CAUSAL, -1>(a, (unsigned)grid, n_qblocks);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_bwd_pre(const BwdArgs& a) {
+  if (a.d == 256) return launch_pre_t<256>(a);
   return a.d == 64 ? launch_pre_t<64>(a) : launch_pre_t<128>(a);
 }
 
+template <bool CAUSAL>
+hipError_t launch_dkdv256_t(const BwdArgs& a) {
+  const int n_kblocks = (a.N + kKv256BK - 1) / kKv256BK;
+  const long long grid = (long long)n_kblocks * a.B * a.H;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((fa2_bwd_dkdv256_kernel<CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0,
+                     a.stream, static_cast<const uint16_t*>(a.q),
+                     static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
+                     static_cast<const uint16_t*>(a.dout), a.lse2, a.delta,
+                     static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), a.N, n_kblocks,
+                     a.B * a.H, a.scale_log2, a.scale);
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd_dkdv(const BwdArgs& a) {
+  if (a.d == 256) return a.causal ? launch_dkdv256_t<true>(a) : launch_dkdv256_t<false>(a);
   if (a.d == 64) return a.causal ? launch_dkdv_t<64, true>(a) : launch_dkdv_t<64, false>(a);
   return a.causal ? launch_dkdv_t<128, true>(a) : launch_dkdv_t<128, false>(a);
 }
 
 hipError_t launch_bwd_dq(const BwdArgs& a) {
+  if (a.d == 256) return a.causal ? launch_dq_t<256, true>(a) : launch_dq_t<256, false>(a);
   if (a.d == 64) return a.causal ? launch_dq_t<64, true>(a) : launch_dq_t<64, false>(a);
   return a.causal ? launch_dq_t<128, true>(a) : launch_dq_t<128, false>(a);
 }

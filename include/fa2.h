@@ -24,9 +24,9 @@
  *   [B, H, N, d] with d fastest. lse: float32 [B, H, N], natural log. All pointers are
  *   device pointers and must be 16-byte aligned. B*H*N*d may exceed 2^31 (64-bit offsets);
  *   one head's slice must stay below 2 GiB (N*d*2 < 2^31 bytes, i.e. N < 8M at d = 128).
- *   Supported head dimensions: d = 64 and d = 128; the forward also takes d = 256 (the
- *   pages give FlashAttention-2 head dimensions up to 256: page "Flash Attention v2",
- *   "Head Dimension Support"). Any N >= 1 (ragged tails are masked).
+ *   Supported head dimensions: d = 64, 128 and 256 (the pages give FlashAttention-2 head
+ *   dimensions up to 256: page "Flash Attention v2", "Head Dimension Support"). Any N >= 1
+ *   (ragged tails are masked).
  *   Empty problems (B, H or N equal to 0, the others >= 0) are valid: the call checks d and
  *   the scale, does nothing else (pointers are not examined, no HIP call) and returns FA2_OK;
  *   fa2_bwd_workspace_bytes is then 0.

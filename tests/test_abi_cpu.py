@@ -92,7 +92,8 @@ def test_bwd_validation_and_workspace():
     assert lib.fa2_bwd_dkdv(*nul[:5], 0, None, None, 1, 0, 5, 64, 1, 0.125, None) == ops.FA2_OK
     assert lib.fa2_bwd_preprocess(*nul[:4], 0, 1, 1, 0, 64, None) == ops.FA2_OK
     assert lib.fa2_bwd_workspace_bytes(1, 1, 100, 80) == 0
-    assert lib.fa2_bwd_workspace_bytes(1, 1, 100, 256) == 0  # backward: d <= 128
+    assert lib.fa2_bwd_workspace_bytes(1, 1, 100, 256) == 2 * 512
+    assert lib.fa2_bwd_workspace_bytes(1, 1, 100, 512) == 0
     base = [P] * 10
     ok_sizes = (2, 3, 100, 64, 1, 0.125)
     # workspace too small
@@ -106,7 +107,7 @@ def test_bwd_validation_and_workspace():
     args[9] = P + 8
     assert lib.fa2_bwd(*args, ws, *ok_sizes, None) == ops.FA2_ERR_INVALID_ARGUMENT
     assert lib.fa2_bwd(*base, ws, 2, 3, 100, 48, 1, 0.125, None) == ops.FA2_ERR_UNSUPPORTED
-    assert lib.fa2_bwd(*base, ws, 2, 3, 100, 256, 1, 0.125, None) == ops.FA2_ERR_UNSUPPORTED
+    assert lib.fa2_bwd(*base, ws, 2, 3, 100, 320, 1, 0.125, None) == ops.FA2_ERR_UNSUPPORTED
     # stage entry points validate the same way
     assert lib.fa2_bwd_preprocess(P, P, P, P, ws - 1, 2, 3, 100, 64, None) == \
         ops.FA2_ERR_INVALID_ARGUMENT

@@ -40,7 +40,8 @@ def check_against_oracle(bq, bk, bv, bdo, causal, scale, what):
 
 
 SMALL = [(1, 1, 1, 64), (1, 1, 5, 128), (2, 3, 77, 64), (1, 2, 200, 128), (1, 1, 129, 128),
-         (1, 2, 383, 64), (1, 1, 1000, 128), (2, 1, 640, 64)]
+         (1, 2, 383, 64), (1, 1, 1000, 128), (2, 1, 640, 64),
+         (1, 1, 1, 256), (1, 2, 45, 256), (2, 1, 161, 256), (1, 1, 700, 256)]
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -63,7 +64,7 @@ def test_fwd_bwd_workload_full_compare(causal):
                          f"workload 5 causal={causal}")
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 256])
 def test_d64_d128_long_sequence_heads(d):
     shape = (1, 2, 2048, d)
     bq, bk, bv, bdo = (normal_bf16(shape, 8500 + d + t) for t in range(4))
@@ -92,12 +93,13 @@ def test_gradient_invariants(causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_deterministic_coverage_and_stages(causal):
+@pytest.mark.parametrize("d", [64, 256])
+def test_deterministic_coverage_and_stages(causal, d):
     """Gradients pre-filled with NaN are fully overwritten; two runs give identical bits; the
     stage entry points (dQ, which fills the workspace, then dK/dV) reproduce fa2_bwd bit for
     bit, and dK/dV after the separate preprocess stage agrees to fp32 rounding of D."""
     fa2 = _fa2()
-    shape = (2, 3, 421, 64)
+    shape = (2, 3, 421, d)
     q, k, v, do = (to_dev(normal_bf16(shape, 8700 + t)) for t in range(4))
     o, lse = fa2.fwd(q, k, v, causal=causal)
     nan = lambda: torch.full(shape, float("nan"), dtype=torch.bfloat16, device=q.device)
