@@ -16,7 +16,8 @@ dense bf16 MFMA peak of MI355X (2.5 PFLOP/s). `traffic` comes from committed roc
 FETCH_SIZE / WRITE_SIZE counter summaries under profiles/ (null if the kernel source changed
 since they were taken). `cpu_baseline` times the CPU float64 oracle on a bounded sample of
 the same workload (whole heads) on the host cores. `forward_workloads` adds the forward
-kernel's TFLOP/s on the forward-only workloads (not part of `value`).
+kernel's TFLOP/s on the forward-only workloads and `d256_steps` the fwd+bwd step at head
+dimension 256 (neither is part of `value`).
 
 Prints ONE JSON line (rank 0).
 """
@@ -149,32 +150,19 @@ def forward_sweep(fa2, torch, dev, reps=10, warm_ms=60.0):
     return res
 
 
-def main():
-    args = parse_args()
-    if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
-                          "(the per-head work is independent, so more GPUs would shard "
-                          "batch x heads without any exchange)"}))
-        sys.exit(2)
+def measure_step(fa2, torch, dev, w, causal, with_bwd, steps, warmup):
+    """Run `warmup` untimed and `steps` timed steps (forward, then dQ and dK/dV) of workload
+    `w`; each stage is bracketed by HIP events on the launch stream. Returns (stage names,
+    their algorithmic FLOP, step FLOP, mean stage ms, wall seconds of the timed steps)."""
+    import numpy as np
 
-    import torch
+    from exact_io_aware_42_amd.inputs import default_scale, workload_tensors
 
-    import exact_io_aware_42_amd as fa2
-    from exact_io_aware_42_amd.inputs import WORKLOADS, default_scale, workload_tensors
-
-    w = WORKLOADS[args.workload]
-    causal = w.causal_modes[0] if args.causal == "default" else args.causal == "causal"
-    with_bwd = args.direction == "both"
     B, H, N, d = w.shape
     scale = default_scale(d)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    fa2.load_library()
-
     t = workload_tensors(w, with_dout=with_bwd)
 
     def dev_t(bits):
-        import numpy as np
         return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
 
     q, k, v = dev_t(t["q"]), dev_t(t["k"]), dev_t(t["v"])
@@ -209,25 +197,51 @@ def main():
             fa2.bwd_dkdv(q, k, v, do, ws, causal=causal, scale=scale, dk=dk, dv=dv)
             mark(3)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
     n_ev = len(kernels) + 1
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
-        step(ev[s])
+    for i in range(steps):
+        step(ev[i])
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    elapsed = t1 - t0
-    ms_per_step = elapsed * 1e3 / args.steps
+    elapsed = time.perf_counter() - t0
 
     kernel_ms = {}
     for i, kname in enumerate(kernels):
-        durs = [ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]
+        durs = [ev[s_][i].elapsed_time(ev[s_][i + 1]) for s_ in range(steps)]
         kernel_ms[kname] = sum(durs) / len(durs)
+    return kernels, algo_flop, step_flop, kernel_ms, elapsed
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
+                          "(the per-head work is independent, so more GPUs would shard "
+                          "batch x heads without any exchange)"}))
+        sys.exit(2)
+
+    import torch
+
+    import exact_io_aware_42_amd as fa2
+    from exact_io_aware_42_amd.inputs import WORKLOADS
+
+    w = WORKLOADS[args.workload]
+    causal = w.causal_modes[0] if args.causal == "default" else args.causal == "causal"
+    with_bwd = args.direction == "both"
+    B, H, N, d = w.shape
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    fa2.load_library()
+
+    kernels, algo_flop, step_flop, kernel_ms, elapsed = measure_step(
+        fa2, torch, dev, w, causal, with_bwd, args.steps, args.warmup)
+    ms_per_step = elapsed * 1e3 / args.steps
+
     dominant = max(kernels, key=lambda kn: kernel_ms[kn])
     achieved = algo_flop[dominant] / (kernel_ms[dominant] * 1e-3) / 1e12
     wtag = f"w{w.wid}_{'causal' if causal else 'full'}"
@@ -271,6 +285,17 @@ def main():
     }
     if not args.no_fwd_sweep:
         out["forward_workloads"] = forward_sweep(fa2, torch, dev)
+        # the fwd+bwd step at head dimension 256 (both masks)
+        w6 = WORKLOADS[6]
+        steps6 = {}
+        for c6 in (True, False):
+            kn6, af6, sf6, km6, el6 = measure_step(fa2, torch, dev, w6, c6, True, 20, 20)
+            steps6[f"{w6.name} {'causal' if c6 else 'non-causal'} fwd+bwd"] = {
+                "ms_per_step": round(el6 * 1e3 / 20, 4),
+                "tflops": round(sf6 * 20 / el6 / 1e12, 1),
+                "kernel_ms": {kn: round(v_, 4) for kn, v_ in km6.items()},
+                "kernel_tflops": {kn: round(af6[kn] / (km6[kn] * 1e-3) / 1e12, 1) for kn in kn6}}
+        out["d256_steps"] = steps6
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, causal, with_bwd, args.cpu_seconds)
     print(json.dumps(out), flush=True)
