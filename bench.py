@@ -16,8 +16,9 @@ dense bf16 MFMA peak of MI355X (2.5 PFLOP/s). `traffic` comes from committed roc
 FETCH_SIZE / WRITE_SIZE counter summaries under profiles/ (null if the kernel source changed
 since they were taken). `cpu_baseline` times the CPU float64 oracle on a bounded sample of
 the same workload (whole heads) on the host cores. `forward_workloads` adds the forward
-kernel's TFLOP/s on the forward-only workloads and `d256_steps` the fwd+bwd step at head
-dimension 256 (neither is part of `value`).
+kernel's TFLOP/s on the forward-only workloads, `d256_steps` the fwd+bwd step at head
+dimension 256 and `gpt_layer_step` a GPT-style attention layer (bf16 projections + attention,
+forward and backward through torch.autograd); none of them is part of `value`.
 
 Prints ONE JSON line (rank 0).
 """
@@ -148,6 +149,37 @@ def forward_sweep(fa2, torch, dev, reps=10, warm_ms=60.0):
             "ms": round(ms, 4), "tflops": round(tf, 1),
             "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
     return res
+
+
+def gpt_layer_step(torch, dev, steps=20, warmup=10):
+    """Forward+backward of a GPT-style causal attention layer (bf16 QKV and output projections
+    by torch matmul, attention by flash_attn_func) at the GPT-style workload's shape
+    (B=4, N=4096, H=16, d=128, C=2048), synthetic weights and data."""
+    from exact_io_aware_42_amd.gpt_layer import layer_flop, layer_forward, make_params
+
+    B, N, H, d = 4, 4096, 16, 128
+    x, w_qkv, w_o, dy = make_params(B, N, H, d, dev, seed=7)
+
+    def step():
+        for t in (x, w_qkv, w_o):
+            t.grad = None
+        layer_forward(x, w_qkv, w_o, H).backward(dy)
+
+    for _ in range(warmup):
+        step()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    fl = layer_flop(B, N, H, d)
+    total = fl["projections"] + fl["attention"]
+    return {"shape": f"B{B} N{N} H{H} d{d} C{H * d} causal", "ms_per_step": round(ms, 4),
+            "tflops": round(total / (ms * 1e-3) / 1e12, 1),
+            "attention_flop_share": round(fl["attention"] / total, 3)}
 
 
 def measure_step(fa2, torch, dev, w, causal, with_bwd, steps, warmup):
@@ -296,6 +328,7 @@ def main():
                 "kernel_ms": {kn: round(v_, 4) for kn, v_ in km6.items()},
                 "kernel_tflops": {kn: round(af6[kn] / (km6[kn] * 1e-3) / 1e12, 1) for kn in kn6}}
         out["d256_steps"] = steps6
+        out["gpt_layer_step"] = gpt_layer_step(torch, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, causal, with_bwd, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -5,11 +5,15 @@
     o, lse = fwd(q, k, v, causal=True)            # bf16 [B, H, N, d] on the GPU
     dq, dk, dv = bwd(q, k, v, o, do, lse, causal=True)
 
+    from exact_io_aware_42_amd import flash_attn_func
+    o = flash_attn_func(q, k, v, causal=True)     # differentiable (torch.autograd)
+
 The library is loaded on first use; if it has not been built the call raises (there is no
 fallback path).
 """
+from .autograd import FlashAttention, flash_attn_func
 from .ops import (FA2Error, bwd, bwd_dkdv, bwd_dq, bwd_preprocess, bwd_workspace_bytes, fwd,
                   load_library)
 
 __all__ = ["fwd", "bwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "bwd_workspace_bytes",
-           "load_library", "FA2Error"]
+           "load_library", "FA2Error", "FlashAttention", "flash_attn_func"]

@@ -1,0 +1,36 @@
+"""torch.autograd face of the fa2 C ABI.
+
+`flash_attn_func(q, k, v, causal, scale)` mirrors the pages' call of the same name (page
+"Flash Attention v2", "Installation and Usage": the output of exact attention, with the
+backward wired to the FlashAttention-2 backward kernels). Layout here is the library's: bf16 [B, H, N, d],
+contiguous, on the GPU. Forward saves q, k, v, O and the per-row LSE; backward calls fa2_bwd
+with the incoming dO. Both run through libfa2.so (there is no fallback).
+"""
+from __future__ import annotations
+
+import torch
+
+from . import ops
+
+
+class FlashAttention(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, k, v, causal: bool, scale: float | None):
+        o, lse = ops.fwd(q, k, v, causal=causal, scale=scale)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.causal = causal
+        ctx.scale = scale
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = ops.bwd(q, k, v, o, do.contiguous(), lse, causal=ctx.causal,
+                             scale=ctx.scale)
+        return dq, dk, dv, None, None
+
+
+def flash_attn_func(q, k, v, causal: bool = False, scale: float | None = None):
+    """softmax(scale * q k^T [+ causal mask]) v for bf16 [B, H, N, d] tensors, differentiable
+    in q, k and v. `scale` defaults to 1/sqrt(d)."""
+    return FlashAttention.apply(q, k, v, bool(causal), scale)
