@@ -11,9 +11,11 @@
 The library is loaded on first use; if it has not been built the call raises (there is no
 fallback path).
 """
-from .autograd import FlashAttention, flash_attn_func
-from .ops import (FA2Error, bwd, bwd_dkdv, bwd_dq, bwd_preprocess, bwd_workspace_bytes, fwd,
-                  load_library)
+from .autograd import (FlashAttention, FlashAttentionKVPacked, flash_attn_func,
+                       flash_attn_kvpacked_func)
+from .ops import (FA2Error, bwd, bwd_dkdv, bwd_dq, bwd_kvpacked, bwd_preprocess,
+                  bwd_workspace_bytes, fwd, fwd_kvpacked, load_library)
 
-__all__ = ["fwd", "bwd", "bwd_preprocess", "bwd_dkdv", "bwd_dq", "bwd_workspace_bytes",
-           "load_library", "FA2Error", "FlashAttention", "flash_attn_func"]
+__all__ = ["fwd", "bwd", "fwd_kvpacked", "bwd_kvpacked", "bwd_preprocess", "bwd_dkdv", "bwd_dq",
+           "bwd_workspace_bytes", "load_library", "FA2Error", "FlashAttention",
+           "FlashAttentionKVPacked", "flash_attn_func", "flash_attn_kvpacked_func"]

@@ -32,5 +32,28 @@ class FlashAttention(torch.autograd.Function):
 
 def flash_attn_func(q, k, v, causal: bool = False, scale: float | None = None):
     """softmax(scale * q k^T [+ causal mask]) v for bf16 [B, H, N, d] tensors, differentiable
-    in q, k and v. `scale` defaults to 1/sqrt(d)."""
+    in q, k and v. `scale` defaults to 1/sqrt(d). k and v may have Hkv heads with Hkv dividing
+    H (query head h uses K/V head h / (H / Hkv))."""
     return FlashAttention.apply(q, k, v, bool(causal), scale)
+
+
+class FlashAttentionKVPacked(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, q, kv, causal: bool, scale: float | None):
+        o, lse = ops.fwd_kvpacked(q, kv, causal=causal, scale=scale)
+        ctx.save_for_backward(q, kv, o, lse)
+        ctx.causal = causal
+        ctx.scale = scale
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, kv, o, lse = ctx.saved_tensors
+        dq, dkv = ops.bwd_kvpacked(q, kv, o, do.contiguous(), lse, causal=ctx.causal,
+                                   scale=ctx.scale)
+        return dq, dkv, None, None
+
+
+def flash_attn_kvpacked_func(q, kv, causal: bool = False, scale: float | None = None):
+    """As flash_attn_func with K and V packed in one bf16 [B, 2, Hkv, N, d] tensor."""
+    return FlashAttentionKVPacked.apply(q, kv, bool(causal), scale)

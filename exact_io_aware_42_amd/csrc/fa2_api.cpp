@@ -49,15 +49,26 @@ fa2_status from_hip(hipError_t e) {
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
-}  // namespace
+// K/V head count and batch stride (elements) for grouped or packed K/V. FA2_OK or the status.
+fa2_status check_kv(int B, int H, int Hkv, int N, int d, long long kv_bstride) {
+  if (Hkv <= 0 || H % Hkv != 0) return FA2_ERR_INVALID_ARGUMENT;
+  const long long head = (long long)N * d;
+  if (kv_bstride < (long long)Hkv * head || (kv_bstride & 7) != 0) return FA2_ERR_INVALID_ARGUMENT;
+  // the grid of the dK/dV kernels and the K/V extent
+  if ((unsigned long long)B * Hkv * ((unsigned long long)(N + 63) / 64) > 0x7fffffffull)
+    return FA2_ERR_INVALID_ARGUMENT;
+  if ((unsigned long long)kv_bstride > (1ull << 50)) return FA2_ERR_INVALID_ARGUMENT;
+  return FA2_OK;
+}
 
-extern "C" {
-
-fa2_status fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                   int H, int N, int d, int causal, float softmax_scale, hipStream_t stream) {
+fa2_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                    int H, int Hkv, int N, int d, long long kv_bstride, int causal,
+                    float softmax_scale, hipStream_t stream) {
   bool empty;
-  const fa2_status st = check_sizes(B, H, N, d, softmax_scale, &empty);
+  fa2_status st = check_sizes(B, H, N, d, softmax_scale, &empty);
   if (st != FA2_OK || empty) return st;
+  st = check_kv(B, H, Hkv, N, d, kv_bstride);
+  if (st != FA2_OK) return st;
   const void* ptrs[] = {q, k, v, o, lse};
   for (const void* p : ptrs)
     if (p == nullptr || !aligned16(p)) return FA2_ERR_INVALID_ARGUMENT;
@@ -71,10 +82,29 @@ fa2_status fa2_fwd(const void* q, const void* k, const void* v, void* o, float* 
   a.H = H;
   a.N = N;
   a.d = d;
+  a.Hkv = Hkv;
+  a.kv_bstride = kv_bstride;
   a.causal = causal != 0;
   a.scale_log2 = static_cast<float>(static_cast<double>(softmax_scale) * kLog2e);
   a.stream = stream;
   return from_hip(fa2::launch_fwd(a));
+}
+
+}  // namespace
+
+extern "C" {
+
+fa2_status fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                   int H, int N, int d, int causal, float softmax_scale, hipStream_t stream) {
+  return fwd_impl(q, k, v, o, lse, B, H, H, N, d, (long long)H * N * d, causal, softmax_scale,
+                  stream);
+}
+
+fa2_status fa2_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                       int H, int Hkv, int N, int d, long long kv_batch_stride, int causal,
+                       float softmax_scale, hipStream_t stream) {
+  return fwd_impl(q, k, v, o, lse, B, H, Hkv, N, d, kv_batch_stride, causal, softmax_scale,
+                  stream);
 }
 
 // Workspace layout: D = rowsum(dO * O) [B*H*N floats], then LSE * log2(e) [B*H*N floats],
@@ -113,6 +143,8 @@ fa2_status bwd_args(const void* q, const void* k, const void* v, const void* o, 
   a->H = H;
   a->N = N;
   a->d = d;
+  a->Hkv = H;
+  a->kv_bstride = (long long)H * N * d;
   a->causal = causal != 0;
   a->scale = softmax_scale;
   a->scale_log2 = static_cast<float>(static_cast<double>(softmax_scale) * kLog2e);
@@ -138,6 +170,24 @@ fa2_status fa2_bwd(const void* q, const void* k, const void* v, const void* o, c
                                  B, H, N, d, causal, softmax_scale, stream, &a, &empty);
   if (st != FA2_OK || empty) return st;
   if (!all_ok({q, k, v, o, dout, lse, dq, dk, dv})) return FA2_ERR_INVALID_ARGUMENT;
+  return from_hip(fa2::launch_bwd(a));
+}
+
+fa2_status fa2_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
+                       const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                       void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int N,
+                       int d, long long kv_batch_stride, int causal, float softmax_scale,
+                       hipStream_t stream) {
+  fa2::BwdArgs a;
+  bool empty;
+  fa2_status st = bwd_args(q, k, v, o, dout, lse, workspace, workspace_bytes, dq, dk, dv, B, H,
+                           N, d, causal, softmax_scale, stream, &a, &empty);
+  if (st != FA2_OK || empty) return st;
+  st = check_kv(B, H, Hkv, N, d, kv_batch_stride);
+  if (st != FA2_OK) return st;
+  if (!all_ok({q, k, v, o, dout, lse, dq, dk, dv})) return FA2_ERR_INVALID_ARGUMENT;
+  a.Hkv = Hkv;
+  a.kv_bstride = kv_batch_stride;
   return from_hip(fa2::launch_bwd(a));
 }
 

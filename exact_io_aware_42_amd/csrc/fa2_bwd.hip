@@ -152,8 +152,8 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse2, const float* __restrict__ delta, uint16_t* __restrict__ dk,
-    uint16_t* __restrict__ dv, int N, int n_kblocks, int bh_count, float scale_log2,
-    float scale) {
+    uint16_t* __restrict__ dv, int N, int n_kblocks, int bh_count, int n_qheads, int group,
+    long long kv_bstride, float scale_log2, float scale) {
   constexpr int KK = D / 16, CB = D / 32, DCH = D / 8;
   // LDS: the two ring stages of Q and dO tiles at the bottom (every ds_read of them is a
   // per-lane base plus a 16-bit immediate), then LSE*log2(e) and D of both stages, then the
@@ -181,14 +181,17 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
   // causal: key block 0 sees every query tile, so ascending order is longest first
   const TileCoord tc = schedule_tile<CAUSAL ? Order::kLongAscending : Order::kHeadMajor>(
       blockIdx.x, n_kblocks, bh_count);
-  const size_t head_off = (size_t)tc.bh * (size_t)N * D;
+  // tc.bh indexes (batch, K/V head); the query heads sharing this K/V head are
+  // qh0 .. qh0 + group - 1, and their contributions to dK, dV are summed here in order.
+  const int n_kvheads = n_qheads / group;
+  const int b_idx = tc.bh / n_kvheads;
+  const int kvh = tc.bh - b_idx * n_kvheads;
+  const int qh0 = b_idx * n_qheads + kvh * group;
+  const size_t head_off =  // K, V, dK, dV
+      (size_t)b_idx * (size_t)kv_bstride + (size_t)kvh * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + head_off, head_bytes);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + head_off, head_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + head_off, head_bytes);
-  const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dout + head_off, head_bytes);
-  const __amdgpu_buffer_rsrc_t rl = make_rsrc(lse2 + (size_t)tc.bh * N, (uint32_t)N * 4);
-  const __amdgpu_buffer_rsrc_t rd = make_rsrc(delta + (size_t)tc.bh * N, (uint32_t)N * 4);
 
   const int key_b0 = tc.qb * kKvBK;
   const int key_w0 = key_b0 + kw * 32;
@@ -220,6 +223,9 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
 
   const int n_qt = (N + kKvBQ - 1) / kKvBQ;
   const int qt_begin = CAUSAL ? key_b0 / kKvBQ : 0;
+  // steps t = 0 .. group*nt - 1 walk query tile qt_begin + t % nt of query head qh0 + t / nt
+  const int nt = n_qt - qt_begin;
+  const int n_steps = group * nt;
   const TileLoader<D, kKvThreads> ld(wave, lane);
   // per-lane read offsets within a stage for this wave's query half: row-wise Q/dO fragments
   // (rows 32hq + kmap(l32)) and transposing reads (k-steps t = 2hq + hf)
@@ -234,7 +240,14 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
       for (int h = 0; h < 2; ++h) qtr[cb][h] = rd_off.tr_off(cb, 2 * hq, h);
   }
 
-  auto load_stage = [&](int it, int stage) {
+  auto load_stage = [&](int t, int stage) {
+    const int gi = t / nt;
+    const int it = qt_begin + (t - gi * nt);
+    const size_t qoff = (size_t)(qh0 + gi) * (size_t)N * D;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + qoff, head_bytes);
+    const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dout + qoff, head_bytes);
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(lse2 + (size_t)(qh0 + gi) * N, (uint32_t)N * 4);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(delta + (size_t)(qh0 + gi) * N, (uint32_t)N * 4);
     unsigned char* st = smem + stage * STAGE;
     const uint32_t soff = (uint32_t)it * kKvBQ * D * 2;
     ld.load(rq, st, soff);
@@ -257,15 +270,16 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
     dvacc[cb] = f32x16_t{};
   }
 
-  if (qt_begin < n_qt) load_stage(qt_begin, 0);
+  if (n_steps > 0) load_stage(0, 0);
   wait_vmem();
   __syncthreads();
 
   // unrolled by two below, so the ring stage is a compile-time constant (LDS addresses are a
   // base register plus an immediate)
-  auto step = [&](auto stage_c, int it) {
+  auto step = [&](auto stage_c, int t) {
     constexpr int stage = decltype(stage_c)::value;
-    if (it + 1 < n_qt) load_stage(it + 1, stage ^ 1);
+    if (t + 1 < n_steps) load_stage(t + 1, stage ^ 1);
+    const int it = qt_begin + t % nt;
     const int q0 = it * kKvBQ + 32 * hq;  // this wave's 32 queries
     // every query of the half precedes every key of the wave: fully masked
     const bool skip = CAUSAL && (q0 + 31 < key_w0);
@@ -341,9 +355,9 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
     wait_vmem();
     __syncthreads();
   };
-  for (int it = qt_begin; it < n_qt; it += 2) {
-    step(std::integral_constant<int, 0>{}, it);
-    if (it + 1 < n_qt) step(std::integral_constant<int, 1>{}, it + 1);
+  for (int t = 0; t < n_steps; t += 2) {
+    step(std::integral_constant<int, 0>{}, t);
+    if (t + 1 < n_steps) step(std::integral_constant<int, 1>{}, t + 1);
   }
 
   // Combine the pair's partial sums through LDS (the loop ended with a barrier, so the tiles are
@@ -405,8 +419,8 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse2, const float* __restrict__ delta, uint16_t* __restrict__ dk,
-    uint16_t* __restrict__ dv, int N, int n_kblocks, int bh_count, float scale_log2,
-    float scale) {
+    uint16_t* __restrict__ dv, int N, int n_kblocks, int bh_count, int n_qheads, int group,
+    long long kv_bstride, float scale_log2, float scale) {
   constexpr int D = 256, KK = D / 16, CB = D / 32, DCH = D / 8;
   constexpr int TILE = kKv256BQ * D * 2;          // 16 KiB
   constexpr int KV_BYTES = kKv256BK * D * 2;      // 32 KiB
@@ -427,14 +441,17 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
 
   const TileCoord tc = schedule_tile<CAUSAL ? Order::kLongAscending : Order::kHeadMajor>(
       blockIdx.x, n_kblocks, bh_count);
-  const size_t head_off = (size_t)tc.bh * (size_t)N * D;
+  // tc.bh indexes (batch, K/V head); the query heads sharing this K/V head are
+  // qh0 .. qh0 + group - 1, and their contributions to dK, dV are summed here in order.
+  const int n_kvheads = n_qheads / group;
+  const int b_idx = tc.bh / n_kvheads;
+  const int kvh = tc.bh - b_idx * n_kvheads;
+  const int qh0 = b_idx * n_qheads + kvh * group;
+  const size_t head_off =  // K, V, dK, dV
+      (size_t)b_idx * (size_t)kv_bstride + (size_t)kvh * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + head_off, head_bytes);
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + head_off, head_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + head_off, head_bytes);
-  const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dout + head_off, head_bytes);
-  const __amdgpu_buffer_rsrc_t rl = make_rsrc(lse2 + (size_t)tc.bh * N, (uint32_t)N * 4);
-  const __amdgpu_buffer_rsrc_t rd = make_rsrc(delta + (size_t)tc.bh * N, (uint32_t)N * 4);
 
   const int key_b0 = tc.qb * kKv256BK;
   const int key_w0 = key_b0 + kw * 32;
@@ -466,10 +483,20 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
 
   const int n_qt = (N + kKv256BQ - 1) / kKv256BQ;
   const int qt_begin = CAUSAL ? key_b0 / kKv256BQ : 0;
+  // steps t = 0 .. group*nt - 1 walk query tile qt_begin + t % nt of query head qh0 + t / nt
+  const int nt = n_qt - qt_begin;
+  const int n_steps = group * nt;
   const TileLoader<D, kThreads, kKv256BQ> ld(wave, lane);
   const TileReads<D> rd_off(lane);
 
-  auto load_stage = [&](int it, int stage) {
+  auto load_stage = [&](int t, int stage) {
+    const int gi = t / nt;
+    const int it = qt_begin + (t - gi * nt);
+    const size_t qoff = (size_t)(qh0 + gi) * (size_t)N * D;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + qoff, head_bytes);
+    const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dout + qoff, head_bytes);
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(lse2 + (size_t)(qh0 + gi) * N, (uint32_t)N * 4);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(delta + (size_t)(qh0 + gi) * N, (uint32_t)N * 4);
     unsigned char* st = smem + stage * STAGE;
     const uint32_t soff = (uint32_t)it * kKv256BQ * D * 2;
     ld.load(rq, st, soff);
@@ -490,13 +517,14 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) acc[cb] = f32x16_t{};
 
-  if (qt_begin < n_qt) load_stage(qt_begin, 0);
+  if (n_steps > 0) load_stage(0, 0);
   wait_vmem();
   __syncthreads();
 
-  auto step = [&](auto stage_c, int it) {
+  auto step = [&](auto stage_c, int t) {
     constexpr int stage = decltype(stage_c)::value;
-    if (it + 1 < n_qt) load_stage(it + 1, stage ^ 1);
+    if (t + 1 < n_steps) load_stage(t + 1, stage ^ 1);
+    const int it = qt_begin + t % nt;
     const int q0 = it * kKv256BQ;
     // every query of the tile precedes every key of the wave: fully masked
     const bool skip = CAUSAL && (q0 + kKv256BQ - 1 < key_w0);
@@ -572,9 +600,9 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
     wait_vmem();
     __syncthreads();
   };
-  for (int it = qt_begin; it < n_qt; it += 2) {
-    step(std::integral_constant<int, 0>{}, it);
-    if (it + 1 < n_qt) step(std::integral_constant<int, 1>{}, it + 1);
+  for (int t = 0; t < n_steps; t += 2) {
+    step(std::integral_constant<int, 0>{}, t);
+    if (t + 1 < n_steps) step(std::integral_constant<int, 1>{}, t + 1);
   }
 
   // dK = scale * dK_acc, dV = dV_acc. Lane holds key my_key, columns 32cb + 8t + 4g + 0..3.
@@ -608,7 +636,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dq_kernel(
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ o,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, float* __restrict__ lse2,
     float* __restrict__ delta, uint16_t* __restrict__ dq, int N, int n_qblocks, int bh_count,
-    float scale_log2, float scale) {
+    int n_qheads, int group, long long kv_bstride, float scale_log2, float scale) {
   constexpr int KK = D / 16, CB = D / 32;
   constexpr int BC = D == 256 ? 32 : 64;   // keys per tile
   constexpr int KB = BC / 32;              // 32-key MFMA blocks per tile
@@ -629,8 +657,12 @@ __global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dq_kernel(
   const size_t head_off = (size_t)tc.bh * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + head_off, head_bytes);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + head_off, head_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + head_off, head_bytes);
+  // K/V head of this query head (grouped heads share one; batch stride may be packed)
+  const int b_idx = tc.bh / n_qheads;
+  const size_t kv_off = (size_t)b_idx * (size_t)kv_bstride +
+                        (size_t)((tc.bh - b_idx * n_qheads) / group) * (size_t)N * D;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + kv_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + kv_off, head_bytes);
   const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dout + head_off, head_bytes);
 
   const int q_block0 = tc.qb * kDqBR;
@@ -781,14 +813,14 @@ hipError_t launch_pre_t(const BwdArgs& a) {
 template <int D, bool CAUSAL>
 hipError_t launch_dkdv_t(const BwdArgs& a) {
   const int n_kblocks = (a.N + kKvBK - 1) / kKvBK;
-  const long long grid = (long long)n_kblocks * a.B * a.H;
+  const long long grid = (long long)n_kblocks * a.B * a.Hkv;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kKvThreads), 0,
                      a.stream, static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                      static_cast<const uint16_t*>(a.dout), a.lse2, a.delta,
                      static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), a.N, n_kblocks,
-                     a.B * a.H, a.scale_log2, a.scale);
+                     a.B * a.Hkv, a.H, a.H / a.Hkv, a.kv_bstride, a.scale_log2, a.scale);
   return hipGetLastError();
 }
 
@@ -799,7 +831,7 @@ hipError_t launch_dq_one(const BwdArgs& a, unsigned grid, int n_qblocks) {
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                      static_cast<const uint16_t*>(a.o), static_cast<const uint16_t*>(a.dout),
                      a.lse, a.lse2, a.delta, static_cast<uint16_t*>(a.dq), a.N, n_qblocks,
-                     a.B * a.H, a.scale_log2, a.scale);
+                     a.B * a.H, a.H, a.H / a.Hkv, a.kv_bstride, a.scale_log2, a.scale);
   return hipGetLastError();
 }
 
@@ -827,14 +859,14 @@ hipError_t launch_bwd_pre(const BwdArgs& a) {
 template <bool CAUSAL>
 hipError_t launch_dkdv256_t(const BwdArgs& a) {
   const int n_kblocks = (a.N + kKv256BK - 1) / kKv256BK;
-  const long long grid = (long long)n_kblocks * a.B * a.H;
+  const long long grid = (long long)n_kblocks * a.B * a.Hkv;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((fa2_bwd_dkdv256_kernel<CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0,
                      a.stream, static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                      static_cast<const uint16_t*>(a.dout), a.lse2, a.delta,
                      static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), a.N, n_kblocks,
-                     a.B * a.H, a.scale_log2, a.scale);
+                     a.B * a.Hkv, a.H, a.H / a.Hkv, a.kv_bstride, a.scale_log2, a.scale);
   return hipGetLastError();
 }
 

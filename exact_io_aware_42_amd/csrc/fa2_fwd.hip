@@ -72,7 +72,8 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
-    int N, int n_qblocks, int bh_count, float scale_log2) {
+    int N, int n_qblocks, int bh_count, int n_qheads, int group, long long kv_bstride,
+    float scale_log2) {
   using S = FwdShape<D>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[S::SMEM];
 
@@ -85,10 +86,14 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
   const TileCoord tc = schedule_tile<CAUSAL ? Order::kLongDescending : Order::kHeadMajor>(
       blockIdx.x, n_qblocks, bh_count);
   const size_t head_off = (size_t)tc.bh * (size_t)N * D;
+  // K/V head of this query head (grouped heads share one; batch stride may be packed)
+  const int b_idx = tc.bh / n_qheads;
+  const size_t kv_off = (size_t)b_idx * (size_t)kv_bstride +
+                        (size_t)((tc.bh - b_idx * n_qheads) / group) * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + head_off, head_bytes);
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + head_off, head_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + head_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + kv_off, head_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + kv_off, head_bytes);
 
   const int q_block0 = tc.qb * kFwdBR;
   const int q_wave0 = q_block0 + wave * 32;
@@ -339,8 +344,8 @@ hipError_t launch_fwd_t(const FwdArgs& a) {
   hipLaunchKernelGGL((fa2_fwd_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kFwdThreads), 0,
                      a.stream, static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
-                     static_cast<uint16_t*>(a.o), a.lse, a.N, n_qblocks, a.B * a.H,
-                     a.scale_log2);
+                     static_cast<uint16_t*>(a.o), a.lse, a.N, n_qblocks, a.B * a.H, a.H,
+                     a.H / a.Hkv, a.kv_bstride, a.scale_log2);
   return hipGetLastError();
 }
 

@@ -7,6 +7,9 @@
 
 namespace fa2 {
 
+// H counts query heads. K and V have Hkv heads (H a multiple of Hkv; query head h reads K/V head
+// h / (H / Hkv)) and kv_bstride elements between batches (Hkv*N*d for their own tensors,
+// 2*Hkv*N*d when packed as [B, 2, Hkv, N, d]); dK, dV are written with the same layout.
 struct FwdArgs {
   const void* q;
   const void* k;
@@ -14,6 +17,8 @@ struct FwdArgs {
   void* o;
   float* lse;
   int B, H, N, d;
+  int Hkv;
+  long long kv_bstride;
   bool causal;
   float scale_log2;  // softmax_scale * log2(e)
   hipStream_t stream;
@@ -32,6 +37,8 @@ struct BwdArgs {
   float* delta;  // workspace: D = rowsum(dO * O), fp32 [B, H, N]
   float* lse2;   // workspace: LSE * log2(e), fp32 [B, H, N]
   int B, H, N, d;
+  int Hkv;
+  long long kv_bstride;
   bool causal;
   float scale;       // softmax_scale
   float scale_log2;  // softmax_scale * log2(e)
@@ -39,7 +46,7 @@ struct BwdArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs& a);
-hipError_t launch_bwd(const BwdArgs& a);  // pre, then dK/dV, then dQ
+hipError_t launch_bwd(const BwdArgs& a);  // dQ (also D and LSE*log2(e)), then dK/dV
 hipError_t launch_bwd_pre(const BwdArgs& a);
 hipError_t launch_bwd_dkdv(const BwdArgs& a);
 hipError_t launch_bwd_dq(const BwdArgs& a);

@@ -24,7 +24,8 @@ FA2_ERR_UNSUPPORTED = 2
 FA2_ERR_HIP = 3
 
 EXPORTED = ("fa2_fwd", "fa2_bwd", "fa2_bwd_workspace_bytes", "fa2_bwd_preprocess",
-            "fa2_bwd_dkdv", "fa2_bwd_dq", "fa2_status_string", "fa2_last_hip_error")
+            "fa2_bwd_dkdv", "fa2_bwd_dq", "fa2_fwd_gqa", "fa2_bwd_gqa", "fa2_status_string",
+            "fa2_last_hip_error")
 
 _lib = None
 _lock = threading.Lock()
@@ -45,6 +46,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                            "`python -m exact_io_aware_42_amd.build` (no fallback exists)")
         lib = ctypes.CDLL(path)
         vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        ll = ctypes.c_longlong
         lib.fa2_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
         lib.fa2_fwd.restype = i
         lib.fa2_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
@@ -56,6 +58,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.fa2_bwd_dkdv.restype = i
         lib.fa2_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, vp, i, i, i, i, i, f, vp]
         lib.fa2_bwd_dq.restype = i
+        lib.fa2_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, ll, i, f, vp]
+        lib.fa2_fwd_gqa.restype = i
+        lib.fa2_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                    i, i, i, i, i, ll, i, f, vp]
+        lib.fa2_bwd_gqa.restype = i
         lib.fa2_bwd_workspace_bytes.argtypes = [i, i, i, i]
         lib.fa2_bwd_workspace_bytes.restype = sz
         lib.fa2_status_string.argtypes = [i]
@@ -97,17 +104,44 @@ def default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
 
 
+def _kv_layout(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
+    """(Hkv, batch stride in elements) of k and v: [B, Hkv, N, d] with heads, rows and columns
+    contiguous, the same strides for both (separate tensors, or views of a packed
+    [B, 2, Hkv, N, d] tensor); H must be a multiple of Hkv."""
+    B, H, N, d = q.shape
+    for t, nm in ((k, "k"), (v, "v")):
+        if not isinstance(t, torch.Tensor) or t.dim() != 4:
+            raise ValueError(f"{nm} must be a [B, Hkv, N, d] tensor")
+    if q.numel() == 0:  # empty problem: nothing is read (the library returns at once)
+        return H, H * N * d
+        if t.device != q.device or t.dtype != torch.bfloat16:
+            raise ValueError(f"{nm} must be bfloat16 on {q.device}")
+    Hkv = k.shape[1]
+    if tuple(k.shape) != (B, Hkv, N, d) or tuple(v.shape) != (B, Hkv, N, d):
+        raise ValueError(f"k, v must be [B, Hkv, N, d] = [{B}, Hkv, {N}, {d}]")
+    if Hkv <= 0 or H % Hkv:
+        raise ValueError(f"the {H} query heads must be a multiple of the {Hkv} K/V heads")
+    inner = (N * d, d, 1)
+    if tuple(k.stride()[1:]) != inner or tuple(v.stride()[1:]) != inner or \
+            k.stride(0) != v.stride(0):
+        raise ValueError("k and v need contiguous heads, rows and columns and equal strides")
+    kvs = k.stride(0) if B > 1 else Hkv * N * d
+    return Hkv, kvs
+
+
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
         scale: float | None = None, out: torch.Tensor | None = None,
         lse: torch.Tensor | None = None):
-    """Attention forward on bf16 [B, H, N, d] tensors. Returns (o bf16, lse fp32 [B, H, N])."""
+    """Attention forward on bf16 [B, H, N, d] tensors. Returns (o bf16, lse fp32 [B, H, N]).
+    k and v may have fewer heads (Hkv dividing H: grouped heads) and may be views of one packed
+    [B, 2, Hkv, N, d] tensor."""
     lib = load_library()
     if q.dim() != 4:
         raise ValueError("q must be [B, H, N, d]")
     B, H, N, d = q.shape
     dev = q.device
-    for t, nm in ((q, "q"), (k, "k"), (v, "v")):
-        _check_tensor(t, nm, (B, H, N, d), device=dev)
+    _check_tensor(q, "q", (B, H, N, d), device=dev)
+    Hkv, kvs = _kv_layout(q, k, v)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
@@ -115,10 +149,23 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
     _check_tensor(out, "out", (B, H, N, d), device=dev)
     _check_tensor(lse, "lse", (B, H, N), dtype=torch.float32, device=dev)
     s = default_scale(d) if scale is None else float(scale)
-    st = lib.fa2_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                     B, H, N, d, int(bool(causal)), s, _stream_ptr(dev))
+    if Hkv == H and kvs == H * N * d:
+        st = lib.fa2_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                         lse.data_ptr(), B, H, N, d, int(bool(causal)), s, _stream_ptr(dev))
+    else:
+        st = lib.fa2_fwd_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                             lse.data_ptr(), B, H, Hkv, N, d, kvs, int(bool(causal)), s,
+                             _stream_ptr(dev))
     _check(st, "fa2_fwd")
     return out, lse
+
+
+def fwd_kvpacked(q: torch.Tensor, kv: torch.Tensor, causal: bool = False,
+                 scale: float | None = None):
+    """Forward with K and V packed in one contiguous bf16 [B, 2, Hkv, N, d] tensor."""
+    if kv.dim() != 5 or kv.shape[1] != 2 or not kv.is_contiguous():
+        raise ValueError("kv must be a contiguous [B, 2, Hkv, N, d] tensor")
+    return fwd(q, kv[:, 0], kv[:, 1], causal=causal, scale=scale)
 
 
 def bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
@@ -127,30 +174,49 @@ def bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
 
 def bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None,
         dq=None, dk=None, dv=None, workspace=None):
-    """Attention backward. Returns (dq, dk, dv) bf16 [B, H, N, d]."""
+    """Attention backward. Returns (dq, dk, dv) bf16; dk, dv have k's and v's layout (grouped
+    and packed K/V as in fwd)."""
     lib = load_library()
     B, H, N, d = q.shape
     dev = q.device
-    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+    for t, nm in ((q, "q"), (o, "o"), (dout, "dout")):
         _check_tensor(t, nm, (B, H, N, d), device=dev)
+    Hkv, kvs = _kv_layout(q, k, v)
     _check_tensor(lse, "lse", (B, H, N), dtype=torch.float32, device=dev)
     dq = torch.empty_like(q) if dq is None else dq
-    dk = torch.empty_like(k) if dk is None else dk
-    dv = torch.empty_like(v) if dv is None else dv
-    for t, nm in ((dq, "dq"), (dk, "dk"), (dv, "dv")):
-        _check_tensor(t, nm, (B, H, N, d), device=dev)
+    _check_tensor(dq, "dq", (B, H, N, d), device=dev)
+    if dk is None:
+        dk = torch.empty_strided(k.shape, k.stride(), dtype=k.dtype, device=dev)
+    if dv is None:
+        dv = torch.empty_strided(v.shape, v.stride(), dtype=v.dtype, device=dev)
+    if _kv_layout(q, dk, dv) != (Hkv, kvs):
+        raise ValueError("dk and dv must have the layout of k and v")
     ws_bytes = bwd_workspace_bytes(B, H, N, d)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     if workspace.device != dev or workspace.numel() * workspace.element_size() < ws_bytes:
         raise ValueError("workspace too small or on another device")
     s = default_scale(d) if scale is None else float(scale)
-    st = lib.fa2_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
-                     lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
-                     workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                     B, H, N, d, int(bool(causal)), s, _stream_ptr(dev))
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size())
+    if Hkv == H and kvs == H * N * d:
+        st = lib.fa2_bwd(*ptrs, B, H, N, d, int(bool(causal)), s, _stream_ptr(dev))
+    else:
+        st = lib.fa2_bwd_gqa(*ptrs, B, H, Hkv, N, d, kvs, int(bool(causal)), s,
+                             _stream_ptr(dev))
     _check(st, "fa2_bwd")
     return dq, dk, dv
+
+
+def bwd_kvpacked(q, kv, o, dout, lse, causal: bool = False, scale: float | None = None):
+    """Backward for packed K/V: returns (dq, dkv) with dkv [B, 2, Hkv, N, d] like kv."""
+    if kv.dim() != 5 or kv.shape[1] != 2 or not kv.is_contiguous():
+        raise ValueError("kv must be a contiguous [B, 2, Hkv, N, d] tensor")
+    dkv = torch.empty_like(kv)
+    dq, _, _ = bwd(q, kv[:, 0], kv[:, 1], o, dout, lse, causal=causal, scale=scale,
+                   dk=dkv[:, 0], dv=dkv[:, 1])
+    return dq, dkv
 
 
 def _ws(workspace: torch.Tensor, B: int, H: int, N: int, d: int):

@@ -112,6 +112,25 @@ fa2_status fa2_bwd_preprocess(const void* o, const void* dout, const float* lse,
                               void* workspace, size_t workspace_bytes,
                               int B, int H, int N, int d, hipStream_t stream);
 
+/* Grouped K/V heads and packed K/V (page "Flash Attention v2", "Migration from v1 to v2", names a
+ * kvpacked entry point among the v2 functions). q, o, dq: [B, H, N, d]; lse: [B, H, N] as above.
+ * k, v and, in the backward, dk, dv: per batch Hkv heads of [N, d], heads contiguous, and
+ * kv_batch_stride elements from one batch to the next: Hkv*N*d for tensors of their own, 2*Hkv*N*d
+ * for K and V packed as [B, 2, Hkv, N, d] (k = kv, v = kv + Hkv*N*d; the same for dk, dv). H must be
+ * a multiple of Hkv; query head h attends to K/V head h / (H / Hkv) (Hkv = 1: one K/V head for
+ * all). dK and dV sum the contributions of the query heads of a group in a fixed order
+ * (deterministic). kv_batch_stride must be a multiple of 8 and at least Hkv*N*d. Otherwise as
+ * fa2_fwd / fa2_bwd (which are these calls with Hkv = H and kv_batch_stride = H*N*d). */
+fa2_status fa2_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int H, int Hkv, int N, int d, long long kv_batch_stride,
+                       int causal, float softmax_scale, hipStream_t stream);
+
+fa2_status fa2_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
+                       const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                       void* workspace, size_t workspace_bytes, int B, int H, int Hkv, int N,
+                       int d, long long kv_batch_stride, int causal, float softmax_scale,
+                       hipStream_t stream);
+
 /* Static, human-readable name of a status code. */
 const char* fa2_status_string(fa2_status s);
 

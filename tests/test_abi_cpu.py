@@ -188,3 +188,30 @@ def test_longest_first_shortens_the_causal_tail():
     ideal = total / 64
     assert _makespan(LONG_DESC) <= 1.15 * ideal
     assert _makespan(LONG_DESC) < _makespan(HEAD_MAJOR)
+
+
+def test_grouped_kv_validation():
+    """fa2_fwd_gqa / fa2_bwd_gqa reject bad K/V head counts and strides before any HIP call
+    (the pointers are fake; every case has an invalid parameter)."""
+    lib = _lib()
+    N, d = 16, 64
+    ok = dict(B=2, H=8, Hkv=2, kvs=2 * N * d)
+    def fwd(B=2, H=8, Hkv=2, kvs=2 * N * d, d_=d):
+        return lib.fa2_fwd_gqa(P, P, P, P, P, B, H, Hkv, N, d_, kvs, 1, 0.125, None)
+    assert fwd(Hkv=3) == ops.FA2_ERR_INVALID_ARGUMENT            # 8 % 3 != 0
+    assert fwd(Hkv=0) == ops.FA2_ERR_INVALID_ARGUMENT
+    assert fwd(Hkv=16) == ops.FA2_ERR_INVALID_ARGUMENT           # more K/V heads than Q heads
+    assert fwd(kvs=2 * N * d - 8) == ops.FA2_ERR_INVALID_ARGUMENT  # batches overlap
+    assert fwd(kvs=2 * N * d + 4) == ops.FA2_ERR_INVALID_ARGUMENT  # not a multiple of 8
+    assert fwd(Hkv=3, d_=96) == ops.FA2_ERR_UNSUPPORTED
+    ws = lib.fa2_bwd_workspace_bytes(2, 8, N, d)
+    base = [P] * 10
+    assert lib.fa2_bwd_gqa(*base, ws, 2, 8, 3, N, d, 3 * N * d, 0, 0.125, None) == \
+        ops.FA2_ERR_INVALID_ARGUMENT
+    assert lib.fa2_bwd_gqa(*base, ws, 2, 8, 2, N, d, N * d, 0, 0.125, None) == \
+        ops.FA2_ERR_INVALID_ARGUMENT
+    assert lib.fa2_bwd_gqa(*base, ws - 1, 2, 8, 2, N, d, 2 * N * d, 0, 0.125, None) == \
+        ops.FA2_ERR_INVALID_ARGUMENT
+    # empty problems stay no-ops
+    assert lib.fa2_fwd_gqa(None, None, None, None, None, 0, 8, 2, N, d, 2 * N * d, 1, 0.125,
+                           None) == ops.FA2_OK
