@@ -17,8 +17,9 @@ FETCH_SIZE / WRITE_SIZE counter summaries under profiles/ (null if the kernel so
 since they were taken). `cpu_baseline` times the CPU float64 oracle on a bounded sample of
 the same workload (whole heads) on the host cores. `forward_workloads` adds the forward
 kernel's TFLOP/s on the forward-only workloads, `d256_steps` the fwd+bwd step at head
-dimension 256 and `gpt_layer_step` a GPT-style attention layer (bf16 projections + attention,
-forward and backward through torch.autograd); none of them is part of `value`.
+dimension 256, `gpt_layer_step` a GPT-style attention layer (bf16 projections + attention,
+forward and backward through torch.autograd) and `gqa_step` the fwd+bwd step with 16 query
+heads sharing 4 K/V heads; none of them is part of `value`.
 
 Prints ONE JSON line (rank 0).
 """
@@ -182,6 +183,34 @@ def gpt_layer_step(torch, dev, steps=20, warmup=10):
             "attention_flop_share": round(fl["attention"] / total, 3)}
 
 
+def gqa_step(fa2, torch, dev, steps=20, warmup=20):
+    """Forward+backward with grouped K/V heads at the fwd+bwd workload's shape: B=4, H=16
+    query heads sharing Hkv=4 K/V heads (groups of 4), N=2048, d=128, causal; i.i.d. N(0,1)
+    bf16 from seeded torch generators. FLOP as for 16 full heads."""
+    B, H, Hkv, N, d = 4, 16, 4, 2048, 128
+    g = torch.Generator(device="cpu").manual_seed(11)
+    mk = lambda h: torch.randn(B, h, N, d, generator=g).to(torch.bfloat16).to(dev)
+    q, k, v, do = mk(H), mk(Hkv), mk(Hkv), mk(H)
+
+    def step():
+        o, lse = fa2.fwd(q, k, v, causal=True)
+        fa2.bwd(q, k, v, o, do, lse, causal=True)
+
+    for _ in range(warmup):
+        step()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flop = 3.5 * fwd_flop(B, H, N, d, True)
+    return {"shape": f"B{B} H{H} Hkv{Hkv} N{N} d{d} causal", "ms_per_step": round(ms, 4),
+            "tflops": round(flop / (ms * 1e-3) / 1e12, 1)}
+
+
 def measure_step(fa2, torch, dev, w, causal, with_bwd, steps, warmup):
     """Run `warmup` untimed and `steps` timed steps (forward, then dQ and dK/dV) of workload
     `w`; each stage is bracketed by HIP events on the launch stream. Returns (stage names,
@@ -329,6 +358,7 @@ def main():
                 "kernel_tflops": {kn: round(af6[kn] / (km6[kn] * 1e-3) / 1e12, 1) for kn in kn6}}
         out["d256_steps"] = steps6
         out["gpt_layer_step"] = gpt_layer_step(torch, dev)
+        out["gqa_step"] = gqa_step(fa2, torch, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, causal, with_bwd, args.cpu_seconds)
     print(json.dumps(out), flush=True)
