@@ -8,6 +8,7 @@ Modules:
   attention   plain definition: forward (O, LSE), probabilities, analytic backward
   bruteforce  scalar loops for tiny shapes
   online      float64 model of the tiled online-softmax recurrence
+  dropout     attention with dropout on P and its counter-based mask generator
 
 Every function here is pinned by CPU tests to something other than itself (brute force,
 closed forms, invariants, finite differences, PyTorch's CPU scaled_dot_product_attention,
@@ -15,6 +16,8 @@ hand-derived values under tests/golden/).
 """
 from .attention import attention_backward, attention_forward, attention_probs, resolve_scale
 from .bruteforce import attention_bruteforce
+from .dropout import (attention_backward_dropout, attention_forward_dropout, keep_mask,
+                      keep_scale, pcg_hash)
 from .online import online_attention_forward
 
 __all__ = [
@@ -24,4 +27,9 @@ __all__ = [
     "resolve_scale",
     "attention_bruteforce",
     "online_attention_forward",
+    "attention_forward_dropout",
+    "attention_backward_dropout",
+    "keep_mask",
+    "keep_scale",
+    "pcg_hash",
 ]
