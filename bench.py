@@ -18,8 +18,9 @@ since they were taken). `cpu_baseline` times the CPU float64 oracle on a bounded
 the same workload (whole heads) on the host cores. `forward_workloads` adds the forward
 kernel's TFLOP/s on the forward-only workloads, `d256_steps` the fwd+bwd step at head
 dimension 256, `gpt_layer_step` a GPT-style attention layer (bf16 projections + attention,
-forward and backward through torch.autograd) and `gqa_step` the fwd+bwd step with 16 query
-heads sharing 4 K/V heads; none of them is part of `value`.
+forward and backward through torch.autograd), `gqa_step` the fwd+bwd step with 16 query
+heads sharing 4 K/V heads and `dropout_step` the fwd+bwd step with dropout p = 0.1 on the
+attention probabilities; none of them is part of `value`.
 
 Prints ONE JSON line (rank 0).
 """
@@ -183,18 +184,17 @@ def gpt_layer_step(torch, dev, steps=20, warmup=10):
             "attention_flop_share": round(fl["attention"] / total, 3)}
 
 
-def gqa_step(fa2, torch, dev, steps=20, warmup=20):
-    """Forward+backward with grouped K/V heads at the fwd+bwd workload's shape: B=4, H=16
-    query heads sharing Hkv=4 K/V heads (groups of 4), N=2048, d=128, causal; i.i.d. N(0,1)
-    bf16 from seeded torch generators. FLOP as for 16 full heads."""
-    B, H, Hkv, N, d = 4, 16, 4, 2048, 128
+def _timed_fwd_bwd(fa2, torch, dev, H, Hkv, steps, warmup, **kw):
+    """Mean wall time (ms) of fwd + bwd at B=4, N=2048, d=128, causal, with H query heads and
+    Hkv K/V heads; i.i.d. N(0,1) bf16 from a seeded torch generator. kw goes to fwd and bwd."""
+    B, N, d = 4, 2048, 128
     g = torch.Generator(device="cpu").manual_seed(11)
     mk = lambda h: torch.randn(B, h, N, d, generator=g).to(torch.bfloat16).to(dev)
     q, k, v, do = mk(H), mk(Hkv), mk(Hkv), mk(H)
 
     def step():
-        o, lse = fa2.fwd(q, k, v, causal=True)
-        fa2.bwd(q, k, v, o, do, lse, causal=True)
+        o, lse = fa2.fwd(q, k, v, causal=True, **kw)
+        fa2.bwd(q, k, v, o, do, lse, causal=True, **kw)
 
     for _ in range(warmup):
         step()
@@ -207,8 +207,24 @@ def gqa_step(fa2, torch, dev, steps=20, warmup=20):
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     flop = 3.5 * fwd_flop(B, H, N, d, True)
-    return {"shape": f"B{B} H{H} Hkv{Hkv} N{N} d{d} causal", "ms_per_step": round(ms, 4),
-            "tflops": round(flop / (ms * 1e-3) / 1e12, 1)}
+    return {"ms_per_step": round(ms, 4), "tflops": round(flop / (ms * 1e-3) / 1e12, 1)}
+
+
+def gqa_step(fa2, torch, dev, steps=20, warmup=20):
+    """Forward+backward with grouped K/V heads at the fwd+bwd workload's shape: B=4, H=16
+    query heads sharing Hkv=4 K/V heads (groups of 4), N=2048, d=128, causal. FLOP as for 16
+    full heads."""
+    r = _timed_fwd_bwd(fa2, torch, dev, 16, 4, steps, warmup)
+    return {"shape": "B4 H16 Hkv4 N2048 d128 causal", **r}
+
+
+def dropout_step(fa2, torch, dev, p=0.1, steps=20, warmup=20):
+    """Forward+backward with dropout p on the attention probabilities (mask regenerated from
+    the counter-based hash in every kernel) at the fwd+bwd workload's shape: B=4, H=16,
+    N=2048, d=128, causal. FLOP as without dropout (the hash work is not counted)."""
+    r = _timed_fwd_bwd(fa2, torch, dev, 16, 16, steps, warmup, dropout_p=p, seed=1234,
+                       offset=0)
+    return {"shape": "B4 H16 N2048 d128 causal", "dropout_p": p, **r}
 
 
 def measure_step(fa2, torch, dev, w, causal, with_bwd, steps, warmup):
@@ -359,6 +375,7 @@ def main():
         out["d256_steps"] = steps6
         out["gpt_layer_step"] = gpt_layer_step(torch, dev)
         out["gqa_step"] = gqa_step(fa2, torch, dev)
+        out["dropout_step"] = dropout_step(fa2, torch, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, causal, with_bwd, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -15,26 +15,32 @@ from . import ops
 
 class FlashAttention(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, q, k, v, causal: bool, scale: float | None):
-        o, lse = ops.fwd(q, k, v, causal=causal, scale=scale)
+    def forward(ctx, q, k, v, causal: bool, scale: float | None, dropout_p: float, seed: int,
+                offset: int):
+        o, lse = ops.fwd(q, k, v, causal=causal, scale=scale, dropout_p=dropout_p, seed=seed,
+                         offset=offset)
         ctx.save_for_backward(q, k, v, o, lse)
-        ctx.causal = causal
-        ctx.scale = scale
+        ctx.args = (causal, scale, dropout_p, seed, offset)
         return o
 
     @staticmethod
     def backward(ctx, do):
         q, k, v, o, lse = ctx.saved_tensors
-        dq, dk, dv = ops.bwd(q, k, v, o, do.contiguous(), lse, causal=ctx.causal,
-                             scale=ctx.scale)
-        return dq, dk, dv, None, None
+        causal, scale, p, seed, offset = ctx.args
+        dq, dk, dv = ops.bwd(q, k, v, o, do.contiguous(), lse, causal=causal, scale=scale,
+                             dropout_p=p, seed=seed, offset=offset)
+        return dq, dk, dv, None, None, None, None, None
 
 
-def flash_attn_func(q, k, v, causal: bool = False, scale: float | None = None):
+def flash_attn_func(q, k, v, dropout_p: float = 0.0, causal: bool = False,
+                    scale: float | None = None, seed: int = 0, offset: int = 0):
     """softmax(scale * q k^T [+ causal mask]) v for bf16 [B, H, N, d] tensors, differentiable
     in q, k and v. `scale` defaults to 1/sqrt(d). k and v may have Hkv heads with Hkv dividing
-    H (query head h uses K/V head h / (H / Hkv))."""
-    return FlashAttention.apply(q, k, v, bool(causal), scale)
+    H (query head h uses K/V head h / (H / Hkv)). dropout_p > 0 drops attention probabilities
+    with the counter-based mask of (seed, offset); pass a new offset for every call that
+    should draw a fresh mask."""
+    return FlashAttention.apply(q, k, v, bool(causal), scale, float(dropout_p), int(seed),
+                                int(offset))
 
 
 class FlashAttentionKVPacked(torch.autograd.Function):

@@ -49,6 +49,31 @@ fa2_status from_hip(hipError_t e) {
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Dropout keys and threshold (the mask generator is documented in fa2.h): the same 32-bit hash
+// the kernels use, applied on the host to the seed and offset halves.
+uint32_t host_pcg_hash(uint32_t x) {
+  const uint32_t state = x * 747796405u + 2891336453u;
+  const uint32_t word = ((state >> ((state >> 28u) + 4u)) ^ state) * 277803737u;
+  return (word >> 22u) ^ word;
+}
+
+struct DropHost {
+  uint32_t k0, k1, thr;
+  float scale;
+};
+
+// FA2_OK and the parameters for 0 < p < 1; p outside [0, 1) is invalid.
+fa2_status drop_params(float p, unsigned long long seed, unsigned long long offset,
+                       DropHost* out) {
+  if (!(p >= 0.0f && p < 1.0f)) return FA2_ERR_INVALID_ARGUMENT;
+  const double t = std::floor((double)p * 4294967296.0);
+  out->thr = t > 4294967295.0 ? 0xFFFFFFFFu : (uint32_t)t;
+  out->scale = (float)(1.0 / (1.0 - (double)out->thr / 4294967296.0));
+  out->k0 = host_pcg_hash((uint32_t)seed ^ host_pcg_hash((uint32_t)(seed >> 32)));
+  out->k1 = host_pcg_hash((uint32_t)offset ^ host_pcg_hash((uint32_t)(offset >> 32)));
+  return FA2_OK;
+}
+
 // K/V head count and batch stride (elements) for grouped or packed K/V. FA2_OK or the status.
 fa2_status check_kv(int B, int H, int Hkv, int N, int d, long long kv_bstride) {
   if (Hkv <= 0 || H % Hkv != 0) return FA2_ERR_INVALID_ARGUMENT;
@@ -63,9 +88,13 @@ fa2_status check_kv(int B, int H, int Hkv, int N, int d, long long kv_bstride) {
 
 fa2_status fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                     int H, int Hkv, int N, int d, long long kv_bstride, int causal,
-                    float softmax_scale, hipStream_t stream) {
+                    float softmax_scale, hipStream_t stream, float dropout_p = 0.f,
+                    unsigned long long seed = 0, unsigned long long offset = 0) {
   bool empty;
   fa2_status st = check_sizes(B, H, N, d, softmax_scale, &empty);
+  if (st != FA2_OK) return st;
+  DropHost drop;
+  st = drop_params(dropout_p, seed, offset, &drop);
   if (st != FA2_OK || empty) return st;
   st = check_kv(B, H, Hkv, N, d, kv_bstride);
   if (st != FA2_OK) return st;
@@ -86,6 +115,11 @@ fa2_status fwd_impl(const void* q, const void* k, const void* v, void* o, float*
   a.kv_bstride = kv_bstride;
   a.causal = causal != 0;
   a.scale_log2 = static_cast<float>(static_cast<double>(softmax_scale) * kLog2e);
+  a.dropout = dropout_p > 0.f;
+  a.drop_k0 = drop.k0;
+  a.drop_k1 = drop.k1;
+  a.drop_thr = drop.thr;
+  a.drop_scale = drop.scale;
   a.stream = stream;
   return from_hip(fa2::launch_fwd(a));
 }
@@ -105,6 +139,15 @@ fa2_status fa2_fwd_gqa(const void* q, const void* k, const void* v, void* o, flo
                        float softmax_scale, hipStream_t stream) {
   return fwd_impl(q, k, v, o, lse, B, H, Hkv, N, d, kv_batch_stride, causal, softmax_scale,
                   stream);
+}
+
+fa2_status fa2_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int Hkv, int N, int d, long long kv_batch_stride,
+                           int causal, float softmax_scale, float dropout_p,
+                           unsigned long long seed, unsigned long long offset,
+                           hipStream_t stream) {
+  return fwd_impl(q, k, v, o, lse, B, H, Hkv, N, d, kv_batch_stride, causal, softmax_scale,
+                  stream, dropout_p, seed, offset);
 }
 
 // Workspace layout: D = rowsum(dO * O) [B*H*N floats], then LSE * log2(e) [B*H*N floats],
@@ -188,6 +231,33 @@ fa2_status fa2_bwd_gqa(const void* q, const void* k, const void* v, const void* 
   if (!all_ok({q, k, v, o, dout, lse, dq, dk, dv})) return FA2_ERR_INVALID_ARGUMENT;
   a.Hkv = Hkv;
   a.kv_bstride = kv_batch_stride;
+  return from_hip(fa2::launch_bwd(a));
+}
+
+fa2_status fa2_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                           void* workspace, size_t workspace_bytes, int B, int H, int Hkv,
+                           int N, int d, long long kv_batch_stride, int causal,
+                           float softmax_scale, float dropout_p, unsigned long long seed,
+                           unsigned long long offset, hipStream_t stream) {
+  fa2::BwdArgs a;
+  bool empty;
+  fa2_status st = bwd_args(q, k, v, o, dout, lse, workspace, workspace_bytes, dq, dk, dv, B, H,
+                           N, d, causal, softmax_scale, stream, &a, &empty);
+  if (st != FA2_OK) return st;
+  DropHost drop;
+  st = drop_params(dropout_p, seed, offset, &drop);
+  if (st != FA2_OK || empty) return st;
+  st = check_kv(B, H, Hkv, N, d, kv_batch_stride);
+  if (st != FA2_OK) return st;
+  if (!all_ok({q, k, v, o, dout, lse, dq, dk, dv})) return FA2_ERR_INVALID_ARGUMENT;
+  a.Hkv = Hkv;
+  a.kv_bstride = kv_batch_stride;
+  a.dropout = dropout_p > 0.f;
+  a.drop_k0 = drop.k0;
+  a.drop_k1 = drop.k1;
+  a.drop_thr = drop.thr;
+  a.drop_scale = drop.scale;
   return from_hip(fa2::launch_bwd(a));
 }
 

@@ -147,13 +147,13 @@ constexpr int kKvBK = 128;
 constexpr int kKvBQ = 64;
 constexpr int kKvThreads = 512;
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse2, const float* __restrict__ delta, uint16_t* __restrict__ dk,
     uint16_t* __restrict__ dv, int N, int n_kblocks, int bh_count, int n_qheads, int group,
-    long long kv_bstride, float scale_log2, float scale) {
+    long long kv_bstride, float scale_log2, float scale, DropParams drop) {
   constexpr int KK = D / 16, CB = D / 32, DCH = D / 8;
   // LDS: the two ring stages of Q and dO tiles at the bottom (every ds_read of them is a
   // per-lane base plus a 16-bit immediate), then LSE*log2(e) and D of both stages, then the
@@ -196,6 +196,7 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
   const int key_b0 = tc.qb * kKvBK;
   const int key_w0 = key_b0 + kw * 32;
   const int my_key = key_w0 + l32;
+  const uint32_t drop_col = (uint32_t)my_key * kDropKeyMul;  // dropout: this lane's key term
 
   // resident K and V rows of the block: 128 rows each, swz-swizzled; 1 KiB block i holds rows
   // (64/DCH)*i ..
@@ -281,6 +282,7 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
     if (t + 1 < n_steps) load_stage(t + 1, stage ^ 1);
     const int it = qt_begin + t % nt;
     const int q0 = it * kKvBQ + 32 * hq;  // this wave's 32 queries
+    const uint32_t drop_head = DROP ? drop_head_key(drop, (uint32_t)(qh0 + t / nt)) : 0u;
     // every query of the half precedes every key of the wave: fully masked
     const bool skip = CAUSAL && (q0 + 31 < key_w0);
     if (!skip) {
@@ -323,8 +325,17 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
         for (int e = 0; e < 8; ++e) {
           const float lv = e < 4 ? l0[e] : l1[e - 4];
           const float dv_ = e < 4 ? d0[e] : d1[e - 4];
-          p[e] = fast_exp2(__builtin_fmaf(s[8 * hf + e], scale_log2, -lv));
-          ds[e] = p[e] * (dp[8 * hf + e] - dv_);
+          const float pe = fast_exp2(__builtin_fmaf(s[8 * hf + e], scale_log2, -lv));
+          if constexpr (DROP) {
+            // query q0 + 16hf + 8g + e of head qh0 + gi: kept with its 1/P(keep) scale or 0
+            const uint32_t row = pcg_hash(drop_head ^ (uint32_t)(q0 + 16 * hf + 8 * g + e));
+            const float zs = pcg_hash(row ^ drop_col) >= drop.thr ? drop.scale : 0.f;
+            p[e] = pe * zs;
+            ds[e] = pe * (dp[8 * hf + e] * zs - dv_);
+          } else {
+            p[e] = pe;
+            ds[e] = pe * (dp[8 * hf + e] - dv_);
+          }
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -414,13 +425,13 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
 constexpr int kKv256BK = 64;
 constexpr int kKv256BQ = 32;
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse2, const float* __restrict__ delta, uint16_t* __restrict__ dk,
     uint16_t* __restrict__ dv, int N, int n_kblocks, int bh_count, int n_qheads, int group,
-    long long kv_bstride, float scale_log2, float scale) {
+    long long kv_bstride, float scale_log2, float scale, DropParams drop) {
   constexpr int D = 256, KK = D / 16, CB = D / 32, DCH = D / 8;
   constexpr int TILE = kKv256BQ * D * 2;          // 16 KiB
   constexpr int KV_BYTES = kKv256BK * D * 2;      // 32 KiB
@@ -456,6 +467,7 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
   const int key_b0 = tc.qb * kKv256BK;
   const int key_w0 = key_b0 + kw * 32;
   const int my_key = key_w0 + l32;
+  const uint32_t drop_col = (uint32_t)my_key * kDropKeyMul;  // dropout: this lane's key term
 
   // resident K and V rows of the block (64 rows each, 2 rows per 1 KiB block)
   {
@@ -526,6 +538,7 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
     if (t + 1 < n_steps) load_stage(t + 1, stage ^ 1);
     const int it = qt_begin + t % nt;
     const int q0 = it * kKv256BQ;
+    const uint32_t drop_head = DROP ? drop_head_key(drop, (uint32_t)(qh0 + t / nt)) : 0u;
     // every query of the tile precedes every key of the wave: fully masked
     const bool skip = CAUSAL && (q0 + kKv256BQ - 1 < key_w0);
     if (!skip) {
@@ -578,7 +591,13 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
           const float lv = e < 4 ? l0[e] : l1[e - 4];
           const float dv_ = e < 4 ? d0[e] : d1[e - 4];
           const float p = fast_exp2(__builtin_fmaf(s[8 * hf + e], scale_log2, -lv));
-          x[e] = dk_wave ? p * (dp[8 * hf + e] - dv_) : p;
+          if constexpr (DROP) {
+            const uint32_t row = pcg_hash(drop_head ^ (uint32_t)(q0 + 16 * hf + 8 * g + e));
+            const float zs = pcg_hash(row ^ drop_col) >= drop.thr ? drop.scale : 0.f;
+            x[e] = dk_wave ? p * (dp[8 * hf + e] * zs - dv_) : p * zs;
+          } else {
+            x[e] = dk_wave ? p * (dp[8 * hf + e] - dv_) : p;
+          }
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) bk[4 * hf + e] = pack_bf16(x[2 * e], x[2 * e + 1]);
@@ -630,13 +649,14 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
 // is the whole row.
 constexpr int kDqBR = 128;
 
-template <int D, bool CAUSAL, int DH>
+template <int D, bool CAUSAL, int DH, bool DROP>
 __global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ o,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, float* __restrict__ lse2,
     float* __restrict__ delta, uint16_t* __restrict__ dq, int N, int n_qblocks, int bh_count,
-    int n_qheads, int group, long long kv_bstride, float scale_log2, float scale) {
+    int n_qheads, int group, long long kv_bstride, float scale_log2, float scale,
+    DropParams drop) {
   constexpr int KK = D / 16, CB = D / 32;
   constexpr int BC = D == 256 ? 32 : 64;   // keys per tile
   constexpr int KB = BC / 32;              // 32-key MFMA blocks per tile
@@ -668,6 +688,8 @@ __global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dq_kernel(
   const int q_block0 = tc.qb * kDqBR;
   const int q_wave0 = q_block0 + wave * 32;
   const int my_q = q_wave0 + l32;
+  const uint32_t drop_row =  // dropout: row key of this lane's query
+      DROP ? pcg_hash(drop_head_key(drop, (uint32_t)tc.bh) ^ (uint32_t)my_q) : 0u;
   const bool valid_q = my_q < N;
 
   // Q and dO fragments (B operands of S^T and dP^T): lane holds row my_q, columns
@@ -758,7 +780,16 @@ __global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dq_kernel(
         for (int i = 0; i < 8; ++i) {
           const float p0 = fast_exp2(__builtin_fmaf(s[kb][2 * i], scale_log2, -lse_q));
           const float p1 = fast_exp2(__builtin_fmaf(s[kb][2 * i + 1], scale_log2, -lse_q));
-          dsk[kb][i] = pack_bf16(p0 * (dp[kb][2 * i] - dlt), p1 * (dp[kb][2 * i + 1] - dlt));
+          float dp0 = dp[kb][2 * i], dp1 = dp[kb][2 * i + 1];
+          if constexpr (DROP) {
+            // keys j*BC + 32kb + 16(2i/8) + 8g + (2i%8) + 0, 1: dP scaled by Z / P(keep)
+            const int key = j * BC + 32 * kb + 16 * ((2 * i) / 8) + 8 * g + (2 * i) % 8;
+            const bool k0 = pcg_hash(drop_row ^ ((uint32_t)key * kDropKeyMul)) >= drop.thr;
+            const bool k1 = pcg_hash(drop_row ^ ((uint32_t)(key + 1) * kDropKeyMul)) >= drop.thr;
+            dp0 = k0 ? dp0 * drop.scale : 0.f;
+            dp1 = k1 ? dp1 * drop.scale : 0.f;
+          }
+          dsk[kb][i] = pack_bf16(p0 * (dp0 - dlt), p1 * (dp1 - dlt));
         }
       __builtin_amdgcn_s_setprio(1);  // as in the dK/dV kernel
       // dQ^T += K^T dS^T; MFMA u covers keys 16u .. 16u+15
@@ -810,42 +841,44 @@ hipError_t launch_pre_t(const BwdArgs& a) {
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 hipError_t launch_dkdv_t(const BwdArgs& a) {
   const int n_kblocks = (a.N + kKvBK - 1) / kKvBK;
   const long long grid = (long long)n_kblocks * a.B * a.Hkv;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kKvThreads), 0,
+  hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, CAUSAL, DROP>), dim3((unsigned)grid), dim3(kKvThreads), 0,
                      a.stream, static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                      static_cast<const uint16_t*>(a.dout), a.lse2, a.delta,
                      static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), a.N, n_kblocks,
-                     a.B * a.Hkv, a.H, a.H / a.Hkv, a.kv_bstride, a.scale_log2, a.scale);
+                     a.B * a.Hkv, a.H, a.H / a.Hkv, a.kv_bstride, a.scale_log2, a.scale,
+                     DropParams{a.drop_k0, a.drop_k1, a.drop_thr, a.drop_scale});
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, int DH>
+template <int D, bool CAUSAL, int DH, bool DROP>
 hipError_t launch_dq_one(const BwdArgs& a, unsigned grid, int n_qblocks) {
-  hipLaunchKernelGGL((fa2_bwd_dq_kernel<D, CAUSAL, DH>), dim3(grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL((fa2_bwd_dq_kernel<D, CAUSAL, DH, DROP>), dim3(grid), dim3(kThreads), 0,
                      a.stream, static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                      static_cast<const uint16_t*>(a.o), static_cast<const uint16_t*>(a.dout),
                      a.lse, a.lse2, a.delta, static_cast<uint16_t*>(a.dq), a.N, n_qblocks,
-                     a.B * a.H, a.H, a.H / a.Hkv, a.kv_bstride, a.scale_log2, a.scale);
+                     a.B * a.H, a.H, a.H / a.Hkv, a.kv_bstride, a.scale_log2, a.scale,
+                     DropParams{a.drop_k0, a.drop_k1, a.drop_thr, a.drop_scale});
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 hipError_t launch_dq_t(const BwdArgs& a) {
   const int n_qblocks = (a.N + kDqBR - 1) / kDqBR;
   const long long grid = (long long)n_qblocks * a.B * a.H;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if constexpr (D == 256) {
-    const hipError_t e = launch_dq_one<D, CAUSAL, 0>(a, (unsigned)grid, n_qblocks);
+    const hipError_t e = launch_dq_one<D, CAUSAL, 0, DROP>(a, (unsigned)grid, n_qblocks);
     if (e != hipSuccess) return e;
-    return launch_dq_one<D, CAUSAL, 1>(a, (unsigned)grid, n_qblocks);
+    return launch_dq_one<D, CAUSAL, 1, DROP>(a, (unsigned)grid, n_qblocks);
   } else {
-    return launch_dq_one<D, CAUSAL, -1>(a, (unsigned)grid, n_qblocks);
+    return launch_dq_one<D, CAUSAL, -1, DROP>(a, (unsigned)grid, n_qblocks);
   }
 }
 
@@ -856,30 +889,44 @@ hipError_t launch_bwd_pre(const BwdArgs& a) {
   return a.d == 64 ? launch_pre_t<64>(a) : launch_pre_t<128>(a);
 }
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool DROP>
 hipError_t launch_dkdv256_t(const BwdArgs& a) {
   const int n_kblocks = (a.N + kKv256BK - 1) / kKv256BK;
   const long long grid = (long long)n_kblocks * a.B * a.Hkv;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fa2_bwd_dkdv256_kernel<CAUSAL>), dim3((unsigned)grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL((fa2_bwd_dkdv256_kernel<CAUSAL, DROP>), dim3((unsigned)grid), dim3(kThreads), 0,
                      a.stream, static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                      static_cast<const uint16_t*>(a.dout), a.lse2, a.delta,
                      static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), a.N, n_kblocks,
-                     a.B * a.Hkv, a.H, a.H / a.Hkv, a.kv_bstride, a.scale_log2, a.scale);
+                     a.B * a.Hkv, a.H, a.H / a.Hkv, a.kv_bstride, a.scale_log2, a.scale,
+                     DropParams{a.drop_k0, a.drop_k1, a.drop_thr, a.drop_scale});
   return hipGetLastError();
 }
 
+template <bool DROP>
+hipError_t launch_bwd_dkdv_drop(const BwdArgs& a) {
+  if (a.d == 256)
+    return a.causal ? launch_dkdv256_t<true, DROP>(a) : launch_dkdv256_t<false, DROP>(a);
+  if (a.d == 64)
+    return a.causal ? launch_dkdv_t<64, true, DROP>(a) : launch_dkdv_t<64, false, DROP>(a);
+  return a.causal ? launch_dkdv_t<128, true, DROP>(a) : launch_dkdv_t<128, false, DROP>(a);
+}
+
 hipError_t launch_bwd_dkdv(const BwdArgs& a) {
-  if (a.d == 256) return a.causal ? launch_dkdv256_t<true>(a) : launch_dkdv256_t<false>(a);
-  if (a.d == 64) return a.causal ? launch_dkdv_t<64, true>(a) : launch_dkdv_t<64, false>(a);
-  return a.causal ? launch_dkdv_t<128, true>(a) : launch_dkdv_t<128, false>(a);
+  return a.dropout ? launch_bwd_dkdv_drop<true>(a) : launch_bwd_dkdv_drop<false>(a);
+}
+
+template <bool DROP>
+hipError_t launch_bwd_dq_drop(const BwdArgs& a) {
+  if (a.d == 256)
+    return a.causal ? launch_dq_t<256, true, DROP>(a) : launch_dq_t<256, false, DROP>(a);
+  if (a.d == 64) return a.causal ? launch_dq_t<64, true, DROP>(a) : launch_dq_t<64, false, DROP>(a);
+  return a.causal ? launch_dq_t<128, true, DROP>(a) : launch_dq_t<128, false, DROP>(a);
 }
 
 hipError_t launch_bwd_dq(const BwdArgs& a) {
-  if (a.d == 256) return a.causal ? launch_dq_t<256, true>(a) : launch_dq_t<256, false>(a);
-  if (a.d == 64) return a.causal ? launch_dq_t<64, true>(a) : launch_dq_t<64, false>(a);
-  return a.causal ? launch_dq_t<128, true>(a) : launch_dq_t<128, false>(a);
+  return a.dropout ? launch_bwd_dq_drop<true>(a) : launch_bwd_dq_drop<false>(a);
 }
 
 hipError_t launch_bwd(const BwdArgs& a) {

@@ -125,6 +125,26 @@ __device__ __forceinline__ int swz(int row) {
   return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
 
+// Dropout mask generator: the 32-bit PCG-based hash of Jarzynski and Olano ("Hash Functions for
+// GPU Rendering", JCGT 9(3), 2020), an LCG step followed by a random xorshift, a multiply and
+// a fixed xorshift. The mask of query head bh is keep(i, j) = hash(r_i ^ j*0x9E3779B9) >= t with
+// r_i = hash(a ^ i), a = hash(k0 ^ hash(k1 ^ bh)); k0, k1 come from the seed and offset, t from
+// the dropout probability (host side).
+__device__ __forceinline__ uint32_t pcg_hash(uint32_t x) {
+  const uint32_t state = x * 747796405u + 2891336453u;
+  const uint32_t word = ((state >> ((state >> 28u) + 4u)) ^ state) * 277803737u;
+  return (word >> 22u) ^ word;
+}
+constexpr uint32_t kDropKeyMul = 0x9E3779B9u;
+struct DropParams {
+  uint32_t k0, k1;  // seed and offset keys
+  uint32_t thr;     // keep iff hash >= thr
+  float scale;      // 1 / P(keep)
+};
+__device__ __forceinline__ uint32_t drop_head_key(const DropParams& dp, uint32_t bh) {
+  return pcg_hash(dp.k0 ^ pcg_hash(dp.k1 ^ bh));
+}
+
 // Workgroup id -> (block, batch*head) order. Workgroups are dealt to the 8 XCDs in turn
 // (id % 8), each XCD with its own L2; when the heads divide evenly, XCD x gets the heads
 // x, x+8, ... only.

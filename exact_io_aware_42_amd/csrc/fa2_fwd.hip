@@ -68,12 +68,12 @@ struct FwdShape {
   static_assert(LOADS >= 1 && DCH >= 8, "tile shape");
 };
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
     int N, int n_qblocks, int bh_count, int n_qheads, int group, long long kv_bstride,
-    float scale_log2) {
+    float scale_log2, DropParams drop) {
   using S = FwdShape<D>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[S::SMEM];
 
@@ -98,6 +98,9 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
   const int q_block0 = tc.qb * kFwdBR;
   const int q_wave0 = q_block0 + wave * 32;
   const int my_q = q_wave0 + l32;
+  // dropout: the row key of this lane's query (unused without dropout)
+  const uint32_t drop_row =
+      DROP ? pcg_hash(drop_head_key(drop, (uint32_t)tc.bh) ^ (uint32_t)my_q) : 0u;
 
   // ---- key tiles this workgroup visits, and the last one not fully masked for this wave
   constexpr int BC = S::BC;
@@ -218,7 +221,12 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
     return max_xor32(m) * scale_log2;
   };
   // p = exp2(s*c - m) -> packed bf16 (the PV B operand); partial sum of p
-  auto probs = [&](const f32x16_t* s, uint32_t (*pk)[8]) {
+  // dropout: p of key j survives iff hash(row key ^ j * kDropKeyMul) >= threshold (the sums
+  // of p for the normaliser and the LSE stay those of the undropped p)
+  auto drop_keep = [&](int key) {
+    return pcg_hash(drop_row ^ ((uint32_t)key * kDropKeyMul)) >= drop.thr;
+  };
+  auto probs = [&](const f32x16_t* s, uint32_t (*pk)[8], int j) {
     const float neg_m = -m_run;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -228,7 +236,13 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
         const float p0 = fast_exp2(__builtin_fmaf(s[kb][2 * i], scale_log2, neg_m));
         const float p1 = fast_exp2(__builtin_fmaf(s[kb][2 * i + 1], scale_log2, neg_m));
         acc[(i & 1) * 2 + kb] += p0 + p1;
-        pk[kb][i] = pack_bf16(p0, p1);
+        if constexpr (DROP) {
+          // registers 2i, 2i+1 of block kb hold keys j*BC + 32kb + 16(2i/8) + 8g + (2i%8) + 0, 1
+          const int key = j * BC + 32 * kb + 16 * ((2 * i) / 8) + 8 * g + (2 * i) % 8;
+          pk[kb][i] = pack_bf16(drop_keep(key) ? p0 : 0.f, drop_keep(key + 1) ? p1 : 0.f);
+        } else {
+          pk[kb][i] = pack_bf16(p0, p1);
+        }
       }
     const float tile_sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
     l_f32 += tile_sum;
@@ -301,13 +315,13 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
         maybe_rescale(m_tile);
       }
       uint32_t pk[S::KB][8];
-      const float tile_sum = probs(s, pk);
+      const float tile_sum = probs(s, pk, j);
       // raised priority while this wave issues its PV MFMAs: the other wave on the SIMD then
       // tends to run its softmax VALU work in between (measured +2-6%)
       __builtin_amdgcn_s_setprio(1);
       pv(slot, pk);
       __builtin_amdgcn_s_setprio(0);
-      if (masked) bf16_correction(pk, tile_sum);
+      if (!DROP && masked) bf16_correction(pk, tile_sum);
     }
     wait_vmem();
     __syncthreads();
@@ -321,7 +335,7 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
   const float l_tot = sum_xor32(l_f32);
   const float l_o = sum_xor32(l_f32 + l_corr);
   if (my_q < N) {
-    const float inv = fast_rcp(l_o);
+    const float inv = DROP ? fast_rcp(l_o) * drop.scale : fast_rcp(l_o);
     uint16_t* orow = o + head_off + (size_t)my_q * D;
 #pragma unroll
     for (int cb = 0; cb < S::CB; ++cb)
@@ -336,25 +350,33 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
   }
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool DROP>
 hipError_t launch_fwd_t(const FwdArgs& a) {
   const int n_qblocks = (a.N + kFwdBR - 1) / kFwdBR;
   const long long grid = (long long)n_qblocks * a.B * a.H;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fa2_fwd_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(kFwdThreads), 0,
-                     a.stream, static_cast<const uint16_t*>(a.q),
+  const DropParams drop{a.drop_k0, a.drop_k1, a.drop_thr, a.drop_scale};
+  hipLaunchKernelGGL((fa2_fwd_kernel<D, CAUSAL, DROP>), dim3((unsigned)grid), dim3(kFwdThreads),
+                     0, a.stream, static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                      static_cast<uint16_t*>(a.o), a.lse, a.N, n_qblocks, a.B * a.H, a.H,
-                     a.H / a.Hkv, a.kv_bstride, a.scale_log2);
+                     a.H / a.Hkv, a.kv_bstride, a.scale_log2, drop);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_fwd_d(const FwdArgs& a) {
+  if (a.dropout)
+    return a.causal ? launch_fwd_t<D, true, true>(a) : launch_fwd_t<D, false, true>(a);
+  return a.causal ? launch_fwd_t<D, true, false>(a) : launch_fwd_t<D, false, false>(a);
 }
 
 }  // namespace
 
 hipError_t launch_fwd(const FwdArgs& a) {
-  if (a.d == 64) return a.causal ? launch_fwd_t<64, true>(a) : launch_fwd_t<64, false>(a);
-  if (a.d == 256) return a.causal ? launch_fwd_t<256, true>(a) : launch_fwd_t<256, false>(a);
-  return a.causal ? launch_fwd_t<128, true>(a) : launch_fwd_t<128, false>(a);
+  if (a.d == 64) return launch_fwd_d<64>(a);
+  if (a.d == 256) return launch_fwd_d<256>(a);
+  return launch_fwd_d<128>(a);
 }
 
 }  // namespace fa2

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdint.h>
 
 namespace fa2 {
 
@@ -21,6 +22,11 @@ struct FwdArgs {
   long long kv_bstride;
   bool causal;
   float scale_log2;  // softmax_scale * log2(e)
+  // dropout on P (dropout false: none): keep iff hash >= drop_thr, kept values scaled by
+  // drop_scale; drop_k0/drop_k1 are the keys derived from the seed and offset
+  bool dropout = false;
+  uint32_t drop_k0 = 0, drop_k1 = 0, drop_thr = 0;
+  float drop_scale = 1.f;
   hipStream_t stream;
 };
 
@@ -42,6 +48,9 @@ struct BwdArgs {
   bool causal;
   float scale;       // softmax_scale
   float scale_log2;  // softmax_scale * log2(e)
+  bool dropout = false;  // as in FwdArgs
+  uint32_t drop_k0 = 0, drop_k1 = 0, drop_thr = 0;
+  float drop_scale = 1.f;
   hipStream_t stream;
 };
 

@@ -24,8 +24,8 @@ FA2_ERR_UNSUPPORTED = 2
 FA2_ERR_HIP = 3
 
 EXPORTED = ("fa2_fwd", "fa2_bwd", "fa2_bwd_workspace_bytes", "fa2_bwd_preprocess",
-            "fa2_bwd_dkdv", "fa2_bwd_dq", "fa2_fwd_gqa", "fa2_bwd_gqa", "fa2_status_string",
-            "fa2_last_hip_error")
+            "fa2_bwd_dkdv", "fa2_bwd_dq", "fa2_fwd_gqa", "fa2_bwd_gqa", "fa2_fwd_dropout",
+            "fa2_bwd_dropout", "fa2_status_string", "fa2_last_hip_error")
 
 _lib = None
 _lock = threading.Lock()
@@ -46,7 +46,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                            "`python -m exact_io_aware_42_amd.build` (no fallback exists)")
         lib = ctypes.CDLL(path)
         vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
-        ll = ctypes.c_longlong
+        ll, ull = ctypes.c_longlong, ctypes.c_ulonglong
         lib.fa2_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
         lib.fa2_fwd.restype = i
         lib.fa2_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
@@ -63,6 +63,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.fa2_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
                                     i, i, i, i, i, ll, i, f, vp]
         lib.fa2_bwd_gqa.restype = i
+        lib.fa2_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, ll, i, f, f, ull, ull,
+                                        vp]
+        lib.fa2_fwd_dropout.restype = i
+        lib.fa2_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                        i, i, i, i, i, ll, i, f, f, ull, ull, vp]
+        lib.fa2_bwd_dropout.restype = i
         lib.fa2_bwd_workspace_bytes.argtypes = [i, i, i, i]
         lib.fa2_bwd_workspace_bytes.restype = sz
         lib.fa2_status_string.argtypes = [i]
@@ -104,6 +110,10 @@ def default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
 
 
+def _u64(x: int) -> int:
+    return int(x) & 0xFFFFFFFFFFFFFFFF
+
+
 def _kv_layout(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
     """(Hkv, batch stride in elements) of k and v: [B, Hkv, N, d] with heads, rows and columns
     contiguous, the same strides for both (separate tensors, or views of a packed
@@ -131,10 +141,12 @@ def _kv_layout(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
 
 def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
         scale: float | None = None, out: torch.Tensor | None = None,
-        lse: torch.Tensor | None = None):
+        lse: torch.Tensor | None = None, dropout_p: float = 0.0, seed: int = 0,
+        offset: int = 0):
     """Attention forward on bf16 [B, H, N, d] tensors. Returns (o bf16, lse fp32 [B, H, N]).
     k and v may have fewer heads (Hkv dividing H: grouped heads) and may be views of one packed
-    [B, 2, Hkv, N, d] tensor."""
+    [B, 2, Hkv, N, d] tensor. dropout_p > 0 drops probabilities with the counter-based mask of
+    (seed, offset) declared in include/fa2.h; bwd must get the same three values."""
     lib = load_library()
     if q.dim() != 4:
         raise ValueError("q must be [B, H, N, d]")
@@ -149,7 +161,11 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
     _check_tensor(out, "out", (B, H, N, d), device=dev)
     _check_tensor(lse, "lse", (B, H, N), dtype=torch.float32, device=dev)
     s = default_scale(d) if scale is None else float(scale)
-    if Hkv == H and kvs == H * N * d:
+    if dropout_p:
+        st = lib.fa2_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                 lse.data_ptr(), B, H, Hkv, N, d, kvs, int(bool(causal)), s,
+                                 float(dropout_p), _u64(seed), _u64(offset), _stream_ptr(dev))
+    elif Hkv == H and kvs == H * N * d:
         st = lib.fa2_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                          lse.data_ptr(), B, H, N, d, int(bool(causal)), s, _stream_ptr(dev))
     else:
@@ -173,9 +189,10 @@ def bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
 
 
 def bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None,
-        dq=None, dk=None, dv=None, workspace=None):
+        dq=None, dk=None, dv=None, workspace=None, dropout_p: float = 0.0, seed: int = 0,
+        offset: int = 0):
     """Attention backward. Returns (dq, dk, dv) bf16; dk, dv have k's and v's layout (grouped
-    and packed K/V as in fwd)."""
+    and packed K/V as in fwd); dropout arguments as given to fwd."""
     lib = load_library()
     B, H, N, d = q.shape
     dev = q.device
@@ -200,7 +217,10 @@ def bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None,
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
             lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
             workspace.numel() * workspace.element_size())
-    if Hkv == H and kvs == H * N * d:
+    if dropout_p:
+        st = lib.fa2_bwd_dropout(*ptrs, B, H, Hkv, N, d, kvs, int(bool(causal)), s,
+                                 float(dropout_p), _u64(seed), _u64(offset), _stream_ptr(dev))
+    elif Hkv == H and kvs == H * N * d:
         st = lib.fa2_bwd(*ptrs, B, H, N, d, int(bool(causal)), s, _stream_ptr(dev))
     else:
         st = lib.fa2_bwd_gqa(*ptrs, B, H, Hkv, N, d, kvs, int(bool(causal)), s,

@@ -131,6 +131,33 @@ fa2_status fa2_bwd_gqa(const void* q, const void* k, const void* v, const void* 
                        int d, long long kv_batch_stride, int causal, float softmax_scale,
                        hipStream_t stream);
 
+/* Dropout on the attention probabilities (page "Flash Attention v2", "Installation and Usage":
+ * flash_attn_func takes dropout_p). Reading: each P[i, j] is kept with probability 1 - p and
+ * then scaled by 1 / P(keep), or zeroed, before it multiplies V; the saved lse is that of the
+ * undropped softmax. The backward takes the same (dropout_p, seed, offset) and recomputes the
+ * same mask:
+ *   dV = (P*Z*s)^T dO,  dS = P * (Z*s*(dO V^T) - D),  D_i = sum_c dO_ic O_ic.
+ * The mask is a counter-based function of (seed, offset, query head bh = b*H + h, i, j):
+ *   h(x)  = the 32-bit PCG-based hash of Jarzynski and Olano (JCGT 9(3), 2020):
+ *           s = x*747796405 + 2891336453; w = ((s >> ((s >> 28) + 4)) ^ s) * 277803737;
+ *           h = (w >> 22) ^ w                                   (uint32, wrapping)
+ *   k0 = h(seed_lo ^ h(seed_hi)), k1 = h(offset_lo ^ h(offset_hi)), a = h(k0 ^ h(k1 ^ bh))
+ *   keep(i, j) = h(h(a ^ i) ^ j*0x9E3779B9) >= t,  t = floor(p * 2^32),  s = 1/(1 - t/2^32)
+ * 0 <= dropout_p < 1 (else FA2_ERR_INVALID_ARGUMENT); dropout_p = 0 runs the kernels without
+ * dropout (results identical to fa2_fwd_gqa / fa2_bwd_gqa). K/V layout as in the _gqa calls. */
+fa2_status fa2_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int Hkv, int N, int d, long long kv_batch_stride,
+                           int causal, float softmax_scale, float dropout_p,
+                           unsigned long long seed, unsigned long long offset,
+                           hipStream_t stream);
+
+fa2_status fa2_bwd_dropout(const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                           void* workspace, size_t workspace_bytes, int B, int H, int Hkv,
+                           int N, int d, long long kv_batch_stride, int causal,
+                           float softmax_scale, float dropout_p, unsigned long long seed,
+                           unsigned long long offset, hipStream_t stream);
+
 /* Static, human-readable name of a status code. */
 const char* fa2_status_string(fa2_status s);
 

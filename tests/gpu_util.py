@@ -47,11 +47,13 @@ def assert_fwd_close(o_gpu: np.ndarray, lse_gpu: np.ndarray, o_ref: np.ndarray,
 
 
 def assert_fwd_within_rounding_bound(o_gpu, lse_gpu, o_ref, o_abs_ref, lse_ref, what=""):
-    """Bound for inputs outside N(0, 1) (stress cases), derived from the arithmetic: with bf16
+    """Bound for inputs outside N(0, 1) (stress cases) and for dropout (kept weights scaled by
+    1/P(keep)), derived from the arithmetic: with bf16
     p (unit roundoff u = 2^-8) normalised by the sum of the same rounded p, the weights are
     w_k (1 + e_k) / (1 + sum_j w_j e_j) with |e_k| <= u, so |O' - O| <= 2u sum_k w_k |v_k| (to
     first order); the bf16 output adds at most u |O|. sum_k w_k |v_k| is the oracle's output
-    for |V| (o_abs_ref). LSE keeps its 1e-3 bound."""
+    for |V| (o_abs_ref; with dropout the w_k include the mask and the keep scale). LSE keeps
+    its 1e-3 bound."""
     u = 2.0 ** -8
     assert np.isfinite(o_gpu).all() and np.isfinite(lse_gpu).all(), f"{what}: non-finite output"
     bound = 2 * u * o_abs_ref * 1.01 + u * np.abs(o_ref) + 1e-6

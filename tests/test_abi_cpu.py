@@ -215,3 +215,26 @@ def test_grouped_kv_validation():
     # empty problems stay no-ops
     assert lib.fa2_fwd_gqa(None, None, None, None, None, 0, 8, 2, N, d, 2 * N * d, 1, 0.125,
                            None) == ops.FA2_OK
+
+
+def test_dropout_validation():
+    """fa2_fwd_dropout / fa2_bwd_dropout reject a probability outside [0, 1) (NaN included)
+    before any HIP call; the pointers are fake and every case has an invalid parameter."""
+    lib = _lib()
+    N, d = 16, 64
+    ws = lib.fa2_bwd_workspace_bytes(2, 8, N, d)
+    for p in (1.0, 1.5, -0.1, float("nan"), float("inf")):
+        assert lib.fa2_fwd_dropout(P, P, P, P, P, 2, 8, 2, N, d, 2 * N * d, 1, 0.125, p, 1, 2,
+                                   None) == ops.FA2_ERR_INVALID_ARGUMENT, p
+        assert lib.fa2_bwd_dropout(*([P] * 10), ws, 2, 8, 2, N, d, 2 * N * d, 0, 0.125, p, 1,
+                                   2, None) == ops.FA2_ERR_INVALID_ARGUMENT, p
+    # a valid probability does not excuse other invalid arguments
+    assert lib.fa2_fwd_dropout(P, P, P, P, P, 2, 8, 3, N, d, 3 * N * d, 1, 0.125, 0.1, 1, 2,
+                               None) == ops.FA2_ERR_INVALID_ARGUMENT
+    assert lib.fa2_fwd_dropout(None, P, P, P, P, 2, 8, 2, N, d, 2 * N * d, 1, 0.125, 0.1, 1, 2,
+                               None) == ops.FA2_ERR_INVALID_ARGUMENT
+    assert lib.fa2_bwd_dropout(*([P] * 10), ws - 1, 2, 8, 2, N, d, 2 * N * d, 0, 0.125, 0.1, 1,
+                               2, None) == ops.FA2_ERR_INVALID_ARGUMENT
+    # empty problems stay no-ops
+    assert lib.fa2_fwd_dropout(None, None, None, None, None, 2, 8, 2, 0, d, 0, 1, 0.125, 0.5, 1,
+                               2, None) == ops.FA2_OK

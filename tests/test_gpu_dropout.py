@@ -1,0 +1,202 @@
+"""Dropout on the attention probabilities through the C ABI (fa2_fwd_dropout, fa2_bwd_dropout)
+against the CPU float64 oracle, which draws the same counter-based mask from its own
+implementation of the published hash. The mask is integer work and is compared bit for bit
+(read out of the kernels' outputs with inputs that make each output element one probability);
+The gradients are compared with the bound of the other parity tests; O against the bf16
+rounding bound derived from the arithmetic (kept probabilities are scaled by 1/P(keep), so O
+can exceed the range the fixed 1e-2 bound was set for), LSE within 1e-3.
+
+The probability crosses the ABI as float32, so every p here is a float32 value and the oracle
+gets that same value.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+import torch
+
+from exact_io_aware_42_amd.inputs import bf16_bits_to_f64, default_scale, normal_bf16
+from oracle import attention_backward_dropout, attention_forward_dropout, keep_mask
+
+from gpu_util import assert_fwd_within_rounding_bound, assert_grad_close, bf16_to_f64, bits_of, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _fa2():
+    import exact_io_aware_42_amd as fa2
+    return fa2
+
+
+def f32(p: float) -> float:
+    return float(np.float32(p))
+
+
+def _oracle(bq, bk, bv, bdo, causal, p, seed, offset):
+    """Oracle (O, LSE, O for |V|, dQ, dK, dV); grouped K/V heads are repeated for their query heads and
+    their gradients summed over the group. The mask is indexed by the query head."""
+    B, H, N, d = bq.shape
+    G = H // bk.shape[1]
+    q64, k64, v64, do64 = (bf16_bits_to_f64(b) for b in (bq, bk, bv, bdo))
+    kr, vr = np.repeat(k64, G, axis=1), np.repeat(v64, G, axis=1)
+    scale = default_scale(d)
+    o, lse = attention_forward_dropout(q64, kr, vr, causal=causal, scale=scale, p=p, seed=seed,
+                                       offset=offset)
+    dq, dk, dv = attention_backward_dropout(q64, kr, vr, do64, causal=causal, scale=scale, p=p,
+                                            seed=seed, offset=offset)
+    o_abs, _ = attention_forward_dropout(q64, kr, np.abs(vr), causal=causal, scale=scale, p=p,
+                                         seed=seed, offset=offset)
+    Hkv = H // G
+    return o, lse, o_abs, dq, dk.reshape(B, Hkv, G, N, d).sum(2), dv.reshape(B, Hkv, G, N, d).sum(2)
+
+
+CASES = [((1, 1, 1, 1, 64), True, 0.25), ((2, 3, 3, 77, 64), False, 0.1),
+         ((2, 3, 3, 77, 64), True, 0.5), ((1, 2, 2, 200, 128), True, 0.3),
+         ((1, 2, 2, 129, 128), False, 0.3), ((1, 1, 1, 383, 64), True, 0.2),
+         ((1, 2, 2, 45, 256), True, 0.3), ((2, 1, 1, 161, 256), False, 0.15),
+         ((2, 8, 2, 150, 64), True, 0.3), ((1, 4, 2, 96, 256), False, 0.2),
+         ((1, 1, 1, 1000, 128), True, 0.1)]
+
+
+@pytest.mark.parametrize("dims,causal,p", CASES,
+                         ids=[f"{b}x{h}/{hk}x{n}x{d}-{'c' if c else 'f'}-p{p}"
+                              for (b, h, hk, n, d), c, p in CASES])
+def test_dropout_matches_oracle(dims, causal, p):
+    fa2 = _fa2()
+    B, H, Hkv, N, d = dims
+    p = f32(p)
+    seed, offset = 0x1234_5678_9ABC + N, 7 * d + H
+    rs = 9600 + H + N + d
+    bq, bdo = normal_bf16((B, H, N, d), rs), normal_bf16((B, H, N, d), rs + 3)
+    bk, bv = normal_bf16((B, Hkv, N, d), rs + 1), normal_bf16((B, Hkv, N, d), rs + 2)
+    print(f"case {dims} causal={causal} p={p}", flush=True)
+    q, k, v, do = (to_dev(b) for b in (bq, bk, bv, bdo))
+    o, lse = fa2.fwd(q, k, v, causal=causal, dropout_p=p, seed=seed, offset=offset)
+    dq, dk, dv = fa2.bwd(q, k, v, o, do, lse, causal=causal, dropout_p=p, seed=seed,
+                         offset=offset)
+    torch.cuda.synchronize()
+    o_ref, lse_ref, o_abs, dq_ref, dk_ref, dv_ref = _oracle(bq, bk, bv, bdo, causal, p, seed,
+                                                             offset)
+    assert_fwd_within_rounding_bound(bf16_to_f64(o), lse.cpu().double().numpy(), o_ref, o_abs,
+                                     lse_ref, str(dims))
+    for name, got, want in (("dq", dq, dq_ref), ("dk", dk, dk_ref), ("dv", dv, dv_ref)):
+        assert_grad_close(bf16_to_f64(got), want, f"{dims} {name}")
+
+
+def _one_hot_block(n_rows, d, start):
+    """[n_rows, d] float with row start + c equal to e_c for c < d (rows outside the block 0)."""
+    x = np.zeros((n_rows, d), dtype=np.float32)
+    for c in range(d):
+        if 0 <= start + c < n_rows:
+            x[start + c, c] = 1.0
+    return x
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_mask_bits_equal_the_oracle_mask(d, causal):
+    """With Q = 0 every probability of row i is 1/(number of visible keys), so with V holding
+    the unit vectors e_0 .. e_{d-1} in the key rows j0 .. j0+d-1, O[i, c] is nonzero exactly
+    when key j0+c is visible and kept. In the backward, dO holding unit vectors in query rows
+    i0 .. i0+d-1 makes dV[j, c] nonzero exactly when query i0+c keeps key j. Both must equal
+    the oracle's mask bit for bit, over several heads, several key tiles and a ragged tail."""
+    fa2 = _fa2()
+    B, H, N = 2, 3, 300
+    p, seed, offset = f32(0.4), 0xDEADBEEF_0BADF00D, 12345
+    dev = torch.device("cuda:0")
+    q = torch.zeros((B, H, N, d), dtype=torch.bfloat16, device=dev)
+    k = torch.from_numpy(np.random.default_rng(9700).standard_normal((B, H, N, d))
+                         .astype(np.float32)).to(dev).bfloat16()
+    vis = np.tril(np.ones((N, N), dtype=bool)) if causal else np.ones((N, N), dtype=bool)
+    for start in sorted({0, 128, N - d} if d < N else {0}):
+        vb = torch.from_numpy(_one_hot_block(N, d, start)).to(dev).bfloat16()
+        v = vb.expand(B, H, N, d).contiguous()
+        o, lse = fa2.fwd(q, k, v, causal=causal, dropout_p=p, seed=seed, offset=offset)
+        do = v.clone()  # unit vectors in query rows start .. start+d-1
+        _, _, dv = fa2.bwd(q, k, v, o, do, lse, causal=causal, dropout_p=p, seed=seed,
+                           offset=offset)
+        torch.cuda.synchronize()
+        o_nz = (o.float() != 0).cpu().numpy()
+        dv_nz = (dv.float() != 0).cpu().numpy()
+        cols = [c for c in range(d) if start + c < N]
+        for b in range(B):
+            for h in range(H):
+                z = keep_mask(seed, offset, b * H + h, np.arange(N), N, p) & vis
+                want_o = z[:, start:start + len(cols)]
+                assert np.array_equal(o_nz[b, h][:, cols], want_o), (b, h, start)
+                want_dv = z[start:start + len(cols), :].T
+                assert np.array_equal(dv_nz[b, h][:, cols], want_dv), (b, h, start)
+
+
+def test_p_zero_equals_plain_path_bitwise():
+    """fa2_fwd_dropout / fa2_bwd_dropout with p = 0 give exactly the bits of the calls
+    without dropout, whatever the seed."""
+    fa2 = _fa2()
+    from exact_io_aware_42_amd import ops
+    lib = ops.load_library()
+    shape = (2, 2, 190, 128)
+    q, k, v, do = (to_dev(normal_bf16(shape, 9750 + t)) for t in range(4))
+    B, H, N, d = shape
+    for causal in (False, True):
+        o, lse = fa2.fwd(q, k, v, causal=causal)
+        dq, dk, dv = fa2.bwd(q, k, v, o, do, lse, causal=causal)
+        o2, lse2 = torch.empty_like(o), torch.empty_like(lse)
+        st = lib.fa2_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o2.data_ptr(),
+                                 lse2.data_ptr(), B, H, H, N, d, H * N * d, int(causal),
+                                 default_scale(d), 0.0, 99, 7, None)
+        assert st == 0
+        g2 = [torch.empty_like(q) for _ in range(3)]
+        ws = torch.empty(fa2.bwd_workspace_bytes(*shape), dtype=torch.uint8, device=q.device)
+        st = lib.fa2_bwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                 do.data_ptr(), lse.data_ptr(), *(g.data_ptr() for g in g2),
+                                 ws.data_ptr(), ws.numel(), B, H, H, N, d, H * N * d,
+                                 int(causal), default_scale(d), 0.0, 99, 7, None)
+        assert st == 0
+        torch.cuda.synchronize()
+        assert np.array_equal(bits_of(o), bits_of(o2))
+        assert torch.equal(lse, lse2)
+        for a, b in zip((dq, dk, dv), g2):
+            assert np.array_equal(bits_of(a), bits_of(b))
+
+
+def test_seed_and_offset_select_the_mask():
+    """The same (seed, offset) gives identical bits; changing either changes the output; and
+    the dropped forward averaged over offsets approaches the undropped one (the 1/P(keep)
+    scale makes each output unbiased)."""
+    fa2 = _fa2()
+    shape = (1, 2, 256, 64)
+    q, k, v = (to_dev(normal_bf16(shape, 9800 + t)) for t in range(3))
+    p = f32(0.3)
+    a, _ = fa2.fwd(q, k, v, dropout_p=p, seed=5, offset=0)
+    b, _ = fa2.fwd(q, k, v, dropout_p=p, seed=5, offset=0)
+    c, _ = fa2.fwd(q, k, v, dropout_p=p, seed=6, offset=0)
+    e, _ = fa2.fwd(q, k, v, dropout_p=p, seed=5, offset=1)
+    ref, _ = fa2.fwd(q, k, v)
+    acc = torch.zeros(shape, dtype=torch.float64, device=q.device)
+    n = 256
+    for off in range(n):
+        acc += fa2.fwd(q, k, v, dropout_p=p, seed=11, offset=off)[0].double()
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert not torch.equal(a, c) and not torch.equal(a, e)
+    err = (acc / n - ref.double()).abs().mean().item()
+    one = (a.double() - ref.double()).abs().mean().item()
+    assert err < one / 8, (err, one)  # spread shrinks like 1/sqrt(n) = 1/16
+
+
+def test_autograd_with_dropout():
+    """flash_attn_func with dropout_p passes the same mask to its backward: gradients equal
+    the direct fwd/bwd calls bit for bit."""
+    fa2 = _fa2()
+    shape = (1, 2, 140, 128)
+    q, k, v, do = (to_dev(normal_bf16(shape, 9900 + t)) for t in range(4))
+    p = f32(0.2)
+    qa, ka, va = (t.clone().requires_grad_() for t in (q, k, v))
+    out = fa2.flash_attn_func(qa, ka, va, dropout_p=p, causal=True, seed=3, offset=4)
+    out.backward(do)
+    o, lse = fa2.fwd(q, k, v, causal=True, dropout_p=p, seed=3, offset=4)
+    dq, dk, dv = fa2.bwd(q, k, v, o, do, lse, causal=True, dropout_p=p, seed=3, offset=4)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), o.view(torch.int16))
+    for a, b in ((qa.grad, dq), (ka.grad, dk), (va.grad, dv)):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
