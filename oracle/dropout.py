@@ -28,8 +28,13 @@ Computer Graphics Techniques 9(3), 2020):
     head key   a = h(s0 ^ h(o0 ^ bh)),  s0 = h(seed_lo ^ h(seed_hi)), o0 = h(off_lo ^ h(off_hi))
                (bh = b * H + h, the query head)
     row key    r_i = h(a ^ i)
-    element    u_ij = h(r_i ^ (j * 0x9E3779B9 mod 2^32))
-    keep       Z[i, j] = u_ij >= t,  t = floor(p * 2^32),  P(keep) = 1 - t / 2^32
+    pair word  w_im = h(r_i ^ (m * 0x9E3779B9 mod 2^32))   for the key pair m = floor(j / 2)
+    uniform    u_ij = low 16 bits of w_im for even j, high 16 bits for odd j
+    keep       Z[i, j] = u_ij >= t,  t = floor(p * 2^16),  P(keep) = 1 - t / 2^16
+
+One hash word serves two neighbouring keys (16 bits each), which halves the hashing; the keep
+probability is p rounded down to a multiple of 2^-16, and the 1/P(keep) scale uses that
+probability, so every output stays unbiased.
 
 Pinned by tests: p = 0 reduces to plain attention exactly; scalar-loop brute force; finite
 differences with the mask held fixed; keep rates and independence statistics of the mask;
@@ -57,15 +62,15 @@ def pcg_hash(x) -> np.ndarray:
 
 
 def dropout_threshold(p: float) -> int:
-    """t = floor(p * 2^32) for 0 <= p < 1."""
+    """t = floor(p * 2^16) for 0 <= p < 1."""
     if not (0.0 <= p < 1.0):
         raise ValueError("dropout probability must be in [0, 1)")
-    return min(int(np.floor(p * 4294967296.0)), 0xFFFFFFFF)
+    return min(int(np.floor(p * 65536.0)), 0xFFFF)
 
 
 def keep_scale(p: float) -> float:
-    """1 / P(keep) = 1 / (1 - t / 2^32)."""
-    return 1.0 / (1.0 - dropout_threshold(p) / 4294967296.0)
+    """1 / P(keep) = 1 / (1 - t / 2^16)."""
+    return 1.0 / (1.0 - dropout_threshold(p) / 65536.0)
 
 
 def _split(x: int):
@@ -86,8 +91,10 @@ def keep_mask(seed: int, offset: int, bh: int, rows, n_keys: int, p: float) -> n
     a = np.uint64(head_key(seed, offset, bh))
     rows = np.asarray(rows, dtype=np.uint64)
     r = pcg_hash(a ^ rows).astype(np.uint64)                              # [R]
-    jm = (np.arange(n_keys, dtype=np.uint64) * np.uint64(0x9E3779B9)) & _M32  # [N]
-    u = pcg_hash(r[:, None] ^ jm[None, :])
+    j = np.arange(n_keys, dtype=np.uint64)
+    mm = ((j >> np.uint64(1)) * np.uint64(0x9E3779B9)) & _M32             # pair term [N]
+    w = pcg_hash(r[:, None] ^ mm[None, :])                                # [R, N]
+    u = np.where((j & np.uint64(1)) == 0, w & np.uint32(0xFFFF), w >> np.uint32(16))
     return u >= np.uint32(dropout_threshold(p))
 
 

@@ -109,6 +109,32 @@ def test_hash_output_uniform():
         assert chi2 <= 255 + 6 * math.sqrt(2 * 255)
 
 
+def test_pair_halves_uniform_and_independent():
+    """The two 16-bit halves of one hash word decide two neighbouring keys: over 2^20 words the
+    pairs (top 4 bits of the low half, top 4 bits of the high half) fill 256 buckets evenly, so
+    the halves are uniform and independent of each other."""
+    x = pcg_hash(np.arange(1 << 20, dtype=np.uint32) * np.uint32(7919))
+    lo, hi = (x & np.uint32(0xFFFF)) >> np.uint32(12), x >> np.uint32(28)
+    counts = np.bincount((lo * 16 + hi).astype(np.int64), minlength=256)
+    expected = x.size / 256
+    chi2 = float(np.sum((counts - expected) ** 2 / expected))
+    assert chi2 <= 255 + 6 * math.sqrt(2 * 255)
+
+
+@pytest.mark.parametrize("p", [0.1, 0.37, 0.999])
+def test_keep_probability_is_p_rounded_to_2_pow_minus_16(p):
+    """P(keep) = 1 - floor(p * 2^16) / 2^16 (p rounded down to the 16-bit grid): the empirical
+    keep rate of even and of odd keys each lands within 6 standard errors of it, and the keep
+    scale is its reciprocal."""
+    t = math.floor(p * 65536)
+    keep = 1.0 - t / 65536
+    assert keep_scale(p) == pytest.approx(1.0 / keep, rel=1e-15)
+    z = keep_mask(99, 3, 1, np.arange(512), 2048, p)
+    sd = math.sqrt(keep * (1 - keep) / (z.size / 2))
+    for part in (z[:, 0::2], z[:, 1::2]):
+        assert abs(part.mean() - keep) <= 6 * sd + 1e-12
+
+
 def test_average_over_seeds_is_unbiased():
     """E[O_dropout] = O: averaging over 400 seeds lands within 5 standard errors."""
     B, H, N, d, p = 1, 1, 6, 4, 0.5
