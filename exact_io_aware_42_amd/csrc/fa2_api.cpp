@@ -2,6 +2,7 @@
 // launches on the caller's stream. No device memory is allocated here.
 #include "fa2.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <initializer_list>
@@ -66,9 +67,9 @@ struct DropHost {
 fa2_status drop_params(float p, unsigned long long seed, unsigned long long offset,
                        DropHost* out) {
   if (!(p >= 0.0f && p < 1.0f)) return FA2_ERR_INVALID_ARGUMENT;
-  const double t = std::floor((double)p * 4294967296.0);
-  out->thr = t > 4294967295.0 ? 0xFFFFFFFFu : (uint32_t)t;
-  out->scale = (float)(1.0 / (1.0 - (double)out->thr / 4294967296.0));
+  const double t = std::min(std::floor((double)p * 65536.0), 65535.0);  // 16-bit uniforms
+  out->thr = (uint32_t)t << 16;
+  out->scale = (float)(65536.0 / (65536.0 - t));
   out->k0 = host_pcg_hash((uint32_t)seed ^ host_pcg_hash((uint32_t)(seed >> 32)));
   out->k1 = host_pcg_hash((uint32_t)offset ^ host_pcg_hash((uint32_t)(offset >> 32)));
   return FA2_OK;

@@ -135,6 +135,51 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_pre_kernel(const uint16_t* _
 }
 
 // ---------------------------------------------------------------------------------------
+// Dropout in the dK/dV kernels (lane = key, registers = queries). The row keys of a query tile
+// go to LDS with the tile (one hash per query, by one wave); the two lanes of a key pair (lanes
+// 2m', 2m'+1 hold keys 2m, 2m+1) need the same word per query, so each hashes half of its 16
+// queries and takes the other half from its neighbour by DPP, then picks its 16-bit half.
+
+// Row key of query row0 + lane of query head qh, stored at rk[lane].
+__device__ __forceinline__ void store_row_key(unsigned char* rk, const DropParams& drop, int qh,
+                                              int row0, int lane) {
+  const uint32_t a = drop_head_key(drop, (uint32_t)qh);
+  reinterpret_cast<uint32_t*>(rk)[lane] = pcg_hash(a ^ (uint32_t)(row0 + lane));
+}
+
+struct DropLanes {
+  uint32_t pair;          // (my_key / 2) * kDropKeyMul
+  int own;                // byte offset of the 4 queries this lane hashes: 16 * (lane & 1)
+  uint32_t sel_lo, sel_hi;  // v_perm selectors: rows e = 0..3 and e = 4..7
+  __device__ __forceinline__ DropLanes(int lane, int my_key) {
+    const bool odd = lane & 1;  // my_key = 32-aligned base + lane % 32: same parity
+    pair = (uint32_t)(my_key >> 1) * kDropKeyMul;
+    own = odd ? 16 : 0;
+    // perm(x, w, sel) reads bytes 0-3 from w (this lane's word), 4-7 from x (the neighbour's);
+    // the key's 16 bits go to the top, zeros below. Even lane: rows 0-3 are its own words (low
+    // half), rows 4-7 its neighbour's (low half); odd lane: rows 0-3 the neighbour's (high
+    // half), rows 4-7 its own (high half).
+    sel_lo = odd ? 0x07060C0Cu : 0x01000C0Cu;
+    sel_hi = odd ? 0x03020C0Cu : 0x05040C0Cu;
+  }
+  // dw[hf][e]: the key's 16 bits (at the top of the word) for the query of register 8hf + e,
+  // i.e. the query at byte 4 * (16hf + e) of the row keys `rk` (the lane's query base applied).
+  __device__ __forceinline__ void words(const unsigned char* rk, uint32_t (&dw)[2][8]) const {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const u32x4_t r = *reinterpret_cast<const u32x4_t*>(rk + 16 * hf * 4 + own);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t w = pcg_hash(r[k] ^ pair);
+        const uint32_t x = swap_adjacent_lanes(w);
+        dw[hf][k] = __builtin_amdgcn_perm(x, w, sel_lo);
+        dw[hf][4 + k] = __builtin_amdgcn_perm(x, w, sel_hi);
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------------------
 // dK, dV. Workgroup = 8 waves over 128 keys, whose K and V rows stay in LDS for the whole
 // kernel; query tiles of 64 stream through a second LDS ring. Waves w and w+4 share the 32 keys
 // 32(w%4) .. +31 and split each query tile: wave w takes queries 0..31, wave w+4 queries 32..63
@@ -162,7 +207,7 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
   constexpr int KV_BYTES = kKvBK * D * 2;
   constexpr int STAGE = 2 * TILE;               // Q, dO
   constexpr int STATS0 = 2 * STAGE;             // per stage: LSE*log2(e), then D (256 B each)
-  constexpr int STATS_STAGE = 2 * kKvBQ * 4;
+  constexpr int STATS_STAGE = (DROP ? 3 : 2) * kKvBQ * 4;  // + dropout row keys
   constexpr int KV0 = STATS0 + 2 * STATS_STAGE;
   constexpr int MAIN_BYTES = KV0 + 2 * KV_BYTES;
   constexpr int ACC_BYTES = CB * 16 * 64 * 4;   // one wave's dK (or dV) accumulator
@@ -196,7 +241,7 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
   const int key_b0 = tc.qb * kKvBK;
   const int key_w0 = key_b0 + kw * 32;
   const int my_key = key_w0 + l32;
-  const uint32_t drop_col = (uint32_t)my_key * kDropKeyMul;  // dropout: this lane's key term
+  const DropLanes dl(lane, my_key);
 
   // resident K and V rows of the block: 128 rows each, swz-swizzled; 1 KiB block i holds rows
   // (64/DCH)*i ..
@@ -261,6 +306,8 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
     } else if (wave == 1) {
       if (lane < 16)
         buffer_load16_to_lds(rd, sst + kKvBQ * 4, (uint32_t)lane * 16, (uint32_t)it * kKvBQ * 4);
+    } else if (DROP && wave == 2) {
+      store_row_key(sst + 2 * kKvBQ * 4, drop, qh0 + gi, it * kKvBQ, lane);
     }
   };
 
@@ -282,7 +329,6 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
     if (t + 1 < n_steps) load_stage(t + 1, stage ^ 1);
     const int it = qt_begin + t % nt;
     const int q0 = it * kKvBQ + 32 * hq;  // this wave's 32 queries
-    const uint32_t drop_head = DROP ? drop_head_key(drop, (uint32_t)(qh0 + t / nt)) : 0u;
     // every query of the half precedes every key of the wave: fully masked
     const bool skip = CAUSAL && (q0 + 31 < key_w0);
     if (!skip) {
@@ -313,6 +359,8 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
       // P = exp2(s*c - LSE*log2e), dS = P * (dP - D); register i is query
       // q0 + 16(i/8) + 8g + i%8
       uint32_t pk[8], dsk[8];
+      uint32_t dw[2][8];  // dropout: the 16 bits deciding (query of register 8hf + e, my_key)
+      if constexpr (DROP) dl.words(ts + 2 * kKvBQ * 4, dw);
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         const unsigned char* sl = ts + 16 * hf * 4;  // queries 32hq + 16hf + 8g + (0..7)
@@ -327,9 +375,8 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
           const float dv_ = e < 4 ? d0[e] : d1[e - 4];
           const float pe = fast_exp2(__builtin_fmaf(s[8 * hf + e], scale_log2, -lv));
           if constexpr (DROP) {
-            // query q0 + 16hf + 8g + e of head qh0 + gi: kept with its 1/P(keep) scale or 0
-            const uint32_t row = pcg_hash(drop_head ^ (uint32_t)(q0 + 16 * hf + 8 * g + e));
-            const float zs = pcg_hash(row ^ drop_col) >= drop.thr ? drop.scale : 0.f;
+            // kept with its 1/P(keep) scale, or 0
+            const float zs = dw[hf][e] >= drop.thr ? drop.scale : 0.f;
             p[e] = pe * zs;
             ds[e] = pe * (dp[8 * hf + e] * zs - dv_);
           } else {
@@ -437,7 +484,7 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
   constexpr int KV_BYTES = kKv256BK * D * 2;      // 32 KiB
   constexpr int STAGE = 2 * TILE;                 // Q, dO
   constexpr int STATS0 = 2 * STAGE;               // per stage: LSE*log2(e), then D (128 B each)
-  constexpr int STATS_STAGE = 2 * kKv256BQ * 4;
+  constexpr int STATS_STAGE = (DROP ? 3 : 2) * kKv256BQ * 4;  // + dropout row keys
   constexpr int KV0 = STATS0 + 2 * STATS_STAGE;
   constexpr int SMEM = KV0 + 2 * KV_BYTES;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
@@ -467,7 +514,7 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
   const int key_b0 = tc.qb * kKv256BK;
   const int key_w0 = key_b0 + kw * 32;
   const int my_key = key_w0 + l32;
-  const uint32_t drop_col = (uint32_t)my_key * kDropKeyMul;  // dropout: this lane's key term
+  const DropLanes dl(lane, my_key);
 
   // resident K and V rows of the block (64 rows each, 2 rows per 1 KiB block)
   {
@@ -522,6 +569,8 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
       if (lane < 8)
         buffer_load16_to_lds(rd, sst + kKv256BQ * 4, (uint32_t)lane * 16,
                              (uint32_t)it * kKv256BQ * 4);
+    } else if (DROP && wave == 2) {
+      if (lane < kKv256BQ) store_row_key(sst + 2 * kKv256BQ * 4, drop, qh0 + gi, it * kKv256BQ, lane);
     }
   };
 
@@ -538,7 +587,6 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
     if (t + 1 < n_steps) load_stage(t + 1, stage ^ 1);
     const int it = qt_begin + t % nt;
     const int q0 = it * kKv256BQ;
-    const uint32_t drop_head = DROP ? drop_head_key(drop, (uint32_t)(qh0 + t / nt)) : 0u;
     // every query of the tile precedes every key of the wave: fully masked
     const bool skip = CAUSAL && (q0 + kKv256BQ - 1 < key_w0);
     if (!skip) {
@@ -578,6 +626,8 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
       // P = exp2(s*c - LSE*log2e); dK waves: dS = P * (dP - D). Register i is query
       // q0 + 16(i/8) + 8g + i%8.
       uint32_t bk[8];
+      uint32_t dw[2][8];  // dropout: the 16 bits deciding (query of register 8hf + e, my_key)
+      if constexpr (DROP) dl.words(ts + 2 * kKv256BQ * 4, dw);
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         const unsigned char* sl = ts + 16 * hf * 4;
@@ -592,8 +642,7 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
           const float dv_ = e < 4 ? d0[e] : d1[e - 4];
           const float p = fast_exp2(__builtin_fmaf(s[8 * hf + e], scale_log2, -lv));
           if constexpr (DROP) {
-            const uint32_t row = pcg_hash(drop_head ^ (uint32_t)(q0 + 16 * hf + 8 * g + e));
-            const float zs = pcg_hash(row ^ drop_col) >= drop.thr ? drop.scale : 0.f;
+            const float zs = dw[hf][e] >= drop.thr ? drop.scale : 0.f;
             x[e] = dk_wave ? p * (dp[8 * hf + e] * zs - dv_) : p * zs;
           } else {
             x[e] = dk_wave ? p * (dp[8 * hf + e] - dv_) : p;
@@ -784,10 +833,9 @@ __global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dq_kernel(
           if constexpr (DROP) {
             // keys j*BC + 32kb + 16(2i/8) + 8g + (2i%8) + 0, 1: dP scaled by Z / P(keep)
             const int key = j * BC + 32 * kb + 16 * ((2 * i) / 8) + 8 * g + (2 * i) % 8;
-            const bool k0 = pcg_hash(drop_row ^ ((uint32_t)key * kDropKeyMul)) >= drop.thr;
-            const bool k1 = pcg_hash(drop_row ^ ((uint32_t)(key + 1) * kDropKeyMul)) >= drop.thr;
-            dp0 = k0 ? dp0 * drop.scale : 0.f;
-            dp1 = k1 ? dp1 * drop.scale : 0.f;
+            const uint32_t w = drop_word(drop_row, (uint32_t)key >> 1);
+            dp0 = (w << 16) >= drop.thr ? dp0 * drop.scale : 0.f;
+            dp1 = w >= drop.thr ? dp1 * drop.scale : 0.f;
           }
           dsk[kb][i] = pack_bf16(p0 * (dp0 - dlt), p1 * (dp1 - dlt));
         }

@@ -127,9 +127,11 @@ __device__ __forceinline__ int swz(int row) {
 
 // Dropout mask generator: the 32-bit PCG-based hash of Jarzynski and Olano ("Hash Functions for
 // GPU Rendering", JCGT 9(3), 2020), an LCG step followed by a random xorshift, a multiply and
-// a fixed xorshift. The mask of query head bh is keep(i, j) = hash(r_i ^ j*0x9E3779B9) >= t with
-// r_i = hash(a ^ i), a = hash(k0 ^ hash(k1 ^ bh)); k0, k1 come from the seed and offset, t from
-// the dropout probability (host side).
+// a fixed xorshift. For query head bh: a = hash(k0 ^ hash(k1 ^ bh)) (k0, k1 from the seed and
+// offset), row key r_i = hash(a ^ i), and one word w = hash(r_i ^ m*0x9E3779B9) per key pair
+// m = j/2: key 2m is kept iff the low 16 bits of w are >= t, key 2m+1 iff the high 16 bits
+// are, t = floor(p * 2^16). The kernels compare whole words against thr = t << 16: the high
+// half as w >= thr, the low half as (w << 16) >= thr.
 __device__ __forceinline__ uint32_t pcg_hash(uint32_t x) {
   const uint32_t state = x * 747796405u + 2891336453u;
   const uint32_t word = ((state >> ((state >> 28u) + 4u)) ^ state) * 277803737u;
@@ -138,11 +140,19 @@ __device__ __forceinline__ uint32_t pcg_hash(uint32_t x) {
 constexpr uint32_t kDropKeyMul = 0x9E3779B9u;
 struct DropParams {
   uint32_t k0, k1;  // seed and offset keys
-  uint32_t thr;     // keep iff hash >= thr
+  uint32_t thr;     // t << 16: keep iff the key's 16 bits, moved to the top, are >= thr
   float scale;      // 1 / P(keep)
 };
 __device__ __forceinline__ uint32_t drop_head_key(const DropParams& dp, uint32_t bh) {
   return pcg_hash(dp.k0 ^ pcg_hash(dp.k1 ^ bh));
+}
+// The word of row key r and key pair m.
+__device__ __forceinline__ uint32_t drop_word(uint32_t r, uint32_t m) {
+  return pcg_hash(r ^ (m * kDropKeyMul));
+}
+// The value of the neighbouring lane (lane ^ 1), by DPP quad_perm [1, 0, 3, 2].
+__device__ __forceinline__ uint32_t swap_adjacent_lanes(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);
 }
 
 // Workgroup id -> (block, batch*head) order. Workgroups are dealt to the 8 XCDs in turn

@@ -221,11 +221,8 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
     return max_xor32(m) * scale_log2;
   };
   // p = exp2(s*c - m) -> packed bf16 (the PV B operand); partial sum of p
-  // dropout: p of key j survives iff hash(row key ^ j * kDropKeyMul) >= threshold (the sums
-  // of p for the normaliser and the LSE stay those of the undropped p)
-  auto drop_keep = [&](int key) {
-    return pcg_hash(drop_row ^ ((uint32_t)key * kDropKeyMul)) >= drop.thr;
-  };
+  // dropout: keys 2m, 2m+1 are decided by the two halves of one word (the sums of p for the
+  // normaliser and the LSE stay those of the undropped p)
   auto probs = [&](const f32x16_t* s, uint32_t (*pk)[8], int j) {
     const float neg_m = -m_run;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
@@ -239,7 +236,8 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
         if constexpr (DROP) {
           // registers 2i, 2i+1 of block kb hold keys j*BC + 32kb + 16(2i/8) + 8g + (2i%8) + 0, 1
           const int key = j * BC + 32 * kb + 16 * ((2 * i) / 8) + 8 * g + (2 * i) % 8;
-          pk[kb][i] = pack_bf16(drop_keep(key) ? p0 : 0.f, drop_keep(key + 1) ? p1 : 0.f);
+          const uint32_t w = drop_word(drop_row, (uint32_t)key >> 1);
+          pk[kb][i] = pack_bf16((w << 16) >= drop.thr ? p0 : 0.f, w >= drop.thr ? p1 : 0.f);
         } else {
           pk[kb][i] = pack_bf16(p0, p1);
         }

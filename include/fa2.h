@@ -142,7 +142,9 @@ fa2_status fa2_bwd_gqa(const void* q, const void* k, const void* v, const void* 
  *           s = x*747796405 + 2891336453; w = ((s >> ((s >> 28) + 4)) ^ s) * 277803737;
  *           h = (w >> 22) ^ w                                   (uint32, wrapping)
  *   k0 = h(seed_lo ^ h(seed_hi)), k1 = h(offset_lo ^ h(offset_hi)), a = h(k0 ^ h(k1 ^ bh))
- *   keep(i, j) = h(h(a ^ i) ^ j*0x9E3779B9) >= t,  t = floor(p * 2^32),  s = 1/(1 - t/2^32)
+ *   w(i, m) = h(h(a ^ i) ^ m*0x9E3779B9) for the key pair m = j/2 (one word, two keys)
+ *   u(i, j) = low 16 bits of w(i, j/2) for even j, high 16 bits for odd j
+ *   keep(i, j) = u(i, j) >= t,  t = floor(p * 2^16),  s = 1/(1 - t/2^16)
  * 0 <= dropout_p < 1 (else FA2_ERR_INVALID_ARGUMENT); dropout_p = 0 runs the kernels without
  * dropout (results identical to fa2_fwd_gqa / fa2_bwd_gqa). K/V layout as in the _gqa calls. */
 fa2_status fa2_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
