@@ -98,16 +98,29 @@ def keep_mask(seed: int, offset: int, bh: int, rows, n_keys: int, p: float) -> n
     return u >= np.uint32(dropout_threshold(p))
 
 
+def _head_ids(B: int, H: int, bh_index):
+    """The mask's query-head index of slice (b, h): b*H + h unless given ([B, H] integers,
+    for slices cut out of a larger batch)."""
+    if bh_index is None:
+        return np.arange(B * H).reshape(B, H)
+    ids = np.asarray(bh_index, dtype=np.int64)
+    if ids.shape != (B, H):
+        raise ValueError("bh_index must have shape [B, H]")
+    return ids
+
+
 def attention_forward_dropout(q, k, v, causal: bool = False, scale=None, p: float = 0.0,
-                              seed: int = 0, offset: int = 0, rows=None, row_chunk: int = 512):
+                              seed: int = 0, offset: int = 0, rows=None, row_chunk: int = 512,
+                              bh_index=None):
     """(O, LSE) of attention with dropout on P; q, k, v [B, H, N, d]. LSE is the undropped
-    softmax's. rows: optional subset of query rows."""
+    softmax's. rows: optional subset of query rows. bh_index: see _head_ids."""
     q, k, v = _as64(q), _as64(k), _as64(v)
     B, H, N, d = q.shape
     scale = resolve_scale(d, scale)
     s_keep = keep_scale(p)
     row_ids = np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64)
     R = row_ids.shape[0]
+    ids = _head_ids(B, H, bh_index)
     o = np.empty((B, H, R, d))
     lse = np.empty((B, H, R))
     for b in range(B):
@@ -115,19 +128,21 @@ def attention_forward_dropout(q, k, v, causal: bool = False, scale=None, p: floa
             for c0 in range(0, R, row_chunk):
                 ri = row_ids[c0:c0 + row_chunk]
                 pr, l = _row_softmax(_masked_scores(q[b, h, ri], ri, k[b, h], causal, scale))
-                z = keep_mask(seed, offset, b * H + h, ri, N, p)
+                z = keep_mask(seed, offset, ids[b, h], ri, N, p)
                 o[b, h, c0:c0 + len(ri)] = (pr * z * s_keep) @ v[b, h]
                 lse[b, h, c0:c0 + len(ri)] = l
     return o, lse
 
 
 def attention_backward_dropout(q, k, v, dout, causal: bool = False, scale=None, p: float = 0.0,
-                               seed: int = 0, offset: int = 0, row_chunk: int = 512):
+                               seed: int = 0, offset: int = 0, row_chunk: int = 512,
+                               bh_index=None):
     """(dQ, dK, dV) of attention_forward_dropout against the cotangent dO."""
     q, k, v, dout = _as64(q), _as64(k), _as64(v), _as64(dout)
     B, H, N, d = q.shape
     scale = resolve_scale(d, scale)
     s_keep = keep_scale(p)
+    ids = _head_ids(B, H, bh_index)
     dq = np.empty_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
@@ -136,7 +151,7 @@ def attention_backward_dropout(q, k, v, dout, causal: bool = False, scale=None, 
             for c0 in range(0, N, row_chunk):
                 ri = np.arange(c0, min(N, c0 + row_chunk))
                 pr, _ = _row_softmax(_masked_scores(q[b, h, ri], ri, k[b, h], causal, scale))
-                zs = keep_mask(seed, offset, b * H + h, ri, N, p) * s_keep
+                zs = keep_mask(seed, offset, ids[b, h], ri, N, p) * s_keep
                 pd = pr * zs
                 o_rows = pd @ v[b, h]
                 do_rows = dout[b, h, ri]

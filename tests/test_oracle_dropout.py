@@ -149,3 +149,22 @@ def test_average_over_seeds_is_unbiased():
     probs = attention_probs(q, k, causal=True)[0, 0]
     var = (probs ** 2) @ (v[0, 0] ** 2) * (keep_scale(p) - 1.0)
     np.testing.assert_allclose(outs.var(axis=0)[0, 0], var, rtol=0.25, atol=1e-3)
+
+
+def test_sampled_heads_match_the_whole_batch():
+    """bh_index lets a slice of a batch use its heads' masks: heads cut out of a [2, 3] batch
+    give the same outputs and gradients as the whole batch's computation."""
+    B, H, N, d, p = 2, 3, 19, 4, 0.35
+    q, k, v, do = (_rand((B, H, N, d), 60 + t) for t in range(4))
+    kw = dict(causal=True, p=p, seed=4, offset=8)
+    o, lse = attention_forward_dropout(q, k, v, **kw)
+    g = attention_backward_dropout(q, k, v, do, **kw)
+    for b, h in ((0, 2), (1, 1)):
+        sl = lambda x: x[b:b + 1, h:h + 1]
+        ids = [[b * H + h]]
+        o1, l1 = attention_forward_dropout(sl(q), sl(k), sl(v), bh_index=ids, **kw)
+        np.testing.assert_array_equal(o1[0, 0], o[b, h])
+        np.testing.assert_array_equal(l1[0, 0], lse[b, h])
+        g1 = attention_backward_dropout(sl(q), sl(k), sl(v), sl(do), bh_index=ids, **kw)
+        for a_, b_ in zip(g1, g):
+            np.testing.assert_array_equal(a_[0, 0], b_[b, h])
