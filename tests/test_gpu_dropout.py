@@ -200,3 +200,30 @@ def test_autograd_with_dropout():
     assert torch.equal(out.view(torch.int16), o.view(torch.int16))
     for a, b in ((qa.grad, dq), (ka.grad, dk), (va.grad, dv)):
         assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_dropout_full_size_step():
+    """Dropout p = 0.1 at the benchmark's fwd+bwd shape (B=4, H=16, N=2048, d=128, causal), in
+    the benchmark's launch configuration: two sampled heads, every element of O, LSE, dQ, dK
+    and dV, against the oracle with those heads' masks."""
+    fa2 = _fa2()
+    B, H, N, d = 4, 16, 2048, 128
+    p, seed, offset = f32(0.1), 1234, 0
+    bq, bk, bv, bdo = (normal_bf16((B, H, N, d), 9600 + t) for t in range(4))
+    q, k, v, do = (to_dev(b_) for b_ in (bq, bk, bv, bdo))
+    o, lse = fa2.fwd(q, k, v, causal=True, dropout_p=p, seed=seed, offset=offset)
+    dq, dk, dv = fa2.bwd(q, k, v, o, do, lse, causal=True, dropout_p=p, seed=seed, offset=offset)
+    torch.cuda.synchronize()
+    scale = default_scale(d)
+    for b, h in ((0, 0), (3, 15)):
+        print(f"batch {b} head {h}", flush=True)
+        sl = lambda x: bf16_bits_to_f64(x[b:b + 1, h:h + 1])
+        kw = dict(causal=True, scale=scale, p=p, seed=seed, offset=offset, bh_index=[[b * H + h]])
+        o_ref, lse_ref = attention_forward_dropout(sl(bq), sl(bk), sl(bv), **kw)
+        o_abs, _ = attention_forward_dropout(sl(bq), sl(bk), np.abs(sl(bv)), **kw)
+        assert_fwd_within_rounding_bound(bf16_to_f64(o[b:b + 1, h:h + 1]),
+                                         lse[b:b + 1, h:h + 1].cpu().double().numpy(),
+                                         o_ref, o_abs, lse_ref, f"b{b} h{h}")
+        refs = attention_backward_dropout(sl(bq), sl(bk), sl(bv), sl(bdo), **kw)
+        for name, got, want in zip(("dq", "dk", "dv"), (dq, dk, dv), refs):
+            assert_grad_close(bf16_to_f64(got[b:b + 1, h:h + 1]), want, f"b{b} h{h} {name}")

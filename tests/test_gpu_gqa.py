@@ -84,3 +84,31 @@ def test_packed_and_strided_kv(causal):
     for a_, b_ in ((dq2, dq), (dkv2[:, 0], dk), (dkv2[:, 1], dv), (dq3, dq), (dk3, dk), (dv3, dv),
                    (qa.grad, dq), (kva.grad[:, 0], dk), (kva.grad[:, 1], dv)):
         assert same(a_, b_)
+
+
+def test_grouped_heads_full_size_step():
+    """The grouped-head step at the benchmark's shape (B=4, 16 query heads on 4 K/V heads,
+    N=2048, d=128, causal), in the benchmark's launch configuration: for two sampled (batch,
+    K/V head) pairs, O and LSE of the group's 4 query heads, their dQ, and the K/V head's
+    group-summed dK and dV, every element, against the oracle."""
+    fa2 = _fa2()
+    B, H, Hkv, N, d = 4, 16, 4, 2048, 128
+    G = H // Hkv
+    bq, bdo = normal_bf16((B, H, N, d), 9501), normal_bf16((B, H, N, d), 9504)
+    bk, bv = normal_bf16((B, Hkv, N, d), 9502), normal_bf16((B, Hkv, N, d), 9503)
+    q, k, v, do = (to_dev(b_) for b_ in (bq, bk, bv, bdo))
+    o, lse = fa2.fwd(q, k, v, causal=True)
+    dq, dk, dv = fa2.bwd(q, k, v, o, do, lse, causal=True)
+    torch.cuda.synchronize()
+    for b, kvh in ((0, 0), (3, 3)):
+        hs = slice(kvh * G, (kvh + 1) * G)
+        print(f"batch {b} K/V head {kvh}", flush=True)
+        o_ref, lse_ref, dq_ref, dk_ref, dv_ref = _oracle(
+            bq[b:b + 1, hs], bk[b:b + 1, kvh:kvh + 1], bv[b:b + 1, kvh:kvh + 1],
+            bdo[b:b + 1, hs], True, default_scale(d))
+        assert_fwd_close(bf16_to_f64(o[b:b + 1, hs]), lse[b:b + 1, hs].cpu().double().numpy(),
+                         o_ref, lse_ref, f"b{b} kv{kvh}")
+        for name, got, want in (("dq", dq[b:b + 1, hs], dq_ref),
+                                ("dk", dk[b:b + 1, kvh:kvh + 1], dk_ref),
+                                ("dv", dv[b:b + 1, kvh:kvh + 1], dv_ref)):
+            assert_grad_close(bf16_to_f64(got), want, f"b{b} kv{kvh} {name}")
