@@ -445,21 +445,11 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
       }
   }
 
-  // dK = scale * dK_acc (wave kw, 0), dV = dV_acc (wave kw, 1). Lane holds key my_key, columns
-  // 32cb + 8t + 4g + 0..3.
-  if (my_key < N) {
-    const float mul = hq == 0 ? scale : 1.f;
-    uint16_t* row = (hq == 0 ? dk : dv) + head_off + (size_t)my_key * D;
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int c = cb * 32 + 8 * t + 4 * g;
-        *reinterpret_cast<u32x2_t*>(row + c) =
-            u32x2_t{pack_bf16(keep[cb][4 * t] * mul, keep[cb][4 * t + 1] * mul),
-                    pack_bf16(keep[cb][4 * t + 2] * mul, keep[cb][4 * t + 3] * mul)};
-      }
-  }
+  // dK = scale * dK_acc (wave kw, 0), dV = dV_acc (wave kw, 1), keys key_w0 .. +31. The
+  // other wave's slot, which only this wave reads, is the transpose scratch.
+  static_assert(store_scratch_bytes(CB) <= ACC_BYTES, "transpose scratch");
+  store_rows_via_lds<CB, D>(smem + (wave ^ 4) * ACC_BYTES, keep, hq == 0 ? scale : 1.f,
+                            (hq == 0 ? dk : dv) + head_off, key_w0, N, lane);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -673,20 +663,10 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
     if (t + 1 < n_steps) step(std::integral_constant<int, 1>{}, t + 1);
   }
 
-  // dK = scale * dK_acc, dV = dV_acc. Lane holds key my_key, columns 32cb + 8t + 4g + 0..3.
-  if (my_key < N) {
-    const float mul = dk_wave ? scale : 1.f;
-    uint16_t* row = (dk_wave ? dk : dv) + head_off + (size_t)my_key * D;
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int c = cb * 32 + 8 * t + 4 * g;
-        *reinterpret_cast<u32x2_t*>(row + c) =
-            u32x2_t{pack_bf16(acc[cb][4 * t] * mul, acc[cb][4 * t + 1] * mul),
-                    pack_bf16(acc[cb][4 * t + 2] * mul, acc[cb][4 * t + 3] * mul)};
-      }
-  }
+  // dK = scale * dK_acc, dV = dV_acc, keys key_w0 .. +31 (the loop ended with a barrier: the
+  // ring is free for the transpose)
+  store_rows_via_lds<CB, D>(smem + wave * store_scratch_bytes(CB), acc, dk_wave ? scale : 1.f,
+                            (dk_wave ? dk : dv) + head_off, key_w0, N, lane);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -862,18 +842,11 @@ __global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dq_kernel(
     if (j + 1 < n_tiles) step(std::integral_constant<int, 1>{}, j + 1);
   }
 
-  if (valid_q) {
-    uint16_t* row = dq + head_off + (size_t)my_q * D;
-#pragma unroll
-    for (int cb = 0; cb < CBO; ++cb)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int c = (CB0 + cb) * 32 + 8 * t + 4 * g;
-        *reinterpret_cast<u32x2_t*>(row + c) =
-            u32x2_t{pack_bf16(dqacc[cb][4 * t] * scale, dqacc[cb][4 * t + 1] * scale),
-                    pack_bf16(dqacc[cb][4 * t + 2] * scale, dqacc[cb][4 * t + 3] * scale)};
-      }
-  }
+  // dQ = scale * dQ_acc, queries q_wave0 .. +31, columns 32*CB0 .. (the loop ended with a
+  // barrier: the K/V tiles are free)
+  static_assert(4 * store_scratch_bytes(CBO) <= 2 * STAGE, "transpose scratch");
+  store_rows_via_lds<CBO, D>(smem + wave * store_scratch_bytes(CBO), dqacc, scale, dq + head_off + 32 * CB0,
+                             q_wave0, N, lane);
 }
 
 // ---------------------------------------------------------------------------------------

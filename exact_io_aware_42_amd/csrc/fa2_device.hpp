@@ -155,6 +155,41 @@ __device__ __forceinline__ uint32_t swap_adjacent_lanes(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xF, 0xF, false);
 }
 
+// Stores a wave's 32-row tile of results, NB column blocks of 32 held as MFMA results (lane l:
+// row l % 32; register 4t + e of block cb: column 32cb + 8t + 4(l/32) + e), times `mul` (per
+// lane, i.e. per row), as bf16 into rows row0 .. row0+31 of `out` (row stride LD elements, `out`
+// at the tile's first column; rows >= n_rows are skipped). Up to 128 columns at a time go
+// through `scratch` (LDS that only this wave uses, store_scratch_bytes(NB) bytes, rows padded
+// by 16 bytes), so that each global store writes whole row segments, 16 bytes per lane, rather
+// than 8 bytes in each of 32 rows.
+constexpr int store_scratch_bytes(int nb) { return 32 * (64 * (nb < 4 ? nb : 4) + 16); }
+template <int NB, int LD>
+__device__ __forceinline__ void store_rows_via_lds(unsigned char* scratch, const f32x16_t* acc,
+                                                   float mul, uint16_t* out, int row0,
+                                                   int n_rows, int lane) {
+  constexpr int W = NB < 4 ? NB : 4;        // column blocks per pass
+  constexpr int PITCH = 64 * W + 16;
+  constexpr int CH = 4 * W, RPI = 64 / CH;  // 16-byte chunks per row, rows per store
+  const int r = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int c0 = 0; c0 < NB; c0 += W) {
+#pragma unroll
+    for (int cb = 0; cb < W; ++cb)
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        *reinterpret_cast<u32x2_t*>(scratch + r * PITCH + (32 * cb + 8 * t + 4 * g) * 2) =
+            u32x2_t{pack_bf16(acc[c0 + cb][4 * t] * mul, acc[c0 + cb][4 * t + 1] * mul),
+                    pack_bf16(acc[c0 + cb][4 * t + 2] * mul, acc[c0 + cb][4 * t + 3] * mul)};
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int rr = i * RPI + lane / CH, ch = lane % CH;
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(scratch + rr * PITCH + ch * 16);
+      if (row0 + rr < n_rows)
+        *reinterpret_cast<u32x4_t*>(out + (size_t)(row0 + rr) * LD + 32 * c0 + ch * 8) = v;
+    }
+  }
+}
+
 // Workgroup id -> (block, batch*head) order. Workgroups are dealt to the 8 XCDs in turn
 // (id % 8), each XCD with its own L2; when the heads divide evenly, XCD x gets the heads
 // x, x+8, ... only.

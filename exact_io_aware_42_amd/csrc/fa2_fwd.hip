@@ -332,20 +332,12 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
   // ---- epilogue: deferred normalisation, bf16 output, LSE
   const float l_tot = sum_xor32(l_f32);
   const float l_o = sum_xor32(l_f32 + l_corr);
-  if (my_q < N) {
-    const float inv = DROP ? fast_rcp(l_o) * drop.scale : fast_rcp(l_o);
-    uint16_t* orow = o + head_off + (size_t)my_q * D;
-#pragma unroll
-    for (int cb = 0; cb < S::CB; ++cb)
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int c = cb * 32 + 8 * t + 4 * g;
-        u32x2_t w = {pack_bf16(oacc[cb][4 * t + 0] * inv, oacc[cb][4 * t + 1] * inv),
-                     pack_bf16(oacc[cb][4 * t + 2] * inv, oacc[cb][4 * t + 3] * inv)};
-        *reinterpret_cast<u32x2_t*>(orow + c) = w;
-      }
-    if (g == 0) lse[(size_t)tc.bh * N + my_q] = (m_run + fast_log2(l_tot)) * kLn2;
-  }
+  const float inv = DROP ? fast_rcp(l_o) * drop.scale : fast_rcp(l_o);
+  // (the loop ended with a barrier: the K/V tiles are free for the transpose)
+  static_assert(4 * store_scratch_bytes(S::CB) <= S::SMEM, "transpose scratch");
+  store_rows_via_lds<S::CB, D>(smem + wave * store_scratch_bytes(S::CB), oacc, inv, o + head_off,
+                               my_q - l32, N, lane);
+  if (my_q < N && g == 0) lse[(size_t)tc.bh * N + my_q] = (m_run + fast_log2(l_tot)) * kLn2;
 }
 
 template <int D, bool CAUSAL, bool DROP>
