@@ -24,7 +24,9 @@
 //   fa2_bwd_pre_kernel   D and LSE*log2(e) alone (HBM-bound), for callers that want dK/dV
 //                        without dQ.
 // dK/dV and dQ each recompute S and dP; dQ's two recompute GEMMs are the price of avoiding
-// atomic dQ accumulation.
+// atomic dQ accumulation. Output tiles leave through LDS as whole row segments. With dropout
+// (DROP) every kernel regenerates the keep bits it needs from the counter-based hash
+// (fa2_device.hpp); dS = P * (Z * dP / P(keep) - D) and dV takes P * Z / P(keep).
 #include <type_traits>
 
 #include "fa2_device.hpp"

@@ -32,7 +32,14 @@
 //    sum(bf16(p)) - sum(p) is added, so a row whose visible keys all lie in masked tiles (every
 //    causal row with fewer than 64 keys, where O mixes only a few V rows) gets exactly
 //    convex bf16 weights; on unmasked tiles the fp32 sum stands in (rows with >= 64 keys, where
-//    the difference averages out).
+//    the difference averages out);
+//  * the O tile leaves through LDS (after the last tile's barrier) as whole row segments;
+//  * head dimension 256: key tiles of 32 (the O^T and Q^T registers leave room for one MFMA
+//    key block of scores);
+//  * dropout (DROP): each kept p is multiplied by 1 (and the 1/P(keep) scale joins 1/l at the
+//    end), each dropped p by 0, before the PV MFMA; the sums for l and the LSE are those of the
+//    undropped p. The keep bits come from the counter-based hash in fa2_device.hpp, one hash
+//    word per key pair.
 #include <type_traits>
 
 #include "fa2_device.hpp"
