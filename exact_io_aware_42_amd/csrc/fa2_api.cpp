@@ -161,7 +161,28 @@ size_t fa2_bwd_workspace_bytes(int B, int H, int N, int d) {
   return 2 * ws_part_bytes(B, H, N);
 }
 
+size_t fa2_bwd_gqa_workspace_bytes(int B, int H, int Hkv, int N, int d) {
+  bool empty;
+  if (check_sizes(B, H, N, d, 1.0f, &empty) != FA2_OK || empty) return 0;
+  if (Hkv <= 0 || H % Hkv != 0) return 0;
+  const int split = fa2::dkdv_split(B, H, Hkv, N, d);
+  const size_t part = split > 1 ? round256((size_t)2 * split * B * Hkv * N * d * sizeof(float)) : 0;
+  return 2 * ws_part_bytes(B, H, N) + part;
+}
+
 namespace {
+
+// Grouped heads: split the dK/dV work of each group when the workspace holds the partial sums
+// (fa2_bwd_gqa_workspace_bytes); with the smaller workspace the groups stay whole.
+void set_kv_split(fa2::BwdArgs* a, void* workspace, size_t workspace_bytes) {
+  const int split = fa2::dkdv_split(a->B, a->H, a->Hkv, a->N, a->d);
+  if (split > 1 &&
+      workspace_bytes >= fa2_bwd_gqa_workspace_bytes(a->B, a->H, a->Hkv, a->N, a->d)) {
+    a->kv_split = split;
+    a->kv_part = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                          2 * ws_part_bytes(a->B, a->H, a->N));
+  }
+}
 
 fa2_status bwd_args(const void* q, const void* k, const void* v, const void* o, const void* dout,
                     const float* lse, void* workspace, size_t workspace_bytes, void* dq, void* dk,
@@ -232,6 +253,7 @@ fa2_status fa2_bwd_gqa(const void* q, const void* k, const void* v, const void* 
   if (!all_ok({q, k, v, o, dout, lse, dq, dk, dv})) return FA2_ERR_INVALID_ARGUMENT;
   a.Hkv = Hkv;
   a.kv_bstride = kv_batch_stride;
+  set_kv_split(&a, workspace, workspace_bytes);
   return from_hip(fa2::launch_bwd(a));
 }
 
@@ -259,6 +281,7 @@ fa2_status fa2_bwd_dropout(const void* q, const void* k, const void* v, const vo
   a.drop_k1 = drop.k1;
   a.drop_thr = drop.thr;
   a.drop_scale = drop.scale;
+  set_kv_split(&a, workspace, workspace_bytes);
   return from_hip(fa2::launch_bwd(a));
 }
 

@@ -200,7 +200,8 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse2, const float* __restrict__ delta, uint16_t* __restrict__ dk,
     uint16_t* __restrict__ dv, int N, int n_kblocks, int bh_count, int n_qheads, int group,
-    long long kv_bstride, float scale_log2, float scale, DropParams drop) {
+    long long kv_bstride, float scale_log2, float scale, DropParams drop,
+    float* __restrict__ part, int split) {
   constexpr int KK = D / 16, CB = D / 32, DCH = D / 8;
   // LDS: the two ring stages of Q and dO tiles at the bottom (every ds_read of them is a
   // per-lane base plus a 16-bit immediate), then LSE*log2(e) and D of both stages, then the
@@ -228,12 +229,16 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
   // causal: key block 0 sees every query tile, so ascending order is longest first
   const TileCoord tc = schedule_tile<CAUSAL ? Order::kLongAscending : Order::kHeadMajor>(
       blockIdx.x, n_kblocks, bh_count);
-  // tc.bh indexes (batch, K/V head); the query heads sharing this K/V head are
-  // qh0 .. qh0 + group - 1, and their contributions to dK, dV are summed here in order.
+  // tc.bh = (batch * Hkv + K/V head) * split + part; the part's query heads are
+  // qh0 .. qh0 + gsz - 1, and their contributions to dK, dV are summed here in order (split > 1:
+  // into fp32 partial sums that fa2_bwd_kv_reduce_kernel adds).
+  const int sj = tc.bh % split;
+  const int bhkv = tc.bh / split;
+  const int gsz = group / split;
   const int n_kvheads = n_qheads / group;
-  const int b_idx = tc.bh / n_kvheads;
-  const int kvh = tc.bh - b_idx * n_kvheads;
-  const int qh0 = b_idx * n_qheads + kvh * group;
+  const int b_idx = bhkv / n_kvheads;
+  const int kvh = bhkv - b_idx * n_kvheads;
+  const int qh0 = b_idx * n_qheads + kvh * group + sj * gsz;
   const size_t head_off =  // K, V, dK, dV
       (size_t)b_idx * (size_t)kv_bstride + (size_t)kvh * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
@@ -273,7 +278,7 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
   const int qt_begin = CAUSAL ? key_b0 / kKvBQ : 0;
   // steps t = 0 .. group*nt - 1 walk query tile qt_begin + t % nt of query head qh0 + t / nt
   const int nt = n_qt - qt_begin;
-  const int n_steps = group * nt;
+  const int n_steps = gsz * nt;
   const TileLoader<D, kKvThreads> ld(wave, lane);
   // per-lane read offsets within a stage for this wave's query half: row-wise Q/dO fragments
   // (rows 32hq + kmap(l32)) and transposing reads (k-steps t = 2hq + hf)
@@ -450,8 +455,16 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
   // dK = scale * dK_acc (wave kw, 0), dV = dV_acc (wave kw, 1), keys key_w0 .. +31. The
   // other wave's slot, which only this wave reads, is the transpose scratch.
   static_assert(store_scratch_bytes(CB) <= ACC_BYTES, "transpose scratch");
-  store_rows_via_lds<CB, D>(smem + (wave ^ 4) * ACC_BYTES, keep, hq == 0 ? scale : 1.f,
-                            (hq == 0 ? dk : dv) + head_off, key_w0, N, lane);
+  const float mul = hq == 0 ? scale : 1.f;
+  if (part == nullptr) {
+    store_rows_via_lds<CB, D>(smem + (wave ^ 4) * ACC_BYTES, keep, mul,
+                              (hq == 0 ? dk : dv) + head_off, key_w0, N, lane);
+  } else {
+    const size_t n_bhkv = (size_t)(bh_count / split);
+    float* dst = part + ((hq == 0 ? 0 : (size_t)split) + sj) * n_bhkv * N * D +
+                 (size_t)bhkv * N * D;
+    store_rows_f32<CB, D>(keep, mul, dst, key_w0, N, lane);
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -470,7 +483,8 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse2, const float* __restrict__ delta, uint16_t* __restrict__ dk,
     uint16_t* __restrict__ dv, int N, int n_kblocks, int bh_count, int n_qheads, int group,
-    long long kv_bstride, float scale_log2, float scale, DropParams drop) {
+    long long kv_bstride, float scale_log2, float scale, DropParams drop,
+    float* __restrict__ part, int split) {
   constexpr int D = 256, KK = D / 16, CB = D / 32, DCH = D / 8;
   constexpr int TILE = kKv256BQ * D * 2;          // 16 KiB
   constexpr int KV_BYTES = kKv256BK * D * 2;      // 32 KiB
@@ -491,12 +505,14 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
 
   const TileCoord tc = schedule_tile<CAUSAL ? Order::kLongAscending : Order::kHeadMajor>(
       blockIdx.x, n_kblocks, bh_count);
-  // tc.bh indexes (batch, K/V head); the query heads sharing this K/V head are
-  // qh0 .. qh0 + group - 1, and their contributions to dK, dV are summed here in order.
+  // tc.bh = (batch * Hkv + K/V head) * split + part, as in the d <= 128 kernel
+  const int sj = tc.bh % split;
+  const int bhkv = tc.bh / split;
+  const int gsz = group / split;
   const int n_kvheads = n_qheads / group;
-  const int b_idx = tc.bh / n_kvheads;
-  const int kvh = tc.bh - b_idx * n_kvheads;
-  const int qh0 = b_idx * n_qheads + kvh * group;
+  const int b_idx = bhkv / n_kvheads;
+  const int kvh = bhkv - b_idx * n_kvheads;
+  const int qh0 = b_idx * n_qheads + kvh * group + sj * gsz;
   const size_t head_off =  // K, V, dK, dV
       (size_t)b_idx * (size_t)kv_bstride + (size_t)kvh * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
@@ -536,7 +552,7 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
   const int qt_begin = CAUSAL ? key_b0 / kKv256BQ : 0;
   // steps t = 0 .. group*nt - 1 walk query tile qt_begin + t % nt of query head qh0 + t / nt
   const int nt = n_qt - qt_begin;
-  const int n_steps = group * nt;
+  const int n_steps = gsz * nt;
   const TileLoader<D, kThreads, kKv256BQ> ld(wave, lane);
   const TileReads<D> rd_off(lane);
 
@@ -667,8 +683,15 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
 
   // dK = scale * dK_acc, dV = dV_acc, keys key_w0 .. +31 (the loop ended with a barrier: the
   // ring is free for the transpose)
-  store_rows_via_lds<CB, D>(smem + wave * store_scratch_bytes(CB), acc, dk_wave ? scale : 1.f,
-                            (dk_wave ? dk : dv) + head_off, key_w0, N, lane);
+  if (part == nullptr) {
+    store_rows_via_lds<CB, D>(smem + wave * store_scratch_bytes(CB), acc, dk_wave ? scale : 1.f,
+                              (dk_wave ? dk : dv) + head_off, key_w0, N, lane);
+  } else {
+    const size_t n_bhkv = (size_t)(bh_count / split);
+    float* dst = part + ((dk_wave ? 0 : (size_t)split) + sj) * n_bhkv * N * D +
+                 (size_t)bhkv * N * D;
+    store_rows_f32<CB, D>(acc, dk_wave ? scale : 1.f, dst, key_w0, N, lane);
+  }
 }
 
 // ---------------------------------------------------------------------------------------
@@ -852,6 +875,50 @@ __global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dq_kernel(
 }
 
 // ---------------------------------------------------------------------------------------
+// dK, dV of grouped K/V heads whose groups were split over `split` workgroups: the sum of the
+// fp32 partial sums (dK's already scaled) in split order, to bf16 in the K/V layout. 8
+// elements per thread over dK (n_elem = B*Hkv*N*D elements), then dV.
+template <int D>
+__global__ __launch_bounds__(kThreads) void fa2_bwd_kv_reduce_kernel(
+    const float* __restrict__ part, uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int N,
+    int n_kvheads, long long kv_bstride, int split, long long n_elem) {
+  const long long e = ((long long)blockIdx.x * kThreads + threadIdx.x) * 8;
+  if (e >= 2 * n_elem) return;
+  const bool is_v = e >= n_elem;
+  const long long ee = is_v ? e - n_elem : e;
+  const float* src = part + (is_v ? (long long)split * n_elem : 0) + ee;
+  f32x4_t lo = f32x4_t{}, hi = f32x4_t{};
+  for (int j = 0; j < split; ++j) {
+    lo += *reinterpret_cast<const f32x4_t*>(src + (long long)j * n_elem);
+    hi += *reinterpret_cast<const f32x4_t*>(src + (long long)j * n_elem + 4);
+  }
+  const long long head_elems = (long long)N * D;
+  const long long bh = ee / head_elems;  // batch * Hkv + K/V head
+  const long long b = bh / n_kvheads;
+  uint16_t* dst = (is_v ? dv : dk) + b * kv_bstride + (bh - b * n_kvheads) * head_elems +
+                  (ee - bh * head_elems);
+  *reinterpret_cast<u32x4_t*>(dst) =
+      u32x4_t{pack_bf16(lo[0], lo[1]), pack_bf16(lo[2], lo[3]), pack_bf16(hi[0], hi[1]),
+              pack_bf16(hi[2], hi[3])};
+}
+
+template <int D>
+hipError_t launch_kv_reduce_t(const BwdArgs& a) {
+  const long long n_elem = (long long)a.B * a.Hkv * a.N * D;
+  const long long grid = (2 * n_elem / 8 + kThreads - 1) / kThreads;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((fa2_bwd_kv_reduce_kernel<D>), dim3((unsigned)grid), dim3(kThreads), 0,
+                     a.stream, a.kv_part, static_cast<uint16_t*>(a.dk),
+                     static_cast<uint16_t*>(a.dv), a.N, a.Hkv, a.kv_bstride, a.kv_split, n_elem);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_reduce(const BwdArgs& a) {
+  if (a.d == 256) return launch_kv_reduce_t<256>(a);
+  if (a.d == 64) return launch_kv_reduce_t<64>(a);
+  return launch_kv_reduce_t<128>(a);
+}
+
 template <int D>
 hipError_t launch_pre_t(const BwdArgs& a) {
   const long long rows = (long long)a.B * a.H * a.N;
@@ -867,15 +934,16 @@ hipError_t launch_pre_t(const BwdArgs& a) {
 template <int D, bool CAUSAL, bool DROP>
 hipError_t launch_dkdv_t(const BwdArgs& a) {
   const int n_kblocks = (a.N + kKvBK - 1) / kKvBK;
-  const long long grid = (long long)n_kblocks * a.B * a.Hkv;
+  const long long grid = (long long)n_kblocks * a.B * a.Hkv * a.kv_split;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, CAUSAL, DROP>), dim3((unsigned)grid), dim3(kKvThreads), 0,
                      a.stream, static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                      static_cast<const uint16_t*>(a.dout), a.lse2, a.delta,
                      static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), a.N, n_kblocks,
-                     a.B * a.Hkv, a.H, a.H / a.Hkv, a.kv_bstride, a.scale_log2, a.scale,
-                     DropParams{a.drop_k0, a.drop_k1, a.drop_thr, a.drop_scale});
+                     a.B * a.Hkv * a.kv_split, a.H, a.H / a.Hkv, a.kv_bstride, a.scale_log2,
+                     a.scale, DropParams{a.drop_k0, a.drop_k1, a.drop_thr, a.drop_scale},
+                     a.kv_split > 1 ? a.kv_part : nullptr, a.kv_split);
   return hipGetLastError();
 }
 
@@ -915,15 +983,16 @@ hipError_t launch_bwd_pre(const BwdArgs& a) {
 template <bool CAUSAL, bool DROP>
 hipError_t launch_dkdv256_t(const BwdArgs& a) {
   const int n_kblocks = (a.N + kKv256BK - 1) / kKv256BK;
-  const long long grid = (long long)n_kblocks * a.B * a.Hkv;
+  const long long grid = (long long)n_kblocks * a.B * a.Hkv * a.kv_split;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((fa2_bwd_dkdv256_kernel<CAUSAL, DROP>), dim3((unsigned)grid), dim3(kThreads), 0,
                      a.stream, static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                      static_cast<const uint16_t*>(a.dout), a.lse2, a.delta,
                      static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), a.N, n_kblocks,
-                     a.B * a.Hkv, a.H, a.H / a.Hkv, a.kv_bstride, a.scale_log2, a.scale,
-                     DropParams{a.drop_k0, a.drop_k1, a.drop_thr, a.drop_scale});
+                     a.B * a.Hkv * a.kv_split, a.H, a.H / a.Hkv, a.kv_bstride, a.scale_log2,
+                     a.scale, DropParams{a.drop_k0, a.drop_k1, a.drop_thr, a.drop_scale},
+                     a.kv_split > 1 ? a.kv_part : nullptr, a.kv_split);
   return hipGetLastError();
 }
 
@@ -937,7 +1006,9 @@ hipError_t launch_bwd_dkdv_drop(const BwdArgs& a) {
 }
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a) {
-  return a.dropout ? launch_bwd_dkdv_drop<true>(a) : launch_bwd_dkdv_drop<false>(a);
+  const hipError_t e = a.dropout ? launch_bwd_dkdv_drop<true>(a) : launch_bwd_dkdv_drop<false>(a);
+  if (e != hipSuccess || a.kv_split <= 1) return e;
+  return launch_kv_reduce(a);
 }
 
 template <bool DROP>

@@ -190,6 +190,23 @@ __device__ __forceinline__ void store_rows_via_lds(unsigned char* scratch, const
   }
 }
 
+// The same 32-row tile (layout as in store_rows_via_lds) times `mul` as fp32 into rows row0 ..
+// row0+31 of `out` (row stride LD floats; rows >= n_rows skipped), 16 bytes per lane.
+template <int NB, int LD>
+__device__ __forceinline__ void store_rows_f32(const f32x16_t* acc, float mul, float* out,
+                                               int row0, int n_rows, int lane) {
+  const int r = lane & 31, g = lane >> 5;
+  if (row0 + r >= n_rows) return;
+  float* row = out + (size_t)(row0 + r) * LD;
+#pragma unroll
+  for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      *reinterpret_cast<f32x4_t*>(row + 32 * cb + 8 * t + 4 * g) =
+          f32x4_t{acc[cb][4 * t] * mul, acc[cb][4 * t + 1] * mul, acc[cb][4 * t + 2] * mul,
+                  acc[cb][4 * t + 3] * mul};
+}
+
 // Workgroup id -> (block, batch*head) order. Workgroups are dealt to the 8 XCDs in turn
 // (id % 8), each XCD with its own L2; when the heads divide evenly, XCD x gets the heads
 // x, x+8, ... only.

@@ -51,8 +51,28 @@ struct BwdArgs {
   bool dropout = false;  // as in FwdArgs
   uint32_t drop_k0 = 0, drop_k1 = 0, drop_thr = 0;
   float drop_scale = 1.f;
+  // grouped K/V heads: with kv_split > 1 the query heads of a group are split over kv_split
+  // dK/dV workgroups per key block, which write fp32 partial sums (dK, scaled, then dV, each
+  // [kv_split][B*Hkv][N][d]) to kv_part; a reduction adds them in split order
+  int kv_split = 1;
+  float* kv_part = nullptr;
   hipStream_t stream;
 };
+
+// Query heads per group share one dK/dV workgroup per (key block, K/V head) unless that leaves
+// fewer than kDkdvMinWorkgroups workgroups (two per CU of a 256-CU part): then the smallest
+// divisor s of the group size that reaches it (or the group size itself) splits each group
+// into s parts.
+constexpr long long kDkdvMinWorkgroups = 512;
+inline int dkdv_split(int B, int H, int Hkv, int N, int d) {
+  const int G = H / Hkv;
+  const long long kblocks = (N + (d == 256 ? 64 : 128) - 1) / (d == 256 ? 64 : 128);
+  const long long base = kblocks * B * Hkv;
+  if (G <= 1 || base >= kDkdvMinWorkgroups) return 1;
+  for (int s = 2; s < G; ++s)
+    if (G % s == 0 && base * s >= kDkdvMinWorkgroups) return s;
+  return G;
+}
 
 hipError_t launch_fwd(const FwdArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);  // dQ (also D and LSE*log2(e)), then dK/dV

@@ -25,7 +25,8 @@ FA2_ERR_HIP = 3
 
 EXPORTED = ("fa2_fwd", "fa2_bwd", "fa2_bwd_workspace_bytes", "fa2_bwd_preprocess",
             "fa2_bwd_dkdv", "fa2_bwd_dq", "fa2_fwd_gqa", "fa2_bwd_gqa", "fa2_fwd_dropout",
-            "fa2_bwd_dropout", "fa2_status_string", "fa2_last_hip_error")
+            "fa2_bwd_dropout", "fa2_bwd_gqa_workspace_bytes", "fa2_status_string",
+            "fa2_last_hip_error")
 
 _lib = None
 _lock = threading.Lock()
@@ -71,6 +72,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.fa2_bwd_dropout.restype = i
         lib.fa2_bwd_workspace_bytes.argtypes = [i, i, i, i]
         lib.fa2_bwd_workspace_bytes.restype = sz
+        lib.fa2_bwd_gqa_workspace_bytes.argtypes = [i, i, i, i, i]
+        lib.fa2_bwd_gqa_workspace_bytes.restype = sz
         lib.fa2_status_string.argtypes = [i]
         lib.fa2_status_string.restype = ctypes.c_char_p
         lib.fa2_last_hip_error.argtypes = []
@@ -184,8 +187,13 @@ def fwd_kvpacked(q: torch.Tensor, kv: torch.Tensor, causal: bool = False,
     return fwd(q, kv[:, 0], kv[:, 1], causal=causal, scale=scale)
 
 
-def bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
-    return int(load_library().fa2_bwd_workspace_bytes(B, H, N, d))
+def bwd_workspace_bytes(B: int, H: int, N: int, d: int, Hkv: int | None = None) -> int:
+    """Backward workspace bytes; with Hkv < H the size that lets grouped heads split their
+    dK/dV work (fa2_bwd_gqa_workspace_bytes)."""
+    lib = load_library()
+    if Hkv is None or Hkv == H:
+        return int(lib.fa2_bwd_workspace_bytes(B, H, N, d))
+    return int(lib.fa2_bwd_gqa_workspace_bytes(B, H, Hkv, N, d))
 
 
 def bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None,
@@ -210,7 +218,8 @@ def bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None,
         raise ValueError("dk and dv must have the layout of k and v")
     ws_bytes = bwd_workspace_bytes(B, H, N, d)
     if workspace is None:
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+        full = bwd_workspace_bytes(B, H, N, d, Hkv)
+        workspace = torch.empty(max(full, 1), dtype=torch.uint8, device=dev)
     if workspace.device != dev or workspace.numel() * workspace.element_size() < ws_bytes:
         raise ValueError("workspace too small or on another device")
     s = default_scale(d) if scale is None else float(scale)

@@ -238,3 +238,41 @@ def test_dropout_validation():
     # empty problems stay no-ops
     assert lib.fa2_fwd_dropout(None, None, None, None, None, 2, 8, 2, 0, d, 0, 1, 0.125, 0.5, 1,
                                2, None) == ops.FA2_OK
+
+
+def _split_model(B, H, Hkv, N, d):
+    """The rule fa2_bwd_gqa uses: split a group's dK/dV work only while (key blocks x B x Hkv)
+    is under 512 workgroups, by the smallest divisor of the group size that reaches 512 (else
+    the group size)."""
+    G = H // Hkv
+    kb = -(-N // (64 if d == 256 else 128))
+    base = kb * B * Hkv
+    if G <= 1 or base >= 512:
+        return 1
+    for s in range(2, G):
+        if G % s == 0 and base * s >= 512:
+            return s
+    return G
+
+
+@pytest.mark.parametrize("B,H,Hkv,N,d", [(4, 16, 4, 2048, 128), (1, 32, 4, 2048, 128),
+                                         (8, 32, 8, 4096, 128), (2, 8, 2, 150, 64),
+                                         (1, 64, 8, 4096, 256), (2, 12, 4, 1000, 64),
+                                         (3, 6, 6, 700, 128), (1, 8, 1, 64, 128)])
+def test_grouped_workspace_size(B, H, Hkv, N, d):
+    """fa2_bwd_gqa_workspace_bytes = the plain workspace plus 2 * parts * B*Hkv*N*d fp32
+    partial sums (rounded up to 256 bytes) when the groups are split."""
+    lib = _lib()
+    base = lib.fa2_bwd_workspace_bytes(B, H, N, d)
+    s = _split_model(B, H, Hkv, N, d)
+    extra = 0 if s == 1 else -(-(2 * s * B * Hkv * N * d * 4) // 256) * 256
+    assert lib.fa2_bwd_gqa_workspace_bytes(B, H, Hkv, N, d) == base + extra
+    assert ops.bwd_workspace_bytes(B, H, N, d, Hkv) == base + extra
+
+
+def test_grouped_workspace_size_invalid():
+    lib = _lib()
+    assert lib.fa2_bwd_gqa_workspace_bytes(2, 8, 3, 64, 128) == 0   # 3 does not divide 8
+    assert lib.fa2_bwd_gqa_workspace_bytes(2, 8, 0, 64, 128) == 0
+    assert lib.fa2_bwd_gqa_workspace_bytes(2, 8, 2, 0, 128) == 0    # empty
+    assert lib.fa2_bwd_gqa_workspace_bytes(2, 8, 2, 64, 96) == 0    # unsupported d

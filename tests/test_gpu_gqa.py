@@ -112,3 +112,35 @@ def test_grouped_heads_full_size_step():
                                 ("dk", dk[b:b + 1, kvh:kvh + 1], dk_ref),
                                 ("dv", dv[b:b + 1, kvh:kvh + 1], dv_ref)):
             assert_grad_close(bf16_to_f64(got), want, f"b{b} kv{kvh} {name}")
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_split_groups_match_whole_groups(d):
+    """With the grouped workspace the dK/dV work of each group is split over several
+    workgroups (fp32 partial sums added in a fixed order); with the plain workspace it is not.
+    Both agree with the oracle, agree with each other to fp32 summation order, leave dQ
+    unchanged, and the split path gives the same bits on a second run."""
+    fa2 = _fa2()
+    from exact_io_aware_42_amd import ops
+    B, H, Hkv, N = 1, 8, 2, 300
+    assert ops.bwd_workspace_bytes(B, H, N, d, Hkv) > ops.bwd_workspace_bytes(B, H, N, d)
+    bq, bdo = normal_bf16((B, H, N, d), 9700 + d), normal_bf16((B, H, N, d), 9703 + d)
+    bk, bv = normal_bf16((B, Hkv, N, d), 9701 + d), normal_bf16((B, Hkv, N, d), 9702 + d)
+    q, k, v, do = (to_dev(b_) for b_ in (bq, bk, bv, bdo))
+    o, lse = fa2.fwd(q, k, v, causal=True)
+    g_split = fa2.bwd(q, k, v, o, do, lse, causal=True)
+    g_split2 = fa2.bwd(q, k, v, o, do, lse, causal=True)
+    small = torch.empty(ops.bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
+    g_whole = fa2.bwd(q, k, v, o, do, lse, causal=True, workspace=small)
+    torch.cuda.synchronize()
+    for a_, b_ in zip(g_split, g_split2):
+        assert torch.equal(a_.view(torch.int16), b_.view(torch.int16))
+    assert torch.equal(g_split[0].view(torch.int16), g_whole[0].view(torch.int16))
+    for a_, b_ in zip(g_split[1:], g_whole[1:]):
+        torch.testing.assert_close(a_.float(), b_.float(), rtol=0,
+                                   atol=1e-2 * b_.float().abs().max().item())
+    _, _, dq_ref, dk_ref, dv_ref = _oracle(bq, bk, bv, bdo, True, default_scale(d))
+    for name, got, want in (("dq", g_split[0], dq_ref), ("dk", g_split[1], dk_ref),
+                            ("dv", g_split[2], dv_ref), ("dk whole", g_whole[1], dk_ref),
+                            ("dv whole", g_whole[2], dv_ref)):
+        assert_grad_close(bf16_to_f64(got), want, f"d{d} {name}")
