@@ -172,8 +172,9 @@ size_t fa2_bwd_gqa_workspace_bytes(int B, int H, int Hkv, int N, int d) {
 
 namespace {
 
-// Grouped heads: split the dK/dV work of each group when the workspace holds the partial sums
-// (fa2_bwd_gqa_workspace_bytes); with the smaller workspace the groups stay whole.
+// Split the dK/dV work of each (key block, K/V head) pair when the problem is too small to fill
+// the chip and the workspace holds the partial sums (fa2_bwd_gqa_workspace_bytes); with the
+// smaller workspace nothing is split.
 void set_kv_split(fa2::BwdArgs* a, void* workspace, size_t workspace_bytes) {
   const int split = fa2::dkdv_split(a->B, a->H, a->Hkv, a->N, a->d);
   if (split > 1 &&
@@ -235,6 +236,7 @@ fa2_status fa2_bwd(const void* q, const void* k, const void* v, const void* o, c
                                  B, H, N, d, causal, softmax_scale, stream, &a, &empty);
   if (st != FA2_OK || empty) return st;
   if (!all_ok({q, k, v, o, dout, lse, dq, dk, dv})) return FA2_ERR_INVALID_ARGUMENT;
+  set_kv_split(&a, workspace, workspace_bytes);
   return from_hip(fa2::launch_bwd(a));
 }
 

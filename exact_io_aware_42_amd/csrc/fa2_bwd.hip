@@ -229,16 +229,16 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
   // causal: key block 0 sees every query tile, so ascending order is longest first
   const TileCoord tc = schedule_tile<CAUSAL ? Order::kLongAscending : Order::kHeadMajor>(
       blockIdx.x, n_kblocks, bh_count);
-  // tc.bh = (batch * Hkv + K/V head) * split + part; the part's query heads are
-  // qh0 .. qh0 + gsz - 1, and their contributions to dK, dV are summed here in order (split > 1:
-  // into fp32 partial sums that fa2_bwd_kv_reduce_kernel adds).
+  // tc.bh = (batch * Hkv + K/V head) * split + part. The query heads sharing this K/V head
+  // are qh0 .. qh0 + group - 1; their (head, query tile) steps are summed here in order, part
+  // sj taking the sj-th of `split` equal ranges of them (split > 1: into fp32 partial sums that
+  // fa2_bwd_kv_reduce_kernel adds).
   const int sj = tc.bh % split;
   const int bhkv = tc.bh / split;
-  const int gsz = group / split;
   const int n_kvheads = n_qheads / group;
   const int b_idx = bhkv / n_kvheads;
   const int kvh = bhkv - b_idx * n_kvheads;
-  const int qh0 = b_idx * n_qheads + kvh * group + sj * gsz;
+  const int qh0 = b_idx * n_qheads + kvh * group;
   const size_t head_off =  // K, V, dK, dV
       (size_t)b_idx * (size_t)kv_bstride + (size_t)kvh * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
@@ -276,9 +276,12 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
 
   const int n_qt = (N + kKvBQ - 1) / kKvBQ;
   const int qt_begin = CAUSAL ? key_b0 / kKvBQ : 0;
-  // steps t = 0 .. group*nt - 1 walk query tile qt_begin + t % nt of query head qh0 + t / nt
+  // step T = 0 .. group*nt - 1 walks query tile qt_begin + T % nt of query head qh0 + T / nt;
+  // this part runs T = t_begin + t for t = 0 .. n_steps - 1
   const int nt = n_qt - qt_begin;
-  const int n_steps = gsz * nt;
+  const long long n_all = (long long)group * nt;
+  const int t_begin = (int)(n_all * sj / split);
+  const int n_steps = (int)(n_all * (sj + 1) / split) - t_begin;
   const TileLoader<D, kKvThreads> ld(wave, lane);
   // per-lane read offsets within a stage for this wave's query half: row-wise Q/dO fragments
   // (rows 32hq + kmap(l32)) and transposing reads (k-steps t = 2hq + hf)
@@ -294,8 +297,8 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
   }
 
   auto load_stage = [&](int t, int stage) {
-    const int gi = t / nt;
-    const int it = qt_begin + (t - gi * nt);
+    const int gi = (t_begin + t) / nt;
+    const int it = qt_begin + (t_begin + t - gi * nt);
     const size_t qoff = (size_t)(qh0 + gi) * (size_t)N * D;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + qoff, head_bytes);
     const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dout + qoff, head_bytes);
@@ -334,7 +337,7 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
   auto step = [&](auto stage_c, int t) {
     constexpr int stage = decltype(stage_c)::value;
     if (t + 1 < n_steps) load_stage(t + 1, stage ^ 1);
-    const int it = qt_begin + t % nt;
+    const int it = qt_begin + (t_begin + t) % nt;
     const int q0 = it * kKvBQ + 32 * hq;  // this wave's 32 queries
     // every query of the half precedes every key of the wave: fully masked
     const bool skip = CAUSAL && (q0 + 31 < key_w0);
@@ -508,11 +511,10 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
   // tc.bh = (batch * Hkv + K/V head) * split + part, as in the d <= 128 kernel
   const int sj = tc.bh % split;
   const int bhkv = tc.bh / split;
-  const int gsz = group / split;
   const int n_kvheads = n_qheads / group;
   const int b_idx = bhkv / n_kvheads;
   const int kvh = bhkv - b_idx * n_kvheads;
-  const int qh0 = b_idx * n_qheads + kvh * group + sj * gsz;
+  const int qh0 = b_idx * n_qheads + kvh * group;
   const size_t head_off =  // K, V, dK, dV
       (size_t)b_idx * (size_t)kv_bstride + (size_t)kvh * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
@@ -550,15 +552,18 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
 
   const int n_qt = (N + kKv256BQ - 1) / kKv256BQ;
   const int qt_begin = CAUSAL ? key_b0 / kKv256BQ : 0;
-  // steps t = 0 .. group*nt - 1 walk query tile qt_begin + t % nt of query head qh0 + t / nt
+  // step T = 0 .. group*nt - 1 walks query tile qt_begin + T % nt of query head qh0 + T / nt;
+  // this part runs T = t_begin + t for t = 0 .. n_steps - 1
   const int nt = n_qt - qt_begin;
-  const int n_steps = gsz * nt;
+  const long long n_all = (long long)group * nt;
+  const int t_begin = (int)(n_all * sj / split);
+  const int n_steps = (int)(n_all * (sj + 1) / split) - t_begin;
   const TileLoader<D, kThreads, kKv256BQ> ld(wave, lane);
   const TileReads<D> rd_off(lane);
 
   auto load_stage = [&](int t, int stage) {
-    const int gi = t / nt;
-    const int it = qt_begin + (t - gi * nt);
+    const int gi = (t_begin + t) / nt;
+    const int it = qt_begin + (t_begin + t - gi * nt);
     const size_t qoff = (size_t)(qh0 + gi) * (size_t)N * D;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + qoff, head_bytes);
     const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dout + qoff, head_bytes);
@@ -593,7 +598,7 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
   auto step = [&](auto stage_c, int t) {
     constexpr int stage = decltype(stage_c)::value;
     if (t + 1 < n_steps) load_stage(t + 1, stage ^ 1);
-    const int it = qt_begin + t % nt;
+    const int it = qt_begin + (t_begin + t) % nt;
     const int q0 = it * kKv256BQ;
     // every query of the tile precedes every key of the wave: fully masked
     const bool skip = CAUSAL && (q0 + kKv256BQ - 1 < key_w0);

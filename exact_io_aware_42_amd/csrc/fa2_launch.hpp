@@ -51,29 +51,29 @@ struct BwdArgs {
   bool dropout = false;  // as in FwdArgs
   uint32_t drop_k0 = 0, drop_k1 = 0, drop_thr = 0;
   float drop_scale = 1.f;
-  // grouped K/V heads: with kv_split > 1 the query heads of a group are split over kv_split
-  // dK/dV workgroups per key block, which write fp32 partial sums (dK, scaled, then dV, each
+  // with kv_split > 1 the steps of each (key block, K/V head) pair are split over kv_split
+  // dK/dV workgroups, which write fp32 partial sums (dK, scaled, then dV, each
   // [kv_split][B*Hkv][N][d]) to kv_part; a reduction adds them in split order
   int kv_split = 1;
   float* kv_part = nullptr;
   hipStream_t stream;
 };
 
-// Query heads per group share one dK/dV workgroup per (key block, K/V head) unless that leaves
-// fewer than kDkdvMinWorkgroups workgroups (two per CU of a 256-CU part): then the smallest
-// divisor s of the group size that reaches it (or the group size itself) splits each group
-// into s parts.
+// The (query head, query tile) steps of a (key block, K/V head) pair run in one dK/dV
+// workgroup unless the pairs alone give fewer than kDkdvMinWorkgroups workgroups (two per CU
+// of a 256-CU part): then each pair's steps are cut into `split` equal ranges, the smallest
+// count from 2 to 8 that reaches it (else 8), whose partial sums are added afterwards.
 constexpr long long kDkdvMinWorkgroups = 512;
+constexpr int kDkdvMaxSplit = 8;
 inline int dkdv_split(int B, int H, int Hkv, int N, int d) {
-  const int G = H / Hkv;
+  (void)H;
   const long long kblocks = (N + (d == 256 ? 64 : 128) - 1) / (d == 256 ? 64 : 128);
   const long long base = kblocks * B * Hkv;
-  if (G <= 1 || base >= kDkdvMinWorkgroups) return 1;
-  for (int s = 2; s < G; ++s)
-    if (G % s == 0 && base * s >= kDkdvMinWorkgroups) return s;
-  return G;
+  if (base >= kDkdvMinWorkgroups) return 1;
+  for (int s = 2; s < kDkdvMaxSplit; ++s)
+    if (base * s >= kDkdvMinWorkgroups) return s;
+  return kDkdvMaxSplit;
 }
-
 hipError_t launch_fwd(const FwdArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);  // dQ (also D and LSE*log2(e)), then dK/dV
 hipError_t launch_bwd_pre(const BwdArgs& a);

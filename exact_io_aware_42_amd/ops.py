@@ -188,10 +188,10 @@ def fwd_kvpacked(q: torch.Tensor, kv: torch.Tensor, causal: bool = False,
 
 
 def bwd_workspace_bytes(B: int, H: int, N: int, d: int, Hkv: int | None = None) -> int:
-    """Backward workspace bytes; with Hkv < H the size that lets grouped heads split their
-    dK/dV work (fa2_bwd_gqa_workspace_bytes)."""
+    """Backward workspace bytes: the minimum (fa2_bwd_workspace_bytes), or with Hkv given the
+    size that lets small problems split their dK/dV work (fa2_bwd_gqa_workspace_bytes)."""
     lib = load_library()
-    if Hkv is None or Hkv == H:
+    if Hkv is None:
         return int(lib.fa2_bwd_workspace_bytes(B, H, N, d))
     return int(lib.fa2_bwd_gqa_workspace_bytes(B, H, Hkv, N, d))
 

@@ -121,19 +121,21 @@ fa2_status fa2_bwd_preprocess(const void* o, const void* dout, const float* lse,
  * all). dK and dV sum the contributions of the query heads of a group in a fixed order
  * (deterministic). kv_batch_stride must be a multiple of 8 and at least Hkv*N*d. Otherwise as
  * fa2_fwd / fa2_bwd (which are these calls with Hkv = H and kv_batch_stride = H*N*d).
- * When the (key block, K/V head) pairs alone are too few to fill the chip and the workspace
- * holds fa2_bwd_gqa_workspace_bytes(...) bytes, fa2_bwd_gqa (and fa2_bwd_dropout) split each
- * group's query heads over several dK/dV workgroups that write fp32 partial sums into the
- * workspace, then add them in a fixed order (deterministic; the sum order differs from the
+ * Small problems: when the (key block of 128 keys, 64 at d = 256; K/V head) pairs are fewer
+ * than 512 and the workspace holds fa2_bwd_gqa_workspace_bytes(...) bytes, fa2_bwd,
+ * fa2_bwd_gqa and fa2_bwd_dropout cut each pair's (query head, query tile) steps into 2..8
+ * equal ranges run by separate dK/dV workgroups, which write fp32 partial sums into the
+ * workspace; a last pass adds them in a fixed order (deterministic; the order differs from the
  * unsplit path's, so results may differ from it in the last bits). With only
- * fa2_bwd_workspace_bytes(...) bytes the groups are never split. */
+ * fa2_bwd_workspace_bytes(...) bytes nothing is split. */
 fa2_status fa2_fwd_gqa(const void* q, const void* k, const void* v, void* o, float* lse,
                        int B, int H, int Hkv, int N, int d, long long kv_batch_stride,
                        int causal, float softmax_scale, hipStream_t stream);
 
-/* Workspace bytes for fa2_bwd_gqa / fa2_bwd_dropout with Hkv K/V heads: fa2_bwd_workspace_bytes
- * plus, when the groups are split, 2 * parts * B*Hkv*N*d fp32 partial sums (rounded up to 256
- * bytes). 0 for invalid or empty sizes or Hkv not dividing H. */
+/* Workspace bytes that let fa2_bwd (Hkv = H), fa2_bwd_gqa and fa2_bwd_dropout split the dK/dV
+ * work of small problems (above): fa2_bwd_workspace_bytes plus, when they split into `parts`,
+ * 2 * parts * B*Hkv*N*d fp32 partial sums (rounded up to 256 bytes). 0 for invalid or empty
+ * sizes or Hkv not dividing H. */
 size_t fa2_bwd_gqa_workspace_bytes(int B, int H, int Hkv, int N, int d);
 
 fa2_status fa2_bwd_gqa(const void* q, const void* k, const void* v, const void* o,

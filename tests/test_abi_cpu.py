@@ -241,27 +241,27 @@ def test_dropout_validation():
 
 
 def _split_model(B, H, Hkv, N, d):
-    """The rule fa2_bwd_gqa uses: split a group's dK/dV work only while (key blocks x B x Hkv)
-    is under 512 workgroups, by the smallest divisor of the group size that reaches 512 (else
-    the group size)."""
-    G = H // Hkv
+    """The rule the backward uses: split each (key block, K/V head) pair's steps only while
+    those pairs number under 512, into the smallest count from 2 to 8 that reaches 512 (else
+    8)."""
     kb = -(-N // (64 if d == 256 else 128))
     base = kb * B * Hkv
-    if G <= 1 or base >= 512:
+    if base >= 512:
         return 1
-    for s in range(2, G):
-        if G % s == 0 and base * s >= 512:
+    for s in range(2, 8):
+        if base * s >= 512:
             return s
-    return G
+    return 8
 
 
 @pytest.mark.parametrize("B,H,Hkv,N,d", [(4, 16, 4, 2048, 128), (1, 32, 4, 2048, 128),
                                          (8, 32, 8, 4096, 128), (2, 8, 2, 150, 64),
                                          (1, 64, 8, 4096, 256), (2, 12, 4, 1000, 64),
-                                         (3, 6, 6, 700, 128), (1, 8, 1, 64, 128)])
+                                         (3, 6, 6, 700, 128), (1, 8, 1, 64, 128),
+                                         (1, 8, 8, 2048, 128), (4, 16, 16, 2048, 128)])
 def test_grouped_workspace_size(B, H, Hkv, N, d):
     """fa2_bwd_gqa_workspace_bytes = the plain workspace plus 2 * parts * B*Hkv*N*d fp32
-    partial sums (rounded up to 256 bytes) when the groups are split."""
+    partial sums (rounded up to 256 bytes) when the dK/dV work is split (Hkv = H included)."""
     lib = _lib()
     base = lib.fa2_bwd_workspace_bytes(B, H, N, d)
     s = _split_model(B, H, Hkv, N, d)

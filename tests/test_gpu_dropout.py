@@ -146,7 +146,7 @@ def test_p_zero_equals_plain_path_bitwise():
                                  default_scale(d), 0.0, 99, 7, None)
         assert st == 0
         g2 = [torch.empty_like(q) for _ in range(3)]
-        ws = torch.empty(fa2.bwd_workspace_bytes(*shape), dtype=torch.uint8, device=q.device)
+        ws = torch.empty(fa2.bwd_workspace_bytes(*shape, H), dtype=torch.uint8, device=q.device)
         st = lib.fa2_bwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                  do.data_ptr(), lse.data_ptr(), *(g.data_ptr() for g in g2),
                                  ws.data_ptr(), ws.numel(), B, H, H, N, d, H * N * d,
