@@ -35,6 +35,13 @@ def check_against_oracle(bq, bk, bv, bdo, causal, scale, what):
     dq, dk, dv = run_bwd(bq, bk, bv, bdo, causal, scale)
     ref = attention_backward(bf16_bits_to_f64(bq), bf16_bits_to_f64(bk), bf16_bits_to_f64(bv),
                              bf16_bits_to_f64(bdo), causal=causal, scale=scale)
+    if bq.shape[2] == 1:
+        # one key: dQ = dK = 0 exactly (P = 1), so no relative bound applies; the GPU is left
+        # with the rounding of D = dO . O against dP = dO . V (one sum in two orders)
+        tiny = 1e-3 * np.abs(bf16_bits_to_f64(bdo)).max()
+        assert np.abs(bf16_to_f64(dq)).max() <= tiny and np.abs(bf16_to_f64(dk)).max() <= tiny
+        assert_grad_close(bf16_to_f64(dv), ref[2], f"{what} dv")
+        return
     for name, got, want in zip(("dq", "dk", "dv"), (dq, dk, dv), ref):
         assert_grad_close(bf16_to_f64(got), want, f"{what} {name}")
 

@@ -144,3 +144,39 @@ def test_split_groups_match_whole_groups(d):
                             ("dv", g_split[2], dv_ref), ("dk whole", g_whole[1], dk_ref),
                             ("dv whole", g_whole[2], dv_ref)):
         assert_grad_close(bf16_to_f64(got), want, f"d{d} {name}")
+
+
+SPLIT_CASES = [((1, 8, 1, 77, 64), True), ((1, 16, 2, 257, 128), False),
+               ((2, 16, 16, 130, 128), True), ((1, 6, 3, 1, 256), True),
+               ((1, 4, 4, 600, 256), False), ((3, 8, 8, 65, 64), True),
+               ((2, 8, 8, 2048, 128), True), ((1, 8, 4, 2048, 64), False)]
+
+
+@pytest.mark.parametrize("dims,causal", SPLIT_CASES,
+                         ids=[f"{b}x{h}/{hk}x{n}x{d}-{'c' if c else 'f'}" for (b, h, hk, n, d), c in SPLIT_CASES])
+def test_split_steps_match_oracle(dims, causal):
+    """Small problems split each (key block, K/V head) pair's steps into parts (here 2, 4 and
+    8, for one K/V head, many heads, a single query, ragged N, both masks): dQ, dK, dV against
+    the oracle."""
+    fa2 = _fa2()
+    from exact_io_aware_42_amd import ops
+    B, H, Hkv, N, d = dims
+    assert ops.bwd_workspace_bytes(B, H, N, d, Hkv) > ops.bwd_workspace_bytes(B, H, N, d)
+    seed = 9900 + H + N + d
+    bq, bdo = normal_bf16((B, H, N, d), seed), normal_bf16((B, H, N, d), seed + 3)
+    bk, bv = normal_bf16((B, Hkv, N, d), seed + 1), normal_bf16((B, Hkv, N, d), seed + 2)
+    print(f"case {dims} causal={causal}", flush=True)
+    q, k, v, do = (to_dev(b_) for b_ in (bq, bk, bv, bdo))
+    o, lse = fa2.fwd(q, k, v, causal=causal)
+    dq, dk, dv = fa2.bwd(q, k, v, o, do, lse, causal=causal)
+    torch.cuda.synchronize()
+    _, _, dq_ref, dk_ref, dv_ref = _oracle(bq, bk, bv, bdo, causal, default_scale(d))
+    if N == 1:
+        # one key: P = 1, so dV is the sum of the group's dO and dQ = dK = 0 up to the rounding
+        # of D = dO . O against dP = dO . V (the same products, summed in another order)
+        assert_grad_close(bf16_to_f64(dv), dv_ref, f"{dims} dv")
+        tiny = 1e-3 * np.abs(bf16_bits_to_f64(bdo)).max()
+        assert np.abs(bf16_to_f64(dq)).max() <= tiny and np.abs(bf16_to_f64(dk)).max() <= tiny
+        return
+    for name, got, want in (("dq", dq, dq_ref), ("dk", dk, dk_ref), ("dv", dv, dv_ref)):
+        assert_grad_close(bf16_to_f64(got), want, f"{dims} {name}")
