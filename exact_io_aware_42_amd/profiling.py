@@ -14,6 +14,10 @@
     # over its kernel-trace duration, from one rocprofv3 --kernel-trace --pmc GRBM_GUI_ACTIVE run
     python -m exact_io_aware_42_amd.profiling clock --dir <rocprofv3 output dir> \
         --out profiles/clock_<workload>.txt --title "..." --cmd "rocprofv3 ..."
+    # SQ counter summary per kernel (median per dispatch over one or more --pmc passes, each
+    # pass its own counter_collection.csv) with the derived busy fractions
+    python -m exact_io_aware_42_amd.profiling counters --csv pass1.csv pass2.csv ... \
+        --out profiles/counters_<workload>.txt --title "..." --cmd "rocprofv3 ..."
     # turn counter CSVs into profiles/traffic_<kernel>_<workload>.txt
     python -m exact_io_aware_42_amd.profiling traffic --kernel fa2_fwd_kernel \\
         --workload w4_full --fetch run_fetch.csv --write run_write.csv \\
@@ -188,6 +192,51 @@ def clock_main(a):
     print(open(a.out).read())
 
 
+# gfx950 part: 8 XCDs of 32 CUs, 4 SIMDs per CU; GRBM_GUI_ACTIVE is summed over the XCDs,
+# SQ_VALU_MFMA_BUSY_CYCLES over the SIMDs (32 per 32x32x16 MFMA), SQ_LDS_IDX_ACTIVE over the
+# CUs, SQ_WAVE_CYCLES and the SQ_WAIT_* / SQ_ACTIVE_INST_* counters over the waves.
+XCDS, CUS, SIMDS_PER_CU = 8, 256, 4
+
+
+def counters_main(a):
+    vals = {}
+    for path in a.csv:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                k = short_name(r["Kernel_Name"])
+                vals.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(
+                    float(r["Counter_Value"]))
+    with open(a.out, "w") as f:
+        f.write(f"# SQ counters per dispatch (median): {a.title}\n")
+        f.write(f"# command: {a.cmd}\n")
+        f.write("# derived: kernel cycles = GRBM_GUI_ACTIVE / 8 (per XCD); MFMA busy = "
+                "SQ_VALU_MFMA_BUSY_CYCLES / (kernel cycles * 1024 SIMDs); LDS active = "
+                "SQ_LDS_IDX_ACTIVE / (kernel cycles * 256 CUs); wait/active shares are of "
+                "SQ_WAVE_CYCLES\n")
+        for k in sorted(vals):
+            m = {c: statistics.median(v) for c, v in vals[k].items()}
+            f.write(f"{k}\n")
+            for c in sorted(m):
+                f.write(f"    {c:28s} {m[c]:.6g}\n")
+            cyc = m.get("GRBM_GUI_ACTIVE", 0) / XCDS
+            if cyc:
+                if "SQ_VALU_MFMA_BUSY_CYCLES" in m:
+                    f.write(f"    -> MFMA busy {m['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc * CUS * SIMDS_PER_CU):.3f}\n")
+                if "SQ_LDS_IDX_ACTIVE" in m:
+                    f.write(f"    -> LDS active {m['SQ_LDS_IDX_ACTIVE'] / (cyc * CUS):.3f}\n")
+            wc = m.get("SQ_WAVE_CYCLES")
+            if wc:
+                for c in ("SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS",
+                          "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS"):
+                    if c in m:
+                        f.write(f"    -> {c} / SQ_WAVE_CYCLES {m[c] / wc:.3f}\n")
+            if m.get("SQ_INSTS_MFMA"):
+                for c in ("SQ_INSTS_VALU", "SQ_INSTS_LDS", "SQ_INSTS_SALU"):
+                    if c in m:
+                        f.write(f"    -> {c} per MFMA {m[c] / m['SQ_INSTS_MFMA']:.2f}\n")
+    print(open(a.out).read())
+
+
 def traffic_main(a):
     fetch = statistics.median(counter_values(a.fetch, "FETCH_SIZE", a.kernel))
     write = statistics.median(counter_values(a.write, "WRITE_SIZE", a.kernel))
@@ -237,6 +286,11 @@ def main(argv=None):
     ck.add_argument("--out", required=True)
     ck.add_argument("--title", required=True)
     ck.add_argument("--cmd", required=True)
+    cn = sub.add_parser("counters")
+    cn.add_argument("--csv", required=True, nargs="+")
+    cn.add_argument("--out", required=True)
+    cn.add_argument("--title", required=True)
+    cn.add_argument("--cmd", required=True)
     t = sub.add_parser("traffic")
     t.add_argument("--kernel", required=True, choices=sorted(KERNEL_SOURCES))
     t.add_argument("--workload", required=True)
@@ -257,6 +311,8 @@ def main(argv=None):
         trace_main(a)
     elif a.sub == "clock":
         clock_main(a)
+    elif a.sub == "counters":
+        counters_main(a)
     else:
         traffic_main(a)
 
