@@ -137,6 +137,22 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_pre_kernel(const uint16_t* _
 }
 
 // ---------------------------------------------------------------------------------------
+// Position in a dK/dV workgroup's walk over (query head, query tile) steps: head qh0 + gi,
+// tile it, advanced one step at a time (no integer division per step).
+struct StepPos {
+  int gi, it;
+  int it0, it_end;
+  __device__ __forceinline__ StepPos(int t, int nt, int qt_begin)
+      : gi(t / nt), it(qt_begin + t % nt), it0(qt_begin), it_end(qt_begin + nt) {}
+  __device__ __forceinline__ void next() {
+    if (++it == it_end) {
+      it = it0;
+      ++gi;
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------------------
 // Dropout in the dK/dV kernels (lane = key, registers = queries). The row keys of a query tile
 // go to LDS with the tile (one hash per query, by one wave); the two lanes of a key pair (lanes
 // 2m', 2m'+1 hold keys 2m, 2m+1) need the same word per query, so each hashes half of its 16
@@ -296,9 +312,12 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
       for (int h = 0; h < 2; ++h) qtr[cb][h] = rd_off.tr_off(cb, 2 * hq, h);
   }
 
+  StepPos ldpos(t_begin, nt, qt_begin);  // the next tile to load (loads go in step order)
   auto load_stage = [&](int t, int stage) {
-    const int gi = (t_begin + t) / nt;
-    const int it = qt_begin + (t_begin + t - gi * nt);
+    (void)t;
+    const int gi = ldpos.gi;
+    const int it = ldpos.it;
+    ldpos.next();
     const size_t qoff = (size_t)(qh0 + gi) * (size_t)N * D;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + qoff, head_bytes);
     const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dout + qoff, head_bytes);
@@ -334,10 +353,12 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
 
   // unrolled by two below, so the ring stage is a compile-time constant (LDS addresses are a
   // base register plus an immediate)
+  StepPos cur(t_begin, nt, qt_begin);  // the tile of the current step
   auto step = [&](auto stage_c, int t) {
     constexpr int stage = decltype(stage_c)::value;
     if (t + 1 < n_steps) load_stage(t + 1, stage ^ 1);
-    const int it = qt_begin + (t_begin + t) % nt;
+    const int it = cur.it;
+    cur.next();
     const int q0 = it * kKvBQ + 32 * hq;  // this wave's 32 queries
     // every query of the half precedes every key of the wave: fully masked
     const bool skip = CAUSAL && (q0 + 31 < key_w0);
@@ -561,9 +582,12 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
   const TileLoader<D, kThreads, kKv256BQ> ld(wave, lane);
   const TileReads<D> rd_off(lane);
 
+  StepPos ldpos(t_begin, nt, qt_begin);  // the next tile to load (loads go in step order)
   auto load_stage = [&](int t, int stage) {
-    const int gi = (t_begin + t) / nt;
-    const int it = qt_begin + (t_begin + t - gi * nt);
+    (void)t;
+    const int gi = ldpos.gi;
+    const int it = ldpos.it;
+    ldpos.next();
     const size_t qoff = (size_t)(qh0 + gi) * (size_t)N * D;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + qoff, head_bytes);
     const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dout + qoff, head_bytes);
@@ -595,10 +619,12 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
   wait_vmem();
   __syncthreads();
 
+  StepPos cur(t_begin, nt, qt_begin);  // the tile of the current step
   auto step = [&](auto stage_c, int t) {
     constexpr int stage = decltype(stage_c)::value;
     if (t + 1 < n_steps) load_stage(t + 1, stage ^ 1);
-    const int it = qt_begin + (t_begin + t) % nt;
+    const int it = cur.it;
+    cur.next();
     const int q0 = it * kKv256BQ;
     // every query of the tile precedes every key of the wave: fully masked
     const bool skip = CAUSAL && (q0 + kKv256BQ - 1 < key_w0);
