@@ -313,16 +313,22 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
   }
 
   StepPos ldpos(t_begin, nt, qt_begin);  // the next tile to load (loads go in step order)
+  // buffer descriptors of the query head being loaded, rebuilt when the walk changes head
+  int ld_head = -1;
+  __amdgpu_buffer_rsrc_t rq, rdo, rl, rd;
   auto load_stage = [&](int t, int stage) {
     (void)t;
     const int gi = ldpos.gi;
     const int it = ldpos.it;
     ldpos.next();
-    const size_t qoff = (size_t)(qh0 + gi) * (size_t)N * D;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + qoff, head_bytes);
-    const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dout + qoff, head_bytes);
-    const __amdgpu_buffer_rsrc_t rl = make_rsrc(lse2 + (size_t)(qh0 + gi) * N, (uint32_t)N * 4);
-    const __amdgpu_buffer_rsrc_t rd = make_rsrc(delta + (size_t)(qh0 + gi) * N, (uint32_t)N * 4);
+    if (gi != ld_head) {
+      ld_head = gi;
+      const size_t qoff = (size_t)(qh0 + gi) * (size_t)N * D;
+      rq = make_rsrc(q + qoff, head_bytes);
+      rdo = make_rsrc(dout + qoff, head_bytes);
+      rl = make_rsrc(lse2 + (size_t)(qh0 + gi) * N, (uint32_t)N * 4);
+      rd = make_rsrc(delta + (size_t)(qh0 + gi) * N, (uint32_t)N * 4);
+    }
     unsigned char* st = smem + stage * STAGE;
     const uint32_t soff = (uint32_t)it * kKvBQ * D * 2;
     ld.load(rq, st, soff);
@@ -583,16 +589,22 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
   const TileReads<D> rd_off(lane);
 
   StepPos ldpos(t_begin, nt, qt_begin);  // the next tile to load (loads go in step order)
+  // buffer descriptors of the query head being loaded, rebuilt when the walk changes head
+  int ld_head = -1;
+  __amdgpu_buffer_rsrc_t rq, rdo, rl, rd;
   auto load_stage = [&](int t, int stage) {
     (void)t;
     const int gi = ldpos.gi;
     const int it = ldpos.it;
     ldpos.next();
-    const size_t qoff = (size_t)(qh0 + gi) * (size_t)N * D;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + qoff, head_bytes);
-    const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dout + qoff, head_bytes);
-    const __amdgpu_buffer_rsrc_t rl = make_rsrc(lse2 + (size_t)(qh0 + gi) * N, (uint32_t)N * 4);
-    const __amdgpu_buffer_rsrc_t rd = make_rsrc(delta + (size_t)(qh0 + gi) * N, (uint32_t)N * 4);
+    if (gi != ld_head) {
+      ld_head = gi;
+      const size_t qoff = (size_t)(qh0 + gi) * (size_t)N * D;
+      rq = make_rsrc(q + qoff, head_bytes);
+      rdo = make_rsrc(dout + qoff, head_bytes);
+      rl = make_rsrc(lse2 + (size_t)(qh0 + gi) * N, (uint32_t)N * 4);
+      rd = make_rsrc(delta + (size_t)(qh0 + gi) * N, (uint32_t)N * 4);
+    }
     unsigned char* st = smem + stage * STAGE;
     const uint32_t soff = (uint32_t)it * kKv256BQ * D * 2;
     ld.load(rq, st, soff);
