@@ -180,3 +180,16 @@ def test_empty_problems_are_no_ops(shape):
             assert g.shape == shape
     assert fa2.bwd_workspace_bytes(*shape) == 0
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_long_single_head_split(causal):
+    """One head of N = 8192 at d = 128: few (key block, head) pairs, so the dK/dV work is split
+    (8 parts) and a workgroup walks 64+ query tiles; every element of every gradient against
+    the oracle."""
+    fa2 = _fa2()
+    shape = (1, 1, 8192, 128)
+    assert fa2.bwd_workspace_bytes(*shape, 1) > fa2.bwd_workspace_bytes(*shape)
+    bq, bk, bv, bdo = (normal_bf16(shape, 8900 + t) for t in range(4))
+    print(f"N=8192 causal={causal}", flush=True)
+    check_against_oracle(bq, bk, bv, bdo, causal, default_scale(128), f"N8192 causal={causal}")
