@@ -125,10 +125,10 @@ def _kv_layout(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
     for t, nm in ((k, "k"), (v, "v")):
         if not isinstance(t, torch.Tensor) or t.dim() != 4:
             raise ValueError(f"{nm} must be a [B, Hkv, N, d] tensor")
-    if q.numel() == 0:  # empty problem: nothing is read (the library returns at once)
-        return H, H * N * d
         if t.device != q.device or t.dtype != torch.bfloat16:
             raise ValueError(f"{nm} must be bfloat16 on {q.device}")
+    if q.numel() == 0:  # empty problem: nothing is read (the library returns at once)
+        return H, H * N * d
     Hkv = k.shape[1]
     if tuple(k.shape) != (B, Hkv, N, d) or tuple(v.shape) != (B, Hkv, N, d):
         raise ValueError(f"k, v must be [B, Hkv, N, d] = [{B}, Hkv, {N}, {d}]")

@@ -191,3 +191,18 @@ def test_invalid_arguments_raise():
     q = to_dev(normal_bf16((1, 1, 16, 64), 1))
     with pytest.raises(fa2.FA2Error, match="INVALID"):
         fa2.fwd(q, q, q, scale=float("nan"))
+    # K/V checks in the binding happen before any library call
+    k16 = q.to(torch.float16)
+    with pytest.raises(ValueError, match="bfloat16"):
+        fa2.fwd(q, k16, q)
+    with pytest.raises(ValueError, match="bfloat16"):
+        fa2.fwd(q, q, q.cpu())
+    q4 = to_dev(normal_bf16((1, 4, 16, 64), 2))
+    k3 = to_dev(normal_bf16((1, 3, 16, 64), 3))
+    with pytest.raises(ValueError, match="multiple"):
+        fa2.fwd(q4, k3, k3)
+    k2 = to_dev(normal_bf16((1, 2, 16, 64), 4))
+    with pytest.raises(ValueError):
+        fa2.fwd(q4, k2, k3)
+    with pytest.raises(ValueError, match="contiguous"):
+        fa2.fwd(q4, q4.transpose(2, 3).contiguous().transpose(2, 3), q4)
