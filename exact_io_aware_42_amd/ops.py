@@ -134,10 +134,13 @@ def _kv_layout(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor):
         raise ValueError(f"k, v must be [B, Hkv, N, d] = [{B}, Hkv, {N}, {d}]")
     if Hkv <= 0 or H % Hkv:
         raise ValueError(f"the {H} query heads must be a multiple of the {Hkv} K/V heads")
+    # strides of size-1 dimensions do not address anything and are not compared
     inner = (N * d, d, 1)
-    if tuple(k.stride()[1:]) != inner or tuple(v.stride()[1:]) != inner or \
-            k.stride(0) != v.stride(0):
-        raise ValueError("k and v need contiguous heads, rows and columns and equal strides")
+    for t in (k, v):
+        if any(t.shape[i + 1] > 1 and t.stride(i + 1) != inner[i] for i in range(3)):
+            raise ValueError("k and v need contiguous heads, rows and columns")
+    if B > 1 and k.stride(0) != v.stride(0):
+        raise ValueError("k and v need equal batch strides")
     kvs = k.stride(0) if B > 1 else Hkv * N * d
     return Hkv, kvs
 
