@@ -78,8 +78,10 @@ size_t fa2_bwd_workspace_bytes(int B, int H, int N, int d);
 /* Backward pass. Inputs: q, k, v, the forward output o and its lse (from fa2_fwd with the
  * same causal flag and scale), and the cotangent dout. Writes dq, dk, dv [B,H,N,d] (bf16,
  * accumulated in fp32). workspace: device buffer of at least fa2_bwd_workspace_bytes(...)
- * bytes, owned by the caller; its contents on entry do not matter and are clobbered.
- * Deterministic (no atomics). Runs fa2_bwd_dq and then fa2_bwd_dkdv below on `stream`. */
+ * bytes, owned by the caller; its contents on entry do not matter and are clobbered. With
+ * fa2_bwd_gqa_workspace_bytes(B, H, H, N, d) bytes, small problems split their dK/dV work (see
+ * fa2_bwd_gqa). Deterministic (no atomics). Runs fa2_bwd_dq and then the dK/dV stage on
+ * `stream`. */
 fa2_status fa2_bwd(const void* q, const void* k, const void* v, const void* o,
                    const void* dout, const float* lse, void* dq, void* dk, void* dv,
                    void* workspace, size_t workspace_bytes,
@@ -87,7 +89,9 @@ fa2_status fa2_bwd(const void* q, const void* k, const void* v, const void* o,
                    hipStream_t stream);
 
 /* The stages of fa2_bwd, for callers that schedule or time them separately (fa2_bwd_dq
- * followed by fa2_bwd_dkdv gives fa2_bwd's results bit for bit). All take the same workspace.
+ * followed by fa2_bwd_dkdv gives the results of fa2_bwd with a workspace of
+ * fa2_bwd_workspace_bytes bytes bit for bit; the stages never split). All take the same
+ * workspace.
  *
  * fa2_bwd_dq: dq [B,H,N,d] (bf16) from q, k, v, o, dout and lse. Parallel over blocks of 128
  *   queries; recomputes P and dP block by block, so no atomics are needed. It also fills the
