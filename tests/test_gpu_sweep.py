@@ -1,0 +1,71 @@
+"""A seeded sweep over the whole interface: random shapes (ragged N from 1 up, every head
+dimension, one to four query heads per K/V head, both masks), with and without dropout,
+through fwd/bwd (which split small problems' dK/dV work) against the CPU float64 oracle.
+Bounds as in the other parity tests: the bf16 rounding bound for O (it covers dropout's
+1/P(keep) scale), 1e-3 for LSE, 2e-2 * max|g| per gradient; single-key heads by their closed
+form."""
+import numpy as np
+import pytest
+import torch
+
+from exact_io_aware_42_amd.inputs import bf16_bits_to_f64, default_scale, normal_bf16
+from oracle import attention_backward_dropout, attention_forward_dropout
+
+from gpu_util import assert_fwd_within_rounding_bound, assert_grad_close, bf16_to_f64, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _cases(n=36, seed=20261202):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        d = int(rng.choice([64, 128, 256]))
+        hkv = int(rng.integers(1, 4))
+        g = int(rng.choice([1, 2, 4]))
+        b = int(rng.integers(1, 3))
+        nmax = 300 if d == 256 else 700
+        N = int(rng.integers(1, nmax)) if i % 6 else int(rng.integers(1, 4))
+        causal = bool(rng.integers(0, 2))
+        p = float(np.float32(rng.choice([0.0, 0.0, 0.2])))
+        out.append((b, hkv * g, hkv, N, d, causal, p, 40000 + i))
+    return out
+
+
+CASES = _cases()
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}x{c[1]}/{c[2]}x{c[3]}x{c[4]}-{'c' if c[5] else 'f'}-p{c[6]:.1f}" for c in CASES])
+def test_sweep(case):
+    import exact_io_aware_42_amd as fa2
+    B, H, Hkv, N, d, causal, p, seed = case
+    G = H // Hkv
+    print(f"case {case}", flush=True)
+    bq, bdo = normal_bf16((B, H, N, d), seed), normal_bf16((B, H, N, d), seed + 3)
+    bk, bv = normal_bf16((B, Hkv, N, d), seed + 1), normal_bf16((B, Hkv, N, d), seed + 2)
+    q, k, v, do = (to_dev(x) for x in (bq, bk, bv, bdo))
+    kw = dict(dropout_p=p, seed=seed, offset=7) if p else {}
+    o, lse = fa2.fwd(q, k, v, causal=causal, **kw)
+    dq, dk, dv = fa2.bwd(q, k, v, o, do, lse, causal=causal, **kw)
+    torch.cuda.synchronize()
+    q64, k64, v64, do64 = (bf16_bits_to_f64(x) for x in (bq, bk, bv, bdo))
+    kr, vr = np.repeat(k64, G, axis=1), np.repeat(v64, G, axis=1)
+    okw = dict(causal=causal, scale=default_scale(d), p=p, seed=seed, offset=7)
+    o_ref, lse_ref = attention_forward_dropout(q64, kr, vr, **okw)
+    o_abs, _ = attention_forward_dropout(q64, kr, np.abs(vr), **okw)
+    assert_fwd_within_rounding_bound(bf16_to_f64(o), lse.cpu().double().numpy(), o_ref, o_abs,
+                                     lse_ref, str(case))
+    gq, gk, gv = attention_backward_dropout(q64, kr, vr, do64, **okw)
+    gk = gk.reshape(B, Hkv, G, N, d).sum(2)
+    gv = gv.reshape(B, Hkv, G, N, d).sum(2)
+    if N == 1:
+        # one key: dS = P * (Z s dP - D) is 0 in exact arithmetic; the GPU's D uses its bf16 O
+        # (O = Z s v rounded, exact only without dropout), so |dS| <= 2^-8 sum_c |dO_c| |O_c|
+        # (with room for the fp32 sums), and dQ, dK follow by scale * |k| and scale * |q|
+        eps = 2.0 ** -8 * np.sum(np.abs(do64) * np.abs(bf16_to_f64(o)), axis=-1).max()
+        tiny = default_scale(d) * eps * max(np.abs(k64).max(), np.abs(q64).max()) * G + 1e-6
+        assert np.abs(bf16_to_f64(dq)).max() <= tiny and np.abs(bf16_to_f64(dk)).max() <= tiny
+        assert_grad_close(bf16_to_f64(dv), gv, f"{case} dv")
+        return
+    for name, got, want in (("dq", dq, gq), ("dk", dk, gk), ("dv", dv, gv)):
+        assert_grad_close(bf16_to_f64(got), want, f"{case} {name}")
