@@ -106,7 +106,25 @@ def _check_tensor(t: torch.Tensor, name: str, shape, dtype=torch.bfloat16, devic
 
 
 def _stream_ptr(device) -> int:
+    """The current torch stream of `device`. The library launches on the calling thread's
+    current HIP device, so the tensors' device must be the current one."""
+    if device.index is not None and device.index != torch.cuda.current_device():
+        raise ValueError(f"tensors are on {device} but the current device is "
+                         f"cuda:{torch.cuda.current_device()}; call under "
+                         f"torch.cuda.device({device.index})")
     return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ws_check(workspace, device, need: int):
+    """Pointer and size of a workspace: a contiguous buffer on `device` of >= `need` bytes."""
+    if not isinstance(workspace, torch.Tensor) or workspace.device != device:
+        raise ValueError(f"workspace must be a tensor on {device}")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    nbytes = workspace.numel() * workspace.element_size()
+    if nbytes < need:
+        raise ValueError(f"workspace has {nbytes} bytes, needs at least {need}")
+    return workspace.data_ptr(), nbytes
 
 
 def default_scale(d: int) -> float:
@@ -219,16 +237,13 @@ def bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None,
         dv = torch.empty_strided(v.shape, v.stride(), dtype=v.dtype, device=dev)
     if _kv_layout(q, dk, dv) != (Hkv, kvs):
         raise ValueError("dk and dv must have the layout of k and v")
-    ws_bytes = bwd_workspace_bytes(B, H, N, d)
     if workspace is None:
         full = bwd_workspace_bytes(B, H, N, d, Hkv)
         workspace = torch.empty(max(full, 1), dtype=torch.uint8, device=dev)
-    if workspace.device != dev or workspace.numel() * workspace.element_size() < ws_bytes:
-        raise ValueError("workspace too small or on another device")
+    ws_ptr, ws_bytes = _ws_check(workspace, dev, bwd_workspace_bytes(B, H, N, d))
     s = default_scale(d) if scale is None else float(scale)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
-            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), workspace.data_ptr(),
-            workspace.numel() * workspace.element_size())
+            lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), ws_ptr, ws_bytes)
     if dropout_p:
         st = lib.fa2_bwd_dropout(*ptrs, B, H, Hkv, N, d, kvs, int(bool(causal)), s,
                                  float(dropout_p), _u64(seed), _u64(offset), _stream_ptr(dev))
@@ -251,12 +266,8 @@ def bwd_kvpacked(q, kv, o, dout, lse, causal: bool = False, scale: float | None 
     return dq, dkv
 
 
-def _ws(workspace: torch.Tensor, B: int, H: int, N: int, d: int):
-    need = bwd_workspace_bytes(B, H, N, d)
-    nbytes = workspace.numel() * workspace.element_size()
-    if workspace.device.type != "cuda" or nbytes < need:
-        raise ValueError(f"workspace must be a GPU buffer of at least {need} bytes")
-    return workspace.data_ptr(), nbytes
+def _ws(workspace: torch.Tensor, device, B: int, H: int, N: int, d: int):
+    return _ws_check(workspace, device, bwd_workspace_bytes(B, H, N, d))
 
 
 def bwd_preprocess(o, dout, lse, workspace):
@@ -268,7 +279,8 @@ def bwd_preprocess(o, dout, lse, workspace):
     _check_tensor(dout, "dout", (B, H, N, d), device=o.device)
     _check_tensor(lse, "lse", (B, H, N), dtype=torch.float32, device=o.device)
     st = lib.fa2_bwd_preprocess(o.data_ptr(), dout.data_ptr(), lse.data_ptr(),
-                                *_ws(workspace, B, H, N, d), B, H, N, d, _stream_ptr(o.device))
+                                *_ws(workspace, o.device, B, H, N, d), B, H, N, d,
+                                _stream_ptr(o.device))
     _check(st, "fa2_bwd_preprocess")
     return workspace
 
@@ -285,7 +297,7 @@ def bwd_dkdv(q, k, v, dout, workspace, causal=False, scale=None, dk=None, dv=Non
     _check_tensor(dv, "dv", (B, H, N, d), device=q.device)
     s = default_scale(d) if scale is None else float(scale)
     st = lib.fa2_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), dout.data_ptr(),
-                          *_ws(workspace, B, H, N, d), dk.data_ptr(), dv.data_ptr(),
+                          *_ws(workspace, q.device, B, H, N, d), dk.data_ptr(), dv.data_ptr(),
                           B, H, N, d, int(bool(causal)), s, _stream_ptr(q.device))
     _check(st, "fa2_bwd_dkdv")
     return dk, dv
@@ -303,7 +315,7 @@ def bwd_dq(q, k, v, o, dout, lse, workspace, causal=False, scale=None, dq=None):
     _check_tensor(dq, "dq", (B, H, N, d), device=q.device)
     s = default_scale(d) if scale is None else float(scale)
     st = lib.fa2_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                        dout.data_ptr(), lse.data_ptr(), *_ws(workspace, B, H, N, d),
+                        dout.data_ptr(), lse.data_ptr(), *_ws(workspace, q.device, B, H, N, d),
                         dq.data_ptr(), B, H, N, d, int(bool(causal)), s, _stream_ptr(q.device))
     _check(st, "fa2_bwd_dq")
     return dq

@@ -193,3 +193,26 @@ def test_long_single_head_split(causal):
     bq, bk, bv, bdo = (normal_bf16(shape, 8900 + t) for t in range(4))
     print(f"N=8192 causal={causal}", flush=True)
     check_against_oracle(bq, bk, bv, bdo, causal, default_scale(128), f"N8192 causal={causal}")
+
+
+def test_workspace_checks_raise():
+    """The binding rejects a workspace that is too small, not contiguous or not a device tensor
+    before any launch, for fa2_bwd and for the stage calls."""
+    fa2 = _fa2()
+    shape = (1, 2, 100, 64)
+    q, k, v, do = (to_dev(normal_bf16(shape, 8950 + t)) for t in range(4))
+    o, lse = fa2.fwd(q, k, v)
+    need = fa2.bwd_workspace_bytes(*shape)
+    small = torch.empty(need - 1, dtype=torch.uint8, device=q.device)
+    strided = torch.empty(2 * need, dtype=torch.uint8, device=q.device)[::2]
+    host = torch.empty(need, dtype=torch.uint8)
+    for ws in (small, strided, host):
+        with pytest.raises(ValueError):
+            fa2.bwd(q, k, v, o, do, lse, workspace=ws)
+        with pytest.raises(ValueError):
+            fa2.bwd_dq(q, k, v, o, do, lse, ws)
+        with pytest.raises(ValueError):
+            fa2.bwd_dkdv(q, k, v, do, ws)
+        with pytest.raises(ValueError):
+            fa2.bwd_preprocess(o, do, lse, ws)
+    torch.cuda.synchronize()
