@@ -29,7 +29,6 @@ fa2_status check_sizes(int B, int H, int N, int d, float scale, bool* empty, int
     *empty = true;
     return FA2_OK;
   }
-  if (!std::isfinite(scale) || !(scale > 0.0f)) return FA2_ERR_INVALID_ARGUMENT;
   const unsigned long long elems =
       (unsigned long long)B * (unsigned long long)H * (unsigned long long)N * (unsigned long long)d;
   if (elems > (1ull << 46)) return FA2_ERR_INVALID_ARGUMENT;
