@@ -5,9 +5,9 @@
 // Works (Tiled Algorithm)") with the three FlashAttention-2 changes (page "FlashAttention-2
 // paper", section "Three changes"): the grid also splits the query dimension, so one head
 // fills the chip; each wavefront owns 32 query rows and keeps their accumulator, running
-// max and running sums in registers; the rescale by exp(m_old - m_new) is deferred until the
-// running max is exceeded by more than 8 (log2 units) and the 1/l normalisation happens once
-// at the end. Fully masked causal tiles are skipped (page "flashattention-2", "FlashAttention-2
+// max and running sums in registers; the rescale by exp(m_old - m_new) is deferred until a
+// tile's exponentials could exceed 2^8 (no per-tile max is taken until then) and the 1/l
+// normalisation happens once at the end. Fully masked causal tiles are skipped (page "flashattention-2", "FlashAttention-2
 // Improvements Over v1").
 //
 // gfx950 mapping (one workgroup = 4 waves = 128 query rows; key tiles of 64):
@@ -55,7 +55,8 @@ namespace {
 
 constexpr int kFwdBR = 128;
 constexpr int kFwdThreads = 256;
-constexpr float kRescaleThreshold = 8.0f;  // log2 units: exponentials stay <= 2^8
+constexpr float kRescaleSum = 256.0f;  // a lane's partial sum of p per tile stays <= 2^8
+constexpr float kRescaleLog2 = 8.0f;   // so each p stays <= 2^8 (log2 units)
 
 // Key tiles of 64 for d <= 128; of 32 at d = 256, where O^T (128 registers) and the resident
 // Q^T fragments (64) leave room for one 32-key score block only. A K or V tile is 16 KiB
@@ -179,7 +180,7 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
   f32x16_t oacc[S::CB];
 #pragma unroll
   for (int cb = 0; cb < S::CB; ++cb) oacc[cb] = f32x16_t{};
-  float m_run;        // running max of scale*log2(e)*s (stale by < threshold)
+  float m_run;        // running max of scale*log2(e)*s (the row max may exceed it by <= 8)
   float l_f32 = 0.f;  // partial sum of p over this lane's keys
   float l_corr = 0.f; // masked tiles: sum of bf16(p) - p
 
@@ -249,9 +250,7 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
           pk[kb][i] = pack_bf16(p0, p1);
         }
       }
-    const float tile_sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-    l_f32 += tile_sum;
-    return tile_sum;
+    return (acc[0] + acc[1]) + (acc[2] + acc[3]);
   };
   // masked tiles: l_corr += sum of bf16(p) - sum of p (after the PV MFMAs, off their path)
   auto bf16_correction = [&](uint32_t (*pk)[8], float tile_sum) {
@@ -279,18 +278,15 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
       }
     }
   };
-  // deferred rescale: raise the running max only when a tile's max exceeds it by > threshold
-  auto maybe_rescale = [&](float m_tile) {
-    const bool raise = m_tile > m_run + kRescaleThreshold;
-    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-      const float m_new = fmaxf(m_run, m_tile);
-      const float alpha = fast_exp2(m_run - m_new);
-      m_run = m_new;
-      l_f32 *= alpha;
-      l_corr *= alpha;
+  // raise the running max to the tile's max (rows whose max is already above keep alpha = 1)
+  auto rescale_to = [&](float m_tile) {
+    const float m_new = fmaxf(m_run, m_tile);
+    const float alpha = fast_exp2(m_run - m_new);
+    m_run = m_new;
+    l_f32 *= alpha;
+    l_corr *= alpha;
 #pragma unroll
-      for (int cb = 0; cb < S::CB; ++cb) oacc[cb] *= alpha;
-    }
+    for (int cb = 0; cb < S::CB; ++cb) oacc[cb] *= alpha;
   };
 
   // ---- main loop: tile j+1 streams into the other LDS slot while tile j is computed
@@ -312,15 +308,34 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
       const bool masked = tile_needs_mask(j);
       if (masked) scores(slot, true, j, s);
       else scores(slot, false, j, s);
-      const float m_tile = row_max(s);
-      if (first) {
-        m_run = m_tile;  // tile 0 holds key 0, visible to every row: finite
-        first = false;
-      } else {
-        maybe_rescale(m_tile);
-      }
       uint32_t pk[S::KB][8];
-      const float tile_sum = probs(s, pk, j);
+      float tile_sum;
+      if constexpr (S::KB == 2) {
+        // deferred rescale without a max per tile: p is formed against the running max, and
+        // only when some lane's partial sum exceeds 2^8 (so that a single p might) does the
+        // wave take the tile's max, rescale and form p again (d <= 128: the scores stay live
+        // until the check, which the d = 256 register budget has no room for)
+        if (first) {
+          m_run = row_max(s);  // tile 0 holds key 0, visible to every row: finite
+          first = false;
+        }
+        tile_sum = probs(s, pk, j);
+        if (__builtin_amdgcn_ballot_w64(!(tile_sum <= kRescaleSum)) != 0) {
+          rescale_to(row_max(s));
+          tile_sum = probs(s, pk, j);
+        }
+      } else {
+        // d = 256: the tile's max first; rescale when it exceeds the running max by > 8
+        const float m_tile = row_max(s);
+        if (first) {
+          m_run = m_tile;
+          first = false;
+        } else if (__builtin_amdgcn_ballot_w64(m_tile > m_run + kRescaleLog2) != 0) {
+          rescale_to(m_tile);
+        }
+        tile_sum = probs(s, pk, j);
+      }
+      l_f32 += tile_sum;
       // raised priority while this wave issues its PV MFMAs: the other wave on the SIMD then
       // tends to run its softmax VALU work in between (measured +2-6%)
       __builtin_amdgcn_s_setprio(1);
