@@ -150,7 +150,7 @@ fa2_status fa2_fwd_dropout(const void* q, const void* k, const void* v, void* o,
                   stream, dropout_p, seed, offset);
 }
 
-// Workspace layout: D = rowsum(dO * O) [B*H*N floats], then LSE * log2(e) [B*H*N floats],
+// Workspace layout: -D, D = rowsum(dO * O) [B*H*N floats], then LSE * log2(e) [B*H*N floats],
 // the second part starting at a 256-byte boundary.
 static size_t ws_part_bytes(int B, int H, int N) { return round256((size_t)B * H * N * sizeof(float)); }
 

@@ -14,7 +14,7 @@
 // Deterministic (no atomics); the backward runs two kernels, dQ first:
 //   fa2_bwd_dq_kernel    grid over (query block of 128, head, batch): the forward's layout
 //                        (lane = query). It first forms D_i = rowsum(dO_i * O_i) from the
-//                        dO and O rows it loads and stores D and LSE*log2(e) of its queries
+//                        dO and O rows it loads and stores -D and LSE*log2(e) of its queries
 //                        in the workspace; then it recomputes S^T and dP^T per key tile and
 //                        accumulates dQ^T = K^T dS^T.
 //   fa2_bwd_dkdv_kernel  grid over (key block of 128, head, batch): the block's K and V rows
@@ -24,7 +24,8 @@
 //   fa2_bwd_pre_kernel   D and LSE*log2(e) alone (HBM-bound), for callers that want dK/dV
 //                        without dQ.
 // dK/dV and dQ each recompute S and dP; dQ's two recompute GEMMs are the price of avoiding
-// atomic dQ accumulation. Output tiles leave through LDS as whole row segments. With dropout
+// atomic dQ accumulation. Without dropout the dP accumulators start at -D, so dP - D comes
+// out of the MFMAs and dS is one multiply. Output tiles leave through LDS as whole row segments. With dropout
 // (DROP) every kernel regenerates the keep bits it needs from the counter-based hash
 // (fa2_device.hpp); dS = P * (Z * dP / P(keep) - D) and dV takes P * Z / P(keep).
 #include <type_traits>
@@ -107,8 +108,10 @@ __device__ __forceinline__ u32x4_t tr_operand(const unsigned char* tile, int off
 }
 
 // ---------------------------------------------------------------------------------------
-// D = rowsum(dO * O): D/8 lanes per row, 16 bytes each, reduced across the row's lanes. The
-// same pass stores LSE * log2(e), the form the other two kernels subtract inside exp2.
+// D = rowsum(dO * O): D/8 lanes per row, 16 bytes each, reduced across the row's lanes. It is
+// stored negated (-D: the dK/dV kernel starts its dP accumulators there, so dP - D comes out of
+// the MFMAs). The same pass stores LSE * log2(e), the form the other two kernels subtract
+// inside exp2.
 template <int D>
 __global__ __launch_bounds__(kThreads) void fa2_bwd_pre_kernel(const uint16_t* __restrict__ o,
                                                                const uint16_t* __restrict__ dout,
@@ -131,7 +134,7 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_pre_kernel(const uint16_t* _
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
   if (row < rows && c == 0) {
-    delta[row] = acc;
+    delta[row] = -acc;
     lse2[row] = lse[row] * kLog2e;
   }
 }
@@ -374,7 +377,24 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
       const unsigned char* ts = smem + statbase + stage * STATS_STAGE;
       const bool masked = (q0 + 32 > N) || (CAUSAL && q0 < key_w0 + 31);
 
-      f32x16_t s, dp = f32x16_t{};
+      // dP starts at -D of each register's query (without dropout), so the MFMAs leave dP - D;
+      // register i is query q0 + 16(i/8) + 8g + i%8
+      f32x16_t s, dp;
+      if constexpr (DROP) {
+        dp = f32x16_t{};
+      } else {
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const unsigned char* sd = ts + 16 * hf * 4 + kKvBQ * 4;
+          const f32x4_t d0 = *reinterpret_cast<const f32x4_t*>(sd);
+          const f32x4_t d1 = *reinterpret_cast<const f32x4_t*>(sd + 16);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            dp[8 * hf + e] = d0[e];
+            dp[8 * hf + 4 + e] = d1[e];
+          }
+        }
+      }
       if (masked) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -393,8 +413,7 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
         s = mfma32(aq, kf, s);
         dp = mfma32(ad, vf, dp);
       }
-      // P = exp2(s*c - LSE*log2e), dS = P * (dP - D); register i is query
-      // q0 + 16(i/8) + 8g + i%8
+      // P = exp2(s*c - LSE*log2e), dS = P * (dP - D)
       uint32_t pk[8], dsk[8];
       uint32_t dw[2][8];  // dropout: the 16 bits deciding (query of register 8hf + e, my_key)
       if constexpr (DROP) dl.words(ts + 2 * kKvBQ * 4, dw);
@@ -403,22 +422,22 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
         const unsigned char* sl = ts + 16 * hf * 4;  // queries 32hq + 16hf + 8g + (0..7)
         const f32x4_t l0 = *reinterpret_cast<const f32x4_t*>(sl);
         const f32x4_t l1 = *reinterpret_cast<const f32x4_t*>(sl + 16);
-        const f32x4_t d0 = *reinterpret_cast<const f32x4_t*>(sl + kKvBQ * 4);
-        const f32x4_t d1 = *reinterpret_cast<const f32x4_t*>(sl + kKvBQ * 4 + 16);
         float p[8], ds[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float lv = e < 4 ? l0[e] : l1[e - 4];
-          const float dv_ = e < 4 ? d0[e] : d1[e - 4];
           const float pe = fast_exp2(__builtin_fmaf(s[8 * hf + e], scale_log2, -lv));
           if constexpr (DROP) {
-            // kept with its 1/P(keep) scale, or 0
+            // kept with its 1/P(keep) scale, or 0; -D from the workspace
+            const f32x4_t d0 = *reinterpret_cast<const f32x4_t*>(sl + kKvBQ * 4);
+            const f32x4_t d1 = *reinterpret_cast<const f32x4_t*>(sl + kKvBQ * 4 + 16);
+            const float neg_d = e < 4 ? d0[e] : d1[e - 4];
             const float zs = dw[hf][e] >= drop.thr ? drop.scale : 0.f;
             p[e] = pe * zs;
-            ds[e] = pe * (dp[8 * hf + e] * zs - dv_);
+            ds[e] = pe * __builtin_fmaf(dp[8 * hf + e], zs, neg_d);
           } else {
             p[e] = pe;
-            ds[e] = pe * (dp[8 * hf + e] - dv_);
+            ds[e] = pe * dp[8 * hf + e];
           }
         }
 #pragma unroll
@@ -690,13 +709,13 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float lv = e < 4 ? l0[e] : l1[e - 4];
-          const float dv_ = e < 4 ? d0[e] : d1[e - 4];
+          const float neg_d = e < 4 ? d0[e] : d1[e - 4];  // -D
           const float p = fast_exp2(__builtin_fmaf(s[8 * hf + e], scale_log2, -lv));
           if constexpr (DROP) {
             const float zs = dw[hf][e] >= drop.thr ? drop.scale : 0.f;
-            x[e] = dk_wave ? p * (dp[8 * hf + e] * zs - dv_) : p * zs;
+            x[e] = dk_wave ? p * __builtin_fmaf(dp[8 * hf + e], zs, neg_d) : p * zs;
           } else {
-            x[e] = dk_wave ? p * (dp[8 * hf + e] - dv_) : p;
+            x[e] = dk_wave ? p * (dp[8 * hf + e] + neg_d) : p;
           }
         }
 #pragma unroll
@@ -813,9 +832,9 @@ __global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dq_kernel(
   // padded queries get LSE = +inf, hence P = 0
   const float lse_q = valid_q ? lse[(size_t)tc.bh * N + my_q] * kLog2e : INFINITY;
   const float dlt = valid_q ? dsum : 0.f;
-  // D and LSE*log2(e) of this block's queries go to the workspace for the dK/dV kernel
+  // -D and LSE*log2(e) of this block's queries go to the workspace for the dK/dV kernel
   if (DH <= 0 && valid_q && g == 0) {
-    delta[(size_t)tc.bh * N + my_q] = dlt;
+    delta[(size_t)tc.bh * N + my_q] = -dlt;
     lse2[(size_t)tc.bh * N + my_q] = lse_q;
   }
 
@@ -835,6 +854,12 @@ __global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dq_kernel(
   f32x16_t dqacc[CBO];
 #pragma unroll
   for (int cb = 0; cb < CBO; ++cb) dqacc[cb] = f32x16_t{};
+  // without dropout (and for d <= 128, where the 16 registers fit) the dP^T chains start at -D
+  // (all 16 registers of a lane are its query), so the MFMAs leave dP - D
+  constexpr bool kInitD = !DROP && D <= 128;
+  f32x16_t dp_init;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) dp_init[i] = kInitD ? -dlt : 0.f;
 
   load_stage(0, 0);
   wait_vmem();
@@ -861,13 +886,12 @@ __global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dq_kernel(
         } else {
           s[kb] = f32x16_t{};
         }
-        dp[kb] = f32x16_t{};
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
           const u32x4_t ak = *reinterpret_cast<const u32x4_t*>(tk + rd_off.row_off(kb, kk));
           s[kb] = mfma32(ak, qf[kk], s[kb]);
           const u32x4_t av = *reinterpret_cast<const u32x4_t*>(tv + rd_off.row_off(kb, kk));
-          dp[kb] = mfma32(av, dof[kk], dp[kb]);
+          dp[kb] = mfma32(av, dof[kk], kk == 0 ? dp_init : dp[kb]);
         }
       }
       uint32_t dsk[KB][8];
@@ -877,15 +901,18 @@ __global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dq_kernel(
         for (int i = 0; i < 8; ++i) {
           const float p0 = fast_exp2(__builtin_fmaf(s[kb][2 * i], scale_log2, -lse_q));
           const float p1 = fast_exp2(__builtin_fmaf(s[kb][2 * i + 1], scale_log2, -lse_q));
-          float dp0 = dp[kb][2 * i], dp1 = dp[kb][2 * i + 1];
-          if constexpr (DROP) {
+          float dp0 = dp[kb][2 * i], dp1 = dp[kb][2 * i + 1];  // dP - D if kInitD
+          if constexpr (!DROP && !kInitD) {
+            dp0 -= dlt;
+            dp1 -= dlt;
+          } else if constexpr (DROP) {
             // keys j*BC + 32kb + 16(2i/8) + 8g + (2i%8) + 0, 1: dP scaled by Z / P(keep)
             const int key = j * BC + 32 * kb + 16 * ((2 * i) / 8) + 8 * g + (2 * i) % 8;
             const uint32_t w = drop_word(drop_row, (uint32_t)key >> 1);
-            dp0 = (w << 16) >= drop.thr ? dp0 * drop.scale : 0.f;
-            dp1 = w >= drop.thr ? dp1 * drop.scale : 0.f;
+            dp0 = ((w << 16) >= drop.thr ? dp0 * drop.scale : 0.f) - dlt;
+            dp1 = (w >= drop.thr ? dp1 * drop.scale : 0.f) - dlt;
           }
-          dsk[kb][i] = pack_bf16(p0 * (dp0 - dlt), p1 * (dp1 - dlt));
+          dsk[kb][i] = pack_bf16(p0 * dp0, p1 * dp1);
         }
       __builtin_amdgcn_s_setprio(1);  // as in the dK/dV kernel
       // dQ^T += K^T dS^T; MFMA u covers keys 16u .. 16u+15

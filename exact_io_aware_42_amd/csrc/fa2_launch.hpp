@@ -40,7 +40,7 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;  // workspace: D = rowsum(dO * O), fp32 [B, H, N]
+  float* delta;  // workspace: -D, D = rowsum(dO * O), fp32 [B, H, N]
   float* lse2;   // workspace: LSE * log2(e), fp32 [B, H, N]
   int B, H, N, d;
   int Hkv;

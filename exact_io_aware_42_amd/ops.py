@@ -271,7 +271,7 @@ def _ws(workspace: torch.Tensor, device, B: int, H: int, N: int, d: int):
 
 
 def bwd_preprocess(o, dout, lse, workspace):
-    """Fill `workspace` with D = rowsum(dout * o) and LSE * log2(e) (bwd_dq does this too;
+    """Fill `workspace` with -D, D = rowsum(dout * o), and LSE * log2(e) (bwd_dq does this too;
     this stage is for callers that need dK/dV only)."""
     lib = load_library()
     B, H, N, d = o.shape

@@ -71,8 +71,8 @@ fa2_status fa2_fwd(const void* q, const void* k, const void* v, void* o, float* 
                    hipStream_t stream);
 
 /* Bytes of device workspace the backward needs for these sizes: two fp32 [B,H,N] arrays (the
- * row term D = rowsum(dO*O) and LSE*log2(e)), each rounded up to 256 bytes. Returns 0 for
- * invalid or empty sizes. */
+ * row term D = rowsum(dO*O), stored negated as -D, and LSE*log2(e)), each rounded up to 256
+ * bytes. Returns 0 for invalid or empty sizes. */
 size_t fa2_bwd_workspace_bytes(int B, int H, int N, int d);
 
 /* Backward pass. Inputs: q, k, v, the forward output o and its lse (from fa2_fwd with the
@@ -95,8 +95,8 @@ fa2_status fa2_bwd(const void* q, const void* k, const void* v, const void* o,
  *
  * fa2_bwd_dq: dq [B,H,N,d] (bf16) from q, k, v, o, dout and lse. Parallel over blocks of 128
  *   queries; recomputes P and dP block by block, so no atomics are needed. It also fills the
- *   workspace with D_i = sum_c dO_ic O_ic (equal to sum_j P_ij dP_ij, the row term of the
- *   softmax gradient) and LSE_i * log2(e) for fa2_bwd_dkdv. */
+ *   workspace with -D_i, D_i = sum_c dO_ic O_ic (equal to sum_j P_ij dP_ij, the row term of
+ *   the softmax gradient), and LSE_i * log2(e) for fa2_bwd_dkdv. */
 fa2_status fa2_bwd_dq(const void* q, const void* k, const void* v, const void* o,
                       const void* dout, const float* lse, void* workspace,
                       size_t workspace_bytes, void* dq, int B, int H, int N, int d, int causal,
@@ -110,7 +110,7 @@ fa2_status fa2_bwd_dkdv(const void* q, const void* k, const void* v, const void*
                         int B, int H, int N, int d, int causal, float softmax_scale,
                         hipStream_t stream);
 
-/* fa2_bwd_preprocess: fills the workspace with D and LSE * log2(e) (the same values
+/* fa2_bwd_preprocess: fills the workspace with -D and LSE * log2(e) (the same values
  *   fa2_bwd_dq stores, summed in a different order), for callers that need dK/dV only. */
 fa2_status fa2_bwd_preprocess(const void* o, const void* dout, const float* lse,
                               void* workspace, size_t workspace_bytes,

@@ -131,7 +131,7 @@ def test_deterministic_coverage_and_stages(causal, d):
         assert torch.equal(a.view(torch.int16), c.view(torch.int16))
     n = shape[0] * shape[1] * shape[2]
     part = ws.numel() // 2
-    for lo in (0, part):  # D, then LSE * log2(e)
+    for lo in (0, part):  # -D, then LSE * log2(e)
         x = ws[lo: lo + 4 * n].view(torch.float32)
         y = ws2[lo: lo + 4 * n].view(torch.float32)
         torch.testing.assert_close(x, y, rtol=1e-5, atol=1e-5)
@@ -145,7 +145,7 @@ def test_deterministic_coverage_and_stages(causal, d):
 
 
 def test_preprocess_matches_rowsum():
-    """The workspace holds D = rowsum(dO * O) and then (at the next 256-byte boundary)
+    """The workspace holds -D, D = rowsum(dO * O), and then (at the next 256-byte boundary)
     LSE * log2(e)."""
     fa2 = _fa2()
     shape = (2, 2, 130, 128)
@@ -158,7 +158,7 @@ def test_preprocess_matches_rowsum():
     torch.cuda.synchronize()
     n = 2 * 2 * 130
     part = ws.numel() // 2
-    got = ws[: n * 4].view(torch.float32).cpu().double().numpy().reshape(2, 2, 130)
+    got = -ws[: n * 4].view(torch.float32).cpu().double().numpy().reshape(2, 2, 130)
     want = np.sum(bf16_bits_to_f64(bo) * bf16_bits_to_f64(bdo), axis=-1)
     np.testing.assert_allclose(got, want, rtol=1e-5, atol=1e-4)
     got2 = ws[part: part + n * 4].view(torch.float32).cpu().double().numpy().reshape(2, 2, 130)
