@@ -139,15 +139,28 @@ def test_score_shift_invariance(causal):
     assert np.abs(bf16_to_f64(o2) - bf16_to_f64(o1)).max() <= 2e-2
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("kind", ["q_times_8", "max_rises_every_tile"])
-def test_rescale_stress(kind, causal):
-    """Inputs that exercise the running-max rescale: scores with sigma ~ 8, and keys built so
-    every key tile raises each row's maximum by more than the deferral threshold. These are
-    not N(0, 1) inputs, so O is held to the rounding bound derived in gpu_util (peaked
+@pytest.mark.parametrize("kind", ["q_times_8", "max_rises_every_tile", "late_jump"])
+def test_rescale_stress(kind, causal, d):
+    """Inputs that exercise the running-max rescale: scores with sigma ~ 8; keys built so
+    every key tile raises each row's maximum by more than the deferral threshold; and one late
+    key tile (keys 320-383) whose scores lie ~200 log2 units above all earlier ones, so an
+    exponential formed against the old running max overflows to +inf before the rescale. These
+    are not N(0, 1) inputs, so O is held to the rounding bound derived in gpu_util (peaked
     softmax rows let one bf16-rounded weight dominate)."""
-    B, H, N, d = 1, 2, 1024, 128
-    if kind == "q_times_8":
+    B, H, N = 1, 2, 1024
+    if kind == "late_jump":
+        rng = np.random.default_rng(115)
+        u = np.abs(rng.standard_normal(d)).astype(np.float32) * 0.5
+        q = np.broadcast_to(u, (B, H, N, d)) + 0.05 * rng.standard_normal((B, H, N, d)).astype(np.float32)
+        alpha = np.zeros(N, np.float32)
+        # scale * q.k = alpha |u|^2 / sqrt(d) = alpha * d / (4 sqrt(d)); 200 log2 units
+        alpha[320:384] = 200.0 / (np.log2(np.e) * np.sqrt(d) / 4.0 * float(np.mean(u * u) * 4.0))
+        k = alpha[None, None, :, None] * u[None, None, None, :] + np.zeros((B, H, N, d), np.float32)
+        bq, bk = f32_to_bf16_bits(q), f32_to_bf16_bits(k)
+        bv = normal_bf16((B, H, N, d), 116)
+    elif kind == "q_times_8":
         bq = normal_bf16((B, H, N, d), 110, sigma=8.0)
         bk, bv = normal_bf16((B, H, N, d), 111), normal_bf16((B, H, N, d), 112)
     else:
