@@ -10,7 +10,8 @@
 // normalisation happens once at the end. Fully masked causal tiles are skipped (page "flashattention-2", "FlashAttention-2
 // Improvements Over v1").
 //
-// gfx950 mapping (one workgroup = 4 waves = 128 query rows; key tiles of 64):
+// gfx950 mapping (one workgroup = 8 waves = 256 query rows at d >= 128, 4 waves = 128 rows at
+// d = 64; key tiles of 64):
 //  * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16: lane l owns
 //    query l%32 of its wave, so row max and row sums are in-lane plus one exchange with lane
 //    l^32; Q^T fragments (the B operand) stay in VGPRs for the whole key loop;
@@ -24,8 +25,8 @@
 //    (tile j+1 streams in while tile j is computed), one barrier per tile;
 //  * exp2 form: p = exp2(s * scale*log2(e) - m) is one FMA + one v_exp_f32. Masked tiles
 //    (causal diagonal, ragged tail) start their score accumulators at -inf instead of 0 for
-//    hidden keys. Two workgroups per CU let one wave's softmax VALU work overlap another
-//    wave's MFMAs. The key loop is unrolled by two so the LDS slot of a tile is a
+//    hidden keys. Two waves per SIMD (three at d = 64) let one wave's softmax VALU work
+//    overlap another wave's MFMAs. The key loop is unrolled by two so the LDS slot of a tile is a
 //    compile-time constant and every LDS address is a base register plus an immediate;
 //  * the LSE uses the fp32 sum of the unrounded p. O is normalised by the sum of the weights
 //    the PV MFMA actually used: on masked tiles (causal diagonal, ragged tail) a correction
@@ -53,31 +54,38 @@ namespace {
 #define FA2_FWD_OCC 2  // waves per SIMD the forward kernel is compiled for
 #endif
 
-constexpr int kFwdBR = 128;
-constexpr int kFwdThreads = 256;
 constexpr float kRescaleSum = 256.0f;  // a lane's partial sum of p per tile stays <= 2^8
 constexpr float kRescaleLog2 = 8.0f;   // so each p stays <= 2^8 (log2 units)
 
 // Key tiles of 64 for d <= 128; of 32 at d = 256, where O^T (128 registers) and the resident
 // Q^T fragments (64) leave room for one 32-key score block only. A K or V tile is 16 KiB
 // (8 KiB at d = 64) either way.
+// Workgroup = NW waves of 32 query rows sharing each K/V tile: 8 waves (256 rows, one workgroup
+// per CU) for d >= 128, which halves the L2 -> LDS tile traffic per FLOP of 4 waves (+1-3.5%);
+// 4 waves at d = 64, whose ~140 registers let three workgroups share a CU (3 waves per SIMD;
+// 8-wave workgroups would leave 2 and ran 7-10% slower).
 template <int D>
 struct FwdShape {
+  static constexpr int NW = D == 64 ? 4 : 8;     // waves per workgroup
+  static constexpr int BR = 32 * NW;             // query rows per workgroup
+  static constexpr int THREADS = 64 * NW;
   static constexpr int BC = D == 256 ? 32 : 64;  // keys per tile
   static constexpr int KB = BC / 32;             // 32-key MFMA blocks per tile
   static constexpr int DCH = D / 8;            // 16-byte chunks per K/V row
   static constexpr int KK = D / 16;            // MFMA k-steps of the score GEMM
   static constexpr int CB = D / 32;            // 32-row blocks of O^T
   static constexpr int TILE_BYTES = BC * D * 2;
-  static constexpr int LOADS = TILE_BYTES / (kFwdThreads * 16);  // 16-byte loads per lane per tile
+  static constexpr int LOADS = TILE_BYTES / (THREADS * 16);  // 16-byte loads per lane per tile
   static constexpr int K_SLOT0 = 0;
   static constexpr int V_SLOT0 = 2 * TILE_BYTES;
-  static constexpr int SMEM = 4 * TILE_BYTES;
+  static constexpr int SMEM = 4 * TILE_BYTES > NW * store_scratch_bytes(CB)
+                                 ? 4 * TILE_BYTES
+                                 : NW * store_scratch_bytes(CB);
   static_assert(LOADS >= 1 && DCH >= 8, "tile shape");
 };
 
 template <int D, bool CAUSAL, bool DROP>
-__global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
+__global__ __launch_bounds__(FwdShape<D>::THREADS, FA2_FWD_OCC) void fa2_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
     int N, int n_qblocks, int bh_count, int n_qheads, int group, long long kv_bstride,
@@ -103,7 +111,7 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
   const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + kv_off, head_bytes);
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + kv_off, head_bytes);
 
-  const int q_block0 = tc.qb * kFwdBR;
+  const int q_block0 = tc.qb * S::BR;
   const int q_wave0 = q_block0 + wave * 32;
   const int my_q = q_wave0 + l32;
   // dropout: the row key of this lane's query (unused without dropout)
@@ -113,18 +121,16 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
   // ---- key tiles this workgroup visits, and the last one not fully masked for this wave
   constexpr int BC = S::BC;
   int n_tiles = (N + BC - 1) / BC;
-  if (CAUSAL) n_tiles = min(N - 1, q_block0 + kFwdBR - 1) / BC + 1;
+  if (CAUSAL) n_tiles = min(N - 1, q_block0 + S::BR - 1) / BC + 1;
   const int wave_last = CAUSAL ? min(n_tiles - 1, (q_wave0 + 31) / BC) : n_tiles - 1;
 
-  // ---- HBM -> LDS tile loads. Load r of wave w writes the 1 KiB block i = 4r + w of the tile
+  // ---- HBM -> LDS tile loads. Load r of wave w writes the 1 KiB block i = NW*r + w of the tile
   // (lane l -> chunk p = 64i + l: row p / DCH, physical chunk p % DCH) and fetches the logical
-  // chunk the row's XOR swizzle maps there. For d <= 128, block 4r + w starts 4*(64/DCH)*r
-  // rows (a multiple of 16) after block w, so the swizzle (row bits 0-3) does not depend on r
-  // and r only adds a constant; at d = 256 (2 rows per block) each load has its own offset.
+  // chunk the row's XOR swizzle maps there.
   uint32_t koff[S::LOADS];
 #pragma unroll
   for (int r = 0; r < S::LOADS; ++r) {
-    const int p = (4 * r + wave) * 64 + lane;
+    const int p = (S::NW * r + wave) * 64 + lane;
     const int row = p / S::DCH;
     const int pc = p % S::DCH;
     koff[r] = (uint32_t)(row * D * 2 + (pc ^ swz<D>(row)) * 16);
@@ -132,13 +138,13 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
   auto load_k = [&](int j, int slot) {
 #pragma unroll
     for (int r = 0; r < S::LOADS; ++r)
-      buffer_load16_to_lds(rk, smem + S::K_SLOT0 + slot * S::TILE_BYTES + (4 * r + wave) * 1024,
+      buffer_load16_to_lds(rk, smem + S::K_SLOT0 + slot * S::TILE_BYTES + (S::NW * r + wave) * 1024,
                            koff[r], (uint32_t)j * BC * D * 2);
   };
   auto load_v = [&](int j, int slot) {
 #pragma unroll
     for (int r = 0; r < S::LOADS; ++r)
-      buffer_load16_to_lds(rv, smem + S::V_SLOT0 + slot * S::TILE_BYTES + (4 * r + wave) * 1024,
+      buffer_load16_to_lds(rv, smem + S::V_SLOT0 + slot * S::TILE_BYTES + (S::NW * r + wave) * 1024,
                            koff[r], (uint32_t)j * BC * D * 2);
   };
 
@@ -356,7 +362,7 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
   const float l_o = sum_xor32(l_f32 + l_corr);
   const float inv = DROP ? fast_rcp(l_o) * drop.scale : fast_rcp(l_o);
   // (the loop ended with a barrier: the K/V tiles are free for the transpose)
-  static_assert(4 * store_scratch_bytes(S::CB) <= S::SMEM, "transpose scratch");
+  static_assert(S::NW * store_scratch_bytes(S::CB) <= S::SMEM, "transpose scratch");
   store_rows_via_lds<S::CB, D>(smem + wave * store_scratch_bytes(S::CB), oacc, inv, o + head_off,
                                my_q - l32, N, lane);
   if (my_q < N && g == 0) lse[(size_t)tc.bh * N + my_q] = (m_run + fast_log2(l_tot)) * kLn2;
@@ -364,11 +370,11 @@ __global__ __launch_bounds__(kFwdThreads, FA2_FWD_OCC) void fa2_fwd_kernel(
 
 template <int D, bool CAUSAL, bool DROP>
 hipError_t launch_fwd_t(const FwdArgs& a) {
-  const int n_qblocks = (a.N + kFwdBR - 1) / kFwdBR;
+  const int n_qblocks = (a.N + FwdShape<D>::BR - 1) / FwdShape<D>::BR;
   const long long grid = (long long)n_qblocks * a.B * a.H;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const DropParams drop{a.drop_k0, a.drop_k1, a.drop_thr, a.drop_scale};
-  hipLaunchKernelGGL((fa2_fwd_kernel<D, CAUSAL, DROP>), dim3((unsigned)grid), dim3(kFwdThreads),
+  hipLaunchKernelGGL((fa2_fwd_kernel<D, CAUSAL, DROP>), dim3((unsigned)grid), dim3(FwdShape<D>::THREADS),
                      0, a.stream, static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                      static_cast<uint16_t*>(a.o), a.lse, a.N, n_qblocks, a.B * a.H, a.H,
