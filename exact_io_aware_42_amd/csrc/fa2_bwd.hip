@@ -757,16 +757,24 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
 }
 
 // ---------------------------------------------------------------------------------------
-// dQ. Workgroup = 4 waves x 32 queries (lane = query, as in the forward); key tiles of 64
-// (32 at d = 256). S^T = K Q^T and dP^T = V dO^T from row-wise K/V tile reads with Q^T/dO^T
+// dQ. Workgroup = DqShape<D>::NW waves x 32 queries (lane = query, as in the forward); key
+// tiles of 64 (32 at d = 256). S^T = K Q^T and dP^T = V dO^T from row-wise K/V tile reads with Q^T/dO^T
 // fragments held in VGPRs; dQ^T += K^T dS^T with K^T fragments from transposing reads of the
 // same K tile. At d = 256 the resident Q^T and dO^T fragments take 128 registers, so a launch
 // accumulates one half of dQ's columns (DH = 0 or 1; two launches recompute S and dP); DH = -1
 // is the whole row.
-constexpr int kDqBR = 128;
+// As in the forward: 8 waves (256 queries, one workgroup per CU) share each K/V tile at d >= 128,
+// halving the L2 -> LDS traffic per FLOP (dQ at B4 H16 N2048 d128 causal: 109 -> 105 us); d = 64
+// keeps 4 waves (three workgroups per CU).
+template <int D>
+struct DqShape {
+  static constexpr int NW = D == 64 ? 4 : 8;  // waves per workgroup
+  static constexpr int BR = 32 * NW;          // query rows per workgroup
+  static constexpr int THREADS = 64 * NW;
+};
 
 template <int D, bool CAUSAL, int DH, bool DROP>
-__global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dq_kernel(
+__global__ __launch_bounds__(DqShape<D>::THREADS, 2) void fa2_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ o,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, float* __restrict__ lse2,
@@ -780,7 +788,10 @@ __global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dq_kernel(
   constexpr int CB0 = DH < 0 ? 0 : DH * CBO;
   constexpr int TILE = BC * D * 2;
   constexpr int STAGE = 2 * TILE;  // K, V
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * STAGE];
+  constexpr int NW = DqShape<D>::NW;
+  constexpr int SCRATCH = NW * store_scratch_bytes(CBO);  // output tiles through LDS
+  constexpr int SMEM = 2 * STAGE > SCRATCH ? 2 * STAGE : SCRATCH;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -801,7 +812,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dq_kernel(
   const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + kv_off, head_bytes);
   const __amdgpu_buffer_rsrc_t rdo = make_rsrc(dout + head_off, head_bytes);
 
-  const int q_block0 = tc.qb * kDqBR;
+  const int q_block0 = tc.qb * DqShape<D>::BR;
   const int q_wave0 = q_block0 + wave * 32;
   const int my_q = q_wave0 + l32;
   const uint32_t drop_row =  // dropout: row key of this lane's query
@@ -839,10 +850,10 @@ __global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dq_kernel(
   }
 
   int n_tiles = (N + BC - 1) / BC;
-  if (CAUSAL) n_tiles = min(N - 1, q_block0 + kDqBR - 1) / BC + 1;
+  if (CAUSAL) n_tiles = min(N - 1, q_block0 + DqShape<D>::BR - 1) / BC + 1;
   const int wave_last = CAUSAL ? min(n_tiles - 1, (q_wave0 + 31) / BC) : n_tiles - 1;
 
-  const TileLoader<D, kThreads, BC> ld(wave, lane);
+  const TileLoader<D, DqShape<D>::THREADS, BC> ld(wave, lane);
   const TileReads<D> rd_off(lane);
   auto load_stage = [&](int j, int stage) {
     unsigned char* st = smem + stage * STAGE;
@@ -939,7 +950,7 @@ __global__ __launch_bounds__(kThreads, 2) void fa2_bwd_dq_kernel(
 
   // dQ = scale * dQ_acc, queries q_wave0 .. +31, columns 32*CB0 .. (the loop ended with a
   // barrier: the K/V tiles are free)
-  static_assert(4 * store_scratch_bytes(CBO) <= 2 * STAGE, "transpose scratch");
+  static_assert(SCRATCH <= SMEM, "transpose scratch");
   store_rows_via_lds<CBO, D>(smem + wave * store_scratch_bytes(CBO), dqacc, scale, dq + head_off + 32 * CB0,
                              q_wave0, N, lane);
 }
@@ -1019,7 +1030,8 @@ hipError_t launch_dkdv_t(const BwdArgs& a) {
 
 template <int D, bool CAUSAL, int DH, bool DROP>
 hipError_t launch_dq_one(const BwdArgs& a, unsigned grid, int n_qblocks) {
-  hipLaunchKernelGGL((fa2_bwd_dq_kernel<D, CAUSAL, DH, DROP>), dim3(grid), dim3(kThreads), 0,
+  hipLaunchKernelGGL((fa2_bwd_dq_kernel<D, CAUSAL, DH, DROP>), dim3(grid),
+                     dim3(DqShape<D>::THREADS), 0,
                      a.stream, static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                      static_cast<const uint16_t*>(a.o), static_cast<const uint16_t*>(a.dout),
@@ -1031,7 +1043,7 @@ hipError_t launch_dq_one(const BwdArgs& a, unsigned grid, int n_qblocks) {
 
 template <int D, bool CAUSAL, bool DROP>
 hipError_t launch_dq_t(const BwdArgs& a) {
-  const int n_qblocks = (a.N + kDqBR - 1) / kDqBR;
+  const int n_qblocks = (a.N + DqShape<D>::BR - 1) / DqShape<D>::BR;
   const long long grid = (long long)n_qblocks * a.B * a.H;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if constexpr (D == 256) {
