@@ -25,9 +25,10 @@
 //                        without dQ.
 // dK/dV and dQ each recompute S and dP; dQ's two recompute GEMMs are the price of avoiding
 // atomic dQ accumulation. Without dropout the dP accumulators start at -D, so dP - D comes
-// out of the MFMAs and dS is one multiply. Output tiles leave through LDS as whole row segments. With dropout
-// (DROP) every kernel regenerates the keep bits it needs from the counter-based hash
-// (fa2_device.hpp); dS = P * (Z * dP / P(keep) - D) and dV takes P * Z / P(keep).
+// out of the MFMAs and dS is one multiply. Output tiles leave through LDS as whole row
+// segments. With dropout (DROP) every kernel regenerates the keep bits it needs from the
+// counter-based hash (fa2_device.hpp); dS = P * (Z * dP / P(keep) - D) and dV takes
+// P * Z / P(keep).
 #include <type_traits>
 
 #include "fa2_device.hpp"
@@ -758,11 +759,11 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
 
 // ---------------------------------------------------------------------------------------
 // dQ. Workgroup = DqShape<D>::NW waves x 32 queries (lane = query, as in the forward); key
-// tiles of 64 (32 at d = 256). S^T = K Q^T and dP^T = V dO^T from row-wise K/V tile reads with Q^T/dO^T
-// fragments held in VGPRs; dQ^T += K^T dS^T with K^T fragments from transposing reads of the
-// same K tile. At d = 256 the resident Q^T and dO^T fragments take 128 registers, so a launch
-// accumulates one half of dQ's columns (DH = 0 or 1; two launches recompute S and dP); DH = -1
-// is the whole row.
+// tiles of 64 (32 at d = 256). S^T = K Q^T and dP^T = V dO^T from row-wise K/V tile reads
+// with Q^T/dO^T fragments held in VGPRs; dQ^T += K^T dS^T with K^T fragments from
+// transposing reads of the same K tile. At d = 256 the resident Q^T and dO^T fragments take
+// 128 registers, so a launch accumulates one half of dQ's columns (DH = 0 or 1; two launches
+// recompute S and dP); DH = -1 is the whole row.
 // As in the forward: 8 waves (256 queries, one workgroup per CU) share each K/V tile at d >= 128,
 // halving the L2 -> LDS traffic per FLOP (dQ at B4 H16 N2048 d128 causal: 109 -> 105 us); d = 64
 // keeps 4 waves (three workgroups per CU).

@@ -7,8 +7,8 @@
 // fills the chip; each wavefront owns 32 query rows and keeps their accumulator, running
 // max and running sums in registers; the rescale by exp(m_old - m_new) is deferred until a
 // tile's exponentials could exceed 2^8 (no per-tile max is taken until then) and the 1/l
-// normalisation happens once at the end. Fully masked causal tiles are skipped (page "flashattention-2", "FlashAttention-2
-// Improvements Over v1").
+// normalisation happens once at the end. Fully masked causal tiles are skipped (page
+// "flashattention-2", "FlashAttention-2 Improvements Over v1").
 //
 // gfx950 mapping (one workgroup = 8 waves = 256 query rows at d >= 128, 4 waves = 128 rows at
 // d = 64; key tiles of 64):
@@ -26,8 +26,8 @@
 //  * exp2 form: p = exp2(s * scale*log2(e) - m) is one FMA + one v_exp_f32. Masked tiles
 //    (causal diagonal, ragged tail) start their score accumulators at -inf instead of 0 for
 //    hidden keys. Two waves per SIMD (three at d = 64) let one wave's softmax VALU work
-//    overlap another wave's MFMAs. The key loop is unrolled by two so the LDS slot of a tile is a
-//    compile-time constant and every LDS address is a base register plus an immediate;
+//    overlap another wave's MFMAs. The key loop is unrolled by two so the LDS slot of a tile
+//    is a compile-time constant and every LDS address is a base register plus an immediate;
 //  * the LSE uses the fp32 sum of the unrounded p. O is normalised by the sum of the weights
 //    the PV MFMA actually used: on masked tiles (causal diagonal, ragged tail) a correction
 //    sum(bf16(p)) - sum(p) is added, so a row whose visible keys all lie in masked tiles (every
@@ -124,9 +124,9 @@ __global__ __launch_bounds__(FwdShape<D>::THREADS, FA2_FWD_OCC) void fa2_fwd_ker
   if (CAUSAL) n_tiles = min(N - 1, q_block0 + S::BR - 1) / BC + 1;
   const int wave_last = CAUSAL ? min(n_tiles - 1, (q_wave0 + 31) / BC) : n_tiles - 1;
 
-  // ---- HBM -> LDS tile loads. Load r of wave w writes the 1 KiB block i = NW*r + w of the tile
-  // (lane l -> chunk p = 64i + l: row p / DCH, physical chunk p % DCH) and fetches the logical
-  // chunk the row's XOR swizzle maps there.
+  // ---- HBM -> LDS tile loads. Load r of wave w writes the 1 KiB block i = NW*r + w of the
+  // tile (lane l -> chunk p = 64i + l: row p / DCH, physical chunk p % DCH) and fetches the
+  // logical chunk the row's XOR swizzle maps there.
   uint32_t koff[S::LOADS];
 #pragma unroll
   for (int r = 0; r < S::LOADS; ++r) {
@@ -138,13 +138,15 @@ __global__ __launch_bounds__(FwdShape<D>::THREADS, FA2_FWD_OCC) void fa2_fwd_ker
   auto load_k = [&](int j, int slot) {
 #pragma unroll
     for (int r = 0; r < S::LOADS; ++r)
-      buffer_load16_to_lds(rk, smem + S::K_SLOT0 + slot * S::TILE_BYTES + (S::NW * r + wave) * 1024,
+      buffer_load16_to_lds(rk,
+                           smem + S::K_SLOT0 + slot * S::TILE_BYTES + (S::NW * r + wave) * 1024,
                            koff[r], (uint32_t)j * BC * D * 2);
   };
   auto load_v = [&](int j, int slot) {
 #pragma unroll
     for (int r = 0; r < S::LOADS; ++r)
-      buffer_load16_to_lds(rv, smem + S::V_SLOT0 + slot * S::TILE_BYTES + (S::NW * r + wave) * 1024,
+      buffer_load16_to_lds(rv,
+                           smem + S::V_SLOT0 + slot * S::TILE_BYTES + (S::NW * r + wave) * 1024,
                            koff[r], (uint32_t)j * BC * D * 2);
   };
 
@@ -374,7 +376,8 @@ hipError_t launch_fwd_t(const FwdArgs& a) {
   const long long grid = (long long)n_qblocks * a.B * a.H;
   if (grid <= 0 || grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const DropParams drop{a.drop_k0, a.drop_k1, a.drop_thr, a.drop_scale};
-  hipLaunchKernelGGL((fa2_fwd_kernel<D, CAUSAL, DROP>), dim3((unsigned)grid), dim3(FwdShape<D>::THREADS),
+  hipLaunchKernelGGL((fa2_fwd_kernel<D, CAUSAL, DROP>), dim3((unsigned)grid),
+                     dim3(FwdShape<D>::THREADS),
                      0, a.stream, static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                      static_cast<uint16_t*>(a.o), a.lse, a.N, n_qblocks, a.B * a.H, a.H,
