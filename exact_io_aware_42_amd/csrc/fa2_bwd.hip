@@ -761,21 +761,25 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
 // dQ. Workgroup = DqShape<D>::NW waves x 32 queries (lane = query, as in the forward); key
 // tiles of 64 (32 at d = 256). S^T = K Q^T and dP^T = V dO^T from row-wise K/V tile reads
 // with Q^T/dO^T fragments held in VGPRs; dQ^T += K^T dS^T with K^T fragments from
-// transposing reads of the same K tile. At d = 256 the resident Q^T and dO^T fragments take
-// 128 registers, so a launch accumulates one half of dQ's columns (DH = 0 or 1; two launches
-// recompute S and dP); DH = -1 is the whole row.
-// As in the forward: 8 waves (256 queries, one workgroup per CU) share each K/V tile at d >= 128,
-// halving the L2 -> LDS traffic per FLOP (dQ at B4 H16 N2048 d128 causal: 109 -> 105 us); d = 64
-// keeps 4 waves (three workgroups per CU).
+// transposing reads of the same K tile.
+//  * d = 128: as in the forward, 8 waves (256 queries, one workgroup per CU) share each K/V
+//    tile, halving the L2 -> LDS traffic per FLOP of 4 waves (dQ at B4 H16 N2048 d128 causal:
+//    109 -> 105 us);
+//  * d = 64: 4 waves, three workgroups per CU;
+//  * d = 256: the resident Q^T and dO^T fragments and the dQ^T accumulators take 256 registers,
+//    so 4 waves with one wave per SIMD (512 registers) accumulate whole rows in one launch. Two
+//    launches of half the columns at two waves per SIMD each recomputed S and dP, 1.7x the
+//    MFMAs, and took 1.47x as long (B2 H16 N4096 causal: 0.61 -> 0.41 ms).
 template <int D>
 struct DqShape {
-  static constexpr int NW = D == 64 ? 4 : 8;  // waves per workgroup
-  static constexpr int BR = 32 * NW;          // query rows per workgroup
+  static constexpr int NW = D == 128 ? 8 : 4;  // waves per workgroup
+  static constexpr int OCC = D == 256 ? 1 : 2; // waves per SIMD the kernel is compiled for
+  static constexpr int BR = 32 * NW;           // query rows per workgroup
   static constexpr int THREADS = 64 * NW;
 };
 
-template <int D, bool CAUSAL, int DH, bool DROP>
-__global__ __launch_bounds__(DqShape<D>::THREADS, 2) void fa2_bwd_dq_kernel(
+template <int D, bool CAUSAL, bool DROP>
+__global__ __launch_bounds__((DqShape<D>::THREADS), (DqShape<D>::OCC)) void fa2_bwd_dq_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ o,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, float* __restrict__ lse2,
@@ -785,12 +789,10 @@ __global__ __launch_bounds__(DqShape<D>::THREADS, 2) void fa2_bwd_dq_kernel(
   constexpr int KK = D / 16, CB = D / 32;
   constexpr int BC = D == 256 ? 32 : 64;   // keys per tile
   constexpr int KB = BC / 32;              // 32-key MFMA blocks per tile
-  constexpr int CBO = DH < 0 ? CB : CB / 2;  // 32-column dQ blocks this launch accumulates
-  constexpr int CB0 = DH < 0 ? 0 : DH * CBO;
   constexpr int TILE = BC * D * 2;
   constexpr int STAGE = 2 * TILE;  // K, V
   constexpr int NW = DqShape<D>::NW;
-  constexpr int SCRATCH = NW * store_scratch_bytes(CBO);  // output tiles through LDS
+  constexpr int SCRATCH = NW * store_scratch_bytes(CB);  // output tiles through LDS
   constexpr int SMEM = 2 * STAGE > SCRATCH ? 2 * STAGE : SCRATCH;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
 
@@ -845,7 +847,7 @@ __global__ __launch_bounds__(DqShape<D>::THREADS, 2) void fa2_bwd_dq_kernel(
   const float lse_q = valid_q ? lse[(size_t)tc.bh * N + my_q] * kLog2e : INFINITY;
   const float dlt = valid_q ? dsum : 0.f;
   // -D and LSE*log2(e) of this block's queries go to the workspace for the dK/dV kernel
-  if (DH <= 0 && valid_q && g == 0) {
+  if (valid_q && g == 0) {
     delta[(size_t)tc.bh * N + my_q] = -dlt;
     lse2[(size_t)tc.bh * N + my_q] = lse_q;
   }
@@ -863,9 +865,9 @@ __global__ __launch_bounds__(DqShape<D>::THREADS, 2) void fa2_bwd_dq_kernel(
     ld.load(rv, st + TILE, soff);
   };
 
-  f32x16_t dqacc[CBO];
+  f32x16_t dqacc[CB];
 #pragma unroll
-  for (int cb = 0; cb < CBO; ++cb) dqacc[cb] = f32x16_t{};
+  for (int cb = 0; cb < CB; ++cb) dqacc[cb] = f32x16_t{};
   // without dropout (and for d <= 128, where the 16 registers fit) the dP^T chains start at -D
   // (all 16 registers of a lane are its query), so the MFMAs leave dP - D
   constexpr bool kInitD = !DROP && D <= 128;
@@ -933,9 +935,8 @@ __global__ __launch_bounds__(DqShape<D>::THREADS, 2) void fa2_bwd_dq_kernel(
         const u32x4_t b = {dsk[u / 2][4 * (u % 2) + 0], dsk[u / 2][4 * (u % 2) + 1],
                            dsk[u / 2][4 * (u % 2) + 2], dsk[u / 2][4 * (u % 2) + 3]};
 #pragma unroll
-        for (int cb = 0; cb < CBO; ++cb) {
-          const u32x4_t a = tr_operand(tk, rd_off.tr_off(CB0 + cb, u, 0),
-                                       rd_off.tr_off(CB0 + cb, u, 1));
+        for (int cb = 0; cb < CB; ++cb) {
+          const u32x4_t a = tr_operand(tk, rd_off.tr_off(cb, u, 0), rd_off.tr_off(cb, u, 1));
           dqacc[cb] = mfma32(a, b, dqacc[cb]);
         }
       }
@@ -949,11 +950,11 @@ __global__ __launch_bounds__(DqShape<D>::THREADS, 2) void fa2_bwd_dq_kernel(
     if (j + 1 < n_tiles) step(std::integral_constant<int, 1>{}, j + 1);
   }
 
-  // dQ = scale * dQ_acc, queries q_wave0 .. +31, columns 32*CB0 .. (the loop ended with a
-  // barrier: the K/V tiles are free)
+  // dQ = scale * dQ_acc, queries q_wave0 .. +31 (the loop ended with a barrier: the K/V tiles
+  // are free)
   static_assert(SCRATCH <= SMEM, "transpose scratch");
-  store_rows_via_lds<CBO, D>(smem + wave * store_scratch_bytes(CBO), dqacc, scale, dq + head_off + 32 * CB0,
-                             q_wave0, N, lane);
+  store_rows_via_lds<CB, D>(smem + wave * store_scratch_bytes(CB), dqacc, scale, dq + head_off,
+                            q_wave0, N, lane);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -1029,31 +1030,19 @@ hipError_t launch_dkdv_t(const BwdArgs& a) {
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, int DH, bool DROP>
-hipError_t launch_dq_one(const BwdArgs& a, unsigned grid, int n_qblocks) {
-  hipLaunchKernelGGL((fa2_bwd_dq_kernel<D, CAUSAL, DH, DROP>), dim3(grid),
-                     dim3(DqShape<D>::THREADS), 0,
-                     a.stream, static_cast<const uint16_t*>(a.q),
+template <int D, bool CAUSAL, bool DROP>
+hipError_t launch_dq_t(const BwdArgs& a) {
+  const int n_qblocks = (a.N + DqShape<D>::BR - 1) / DqShape<D>::BR;
+  const long long grid = (long long)n_qblocks * a.B * a.H;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((fa2_bwd_dq_kernel<D, CAUSAL, DROP>), dim3((unsigned)grid),
+                     dim3(DqShape<D>::THREADS), 0, a.stream, static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                      static_cast<const uint16_t*>(a.o), static_cast<const uint16_t*>(a.dout),
                      a.lse, a.lse2, a.delta, static_cast<uint16_t*>(a.dq), a.N, n_qblocks,
                      a.B * a.H, a.H, a.H / a.Hkv, a.kv_bstride, a.scale_log2, a.scale,
                      DropParams{a.drop_k0, a.drop_k1, a.drop_thr, a.drop_scale});
   return hipGetLastError();
-}
-
-template <int D, bool CAUSAL, bool DROP>
-hipError_t launch_dq_t(const BwdArgs& a) {
-  const int n_qblocks = (a.N + DqShape<D>::BR - 1) / DqShape<D>::BR;
-  const long long grid = (long long)n_qblocks * a.B * a.H;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  if constexpr (D == 256) {
-    const hipError_t e = launch_dq_one<D, CAUSAL, 0, DROP>(a, (unsigned)grid, n_qblocks);
-    if (e != hipSuccess) return e;
-    return launch_dq_one<D, CAUSAL, 1, DROP>(a, (unsigned)grid, n_qblocks);
-  } else {
-    return launch_dq_one<D, CAUSAL, -1, DROP>(a, (unsigned)grid, n_qblocks);
-  }
 }
 
 }  // namespace
