@@ -396,13 +396,8 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
           }
         }
       }
-      if (masked) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int qi = q0 + 16 * (i / 8) + 8 * g + (i % 8);
-          s[i] = (qi >= N || (CAUSAL && my_key > qi)) ? -INFINITY : 0.f;
-        }
-      } else {
+      if (masked) mask_queries<CAUSAL>(s, q0 + 8 * g, my_key, N, q0 + 32 > N);
+      else {
         s = f32x16_t{};
       }
 #pragma unroll
@@ -666,13 +661,8 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
       const unsigned char* ts = smem + statbase + stage * STATS_STAGE;
       const bool masked = (q0 + kKv256BQ > N) || (CAUSAL && q0 < key_w0 + 31);
       f32x16_t s, dp = f32x16_t{};
-      if (masked) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int qi = q0 + 16 * (i / 8) + 8 * g + (i % 8);
-          s[i] = (qi >= N || (CAUSAL && my_key > qi)) ? -INFINITY : 0.f;
-        }
-      } else {
+      if (masked) mask_queries<CAUSAL>(s, q0 + 8 * g, my_key, N, q0 + 32 > N);
+      else {
         s = f32x16_t{};
       }
       // S = Q K^T (both roles) and dP = dO V^T (dK waves), lane = key, registers = queries
@@ -821,6 +811,8 @@ __global__ __launch_bounds__((DqShape<D>::THREADS), (DqShape<D>::OCC)) void fa2_
   const uint32_t drop_row =  // dropout: row key of this lane's query
       DROP ? pcg_hash(drop_head_key(drop, (uint32_t)tc.bh) ^ (uint32_t)my_q) : 0u;
   const bool valid_q = my_q < N;
+  // masked tiles hide the keys above key_lim (the causal diagonal and the ragged tail)
+  const int key_lim = CAUSAL ? min(my_q, N - 1) : N - 1;
 
   // Q and dO fragments (B operands of S^T and dP^T): lane holds row my_q, columns
   // 16kk + 8g .. +7; the O fragments of the same columns give this lane's half of
@@ -892,11 +884,7 @@ __global__ __launch_bounds__((DqShape<D>::THREADS), (DqShape<D>::OCC)) void fa2_
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         if (masked) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = key0 + kb * 32 + (i / 8) * 16 + g * 8 + (i % 8);
-            s[kb][i] = (key >= N || (CAUSAL && key > my_q)) ? -INFINITY : 0.f;
-          }
+          mask_keys(s[kb], key0 + kb * 32 + 8 * g - key_lim);
         } else {
           s[kb] = f32x16_t{};
         }

@@ -207,6 +207,35 @@ __device__ __forceinline__ void store_rows_f32(const f32x16_t* acc, float mul, f
                   acc[cb][4 * t + 3] * mul};
 }
 
+// Accumulator start values of a masked 32x32 score block: -inf for hidden entries, 0 otherwise.
+// Lane = query, registers = keys (the forward and dQ layout): register i holds key
+// base + 16(i/8) + 8g + i%8; mask_keys takes rel = (key of register 0) - key_lim, the lane's
+// key_lim being the last visible key (min(query, N - 1) causal, N - 1 otherwise), so register i
+// is hidden iff rel + 16(i/8) + i%8 > 0: one compare against a constant per register.
+__device__ __forceinline__ void mask_keys(f32x16_t& s, int rel) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s[i] = rel > -(16 * (i / 8) + (i % 8)) ? -INFINITY : 0.f;
+}
+// Lane = key, registers = queries (the dK/dV layout): register i holds query
+// q_base + 16(i/8) + i%8 (q_base = the tile's first query + 8g). Hidden iff the query is past N
+// (only when the tile crosses N) or, causal, before the lane's key.
+template <bool CAUSAL>
+__device__ __forceinline__ void mask_queries(f32x16_t& s, int q_base, int my_key, int N,
+                                             bool tail) {
+  const int lo = q_base - my_key;  // query - key of register 0
+  const int hi = q_base - N;       // query - N of register 0
+  if (tail) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int c = 16 * (i / 8) + (i % 8);
+      s[i] = (hi >= -c || (CAUSAL && lo < -c)) ? -INFINITY : 0.f;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s[i] = (CAUSAL && lo < -(16 * (i / 8) + (i % 8))) ? -INFINITY : 0.f;
+  }
+}
+
 // Workgroup id -> (block, batch*head) order. Workgroups are dealt to the 8 XCDs in turn
 // (id % 8), each XCD with its own L2; when the heads divide evenly, XCD x gets the heads
 // x, x+8, ... only.

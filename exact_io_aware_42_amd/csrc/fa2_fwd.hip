@@ -197,16 +197,11 @@ __global__ __launch_bounds__(FwdShape<D>::THREADS, FA2_FWD_OCC) void fa2_fwd_ker
     const int key0 = j * BC;
     return (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > q_wave0);
   };
+  // (hidden iff key > key_lim: one compare per score)
+  const int key_lim = CAUSAL ? min(my_q, N - 1) : N - 1;
   auto mask_bias = [&](int j, f32x16_t* s) {
-    const int key0 = j * BC;
 #pragma unroll
-    for (int kb = 0; kb < S::KB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = key0 + kb * 32 + (i / 8) * 16 + g * 8 + (i % 8);
-        const bool hidden = (key >= N) || (CAUSAL && key > my_q);
-        s[kb][i] = hidden ? -INFINITY : 0.f;
-      }
+    for (int kb = 0; kb < S::KB; ++kb) mask_keys(s[kb], j * BC + kb * 32 + 8 * g - key_lim);
   };
   // S^T tile j from K slot `slot`: KB 32-key blocks x 32 queries
   auto scores = [&](int slot, bool masked, int j, f32x16_t* s) {
