@@ -16,8 +16,8 @@ dense bf16 MFMA peak of MI355X (2.5 PFLOP/s). `traffic` comes from committed roc
 FETCH_SIZE / WRITE_SIZE counter summaries under profiles/ (null if the kernel source changed
 since they were taken). `cpu_baseline` times the CPU float64 oracle on a bounded sample of
 the same workload (whole heads) on the host cores. `forward_workloads` adds the forward
-kernel's TFLOP/s on the forward-only workloads, `d256_steps` the fwd+bwd step at head
-dimension 256, `gpt_layer_step` a GPT-style attention layer (bf16 projections + attention,
+kernel's TFLOP/s on the forward-only workloads, `non_causal_step` the same fwd+bwd step
+without the causal mask, `d256_steps` the fwd+bwd step at head dimension 256, `gpt_layer_step` a GPT-style attention layer (bf16 projections + attention,
 forward and backward through torch.autograd), `gqa_step` the fwd+bwd step with 16 query
 heads sharing 4 K/V heads and `dropout_step` the fwd+bwd step with dropout p = 0.1 on the
 attention probabilities; none of them is part of `value`.
@@ -38,6 +38,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0
+WARM_MS = 300.0  # GPU time of untimed steps before the counted warm-up
 METRIC = "attention fwd/bwd TFLOP/s (bf16, causal+non-causal) and % of MFMA peak, 1 GPU"
 
 
@@ -70,11 +71,10 @@ def cpu_baseline(w, causal, with_bwd, budget_s):
     from exact_io_aware_42_amd.inputs import bf16_bits_to_f64, default_scale, workload_tensors
     from oracle import attention_backward, attention_forward
 
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+    from threadpoolctl import threadpool_info
+
+    blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+    cores = max([p.get("num_threads", 1) for p in blas] or [1])
     t = workload_tensors(w, with_dout=with_bwd)
     scale = default_scale(w.d)
     per_head = fwd_flop(1, 1, w.N, w.d, causal) * (3.5 if with_bwd else 1.0)
@@ -102,7 +102,25 @@ def cpu_baseline(w, causal, with_bwd, budget_s):
         "sample": (f"{heads} of {w.B * w.H} (batch, head) slices, "
                    f"{'forward+backward' if with_bwd else 'forward'}, float64 numpy, "
                    f"{el:.1f} s"),
+        "cpu_model": cpu_model(),
+        "logical_cpus": os.cpu_count(),
+        "blas": ", ".join(f"{p.get('internal_api')} {p.get('version')} "
+                          f"({p.get('threading_layer')}, {p.get('num_threads')} threads)"
+                          for p in blas) or "none found",
     }
+
+
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 FWD_SWEEP = ((2, False), (2, True), (3, True), (4, True), (4, False), (6, True), (6, False))
@@ -227,13 +245,15 @@ def dropout_step(fa2, torch, dev, p=0.1, steps=20, warmup=20):
     return {"shape": "B4 H16 N2048 d128 causal", "dropout_p": p, **r}
 
 
-def measure_step(fa2, torch, dev, w, causal, with_bwd, steps, warmup):
-    """Run `warmup` untimed and `steps` timed steps (forward, then dQ and dK/dV) of workload
-    `w`. Inside the timed steps only the last stage (dK/dV, or the forward alone) is bracketed
-    by HIP events on the launch stream: each event record costs the step about 2 us. The other
+def measure_step(fa2, torch, dev, w, causal, with_bwd, steps, warmup, warm_ms=WARM_MS):
+    """Run untimed steps (forward, then dQ and dK/dV) of workload `w` for at least `warm_ms` of
+    GPU time (the clock needs a few hundred milliseconds of load to settle; a step count alone
+    left short runs about 10% low), then `warmup` more untimed steps and `steps` timed ones.
+    Inside the timed steps only the last stage (dK/dV, or the forward alone) is bracketed by
+    HIP events on the launch stream: each event record costs the step about 2 us. The other
     stages are timed the same way over a further min(steps, 20) steps after the timed region.
     Returns (stage names, their algorithmic FLOP, step FLOP, mean stage ms, wall seconds of the
-    timed steps)."""
+    timed steps, GPU milliseconds of the time-based warm-up)."""
     import numpy as np
 
     from exact_io_aware_42_amd.inputs import default_scale, workload_tensors
@@ -277,6 +297,18 @@ def measure_step(fa2, torch, dev, w, causal, with_bwd, steps, warmup):
             fa2.bwd_dkdv(q, k, v, do, ws, causal=causal, scale=scale, dk=dk, dv=dv)
             mark(3)
 
+    # time-based warm-up: batches of steps until warm_ms of GPU time have passed
+    warm_done = 0.0
+    batch = 1
+    while warm_done < warm_ms:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(batch):
+            step()
+        e1.record(stream)
+        e1.synchronize()
+        warm_done += e0.elapsed_time(e1)
+        batch = min(batch * 2, 256)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -304,7 +336,7 @@ def measure_step(fa2, torch, dev, w, causal, with_bwd, steps, warmup):
         torch.cuda.synchronize()
         for i, kname in enumerate(kernels[:-1]):
             kernel_ms[kname] = mean_ms(ev2, i)
-    return kernels, algo_flop, step_flop, kernel_ms, elapsed
+    return kernels, algo_flop, step_flop, kernel_ms, elapsed, warm_done
 
 
 def main():
@@ -328,7 +360,7 @@ def main():
     torch.cuda.set_device(dev)
     fa2.load_library()
 
-    kernels, algo_flop, step_flop, kernel_ms, elapsed = measure_step(
+    kernels, algo_flop, step_flop, kernel_ms, elapsed, warm_done = measure_step(
         fa2, torch, dev, w, causal, with_bwd, args.steps, args.warmup)
     ms_per_step = elapsed * 1e3 / args.steps
 
@@ -348,6 +380,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_gpu_ms": round(warm_done, 1),
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -377,17 +410,21 @@ def main():
     }
     if not args.no_fwd_sweep:
         out["forward_workloads"] = forward_sweep(fa2, torch, dev)
-        # the fwd+bwd step at head dimension 256 (both masks)
+
+        def other_step(wo, co):
+            kn, af, sf, km, el, _ = measure_step(fa2, torch, dev, wo, co, True, 20, 20)
+            return {"ms_per_step": round(el * 1e3 / 20, 4),
+                    "tflops": round(sf * 20 / el / 1e12, 1),
+                    "kernel_ms": {k_: round(v_, 4) for k_, v_ in km.items()},
+                    "kernel_tflops": {k_: round(af[k_] / (km[k_] * 1e-3) / 1e12, 1) for k_ in kn}}
+
+        # the same fwd+bwd step without the causal mask (the metric names both masks), and the
+        # fwd+bwd step at head dimension 256 (both masks)
+        if w.backward and causal:
+            out["non_causal_step"] = {f"{w.name} non-causal fwd+bwd": other_step(w, False)}
         w6 = WORKLOADS[6]
-        steps6 = {}
-        for c6 in (True, False):
-            kn6, af6, sf6, km6, el6 = measure_step(fa2, torch, dev, w6, c6, True, 20, 20)
-            steps6[f"{w6.name} {'causal' if c6 else 'non-causal'} fwd+bwd"] = {
-                "ms_per_step": round(el6 * 1e3 / 20, 4),
-                "tflops": round(sf6 * 20 / el6 / 1e12, 1),
-                "kernel_ms": {kn: round(v_, 4) for kn, v_ in km6.items()},
-                "kernel_tflops": {kn: round(af6[kn] / (km6[kn] * 1e-3) / 1e12, 1) for kn in kn6}}
-        out["d256_steps"] = steps6
+        out["d256_steps"] = {f"{w6.name} {'causal' if c6 else 'non-causal'} fwd+bwd":
+                             other_step(w6, c6) for c6 in (True, False)}
         out["gpt_layer_step"] = gpt_layer_step(torch, dev)
         out["gqa_step"] = gqa_step(fa2, torch, dev)
         out["dropout_step"] = dropout_step(fa2, torch, dev)

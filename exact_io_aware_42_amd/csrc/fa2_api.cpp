@@ -23,7 +23,9 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 fa2_status check_sizes(int B, int H, int N, int d, float scale, bool* empty, int max_d = 256) {
   *empty = false;
   if (B < 0 || H < 0 || N < 0 || d <= 0) return FA2_ERR_INVALID_ARGUMENT;
-  if (!std::isfinite(scale) || !(scale > 0.0f)) return FA2_ERR_INVALID_ARGUMENT;
+  // any finite scale whose magnitude times log2(e) is a finite float
+  if (!std::isfinite(scale) || !std::isfinite(static_cast<float>(std::fabs(scale) * kLog2e)))
+    return FA2_ERR_INVALID_ARGUMENT;
   if ((d != 64 && d != 128 && d != 256) || d > max_d) return FA2_ERR_UNSUPPORTED;
   if (B == 0 || H == 0 || N == 0) {
     *empty = true;
@@ -39,6 +41,23 @@ fa2_status check_sizes(int B, int H, int N, int d, float scale, bool* empty, int
   if ((unsigned long long)B * H * ((unsigned long long)(N + 63) / 64) > 0x7fffffffull)
     return FA2_ERR_INVALID_ARGUMENT;
   return FA2_OK;
+}
+
+// How the kernels apply a softmax scale of any sign (they need a positive multiplier c): c =
+// |scale| * log2(e) with one operand of the score product negated when the scale is negative,
+// or zeroed (every score 0) with c = log2(e) when it is 0. Masks for the operand's bf16 pairs:
+// x -> (x & and_mask) ^ xor_mask.
+struct ScaleForm {
+  float scale_log2;
+  uint32_t and_mask, xor_mask;
+};
+ScaleForm scale_form(float scale) {
+  ScaleForm f;
+  f.and_mask = scale == 0.0f ? 0u : ~0u;
+  f.xor_mask = scale < 0.0f ? 0x80008000u : 0u;
+  f.scale_log2 =
+      scale == 0.0f ? static_cast<float>(kLog2e) : static_cast<float>(std::fabs(scale) * kLog2e);
+  return f;
 }
 
 fa2_status from_hip(hipError_t e) {
@@ -114,7 +133,10 @@ fa2_status fwd_impl(const void* q, const void* k, const void* v, void* o, float*
   a.Hkv = Hkv;
   a.kv_bstride = kv_bstride;
   a.causal = causal != 0;
-  a.scale_log2 = static_cast<float>(static_cast<double>(softmax_scale) * kLog2e);
+  const ScaleForm sf = scale_form(softmax_scale);
+  a.scale_log2 = sf.scale_log2;
+  a.q_and = sf.and_mask;
+  a.q_xor = sf.xor_mask;
   a.dropout = dropout_p > 0.f;
   a.drop_k0 = drop.k0;
   a.drop_k1 = drop.k1;
@@ -212,7 +234,10 @@ fa2_status bwd_args(const void* q, const void* k, const void* v, const void* o, 
   a->kv_bstride = (long long)H * N * d;
   a->causal = causal != 0;
   a->scale = softmax_scale;
-  a->scale_log2 = static_cast<float>(static_cast<double>(softmax_scale) * kLog2e);
+  const ScaleForm sf = scale_form(softmax_scale);
+  a->scale_log2 = sf.scale_log2;
+  a->sgn_and = sf.and_mask;
+  a->sgn_xor = sf.xor_mask;
   a->stream = stream;
   return FA2_OK;
 }

@@ -220,7 +220,7 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse2, const float* __restrict__ delta, uint16_t* __restrict__ dk,
     uint16_t* __restrict__ dv, int N, int n_kblocks, int bh_count, int n_qheads, int group,
-    long long kv_bstride, float scale_log2, float scale, DropParams drop,
+    long long kv_bstride, float scale_log2, float scale, OperandSign ksign, DropParams drop,
     float* __restrict__ part, int split) {
   constexpr int KK = D / 16, CB = D / 32, DCH = D / 8;
   // LDS: the two ring stages of Q and dO tiles at the bottom (every ds_read of them is a
@@ -360,6 +360,13 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
   if (n_steps > 0) load_stage(0, 0);
   wait_vmem();
   __syncthreads();
+  if (ksign.and_mask != ~0u || ksign.xor_mask != 0u) {
+    // a scale <= 0: its sign goes into the resident K rows, once (see OperandSign)
+    for (int i = tid * 16; i < KV_BYTES; i += kKvThreads * 16)
+      *reinterpret_cast<u32x4_t*>(smem + KV0 + i) =
+          apply_sign(*reinterpret_cast<const u32x4_t*>(smem + KV0 + i), ksign);
+    __syncthreads();
+  }
 
   // unrolled by two below, so the ring stage is a compile-time constant (LDS addresses are a
   // base register plus an immediate)
@@ -528,7 +535,7 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse2, const float* __restrict__ delta, uint16_t* __restrict__ dk,
     uint16_t* __restrict__ dv, int N, int n_kblocks, int bh_count, int n_qheads, int group,
-    long long kv_bstride, float scale_log2, float scale, DropParams drop,
+    long long kv_bstride, float scale_log2, float scale, OperandSign ksign, DropParams drop,
     float* __restrict__ part, int split) {
   constexpr int D = 256, KK = D / 16, CB = D / 32, DCH = D / 8;
   constexpr int TILE = kKv256BQ * D * 2;          // 16 KiB
@@ -645,6 +652,13 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
   if (n_steps > 0) load_stage(0, 0);
   wait_vmem();
   __syncthreads();
+  if (ksign.and_mask != ~0u || ksign.xor_mask != 0u) {
+    // a scale <= 0: its sign goes into the resident K rows, once (see OperandSign)
+    for (int i = tid * 16; i < KV_BYTES; i += kThreads * 16)
+      *reinterpret_cast<u32x4_t*>(smem + KV0 + i) =
+          apply_sign(*reinterpret_cast<const u32x4_t*>(smem + KV0 + i), ksign);
+    __syncthreads();
+  }
 
   StepPos cur(t_begin, nt, qt_begin);  // the tile of the current step
   auto step = [&](auto stage_c, int t) {
@@ -775,7 +789,7 @@ __global__ __launch_bounds__((DqShape<D>::THREADS), (DqShape<D>::OCC)) void fa2_
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, float* __restrict__ lse2,
     float* __restrict__ delta, uint16_t* __restrict__ dq, int N, int n_qblocks, int bh_count,
     int n_qheads, int group, long long kv_bstride, float scale_log2, float scale,
-    DropParams drop) {
+    OperandSign qsign, DropParams drop) {
   constexpr int KK = D / 16, CB = D / 32;
   constexpr int BC = D == 256 ? 32 : 64;   // keys per tile
   constexpr int KB = BC / 32;              // 32-key MFMA blocks per tile
@@ -823,7 +837,8 @@ __global__ __launch_bounds__((DqShape<D>::THREADS), (DqShape<D>::OCC)) void fa2_
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(o + head_off, head_bytes);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      qf[kk] = buffer_load16(rq, (uint32_t)my_q * D * 2 + (2 * kk + g) * 16, 0);
+      // the scale's sign applied to Q (negated for a negative scale, zeroed for scale 0)
+      qf[kk] = apply_sign(buffer_load16(rq, (uint32_t)my_q * D * 2 + (2 * kk + g) * 16, 0), qsign);
       dof[kk] = buffer_load16(rdo, (uint32_t)my_q * D * 2 + (2 * kk + g) * 16, 0);
     }
 #pragma unroll
@@ -1013,7 +1028,8 @@ hipError_t launch_dkdv_t(const BwdArgs& a) {
                      static_cast<const uint16_t*>(a.dout), a.lse2, a.delta,
                      static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), a.N, n_kblocks,
                      a.B * a.Hkv * a.kv_split, a.H, a.H / a.Hkv, a.kv_bstride, a.scale_log2,
-                     a.scale, DropParams{a.drop_k0, a.drop_k1, a.drop_thr, a.drop_scale},
+                     a.scale, OperandSign{a.sgn_and, a.sgn_xor},
+                     DropParams{a.drop_k0, a.drop_k1, a.drop_thr, a.drop_scale},
                      a.kv_split > 1 ? a.kv_part : nullptr, a.kv_split);
   return hipGetLastError();
 }
@@ -1029,6 +1045,7 @@ hipError_t launch_dq_t(const BwdArgs& a) {
                      static_cast<const uint16_t*>(a.o), static_cast<const uint16_t*>(a.dout),
                      a.lse, a.lse2, a.delta, static_cast<uint16_t*>(a.dq), a.N, n_qblocks,
                      a.B * a.H, a.H, a.H / a.Hkv, a.kv_bstride, a.scale_log2, a.scale,
+                     OperandSign{a.sgn_and, a.sgn_xor},
                      DropParams{a.drop_k0, a.drop_k1, a.drop_thr, a.drop_scale});
   return hipGetLastError();
 }
@@ -1051,7 +1068,8 @@ hipError_t launch_dkdv256_t(const BwdArgs& a) {
                      static_cast<const uint16_t*>(a.dout), a.lse2, a.delta,
                      static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), a.N, n_kblocks,
                      a.B * a.Hkv * a.kv_split, a.H, a.H / a.Hkv, a.kv_bstride, a.scale_log2,
-                     a.scale, DropParams{a.drop_k0, a.drop_k1, a.drop_thr, a.drop_scale},
+                     a.scale, OperandSign{a.sgn_and, a.sgn_xor},
+                     DropParams{a.drop_k0, a.drop_k1, a.drop_thr, a.drop_scale},
                      a.kv_split > 1 ? a.kv_part : nullptr, a.kv_split);
   return hipGetLastError();
 }

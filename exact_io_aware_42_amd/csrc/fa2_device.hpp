@@ -125,6 +125,20 @@ __device__ __forceinline__ int swz(int row) {
   return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
 }
 
+// The sign of the softmax scale, carried by one operand of the score product. The kernels form
+// scores as c * (q . k) with c > 0 (the running max and the -inf mask start rely on it); a
+// scale < 0 is applied as c = |scale| with one operand's bf16 sign bits flipped (flipping is
+// exact, and (-q) . k = -(q . k) wherever the accumulation rounds symmetrically in sign, as
+// round-to-nearest does), and scale = 0 as that operand zeroed (every score exactly 0, any
+// c > 0). x -> (x & and_mask) ^ xor_mask on each dword: (~0, 0) keeps the operand,
+// (~0, 0x80008000) negates it, (0, 0) zeroes it.
+struct OperandSign {
+  uint32_t and_mask, xor_mask;
+};
+__device__ __forceinline__ u32x4_t apply_sign(u32x4_t x, const OperandSign& sg) {
+  return (x & sg.and_mask) ^ sg.xor_mask;
+}
+
 // Dropout mask generator: the 32-bit PCG-based hash of Jarzynski and Olano ("Hash Functions for
 // GPU Rendering", JCGT 9(3), 2020), an LCG step followed by a random xorshift, a multiply and
 // a fixed xorshift. For query head bh: a = hash(k0 ^ hash(k1 ^ bh)) (k0, k1 from the seed and

@@ -89,7 +89,7 @@ __global__ __launch_bounds__(FwdShape<D>::THREADS, FA2_FWD_OCC) void fa2_fwd_ker
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
     int N, int n_qblocks, int bh_count, int n_qheads, int group, long long kv_bstride,
-    float scale_log2, DropParams drop) {
+    float scale_log2, OperandSign qsign, DropParams drop) {
   using S = FwdShape<D>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[S::SMEM];
 
@@ -179,10 +179,12 @@ __global__ __launch_bounds__(FwdShape<D>::THREADS, FA2_FWD_OCC) void fa2_fwd_ker
     return vbase[cb % 4][h] + (cb / 4) * 256 + 16 * u * D * 2;
   };
 
-  // ---- Q^T fragments (B operand of S^T): lane holds q[my_q][16kk + 8g .. +7]; zeros past N
+  // ---- Q^T fragments (B operand of S^T): lane holds q[my_q][16kk + 8g .. +7]; zeros past N;
+  // the scale's sign applied (negated for a negative scale, zeroed for scale 0)
   u32x4_t qf[S::KK];
 #pragma unroll
-  for (int kk = 0; kk < S::KK; ++kk) qf[kk] = buffer_load16(rq, (uint32_t)my_q * D * 2 + (2 * kk + g) * 16, 0);
+  for (int kk = 0; kk < S::KK; ++kk)
+    qf[kk] = apply_sign(buffer_load16(rq, (uint32_t)my_q * D * 2 + (2 * kk + g) * 16, 0), qsign);
 
   // ---- accumulators and row statistics (per lane: query my_q, key half g)
   f32x16_t oacc[S::CB];
@@ -376,7 +378,8 @@ hipError_t launch_fwd_t(const FwdArgs& a) {
                      0, a.stream, static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                      static_cast<uint16_t*>(a.o), a.lse, a.N, n_qblocks, a.B * a.H, a.H,
-                     a.H / a.Hkv, a.kv_bstride, a.scale_log2, drop);
+                     a.H / a.Hkv, a.kv_bstride, a.scale_log2, OperandSign{a.q_and, a.q_xor},
+                     drop);
   return hipGetLastError();
 }
 

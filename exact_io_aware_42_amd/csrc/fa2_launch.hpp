@@ -21,7 +21,8 @@ struct FwdArgs {
   int Hkv;
   long long kv_bstride;
   bool causal;
-  float scale_log2;  // softmax_scale * log2(e)
+  float scale_log2;  // |softmax_scale| * log2(e) (log2(e) when the scale is 0)
+  uint32_t q_and = ~0u, q_xor = 0u;  // the scale's sign, applied to Q (see OperandSign)
   // dropout on P (dropout false: none): keep iff hash >= drop_thr, kept values scaled by
   // drop_scale; drop_k0/drop_k1 are the keys derived from the seed and offset
   bool dropout = false;
@@ -46,8 +47,11 @@ struct BwdArgs {
   int Hkv;
   long long kv_bstride;
   bool causal;
-  float scale;       // softmax_scale
-  float scale_log2;  // softmax_scale * log2(e)
+  float scale;       // softmax_scale (multiplies dQ and dK)
+  float scale_log2;  // |softmax_scale| * log2(e) (log2(e) when the scale is 0)
+  // the scale's sign (see OperandSign), applied to Q in the dQ kernel and to the resident K
+  // rows in the dK/dV kernels
+  uint32_t sgn_and = ~0u, sgn_xor = 0u;
   bool dropout = false;  // as in FwdArgs
   uint32_t drop_k0 = 0, drop_k1 = 0, drop_thr = 0;
   float drop_scale = 1.f;

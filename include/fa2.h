@@ -39,8 +39,9 @@
  * Asynchrony and errors
  *   Arguments are validated on the host before any HIP call. Invalid arguments return
  *   FA2_ERR_INVALID_ARGUMENT (null or misaligned pointers, negative sizes or d <= 0, a
- *   non-finite scale, a scale that is not > 0, a workspace that is too small, sizes beyond the
- *   limits above); an unsupported head dimension returns FA2_ERR_UNSUPPORTED. Otherwise the kernels are enqueued on `stream`
+ *   non-finite scale or one whose magnitude times log2(e) overflows a float, i.e. |scale| above
+ *   about 2.3e38, a workspace that is too small, sizes beyond the limits above); an
+ *   unsupported head dimension returns FA2_ERR_UNSUPPORTED. Otherwise the kernels are enqueued on `stream`
  *   (0 = the default stream) and the call returns FA2_OK, or FA2_ERR_HIP when the launch
  *   fails (the HIP error code is then available from fa2_last_hip_error()). Results are
  *   valid once the stream has been synchronised. No C++ exception crosses this interface.
@@ -64,8 +65,12 @@ typedef enum fa2_status {
 
 /* Forward pass. Writes o [B,H,N,d] (bf16) and lse [B,H,N] (fp32).
  * softmax_scale multiplies the scores before the softmax (1/sqrt(d) is the usual choice;
- * page "Flash Attention v2", "Detailed Algorithm Comparison", scores divided by sqrt(d)).
- * causal != 0 applies the causal mask. Deterministic: identical inputs give identical bits. */
+ * page "Flash Attention v2", "Detailed Algorithm Comparison", scores divided by sqrt(d)). Any
+ * finite value is valid: 0 weighs the visible keys equally (O_i is the mean of the visible V
+ * rows, LSE_i the log of their count), a negative value favours the smallest scores. It
+ * enters the kernels as |scale| * log2(e) with the sign carried by the queries (negated, or
+ * zeroed for 0). causal != 0 applies the causal mask. Deterministic: identical inputs give
+ * identical bits. */
 fa2_status fa2_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                    int B, int H, int N, int d, int causal, float softmax_scale,
                    hipStream_t stream);
@@ -93,8 +98,9 @@ fa2_status fa2_bwd(const void* q, const void* k, const void* v, const void* o,
  * fa2_bwd_workspace_bytes bytes bit for bit; the stages never split). All take the same
  * workspace.
  *
- * fa2_bwd_dq: dq [B,H,N,d] (bf16) from q, k, v, o, dout and lse. Parallel over blocks of 128
- *   queries; recomputes P and dP block by block, so no atomics are needed. It also fills the
+ * fa2_bwd_dq: dq [B,H,N,d] (bf16) from q, k, v, o, dout and lse. Parallel over blocks of 256
+ *   queries at d = 128 (128 at d = 64 and 256); recomputes P and dP block by block, so no
+ *   atomics are needed. It also fills the
  *   workspace with -D_i, D_i = sum_c dO_ic O_ic (equal to sum_j P_ij dP_ij, the row term of
  *   the softmax gradient), and LSE_i * log2(e) for fa2_bwd_dkdv. */
 fa2_status fa2_bwd_dq(const void* q, const void* k, const void* v, const void* o,
@@ -104,7 +110,8 @@ fa2_status fa2_bwd_dq(const void* q, const void* k, const void* v, const void* o
 
 /* fa2_bwd_dkdv: dk and dv [B,H,N,d] (bf16) from q, k, v, dout and a workspace filled by
  *   fa2_bwd_dq or fa2_bwd_preprocess (earlier on the same stream). Parallel over blocks of 128
- *   keys; recomputes P block by block. */
+ *   keys (64 at d = 256); recomputes P block by block. A scale <= 0 reaches this stage through
+ *   the resident K rows (negated, or zeroed for 0), dK = scale * dS^T Q as for any scale. */
 fa2_status fa2_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
                         const void* workspace, size_t workspace_bytes, void* dk, void* dv,
                         int B, int H, int N, int d, int causal, float softmax_scale,

@@ -67,8 +67,13 @@ P = 0x10000
     ((None, None, None, None, None, 1, 1, 0, 64, 0, float("nan")), ops.FA2_ERR_INVALID_ARGUMENT),
     ((P, P, P, P, P, 1, 1, 16, 64, 0, float("nan")), ops.FA2_ERR_INVALID_ARGUMENT),
     ((P, P, P, P, P, 1, 1, 16, 64, 0, float("inf")), ops.FA2_ERR_INVALID_ARGUMENT),
-    ((P, P, P, P, P, 1, 1, 16, 64, 0, 0.0), ops.FA2_ERR_INVALID_ARGUMENT),
-    ((P, P, P, P, P, 1, 1, 16, 64, 0, -0.5), ops.FA2_ERR_INVALID_ARGUMENT),
+    # any finite scale is accepted (0: uniform weights; < 0: reversed order), checked on
+    # empty problems so that nothing is launched; |scale| * log2(e) must be a finite float
+    ((None, None, None, None, None, 0, 1, 16, 64, 0, 0.0), ops.FA2_OK),
+    ((None, None, None, None, None, 0, 1, 16, 64, 1, -0.5), ops.FA2_OK),
+    ((None, None, None, None, None, 0, 1, 16, 64, 1, -3e38), ops.FA2_ERR_INVALID_ARGUMENT),
+    ((P, P, P, P, P, 1, 1, 16, 64, 0, 3e38), ops.FA2_ERR_INVALID_ARGUMENT),
+    ((P, P, P, P, P, 1, 1, 16, 64, 0, float("-inf")), ops.FA2_ERR_INVALID_ARGUMENT),
     ((P, P, P, P, P, 1, 1, 16, 96, 0, 0.125), ops.FA2_ERR_UNSUPPORTED),           # d = 96
     ((P, P, P, P, P, 1, 1, 16, 512, 1, 0.125), ops.FA2_ERR_UNSUPPORTED),
     ((P, P, P, P, P, 1 << 20, 1 << 10, 1 << 20, 128, 0, 0.1), ops.FA2_ERR_INVALID_ARGUMENT),
@@ -117,8 +122,13 @@ def test_bwd_validation_and_workspace():
         ops.FA2_ERR_UNSUPPORTED
     assert lib.fa2_bwd_dq(P, P, P, P, P, P, P, ws, None, 2, 3, 100, 64, 1, 0.1, None) == \
         ops.FA2_ERR_INVALID_ARGUMENT
-    assert lib.fa2_bwd_dq(P, P, P, P, P, P, P, ws, P, 2, 3, 100, 64, 1, -1.0, None) == \
+    assert lib.fa2_bwd_dq(P, P, P, P, P, P, P, ws, P, 2, 3, 100, 64, 1, 3e38, None) == \
         ops.FA2_ERR_INVALID_ARGUMENT
+    assert lib.fa2_bwd_dkdv(P, P, P, P, P, ws, P, P, 2, 3, 100, 64, 1, float("nan"), None) == \
+        ops.FA2_ERR_INVALID_ARGUMENT
+    # a negative or zero scale is valid (empty problem: nothing launched)
+    assert lib.fa2_bwd(*nul, 0, 2, 3, 0, 64, 1, -0.125, None) == ops.FA2_OK
+    assert lib.fa2_bwd(*nul, 0, 2, 3, 0, 64, 1, 0.0, None) == ops.FA2_OK
     assert lib.fa2_bwd_dq(P, P, P, None, P, P, P, ws, P, 2, 3, 100, 64, 1, 0.1, None) == \
         ops.FA2_ERR_INVALID_ARGUMENT  # null o
     assert lib.fa2_bwd_dq(P, P, P, P, P, P + 4, P, ws, P, 2, 3, 100, 64, 1, 0.1, None) == \

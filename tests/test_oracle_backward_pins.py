@@ -36,12 +36,12 @@ def _loss(q, k, v, do, causal, scale):
     return float(np.sum(o * do))
 
 
+@pytest.mark.parametrize("scale", [0.8, -0.8, 0.0])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("n,d", [(1, 2), (3, 2), (5, 4), (8, 4)])
-def test_finite_differences(n, d, causal):
+def test_finite_differences(n, d, causal, scale):
     shape = (1, 1, n, d)
     q, k, v, do = (_rand(shape, s) for s in (201, 202, 203, 204))
-    scale = 0.8
     grads = attention_backward(q, k, v, do, causal=causal, scale=scale)
     h = 1e-6
     for idx, (x, g) in enumerate(zip((q, k, v), grads)):
@@ -71,13 +71,18 @@ def test_diagonal_only_softmax_gradient_is_rejected():
     assert np.max(np.abs(dk_wrong - dk_true[0, 0])) > 1e-3
 
 
+@pytest.mark.parametrize("scale", [0.2, -0.2])
 @pytest.mark.parametrize("causal", [False, True])
-def test_matches_torch_autograd(causal):
+def test_matches_torch_autograd(causal, scale):
     shape = (2, 2, 29, 16)
     q, k, v, do = (_rand(shape, s) for s in (221, 222, 223, 224))
-    dq, dk, dv = attention_backward(q, k, v, do, causal=causal, scale=0.2, row_chunk=8)
+    dq, dk, dv = attention_backward(q, k, v, do, causal=causal, scale=scale, row_chunk=8)
     tq, tk, tv = (torch.from_numpy(x.copy()).requires_grad_() for x in (q, k, v))
-    to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=0.2)
+    # the causal mask as an explicit boolean mask (torch's is_causal path returns NaN for a
+    # negative scale: it masks with -inf before the scale multiplies)
+    mask = torch.ones(29, 29, dtype=torch.bool).tril() if causal else None
+    to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask,
+                                                          scale=scale)
     to.backward(torch.from_numpy(do))
     np.testing.assert_allclose(dq, tq.grad.numpy(), rtol=0, atol=1e-11)
     np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=0, atol=1e-11)

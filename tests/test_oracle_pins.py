@@ -51,11 +51,11 @@ def test_hand_examples_forward(ex, causal):
     np.testing.assert_allclose(lse[0, 0], np.array(_parse(ref["lse"])), rtol=0, atol=1e-14)
 
 
+@pytest.mark.parametrize("scale", [0.7, -0.7])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("n,d", [(1, 1), (2, 1), (3, 2), (5, 4), (8, 4), (8, 3)])
-def test_matches_bruteforce(n, d, causal):
+def test_matches_bruteforce(n, d, causal, scale):
     q, k, v = _rand((n, d), 1), _rand((n, d), 2), _rand((n, d), 3)
-    scale = 0.7
     ob, lb = attention_bruteforce(q.tolist(), k.tolist(), v.tolist(), causal=causal, scale=scale)
     o, lse = attention_forward(q[None, None], k[None, None], v[None, None], causal=causal,
                                scale=scale)
@@ -64,7 +64,7 @@ def test_matches_bruteforce(n, d, causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("scale", [None, 0.3])
+@pytest.mark.parametrize("scale", [None, 0.3, -0.3])
 def test_matches_torch_sdpa(causal, scale):
     """torch's CPU scaled_dot_product_attention (PyTorch's built-in attention, page
     'flashattention-2', 'Adoption') is an implementation written independently of this one."""
@@ -72,7 +72,10 @@ def test_matches_torch_sdpa(causal, scale):
     q, k, v = _rand(shape, 11), _rand(shape, 12), _rand(shape, 13)
     o, lse = attention_forward(q, k, v, causal=causal, scale=scale)
     tq, tk, tv = (torch.from_numpy(x) for x in (q, k, v))
-    to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=causal,
+    # the causal mask as an explicit boolean mask (torch's is_causal path returns NaN for a
+    # negative scale: it masks with -inf before the scale multiplies)
+    mask = torch.ones(37, 37, dtype=torch.bool).tril() if causal else None
+    to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask,
                                                           scale=scale)
     np.testing.assert_allclose(o, to.numpy(), rtol=0, atol=1e-12)
     # LSE against torch.logsumexp over the explicitly masked scores
