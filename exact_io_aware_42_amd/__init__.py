@@ -13,9 +13,10 @@ fallback path).
 """
 from .autograd import (FlashAttention, FlashAttentionKVPacked, flash_attn_func,
                        flash_attn_kvpacked_func)
-from .ops import (FA2Error, bwd, bwd_dkdv, bwd_dq, bwd_kvpacked, bwd_preprocess,
-                  bwd_workspace_bytes, fwd, fwd_kvpacked, load_library)
+from .ops import (FA2Error, bwd, bwd_dkdv, bwd_dq, bwd_kvpacked, bwd_noalloc,
+                  bwd_noalloc_max_rows, bwd_preprocess, bwd_workspace_bytes, fwd, fwd_kvpacked,
+                  load_library)
 
 __all__ = ["fwd", "bwd", "fwd_kvpacked", "bwd_kvpacked", "bwd_preprocess", "bwd_dkdv", "bwd_dq",
-           "bwd_workspace_bytes", "load_library", "FA2Error", "FlashAttention",
+           "bwd_noalloc", "bwd_noalloc_max_rows", "bwd_workspace_bytes", "load_library", "FA2Error", "FlashAttention",
            "FlashAttentionKVPacked", "flash_attn_func", "flash_attn_kvpacked_func"]

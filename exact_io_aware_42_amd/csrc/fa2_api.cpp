@@ -206,15 +206,10 @@ void set_kv_split(fa2::BwdArgs* a, void* workspace, size_t workspace_bytes) {
   }
 }
 
-fa2_status bwd_args(const void* q, const void* k, const void* v, const void* o, const void* dout,
-                    const float* lse, void* workspace, size_t workspace_bytes, void* dq, void* dk,
-                    void* dv, int B, int H, int N, int d, int causal, float softmax_scale,
-                    hipStream_t stream, fa2::BwdArgs* a, bool* empty) {
-  const fa2_status st = check_sizes(B, H, N, d, softmax_scale, empty);
-  if (st != FA2_OK || *empty) return st;
-  if (workspace == nullptr || !aligned16(workspace) ||
-      workspace_bytes < fa2_bwd_workspace_bytes(B, H, N, d))
-    return FA2_ERR_INVALID_ARGUMENT;
+// The backward argument block without its workspace fields (sizes already validated).
+void fill_bwd_args(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                   int causal, float softmax_scale, hipStream_t stream, fa2::BwdArgs* a) {
   a->q = q;
   a->k = k;
   a->v = v;
@@ -224,8 +219,6 @@ fa2_status bwd_args(const void* q, const void* k, const void* v, const void* o, 
   a->dq = dq;
   a->dk = dk;
   a->dv = dv;
-  a->delta = static_cast<float*>(workspace);
-  a->lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws_part_bytes(B, H, N));
   a->B = B;
   a->H = H;
   a->N = N;
@@ -239,6 +232,20 @@ fa2_status bwd_args(const void* q, const void* k, const void* v, const void* o, 
   a->sgn_and = sf.and_mask;
   a->sgn_xor = sf.xor_mask;
   a->stream = stream;
+}
+
+fa2_status bwd_args(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                    const float* lse, void* workspace, size_t workspace_bytes, void* dq, void* dk,
+                    void* dv, int B, int H, int N, int d, int causal, float softmax_scale,
+                    hipStream_t stream, fa2::BwdArgs* a, bool* empty) {
+  const fa2_status st = check_sizes(B, H, N, d, softmax_scale, empty);
+  if (st != FA2_OK || *empty) return st;
+  if (workspace == nullptr || !aligned16(workspace) ||
+      workspace_bytes < fa2_bwd_workspace_bytes(B, H, N, d))
+    return FA2_ERR_INVALID_ARGUMENT;
+  fill_bwd_args(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, causal, softmax_scale, stream, a);
+  a->delta = static_cast<float*>(workspace);
+  a->lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + ws_part_bytes(B, H, N));
   return FA2_OK;
 }
 
@@ -263,6 +270,24 @@ fa2_status fa2_bwd(const void* q, const void* k, const void* v, const void* o, c
   set_kv_split(&a, workspace, workspace_bytes);
   return from_hip(fa2::launch_bwd(a));
 }
+
+fa2_status fa2_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                           int B, int H, int N, int d, int causal, float softmax_scale,
+                           hipStream_t stream) {
+  bool empty;
+  const fa2_status st = check_sizes(B, H, N, d, softmax_scale, &empty);
+  if (st != FA2_OK || empty) return st;
+  if (!all_ok({q, k, v, o, dout, lse, dq, dk, dv})) return FA2_ERR_INVALID_ARGUMENT;
+  const size_t part = ws_part_bytes(B, H, N);
+  if (2 * part > fa2::kBwdScratchBytes) return FA2_ERR_SCRATCH_LIMIT;
+  // fa2_bwd's arguments; the workspace parts come from the static scratch array
+  fa2::BwdArgs a;
+  fill_bwd_args(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, causal, softmax_scale, stream, &a);
+  return from_hip(fa2::launch_bwd_noalloc(a, part));
+}
+
+size_t fa2_bwd_noalloc_max_rows(void) { return fa2::kBwdScratchBytes / (2 * sizeof(float)); }
 
 fa2_status fa2_bwd_gqa(const void* q, const void* k, const void* v, const void* o,
                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
@@ -360,6 +385,8 @@ const char* fa2_status_string(fa2_status s) {
       return "FA2_ERR_UNSUPPORTED";
     case FA2_ERR_HIP:
       return "FA2_ERR_HIP";
+    case FA2_ERR_SCRATCH_LIMIT:
+      return "FA2_ERR_SCRATCH_LIMIT";
   }
   return "FA2_UNKNOWN_STATUS";
 }

@@ -29,6 +29,7 @@
 // segments. With dropout (DROP) every kernel regenerates the keep bits it needs from the
 // counter-based hash (fa2_device.hpp); dS = P * (Z * dP / P(keep) - D) and dV takes
 // P * Z / P(keep).
+#include <mutex>
 #include <type_traits>
 
 #include "fa2_device.hpp"
@@ -1105,6 +1106,50 @@ hipError_t launch_bwd(const BwdArgs& a) {
   const hipError_t e = launch_bwd_dq(a);  // also fills the workspace (D, LSE*log2(e))
   if (e != hipSuccess) return e;
   return launch_bwd_dkdv(a);
+}
+
+// ---------------------------------------------------------------------------------------
+// Backward without a caller workspace, for callers that cannot allocate device memory. The
+// workspace (-D and LSE*log2(e), two fp32 [B*H*N] parts at 256-byte boundaries) lives in this
+// file-scope array instead: kBwdScratchBytes on every GPU the library runs on, held from module
+// load until the process ends. Each call on a GPU reuses that GPU's copy (the dQ kernel writes
+// every value the dK/dV kernel reads, so nothing needs clearing), so calls that overlap on one
+// GPU race.
+static __device__ __align__(256) unsigned char scratch[kBwdScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};  // device address of `scratch`, per device
+
+// The current device's copy of `scratch`: looked up once per device (with that device current)
+// by hipGetSymbolAddress, since the array's name is only a host-side stand-in.
+hipError_t scratch_for_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_bwd_noalloc(BwdArgs a, size_t part_bytes) {
+  void* base = nullptr;
+  const hipError_t e = scratch_for_current_device(&base);
+  if (e != hipSuccess) return e;
+  a.delta = static_cast<float*>(base);
+  a.lse2 = reinterpret_cast<float*>(static_cast<unsigned char*>(base) + part_bytes);
+  a.kv_split = 1;
+  a.kv_part = nullptr;
+  return launch_bwd(a);
 }
 
 }  // namespace fa2

@@ -78,10 +78,17 @@ inline int dkdv_split(int B, int H, int Hkv, int N, int d) {
     if (base * s >= kDkdvMinWorkgroups) return s;
   return kDkdvMaxSplit;
 }
+// Size of the backward scratch array that fa2_bwd_noalloc uses in place of a workspace (per
+// GPU): room for -D and LSE*log2(e) of up to 2M (batch, head, query) rows.
+constexpr size_t kBwdScratchBytes = size_t(16) << 20;
+
 hipError_t launch_fwd(const FwdArgs& a);
 hipError_t launch_bwd(const BwdArgs& a);  // dQ (also D and LSE*log2(e)), then dK/dV
 hipError_t launch_bwd_pre(const BwdArgs& a);
 hipError_t launch_bwd_dkdv(const BwdArgs& a);
 hipError_t launch_bwd_dq(const BwdArgs& a);
+// launch_bwd with the workspace parts (each part_bytes long) in the library's static scratch
+// array of the current device; a.delta, a.lse2 and the split fields are replaced
+hipError_t launch_bwd_noalloc(BwdArgs a, size_t part_bytes);
 
 }  // namespace fa2

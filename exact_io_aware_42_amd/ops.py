@@ -22,11 +22,12 @@ FA2_OK = 0
 FA2_ERR_INVALID_ARGUMENT = 1
 FA2_ERR_UNSUPPORTED = 2
 FA2_ERR_HIP = 3
+FA2_ERR_SCRATCH_LIMIT = 4
 
 EXPORTED = ("fa2_fwd", "fa2_bwd", "fa2_bwd_workspace_bytes", "fa2_bwd_preprocess",
             "fa2_bwd_dkdv", "fa2_bwd_dq", "fa2_fwd_gqa", "fa2_bwd_gqa", "fa2_fwd_dropout",
-            "fa2_bwd_dropout", "fa2_bwd_gqa_workspace_bytes", "fa2_status_string",
-            "fa2_last_hip_error")
+            "fa2_bwd_dropout", "fa2_bwd_gqa_workspace_bytes", "fa2_bwd_noalloc",
+            "fa2_bwd_noalloc_max_rows", "fa2_status_string", "fa2_last_hip_error")
 
 _lib = None
 _lock = threading.Lock()
@@ -74,6 +75,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.fa2_bwd_workspace_bytes.restype = sz
         lib.fa2_bwd_gqa_workspace_bytes.argtypes = [i, i, i, i, i]
         lib.fa2_bwd_gqa_workspace_bytes.restype = sz
+        lib.fa2_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+        lib.fa2_bwd_noalloc.restype = i
+        lib.fa2_bwd_noalloc_max_rows.argtypes = []
+        lib.fa2_bwd_noalloc_max_rows.restype = sz
         lib.fa2_status_string.argtypes = [i]
         lib.fa2_status_string.restype = ctypes.c_char_p
         lib.fa2_last_hip_error.argtypes = []
@@ -254,6 +259,30 @@ def bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None,
                              _stream_ptr(dev))
     _check(st, "fa2_bwd")
     return dq, dk, dv
+
+
+def bwd_noalloc(q, k, v, o, dout, lse, dq, dk, dv, causal: bool = False,
+                scale: float | None = None):
+    """Backward into caller-given dq, dk, dv with the library's static scratch in place of a
+    workspace (fa2_bwd_noalloc: nothing is allocated, here or in the library). Same results
+    as bwd with the minimum workspace; B*H*N at most fa2_bwd_noalloc_max_rows()."""
+    lib = load_library()
+    B, H, N, d = q.shape
+    dev = q.device
+    for t, nm in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout"), (dq, "dq"),
+                  (dk, "dk"), (dv, "dv")):
+        _check_tensor(t, nm, (B, H, N, d), device=dev)
+    _check_tensor(lse, "lse", (B, H, N), dtype=torch.float32, device=dev)
+    s = default_scale(d) if scale is None else float(scale)
+    st = lib.fa2_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                             dout.data_ptr(), lse.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                             dv.data_ptr(), B, H, N, d, int(bool(causal)), s, _stream_ptr(dev))
+    _check(st, "fa2_bwd_noalloc")
+    return dq, dk, dv
+
+
+def bwd_noalloc_max_rows() -> int:
+    return int(load_library().fa2_bwd_noalloc_max_rows())
 
 
 def bwd_kvpacked(q, kv, o, dout, lse, causal: bool = False, scale: float | None = None):

@@ -60,7 +60,8 @@ typedef enum fa2_status {
   FA2_OK = 0,
   FA2_ERR_INVALID_ARGUMENT = 1,
   FA2_ERR_UNSUPPORTED = 2,
-  FA2_ERR_HIP = 3
+  FA2_ERR_HIP = 3,
+  FA2_ERR_SCRATCH_LIMIT = 4  /* fa2_bwd_noalloc: the problem exceeds the static scratch */
 } fa2_status;
 
 /* Forward pass. Writes o [B,H,N,d] (bf16) and lse [B,H,N] (fp32).
@@ -183,6 +184,24 @@ fa2_status fa2_bwd_dropout(const void* q, const void* k, const void* v, const vo
                            int N, int d, long long kv_batch_stride, int causal,
                            float softmax_scale, float dropout_p, unsigned long long seed,
                            unsigned long long offset, hipStream_t stream);
+
+/* Backward without a workspace argument, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation). Arguments and
+ * results as fa2_bwd with a workspace of fa2_bwd_workspace_bytes(B, H, N, d) bytes (the same
+ * kernels, so the same bits; no dK/dV split). The workspace is a static array of 16 MiB inside
+ * the library, one per GPU, held from the library's load until the process ends; it fits
+ * B*H*N <= fa2_bwd_noalloc_max_rows() (2^21) rows, larger problems return
+ * FA2_ERR_SCRATCH_LIMIT before any HIP call. The first call on a device looks up that device's
+ * copy (hipGetSymbolAddress, no allocation); no call allocates or frees memory. Every call on
+ * a GPU shares its copy, so calls that overlap on one GPU (other streams, other threads)
+ * race: order them on one stream or serialise them. */
+fa2_status fa2_bwd_noalloc(const void* q, const void* k, const void* v, const void* o,
+                           const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                           int B, int H, int N, int d, int causal, float softmax_scale,
+                           hipStream_t stream);
+
+/* The most (batch, head, query) rows fa2_bwd_noalloc accepts: B*H*N up to this value. */
+size_t fa2_bwd_noalloc_max_rows(void);
 
 /* Static, human-readable name of a status code. */
 const char* fa2_status_string(fa2_status s);

@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol():
 def test_status_strings():
     lib = _lib()
     for code, name in ((0, "FA2_OK"), (1, "FA2_ERR_INVALID_ARGUMENT"), (2, "FA2_ERR_UNSUPPORTED"),
-                       (3, "FA2_ERR_HIP")):
+                       (3, "FA2_ERR_HIP"), (4, "FA2_ERR_SCRATCH_LIMIT")):
         assert lib.fa2_status_string(code).decode() == name
     assert lib.fa2_last_hip_error() == 0
 
@@ -286,3 +286,30 @@ def test_grouped_workspace_size_invalid():
     assert lib.fa2_bwd_gqa_workspace_bytes(2, 8, 0, 64, 128) == 0
     assert lib.fa2_bwd_gqa_workspace_bytes(2, 8, 2, 0, 128) == 0    # empty
     assert lib.fa2_bwd_gqa_workspace_bytes(2, 8, 2, 64, 96) == 0    # unsupported d
+
+
+def test_noalloc_validation_and_limit():
+    """fa2_bwd_noalloc validates like fa2_bwd and refuses problems beyond its static scratch
+    (B*H*N rows above fa2_bwd_noalloc_max_rows) before any HIP call."""
+    lib = _lib()
+    max_rows = lib.fa2_bwd_noalloc_max_rows()
+    assert max_rows == 1 << 21
+    nul = [None] * 9
+    assert lib.fa2_bwd_noalloc(*nul, 0, 2, 3, 64, 1, 0.125, None) == ops.FA2_OK  # empty
+    base = [P] * 9
+    assert lib.fa2_bwd_noalloc(*base, 2, 3, 100, 96, 1, 0.125, None) == ops.FA2_ERR_UNSUPPORTED
+    assert lib.fa2_bwd_noalloc(*base, 2, 3, 100, 64, 1, float("nan"), None) == \
+        ops.FA2_ERR_INVALID_ARGUMENT
+    args = list(base)
+    args[6] = None  # null dq
+    assert lib.fa2_bwd_noalloc(*args, 2, 3, 100, 64, 1, 0.125, None) == \
+        ops.FA2_ERR_INVALID_ARGUMENT
+    args = list(base)
+    args[5] = P + 4  # misaligned lse
+    assert lib.fa2_bwd_noalloc(*args, 2, 3, 100, 64, 1, 0.125, None) == \
+        ops.FA2_ERR_INVALID_ARGUMENT
+    # one row past the limit: B*H*N = 2^21 + 1 (as 1 x 1 x N), and a larger batch
+    assert lib.fa2_bwd_noalloc(*base, 1, 1, max_rows + 1, 64, 0, 0.125, None) == \
+        ops.FA2_ERR_SCRATCH_LIMIT
+    assert lib.fa2_bwd_noalloc(*base, 8, 32, 16384, 128, 1, 0.125, None) == \
+        ops.FA2_ERR_SCRATCH_LIMIT
