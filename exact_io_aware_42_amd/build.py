@@ -1,8 +1,9 @@
 """Build libfa2.so in-tree with hipcc for gfx950.
 
-    python -m exact_io_aware_42_amd.build
+    python -m exact_io_aware_42_amd.build [--all]
 
-Compiles the HIP kernels and the C ABI into exact_io_aware_42_amd/libfa2.so. Packed-fp32
+Compiles the HIP kernels and the C ABI into exact_io_aware_42_amd/libfa2.so (with --all also
+libfa2_debug_sync.so, the race-check build). Packed-fp32
 VALU instructions are disabled for all device code.
 """
 from __future__ import annotations
@@ -17,6 +18,9 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libfa2.so")
+# the same sources with an extra wait and workgroup barrier at every LDS stage hand-over
+# (FA2_DEBUG_SYNC); its outputs must equal libfa2.so's bit for bit (a race check)
+DEBUG_SYNC_LIB_PATH = os.path.join(PKG_DIR, "libfa2_debug_sync.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["fa2_api.cpp", "fa2_fwd.hip", "fa2_bwd.hip"]
@@ -74,5 +78,15 @@ def build(verbose: bool = False, extra_flags=None, out_path: str = LIB_PATH) -> 
     return out_path
 
 
+def build_all(verbose: bool = False):
+    """libfa2.so and its FA2_DEBUG_SYNC twin; returns both paths."""
+    return (build(verbose=verbose),
+            build(verbose=verbose, extra_flags=["-DFA2_DEBUG_SYNC"],
+                  out_path=DEBUG_SYNC_LIB_PATH))
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--all" in sys.argv:
+        print(*build_all(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -374,7 +374,9 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
   StepPos cur(t_begin, nt, qt_begin);  // the tile of the current step
   auto step = [&](auto stage_c, int t) {
     constexpr int stage = decltype(stage_c)::value;
+    FA2_STAGE_SYNC();
     if (t + 1 < n_steps) load_stage(t + 1, stage ^ 1);
+    FA2_STAGE_SYNC();
     const int it = cur.it;
     cur.next();
     const int q0 = it * kKvBQ + 32 * hq;  // this wave's 32 queries
@@ -470,6 +472,7 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
       }
       __builtin_amdgcn_s_setprio(0);
     }
+    FA2_STAGE_SYNC();
     wait_vmem();
     __syncthreads();
   };
@@ -664,7 +667,9 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
   StepPos cur(t_begin, nt, qt_begin);  // the tile of the current step
   auto step = [&](auto stage_c, int t) {
     constexpr int stage = decltype(stage_c)::value;
+    FA2_STAGE_SYNC();
     if (t + 1 < n_steps) load_stage(t + 1, stage ^ 1);
+    FA2_STAGE_SYNC();
     const int it = cur.it;
     cur.next();
     const int q0 = it * kKv256BQ;
@@ -741,6 +746,7 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
       }
       __builtin_amdgcn_s_setprio(0);
     }
+    FA2_STAGE_SYNC();
     wait_vmem();
     __syncthreads();
   };
@@ -890,7 +896,9 @@ __global__ __launch_bounds__((DqShape<D>::THREADS), (DqShape<D>::OCC)) void fa2_
   // unrolled by two below: the stage is a compile-time constant
   auto step = [&](auto stage_c, int j) {
     constexpr int stage = decltype(stage_c)::value;
+    FA2_STAGE_SYNC();
     if (j + 1 < n_tiles) load_stage(j + 1, stage ^ 1);
+    FA2_STAGE_SYNC();
     if (j <= wave_last) {
       const unsigned char* tk = smem + stage * STAGE;
       const unsigned char* tv = tk + TILE;
@@ -946,6 +954,7 @@ __global__ __launch_bounds__((DqShape<D>::THREADS), (DqShape<D>::OCC)) void fa2_
       }
       __builtin_amdgcn_s_setprio(0);
     }
+    FA2_STAGE_SYNC();
     wait_vmem();
     __syncthreads();
   };

@@ -52,6 +52,23 @@ __device__ __forceinline__ u32x2_t lds_read_tr16(const void* p) {
 // Wait until this wave's outstanding vector-memory loads (including loads into LDS) are done.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Extra synchronisation for race checks (builds with -DFA2_DEBUG_SYNC): at every hand-over of an
+// LDS stage, each wave waits for all of its outstanding loads and the workgroup meets at a
+// barrier, so no tile is read before every wave's loads into it have landed and no stage is
+// refilled while a wave may still read it, whatever the normal build's waits allow. Results
+// must not change by a single bit; the normal build compiles this away.
+#ifdef FA2_DEBUG_SYNC
+#define FA2_STAGE_SYNC()  \
+  do {                    \
+    wait_vmem();          \
+    __syncthreads();      \
+  } while (0)
+#else
+#define FA2_STAGE_SYNC() \
+  do {                   \
+  } while (0)
+#endif
+
 constexpr float kLn2 = 0.69314718055994530942f;
 
 // D(32x32) += A(32x16) * B(16x32), bf16 inputs, fp32 accumulate (v_mfma_f32_32x32x16_bf16).

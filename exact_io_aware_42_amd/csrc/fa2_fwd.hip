@@ -304,10 +304,12 @@ __global__ __launch_bounds__(FwdShape<D>::THREADS, FA2_FWD_OCC) void fa2_fwd_ker
   auto step = [&](auto slot_c, int j) {
     constexpr int slot = decltype(slot_c)::value;
     // slot ^ 1 held tile j-1, whose readers all passed the barrier that ended step j-1
+    FA2_STAGE_SYNC();
     if (j + 1 < n_tiles) {
       load_k(j + 1, slot ^ 1);
       load_v(j + 1, slot ^ 1);
     }
+    FA2_STAGE_SYNC();
     if (j <= wave_last) {
       f32x16_t s[S::KB];
       const bool masked = tile_needs_mask(j);
@@ -348,6 +350,7 @@ __global__ __launch_bounds__(FwdShape<D>::THREADS, FA2_FWD_OCC) void fa2_fwd_ker
       __builtin_amdgcn_s_setprio(0);
       if (!DROP && masked) bf16_correction(pk, tile_sum);
     }
+    FA2_STAGE_SYNC();
     wait_vmem();
     __syncthreads();
   };

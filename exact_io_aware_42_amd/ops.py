@@ -41,50 +41,55 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     """Load libfa2.so once and declare its signatures. Raises if it has not been built."""
     global _lib
     with _lock:
-        if _lib is not None:
-            return _lib
-        if not os.path.exists(path):
-            raise FA2Error(f"{path} is missing: build it with "
-                           "`python -m exact_io_aware_42_amd.build` (no fallback exists)")
-        lib = ctypes.CDLL(path)
-        vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
-        ll, ull = ctypes.c_longlong, ctypes.c_ulonglong
-        lib.fa2_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
-        lib.fa2_fwd.restype = i
-        lib.fa2_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
-                                i, i, i, i, i, f, vp]
-        lib.fa2_bwd.restype = i
-        lib.fa2_bwd_preprocess.argtypes = [vp, vp, vp, vp, sz, i, i, i, i, vp]
-        lib.fa2_bwd_preprocess.restype = i
-        lib.fa2_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, sz, vp, vp, i, i, i, i, i, f, vp]
-        lib.fa2_bwd_dkdv.restype = i
-        lib.fa2_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, vp, i, i, i, i, i, f, vp]
-        lib.fa2_bwd_dq.restype = i
-        lib.fa2_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, ll, i, f, vp]
-        lib.fa2_fwd_gqa.restype = i
-        lib.fa2_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
-                                    i, i, i, i, i, ll, i, f, vp]
-        lib.fa2_bwd_gqa.restype = i
-        lib.fa2_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, ll, i, f, f, ull, ull,
-                                        vp]
-        lib.fa2_fwd_dropout.restype = i
-        lib.fa2_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
-                                        i, i, i, i, i, ll, i, f, f, ull, ull, vp]
-        lib.fa2_bwd_dropout.restype = i
-        lib.fa2_bwd_workspace_bytes.argtypes = [i, i, i, i]
-        lib.fa2_bwd_workspace_bytes.restype = sz
-        lib.fa2_bwd_gqa_workspace_bytes.argtypes = [i, i, i, i, i]
-        lib.fa2_bwd_gqa_workspace_bytes.restype = sz
-        lib.fa2_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
-        lib.fa2_bwd_noalloc.restype = i
-        lib.fa2_bwd_noalloc_max_rows.argtypes = []
-        lib.fa2_bwd_noalloc_max_rows.restype = sz
-        lib.fa2_status_string.argtypes = [i]
-        lib.fa2_status_string.restype = ctypes.c_char_p
-        lib.fa2_last_hip_error.argtypes = []
-        lib.fa2_last_hip_error.restype = i
-        _lib = lib
-        return lib
+        if _lib is None:
+            _lib = open_library(path)
+        return _lib
+
+
+def open_library(path: str) -> ctypes.CDLL:
+    """A new handle on a build of the library at `path` (e.g. the FA2_DEBUG_SYNC build), with
+    its signatures declared; not cached. Raises if the file is missing."""
+    if not os.path.exists(path):
+        raise FA2Error(f"{path} is missing: build it with "
+                       "`python -m exact_io_aware_42_amd.build` (no fallback exists)")
+    lib = ctypes.CDLL(path)
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    ll, ull = ctypes.c_longlong, ctypes.c_ulonglong
+    lib.fa2_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+    lib.fa2_fwd.restype = i
+    lib.fa2_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                            i, i, i, i, i, f, vp]
+    lib.fa2_bwd.restype = i
+    lib.fa2_bwd_preprocess.argtypes = [vp, vp, vp, vp, sz, i, i, i, i, vp]
+    lib.fa2_bwd_preprocess.restype = i
+    lib.fa2_bwd_dkdv.argtypes = [vp, vp, vp, vp, vp, sz, vp, vp, i, i, i, i, i, f, vp]
+    lib.fa2_bwd_dkdv.restype = i
+    lib.fa2_bwd_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, sz, vp, i, i, i, i, i, f, vp]
+    lib.fa2_bwd_dq.restype = i
+    lib.fa2_fwd_gqa.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, ll, i, f, vp]
+    lib.fa2_fwd_gqa.restype = i
+    lib.fa2_bwd_gqa.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                i, i, i, i, i, ll, i, f, vp]
+    lib.fa2_bwd_gqa.restype = i
+    lib.fa2_fwd_dropout.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, ll, i, f, f, ull, ull,
+                                    vp]
+    lib.fa2_fwd_dropout.restype = i
+    lib.fa2_bwd_dropout.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                    i, i, i, i, i, ll, i, f, f, ull, ull, vp]
+    lib.fa2_bwd_dropout.restype = i
+    lib.fa2_bwd_workspace_bytes.argtypes = [i, i, i, i]
+    lib.fa2_bwd_workspace_bytes.restype = sz
+    lib.fa2_bwd_gqa_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.fa2_bwd_gqa_workspace_bytes.restype = sz
+    lib.fa2_bwd_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, f, vp]
+    lib.fa2_bwd_noalloc.restype = i
+    lib.fa2_bwd_noalloc_max_rows.argtypes = []
+    lib.fa2_bwd_noalloc_max_rows.restype = sz
+    lib.fa2_status_string.argtypes = [i]
+    lib.fa2_status_string.restype = ctypes.c_char_p
+    lib.fa2_last_hip_error.argtypes = []
+    lib.fa2_last_hip_error.restype = i
+    return lib
 
 
 def _check(status: int, what: str):
