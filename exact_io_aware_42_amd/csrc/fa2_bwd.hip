@@ -220,8 +220,8 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse2, const float* __restrict__ delta, uint16_t* __restrict__ dk,
-    uint16_t* __restrict__ dv, int N, int n_kblocks, int bh_count, int n_qheads, int group,
-    long long kv_bstride, float scale_log2, float scale, OperandSign ksign, DropParams drop,
+    uint16_t* __restrict__ dv, int N, int n_kblocks, int bh_count, int window, int n_qheads,
+    int group, long long kv_bstride, float scale_log2, float scale, OperandSign ksign, DropParams drop,
     float* __restrict__ part, int split) {
   constexpr int KK = D / 16, CB = D / 32, DCH = D / 8;
   // LDS: the two ring stages of Q and dO tiles at the bottom (every ds_read of them is a
@@ -249,7 +249,7 @@ __global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
 
   // causal: key block 0 sees every query tile, so ascending order is longest first
   const TileCoord tc = schedule_tile<CAUSAL ? Order::kLongAscending : Order::kHeadMajor>(
-      blockIdx.x, n_kblocks, bh_count);
+      blockIdx.x, n_kblocks, bh_count, window);
   // tc.bh = (batch * Hkv + K/V head) * split + part. The query heads sharing this K/V head
   // are qh0 .. qh0 + group - 1; their (head, query tile) steps are summed here in order, part
   // sj taking the sj-th of `split` equal ranges of them (split > 1: into fp32 partial sums that
@@ -538,8 +538,8 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
     const float* __restrict__ lse2, const float* __restrict__ delta, uint16_t* __restrict__ dk,
-    uint16_t* __restrict__ dv, int N, int n_kblocks, int bh_count, int n_qheads, int group,
-    long long kv_bstride, float scale_log2, float scale, OperandSign ksign, DropParams drop,
+    uint16_t* __restrict__ dv, int N, int n_kblocks, int bh_count, int window, int n_qheads,
+    int group, long long kv_bstride, float scale_log2, float scale, OperandSign ksign, DropParams drop,
     float* __restrict__ part, int split) {
   constexpr int D = 256, KK = D / 16, CB = D / 32, DCH = D / 8;
   constexpr int TILE = kKv256BQ * D * 2;          // 16 KiB
@@ -560,7 +560,7 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
   const int g = lane >> 5;
 
   const TileCoord tc = schedule_tile<CAUSAL ? Order::kLongAscending : Order::kHeadMajor>(
-      blockIdx.x, n_kblocks, bh_count);
+      blockIdx.x, n_kblocks, bh_count, window);
   // tc.bh = (batch * Hkv + K/V head) * split + part, as in the d <= 128 kernel
   const int sj = tc.bh % split;
   const int bhkv = tc.bh / split;
@@ -795,7 +795,7 @@ __global__ __launch_bounds__((DqShape<D>::THREADS), (DqShape<D>::OCC)) void fa2_
     const uint16_t* __restrict__ v, const uint16_t* __restrict__ o,
     const uint16_t* __restrict__ dout, const float* __restrict__ lse, float* __restrict__ lse2,
     float* __restrict__ delta, uint16_t* __restrict__ dq, int N, int n_qblocks, int bh_count,
-    int n_qheads, int group, long long kv_bstride, float scale_log2, float scale,
+    int window, int n_qheads, int group, long long kv_bstride, float scale_log2, float scale,
     OperandSign qsign, DropParams drop) {
   constexpr int KK = D / 16, CB = D / 32;
   constexpr int BC = D == 256 ? 32 : 64;   // keys per tile
@@ -814,7 +814,7 @@ __global__ __launch_bounds__((DqShape<D>::THREADS), (DqShape<D>::OCC)) void fa2_
   const int g = lane >> 5;
 
   const TileCoord tc = schedule_tile<CAUSAL ? Order::kLongDescending : Order::kHeadMajor>(
-      blockIdx.x, n_qblocks, bh_count);
+      blockIdx.x, n_qblocks, bh_count, window);
   const size_t head_off = (size_t)tc.bh * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
   const __amdgpu_buffer_rsrc_t rq = make_rsrc(q + head_off, head_bytes);
@@ -1037,7 +1037,11 @@ hipError_t launch_dkdv_t(const BwdArgs& a) {
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                      static_cast<const uint16_t*>(a.dout), a.lse2, a.delta,
                      static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), a.N, n_kblocks,
-                     a.B * a.Hkv * a.kv_split, a.H, a.H / a.Hkv, a.kv_bstride, a.scale_log2,
+                     a.B * a.Hkv * a.kv_split,
+                     causal_window(a.B * a.Hkv * a.kv_split,
+                                   4ll * a.N * D * (a.H / a.Hkv) / a.kv_split, n_kblocks, 1,
+                                   window_budget(D)),
+                     a.H, a.H / a.Hkv, a.kv_bstride, a.scale_log2,
                      a.scale, OperandSign{a.sgn_and, a.sgn_xor},
                      DropParams{a.drop_k0, a.drop_k1, a.drop_thr, a.drop_scale},
                      a.kv_split > 1 ? a.kv_part : nullptr, a.kv_split);
@@ -1054,7 +1058,9 @@ hipError_t launch_dq_t(const BwdArgs& a) {
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                      static_cast<const uint16_t*>(a.o), static_cast<const uint16_t*>(a.dout),
                      a.lse, a.lse2, a.delta, static_cast<uint16_t*>(a.dq), a.N, n_qblocks,
-                     a.B * a.H, a.H, a.H / a.Hkv, a.kv_bstride, a.scale_log2, a.scale,
+                     a.B * a.H, causal_window(a.B * a.H, 4ll * a.N * D, n_qblocks, D == 64 ? 2 : 1,
+                                   window_budget(D)),
+                     a.H, a.H / a.Hkv, a.kv_bstride, a.scale_log2, a.scale,
                      OperandSign{a.sgn_and, a.sgn_xor},
                      DropParams{a.drop_k0, a.drop_k1, a.drop_thr, a.drop_scale});
   return hipGetLastError();
@@ -1077,7 +1083,11 @@ hipError_t launch_dkdv256_t(const BwdArgs& a) {
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                      static_cast<const uint16_t*>(a.dout), a.lse2, a.delta,
                      static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), a.N, n_kblocks,
-                     a.B * a.Hkv * a.kv_split, a.H, a.H / a.Hkv, a.kv_bstride, a.scale_log2,
+                     a.B * a.Hkv * a.kv_split,
+                     causal_window(a.B * a.Hkv * a.kv_split,
+                                   4ll * a.N * 256 * (a.H / a.Hkv) / a.kv_split, n_kblocks, 1,
+                                   window_budget(256)),
+                     a.H, a.H / a.Hkv, a.kv_bstride, a.scale_log2,
                      a.scale, OperandSign{a.sgn_and, a.sgn_xor},
                      DropParams{a.drop_k0, a.drop_k1, a.drop_thr, a.drop_scale},
                      a.kv_split > 1 ? a.kv_part : nullptr, a.kv_split);

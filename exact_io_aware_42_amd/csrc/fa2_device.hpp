@@ -272,19 +272,26 @@ __device__ __forceinline__ void mask_queries(f32x16_t& s, int q_base, int my_key
 // x, x+8, ... only.
 //  * kHeadMajor (equal-length blocks, no mask): an XCD runs one head's blocks back to back,
 //    so that head's K/V tiles are re-read from its L2.
-//  * kLongDescending / kLongAscending (causal: block lengths differ): an XCD deals the blocks
-//    of all its heads longest first (rank-major over its heads: a list schedule in
-//    longest-processing-time order, so no long block starts near the end). Descending: the
-//    highest block index is the longest (query blocks of the forward and dQ); ascending: the
-//    lowest is (key blocks of dK/dV). Blocks of one head that run together walk the same K/V
-//    (or Q/dO) tiles in step, which keeps the L2 working set small.
+//  * kLongDescending / kLongAscending (causal: block lengths differ): an XCD takes its heads in
+//    windows of `window` heads and deals each window's blocks longest first (rank-major over
+//    the window's heads: a list schedule in longest-processing-time order, so no long block
+//    starts near the end of the window), one window after the other. The window is as many
+//    heads as a budget of L2 bytes holds the streamed tiles of (at least enough blocks to fill
+//    the XCD), so the blocks in flight walk the tiles of fewer heads. At d = 64 (three forward
+//    workgroups per CU, 96 blocks of 32 heads in flight) dealing all heads at once moved 3.8x
+//    the compulsory bytes and bound the forward on memory; windows of 16 heads cut that and ran
+//    the forward 6.6% faster. At d >= 128 the kernels are not bound by these refetches and
+//    smaller windows measured neutral to 3% slower, so the window is all of the XCD's heads.
+//    Descending: the highest block index is the longest (query blocks of the forward and dQ);
+//    ascending: the lowest is (key blocks of dK/dV).
 enum class Order { kHeadMajor, kLongDescending, kLongAscending };
 struct TileCoord {
   int qb;
   int bh;
 };
 template <Order O>
-__device__ __forceinline__ TileCoord schedule_tile(int wg, int n_blocks, int bh_count) {
+__device__ __forceinline__ TileCoord schedule_tile(int wg, int n_blocks, int bh_count,
+                                                   int window) {
   int r, bh;
   if ((bh_count & 7) == 0) {
     const int xcd = wg & 7;
@@ -294,8 +301,17 @@ __device__ __forceinline__ TileCoord schedule_tile(int wg, int n_blocks, int bh_
       r = j % n_blocks;
     } else {
       const int hpx = bh_count >> 3;
-      bh = (j % hpx) * 8 + xcd;
-      r = j / hpx;
+      if (window >= hpx) {  // one window: rank-major over all of the XCD's heads
+        bh = (j % hpx) * 8 + xcd;
+        r = j / hpx;
+      } else {
+        const int per_window = window * n_blocks;
+        const int w = j / per_window;
+        const int in = j - w * per_window;
+        const int wh = min(window, hpx - w * window);  // heads in this (possibly last) window
+        bh = (w * window + in % wh) * 8 + xcd;
+        r = in / wh;
+      }
     }
   } else {
     bh = wg % bh_count;

@@ -88,8 +88,8 @@ template <int D, bool CAUSAL, bool DROP>
 __global__ __launch_bounds__(FwdShape<D>::THREADS, FA2_FWD_OCC) void fa2_fwd_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ v, uint16_t* __restrict__ o, float* __restrict__ lse,
-    int N, int n_qblocks, int bh_count, int n_qheads, int group, long long kv_bstride,
-    float scale_log2, OperandSign qsign, DropParams drop) {
+    int N, int n_qblocks, int bh_count, int window, int n_qheads, int group,
+    long long kv_bstride, float scale_log2, OperandSign qsign, DropParams drop) {
   using S = FwdShape<D>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[S::SMEM];
 
@@ -100,7 +100,7 @@ __global__ __launch_bounds__(FwdShape<D>::THREADS, FA2_FWD_OCC) void fa2_fwd_ker
   const int g = lane >> 5;
 
   const TileCoord tc = schedule_tile<CAUSAL ? Order::kLongDescending : Order::kHeadMajor>(
-      blockIdx.x, n_qblocks, bh_count);
+      blockIdx.x, n_qblocks, bh_count, window);
   const size_t head_off = (size_t)tc.bh * (size_t)N * D;
   // K/V head of this query head (grouped heads share one; batch stride may be packed)
   const int b_idx = tc.bh / n_qheads;
@@ -380,7 +380,9 @@ hipError_t launch_fwd_t(const FwdArgs& a) {
                      dim3(FwdShape<D>::THREADS),
                      0, a.stream, static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
-                     static_cast<uint16_t*>(a.o), a.lse, a.N, n_qblocks, a.B * a.H, a.H,
+                     static_cast<uint16_t*>(a.o), a.lse, a.N, n_qblocks, a.B * a.H,
+                     causal_window(a.B * a.H, 4ll * a.N * D, n_qblocks, D == 64 ? 3 : 1,
+                                   window_budget(D)), a.H,
                      a.H / a.Hkv, a.kv_bstride, a.scale_log2, OperandSign{a.q_and, a.q_xor},
                      drop);
   return hipGetLastError();

@@ -142,6 +142,22 @@ int main() {
   CHECK(fa2_bwd_noalloc(P, P, P, P, P, F, P, P, P, 2, 3, 100, 64, 1, sc, nullptr) == FA2_OK);
   CHECK(g_launches == before + 1 && g_noalloc_part == ws / 2 && g_bwd.kv_split == 1);
 
+  // ---- causal window (heads per window of the causal workgroup order)
+  CHECK(fa2::causal_window(256, 4ll * 2048 * 64, 16, 3, 4ll << 20) == 8);    // fwd B8 H32 N2048 d64
+  CHECK(fa2::causal_window(64, 4ll * 4096 * 128, 16, 1, 4ll << 20) == 2);    // fwd B4 H16 N4096 d128
+  CHECK(fa2::causal_window(16, 4ll * 16384 * 128, 64, 1, 4ll << 20) == 1);   // fwd B1 H16 N16384 d128
+  CHECK(fa2::causal_window(64, 4ll * 2048 * 128, 8, 1, 4ll << 20) == 4);     // dQ B4 H16 N2048 d128
+  CHECK(fa2::causal_window(64, 4ll * 2048 * 128, 16, 1, 4ll << 20) == 4);    // dK/dV B4 H16 N2048 d128
+  CHECK(fa2::causal_window(8, 1ll << 20, 16, 1, 4ll << 20) == 1);           // one head per XCD
+  CHECK(fa2::causal_window(64, 1, 16, 1, 4ll << 20) == 8);                  // tiny heads: all of them
+
+  CHECK(fa2::causal_window(256, 4ll * 2048 * 64, 16, 3, 0) == 32);  // budget 0: all heads
+  // the budgets the launchers use: 8 MiB at d = 64 (16 heads at B8 H32 N2048), all heads above
+  CHECK(fa2::window_budget(64) == (8ll << 20) && fa2::window_budget(128) == 0 &&
+        fa2::window_budget(256) == 0);
+  CHECK(fa2::causal_window(256, 4ll * 2048 * 64, 16, 3, fa2::window_budget(64)) == 16);
+  CHECK(fa2::causal_window(64, 4ll * 4096 * 128, 16, 1, fa2::window_budget(128)) == 8);
+
   // ---- status strings
   CHECK(std::strcmp(fa2_status_string(FA2_ERR_SCRATCH_LIMIT), "FA2_ERR_SCRATCH_LIMIT") == 0);
   CHECK(std::strcmp(fa2_status_string(static_cast<fa2_status>(99)), "FA2_UNKNOWN_STATUS") == 0);
