@@ -47,7 +47,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 // MFMA operand reads and the transposing reads), by a workgroup of NT threads. Load i of wave w
 // writes the 1 KiB block (NT/64)i + w, lane l its 16 bytes at 16l: the physical chunk
 // p = 64*block + l of the tile, which holds the logical chunk (p % DCH) ^ swz(row).
-template <int D, int NT = kThreads, int ROWS = 64>
+template <int D, int NT = kThreads, int ROWS = 64, bool SWZ16 = false>
 struct TileLoader {
   static constexpr int DCH = D / 8;
   static constexpr int WAVES = NT / 64;
@@ -60,7 +60,8 @@ struct TileLoader {
     for (int i = 0; i < LOADS; ++i) {
       const int p = (WAVES * i + wave) * 64 + lane;
       const int row = p / DCH;
-      off[i] = (uint32_t)(row * D * 2 + ((p % DCH) ^ swz<D>(row)) * 16);
+      const int sw = SWZ16 ? swz16<D>(row) : swz<D>(row);
+      off[i] = (uint32_t)(row * D * 2 + ((p % DCH) ^ sw) * 16);
     }
   }
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t r, unsigned char* dst,
@@ -769,6 +770,246 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
 }
 
 // ---------------------------------------------------------------------------------------
+// dK, dV with 16 keys per wave (v_mfma_f32_16x16x32_bf16), without dropout. Workgroup = 4 waves
+// over 64 keys, one wave per SIMD, and several workgroups per CU (4 at d = 64, 3 at d = 128, 2
+// at d = 256), so each SIMD runs waves of independent workgroups. A wave keeps its 16 keys' K
+// and V fragments in registers (loaded once, the scale's sign applied to K) and its dK^T, dV^T
+// accumulators (d x 16 keys); 32-query tiles of Q and dO with their LSE*log2(e) and -D stream
+// through a 2-stage LDS ring (swz16 layout). Per tile, S = Q K^T and dP = dO V^T come out as two
+// 16-query blocks with lane = key (query order: block b, register r of lane group g is query
+// 16b + 4g + r), so the packed P and dS are directly the B operands of dV^T += dO^T P and
+// dK^T += Q^T dS over the tile's 32 queries, whose A operands (dO^T, Q^T) come from transposing
+// reads of the same tiles. S is formed once per (key, query) pair and dK, dV share it, where the
+// 32-key d = 256 kernel forms it twice; the K/V operands come from registers instead of LDS.
+template <int D>
+struct Kv16Shape {
+  static constexpr int NW = 4, THREADS = 256, BK = 64, BQ = 32;
+  static constexpr int OCC = D == 64 ? 4 : (D == 128 ? 3 : 2);  // waves per SIMD
+  static constexpr int KS = D / 32;                             // k-steps of S and dP
+  static constexpr int DB = D / 16;                             // 16-row blocks of dV^T, dK^T
+  static constexpr int TILE = BQ * D * 2;
+  static constexpr int STATS = 2 * BQ * 4;  // LSE*log2(e) of the 32 queries, then -D
+  static constexpr int STAGE = 2 * TILE + STATS;
+  static constexpr int SMEM = 2 * STAGE;
+};
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(256, Kv16Shape<D>::OCC)
+__attribute__((amdgpu_waves_per_eu(Kv16Shape<D>::OCC, Kv16Shape<D>::OCC))) void
+fa2_bwd_dkdv16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                      const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
+                      const float* __restrict__ lse2, const float* __restrict__ delta,
+                      uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int N, int n_kblocks,
+                      int bh_count, int window, int n_qheads, int group, long long kv_bstride,
+                      float scale_log2, float scale, OperandSign ksign, float* __restrict__ part,
+                      int split) {
+  using S = Kv16Shape<D>;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[S::SMEM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kl = lane & 15;  // this lane's key within the wave's 16
+  const int g = lane >> 4;   // lane group: queries 4g .. 4g+3 of each 16-query block
+
+  // causal: key block 0 sees every query tile, so ascending order is longest first
+  const TileCoord tc = schedule_tile<CAUSAL ? Order::kLongAscending : Order::kHeadMajor>(
+      blockIdx.x, n_kblocks, bh_count, window);
+  // tc.bh = (batch * Hkv + K/V head) * split + part, as in the 32-key kernels
+  const int sj = tc.bh % split;
+  const int bhkv = tc.bh / split;
+  const int n_kvheads = n_qheads / group;
+  const int b_idx = bhkv / n_kvheads;
+  const int kvh = bhkv - b_idx * n_kvheads;
+  const int qh0 = b_idx * n_qheads + kvh * group;
+  const size_t head_off =  // K, V, dK, dV
+      (size_t)b_idx * (size_t)kv_bstride + (size_t)kvh * (size_t)N * D;
+  const uint32_t head_bytes = (uint32_t)N * D * 2;
+  const int key_w0 = tc.qb * S::BK + wave * 16;
+  const int my_key = key_w0 + kl;
+
+  // K and V fragments of the wave's keys (B operands of S^T-blocks' transposes, i.e. of
+  // S = Q K^T): lane holds row my_key, columns 32ks + 8g .. +7 (zeros past N)
+  u32x4_t kf[S::KS], vf[S::KS];
+  {
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + head_off, head_bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + head_off, head_bytes);
+#pragma unroll
+    for (int ks = 0; ks < S::KS; ++ks) {
+      const uint32_t off = (uint32_t)my_key * D * 2 + (32 * ks + 8 * g) * 2;
+      kf[ks] = apply_sign(buffer_load16(rk, off, 0), ksign);
+      vf[ks] = buffer_load16(rv, off, 0);
+    }
+  }
+
+  // per-lane LDS offsets within a tile: operand rows (query 16b + kl, logical chunk 4ks + g) at
+  // row_base + 16*D*2*b + ((64*ks) ^ row_x); transposing reads (queries 4g + 16h + j/4, d
+  // columns 16blk + 4(j%4)) at tr_base[h] + ((32*blk) ^ tr_x[h])
+  const int row_base = kl * D * 2;
+  const int row_x = 16 * (g ^ swz16<D>(kl));
+  int tr_base[2], tr_x[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int j = lane & 15;
+    const int row = 4 * g + 16 * h + (j >> 2);
+    tr_base[h] = row * D * 2 + 8 * (j & 1);
+    tr_x[h] = 16 * (((j & 3) >> 1) ^ swz16<D>(row));
+  }
+
+  const int n_qt = (N + S::BQ - 1) / S::BQ;
+  const int qt_begin = CAUSAL ? (tc.qb * S::BK) / S::BQ : 0;
+  const int nt = n_qt - qt_begin;
+  const long long n_all = (long long)group * nt;
+  const int t_begin = (int)(n_all * sj / split);
+  const int n_steps = (int)(n_all * (sj + 1) / split) - t_begin;
+  const TileLoader<D, S::THREADS, S::BQ, true> ld(wave, lane);
+
+  StepPos ldpos(t_begin, nt, qt_begin);  // the next tile to load (loads go in step order)
+  int ld_head = -1;
+  __amdgpu_buffer_rsrc_t rq, rdo, rl, rd;
+  auto load_stage = [&](int stage) {
+    const int gi = ldpos.gi;
+    const int it = ldpos.it;
+    ldpos.next();
+    if (gi != ld_head) {
+      ld_head = gi;
+      const size_t qoff = (size_t)(qh0 + gi) * (size_t)N * D;
+      rq = make_rsrc(q + qoff, head_bytes);
+      rdo = make_rsrc(dout + qoff, head_bytes);
+      rl = make_rsrc(lse2 + (size_t)(qh0 + gi) * N, (uint32_t)N * 4);
+      rd = make_rsrc(delta + (size_t)(qh0 + gi) * N, (uint32_t)N * 4);
+    }
+    unsigned char* st = smem + stage * S::STAGE;
+    const uint32_t soff = (uint32_t)it * S::BQ * D * 2;
+    ld.load(rq, st, soff);
+    ld.load(rdo, st + S::TILE, soff);
+    // LSE*log2(e) and -D of the tile's 32 queries (128 bytes each): 8 lanes of waves 0 and 1
+    unsigned char* sst = st + 2 * S::TILE;
+    if (wave == 0) {
+      if (lane < 8) buffer_load16_to_lds(rl, sst, (uint32_t)lane * 16, (uint32_t)it * S::BQ * 4);
+    } else if (wave == 1) {
+      if (lane < 8)
+        buffer_load16_to_lds(rd, sst + S::BQ * 4, (uint32_t)lane * 16, (uint32_t)it * S::BQ * 4);
+    }
+  };
+
+  f32x4_t dkacc[S::DB], dvacc[S::DB];
+#pragma unroll
+  for (int b = 0; b < S::DB; ++b) {
+    dkacc[b] = f32x4_t{};
+    dvacc[b] = f32x4_t{};
+  }
+
+  if (n_steps > 0) load_stage(0);
+  wait_vmem();
+  __syncthreads();
+
+  StepPos cur(t_begin, nt, qt_begin);  // the tile of the current step
+  auto step = [&](auto stage_c, int t) {
+    constexpr int stage = decltype(stage_c)::value;
+    FA2_STAGE_SYNC();
+    if (t + 1 < n_steps) load_stage(stage ^ 1);
+    FA2_STAGE_SYNC();
+    const int it = cur.it;
+    cur.next();
+    const int q0 = it * S::BQ;
+    // every query of the tile precedes every key of the wave: fully masked
+    const bool skip = CAUSAL && (q0 + S::BQ - 1 < key_w0);
+    if (!skip) {
+      const unsigned char* tq = smem + stage * S::STAGE;
+      const unsigned char* tdo = tq + S::TILE;
+      const unsigned char* ts = tq + 2 * S::TILE;
+      // LSE*log2(e) and -D of this lane's queries 16b + 4g + (0..3)
+      const f32x4_t lsv[2] = {*reinterpret_cast<const f32x4_t*>(ts + 16 * g),
+                              *reinterpret_cast<const f32x4_t*>(ts + 64 + 16 * g)};
+      // dP starts at -D, so the MFMAs leave dP - D
+      f32x4_t sacc[2] = {f32x4_t{}, f32x4_t{}};
+      f32x4_t dpacc[2] = {*reinterpret_cast<const f32x4_t*>(ts + S::BQ * 4 + 16 * g),
+                          *reinterpret_cast<const f32x4_t*>(ts + S::BQ * 4 + 64 + 16 * g)};
+#pragma unroll
+      for (int ks = 0; ks < S::KS; ++ks) {
+        const int off = row_base + ((64 * ks) ^ row_x);
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const u32x4_t aq = *reinterpret_cast<const u32x4_t*>(tq + off + b * 16 * D * 2);
+          const u32x4_t ad = *reinterpret_cast<const u32x4_t*>(tdo + off + b * 16 * D * 2);
+          sacc[b] = mfma16(aq, kf[ks], sacc[b]);
+          dpacc[b] = mfma16(ad, vf[ks], dpacc[b]);
+        }
+      }
+      // hidden pairs (query past N, or causal query before the key) get S = -inf, so P = 0
+      const bool masked = (q0 + S::BQ > N) || (CAUSAL && q0 < key_w0 + 15);
+      if (masked) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int qq = q0 + 16 * b + 4 * g + r;
+            if (qq >= N || (CAUSAL && qq < my_key)) sacc[b][r] = -INFINITY;
+          }
+      }
+      // P = exp2(S*c - LSE*log2(e)), dS = P * (dP - D), packed as the B operands (queries
+      // 8g .. 8g+7 of the MFMA's k range = block 0 registers, then block 1 registers)
+      float pv[8], dsv[8];
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = fast_exp2(__builtin_fmaf(sacc[b][r], scale_log2, -lsv[b][r]));
+          pv[4 * b + r] = p;
+          dsv[4 * b + r] = p * dpacc[b][r];
+        }
+      const u32x4_t bp = {pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]),
+                          pack_bf16(pv[4], pv[5]), pack_bf16(pv[6], pv[7])};
+      const u32x4_t bs = {pack_bf16(dsv[0], dsv[1]), pack_bf16(dsv[2], dsv[3]),
+                          pack_bf16(dsv[4], dsv[5]), pack_bf16(dsv[6], dsv[7])};
+      // raised priority while the wave issues its dV/dK MFMAs
+      __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+      for (int blk = 0; blk < S::DB; ++blk) {
+        const int o0 = tr_base[0] + ((32 * blk) ^ tr_x[0]);
+        const int o1 = tr_base[1] + ((32 * blk) ^ tr_x[1]);
+        dvacc[blk] = mfma16(tr_operand(tdo, o0, o1), bp, dvacc[blk]);
+        dkacc[blk] = mfma16(tr_operand(tq, o0, o1), bs, dkacc[blk]);
+      }
+      __builtin_amdgcn_s_setprio(0);
+    }
+    FA2_STAGE_SYNC();
+    wait_vmem();
+    __syncthreads();
+  };
+  for (int t = 0; t < n_steps; t += 2) {
+    step(std::integral_constant<int, 0>{}, t);
+    if (t + 1 < n_steps) step(std::integral_constant<int, 1>{}, t + 1);
+  }
+
+  // dK = scale * dK_acc, dV = dV_acc: lane holds key my_key, d columns 16blk + 4g + (0..3)
+  if (my_key >= N) return;
+  if (part == nullptr) {
+    uint16_t* dkrow = dk + head_off + (size_t)my_key * D + 4 * g;
+    uint16_t* dvrow = dv + head_off + (size_t)my_key * D + 4 * g;
+#pragma unroll
+    for (int blk = 0; blk < S::DB; ++blk) {
+      *reinterpret_cast<u32x2_t*>(dkrow + 16 * blk) =
+          u32x2_t{pack_bf16(dkacc[blk][0] * scale, dkacc[blk][1] * scale),
+                  pack_bf16(dkacc[blk][2] * scale, dkacc[blk][3] * scale)};
+      *reinterpret_cast<u32x2_t*>(dvrow + 16 * blk) =
+          u32x2_t{pack_bf16(dvacc[blk][0], dvacc[blk][1]), pack_bf16(dvacc[blk][2], dvacc[blk][3])};
+    }
+  } else {
+    const size_t n_bhkv = (size_t)(bh_count / split);
+    float* pk = part + (size_t)sj * n_bhkv * N * D + (size_t)bhkv * N * D + (size_t)my_key * D + 4 * g;
+    float* pvv = part + ((size_t)split + sj) * n_bhkv * N * D + (size_t)bhkv * N * D +
+                 (size_t)my_key * D + 4 * g;
+#pragma unroll
+    for (int blk = 0; blk < S::DB; ++blk) {
+      *reinterpret_cast<f32x4_t*>(pk + 16 * blk) = dkacc[blk] * scale;
+      *reinterpret_cast<f32x4_t*>(pvv + 16 * blk) = dvacc[blk];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
 // dQ. Workgroup = DqShape<D>::NW waves x 32 queries (lane = query, as in the forward); key
 // tiles of 64 (32 at d = 256). S^T = K Q^T and dP^T = V dO^T from row-wise K/V tile reads
 // with Q^T/dO^T fragments held in VGPRs; dQ^T += K^T dS^T with K^T fragments from
@@ -1094,13 +1335,45 @@ hipError_t launch_dkdv256_t(const BwdArgs& a) {
   return hipGetLastError();
 }
 
+template <int D, bool CAUSAL>
+hipError_t launch_dkdv16_t(const BwdArgs& a) {
+  using S = Kv16Shape<D>;
+  const int n_kblocks = (a.N + S::BK - 1) / S::BK;
+  const long long grid = (long long)n_kblocks * a.B * a.Hkv * a.kv_split;
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const int bh_count = a.B * a.Hkv * a.kv_split;
+  hipLaunchKernelGGL((fa2_bwd_dkdv16_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(S::THREADS),
+                     0, a.stream, static_cast<const uint16_t*>(a.q),
+                     static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
+                     static_cast<const uint16_t*>(a.dout), a.lse2, a.delta,
+                     static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), a.N, n_kblocks,
+                     bh_count,
+                     causal_window(bh_count, 4ll * a.N * D * (a.H / a.Hkv) / a.kv_split,
+                                   n_kblocks, S::OCC, window_budget(D)),
+                     a.H, a.H / a.Hkv, a.kv_bstride, a.scale_log2, a.scale,
+                     OperandSign{a.sgn_and, a.sgn_xor}, a.kv_split > 1 ? a.kv_part : nullptr,
+                     a.kv_split);
+  return hipGetLastError();
+}
+
 template <bool DROP>
 hipError_t launch_bwd_dkdv_drop(const BwdArgs& a) {
-  if (a.d == 256)
-    return a.causal ? launch_dkdv256_t<true, DROP>(a) : launch_dkdv256_t<false, DROP>(a);
-  if (a.d == 64)
-    return a.causal ? launch_dkdv_t<64, true, DROP>(a) : launch_dkdv_t<64, false, DROP>(a);
-  return a.causal ? launch_dkdv_t<128, true, DROP>(a) : launch_dkdv_t<128, false, DROP>(a);
+  if constexpr (!DROP) {
+    // 16 keys per wave at d = 64 and 256 (fwd+bwd step at B2 H16 N4096 d256 +23-24%, at B8 H32
+    // N2048 d64 +2% non-causal); at d = 128 the 32-key kernel, which reads 30% fewer LDS bytes
+    // per MFMA, stays ahead (the 16-key kernel's step measured 5-7.5% slower there)
+    if (a.d == 256)
+      return a.causal ? launch_dkdv16_t<256, true>(a) : launch_dkdv16_t<256, false>(a);
+    if (a.d == 64) return a.causal ? launch_dkdv16_t<64, true>(a) : launch_dkdv16_t<64, false>(a);
+    return a.causal ? launch_dkdv_t<128, true, false>(a) : launch_dkdv_t<128, false, false>(a);
+  } else {
+    // dropout: the 32-key kernels (their lane pairs share the keep bits of a key pair)
+    if (a.d == 256)
+      return a.causal ? launch_dkdv256_t<true, DROP>(a) : launch_dkdv256_t<false, DROP>(a);
+    if (a.d == 64)
+      return a.causal ? launch_dkdv_t<64, true, DROP>(a) : launch_dkdv_t<64, false, DROP>(a);
+    return a.causal ? launch_dkdv_t<128, true, DROP>(a) : launch_dkdv_t<128, false, DROP>(a);
+  }
 }
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a) {

@@ -156,6 +156,29 @@ __device__ __forceinline__ u32x4_t apply_sign(u32x4_t x, const OperandSign& sg) 
   return (x & sg.and_mask) ^ sg.xor_mask;
 }
 
+// XOR swizzle of the query tiles of the 16-key dK/dV kernel, whose read patterns differ from the
+// ones above: (a) MFMA operand rows: 16 lanes read one logical chunk of 16 aligned consecutive
+// rows; (b) transposing reads: 32 lanes read 8 aligned consecutive rows, an even chunk and the
+// next in each. For D >= 128 (a row fills the 256-byte bank window; at D = 256 chunk bit 4 stays)
+// (a) needs swz bijective on row bits 0-3 and (b) needs swz bits 1-3 to differ across the 8 rows:
+// swz = (row & 7) << 1 | bit 3 of row. For D = 64 (two rows per window, the row parity picks the
+// half) (a) needs swz bijective on row bits 1-3 and (b) swz bits 1-2 to differ across the 4 rows
+// of one parity: swz = ((row >> 1) & 3) << 1 | bit 3 of row.
+template <int D>
+__device__ __forceinline__ int swz16(int row) {
+  static_assert(D == 64 || D == 128 || D == 256, "head dimension");
+  if constexpr (D >= 128) return ((row & 7) << 1) | ((row >> 3) & 1);
+  return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
+}
+
+// D(16x16) += A(16x32) * B(32x16), bf16 inputs, fp32 accumulate (v_mfma_f32_16x16x32_bf16).
+// Lane l holds A[l%16][8*(l/16) + i] and B[8*(l/16) + i][l%16] for i = 0..7; the result
+// register r of lane l is D[4*(l/16) + r][l%16] (layout checked on gfx950 against a CPU product).
+__device__ __forceinline__ f32x4_t mfma16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
 // Dropout mask generator: the 32-bit PCG-based hash of Jarzynski and Olano ("Hash Functions for
 // GPU Rendering", JCGT 9(3), 2020), an LCG step followed by a random xorshift, a multiply and
 // a fixed xorshift. For query head bh: a = hash(k0 ^ hash(k1 ^ bh)) (k0, k1 from the seed and

@@ -71,7 +71,9 @@ constexpr long long kDkdvMinWorkgroups = 512;
 constexpr int kDkdvMaxSplit = 8;
 inline int dkdv_split(int B, int H, int Hkv, int N, int d) {
   (void)H;
-  const long long kblocks = (N + (d == 256 ? 64 : 128) - 1) / (d == 256 ? 64 : 128);
+  // key blocks of the dK/dV kernel without dropout: 128 keys at d = 128, 64 otherwise
+  const int bk = d == 128 ? 128 : 64;
+  const long long kblocks = (N + bk - 1) / bk;
   const long long base = kblocks * B * Hkv;
   if (base >= kDkdvMinWorkgroups) return 1;
   for (int s = 2; s < kDkdvMaxSplit; ++s)

@@ -149,7 +149,7 @@ def test_split_groups_match_whole_groups(d):
 SPLIT_CASES = [((1, 8, 1, 77, 64), True), ((1, 16, 2, 257, 128), False),
                ((2, 16, 16, 130, 128), True), ((1, 6, 3, 1, 256), True),
                ((1, 4, 4, 600, 256), False), ((3, 8, 8, 65, 64), True),
-               ((2, 8, 8, 2048, 128), True), ((1, 8, 4, 2048, 64), False)]
+               ((1, 8, 8, 2048, 128), True), ((1, 8, 4, 2048, 64), False)]
 
 
 @pytest.mark.parametrize("dims,causal", SPLIT_CASES,
