@@ -277,9 +277,10 @@ def measure_step(fa2, torch, dev, w, causal, with_bwd, steps, warmup, warm_ms=WA
     stream = torch.cuda.current_stream(dev)
     kernels = ["fa2_fwd_kernel"]
     if with_bwd:
-        kernels += ["fa2_bwd_dq_kernel", "fa2_bwd_dkdv_kernel"]
+        # dK/dV without dropout runs fa2_bwd_dkdv16_kernel at every head dimension
+        kernels += ["fa2_bwd_dq_kernel", "fa2_bwd_dkdv16_kernel"]
     f_fwd = fwd_flop(B, H, N, d, causal)
-    algo_flop = {"fa2_fwd_kernel": f_fwd, "fa2_bwd_dkdv_kernel": 2.0 * f_fwd,
+    algo_flop = {"fa2_fwd_kernel": f_fwd, "fa2_bwd_dkdv16_kernel": 2.0 * f_fwd,
                  "fa2_bwd_dq_kernel": 0.5 * f_fwd}
     step_flop = f_fwd * (3.5 if with_bwd else 1.0)
 

@@ -781,21 +781,28 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
 // dK^T += Q^T dS over the tile's 32 queries, whose A operands (dO^T, Q^T) come from transposing
 // reads of the same tiles. S is formed once per (key, query) pair and dK, dV share it, where the
 // 32-key d = 256 kernel forms it twice; the K/V operands come from registers instead of LDS.
-template <int D>
+// KP = 2 (d = 64, 128): each wave takes two 16-key sub-blocks (32 keys) that share every Q and
+// dO operand read, which halves the LDS reads per MFMA of those operands; the 128 keys' K rows
+// then stay in LDS (read per step) and only V's fragments live in registers, and 3 (d = 64) or
+// 2 (d = 128) workgroups of 4 waves share a CU, each SIMD interleaving independent workgroups.
+template <int D, int KP = 1>
 struct Kv16Shape {
-  static constexpr int NW = 4, THREADS = 256, BK = 64, BQ = 32;
-  static constexpr int OCC = D == 64 ? 4 : (D == 128 ? 3 : 2);  // waves per SIMD
+  static constexpr int NW = 4, THREADS = 256, BQ = 32;
+  static constexpr int BK = 64 * KP;                            // keys per workgroup
+  static constexpr int OCC = KP > 1 ? (D == 64 ? 3 : 2) : (D == 64 ? 4 : (D == 128 ? 3 : 2));
   static constexpr int KS = D / 32;                             // k-steps of S and dP
   static constexpr int DB = D / 16;                             // 16-row blocks of dV^T, dK^T
   static constexpr int TILE = BQ * D * 2;
   static constexpr int STATS = 2 * BQ * 4;  // LSE*log2(e) of the 32 queries, then -D
   static constexpr int STAGE = 2 * TILE + STATS;
-  static constexpr int SMEM = 2 * STAGE;
+  static constexpr int KRES0 = 2 * STAGE;                // resident K rows (KP > 1)
+  static constexpr int KRES = KP > 1 ? BK * D * 2 : 0;
+  static constexpr int SMEM = KRES0 + KRES;
 };
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, Kv16Shape<D>::OCC)
-__attribute__((amdgpu_waves_per_eu(Kv16Shape<D>::OCC, Kv16Shape<D>::OCC))) void
+template <int D, bool CAUSAL, int KP>
+__global__ __launch_bounds__(256, (Kv16Shape<D, KP>::OCC))
+__attribute__((amdgpu_waves_per_eu(Kv16Shape<D, KP>::OCC, Kv16Shape<D, KP>::OCC))) void
 fa2_bwd_dkdv16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                       const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
                       const float* __restrict__ lse2, const float* __restrict__ delta,
@@ -803,13 +810,13 @@ fa2_bwd_dkdv16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
                       int bh_count, int window, int n_qheads, int group, long long kv_bstride,
                       float scale_log2, float scale, OperandSign ksign, float* __restrict__ part,
                       int split) {
-  using S = Kv16Shape<D>;
+  using S = Kv16Shape<D, KP>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[S::SMEM];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kl = lane & 15;  // this lane's key within the wave's 16
+  const int kl = lane & 15;  // this lane's key within each 16-key sub-block
   const int g = lane >> 4;   // lane group: queries 4g .. 4g+3 of each 16-query block
 
   // causal: key block 0 sees every query tile, so ascending order is longest first
@@ -825,26 +832,12 @@ fa2_bwd_dkdv16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   const size_t head_off =  // K, V, dK, dV
       (size_t)b_idx * (size_t)kv_bstride + (size_t)kvh * (size_t)N * D;
   const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const int key_w0 = tc.qb * S::BK + wave * 16;
-  const int my_key = key_w0 + kl;
+  const int key_b0 = tc.qb * S::BK;
+  const int key_w0 = key_b0 + wave * 16 * KP;  // sub-block kp: keys key_w0 + 16kp + (0..15)
 
-  // K and V fragments of the wave's keys (B operands of S^T-blocks' transposes, i.e. of
-  // S = Q K^T): lane holds row my_key, columns 32ks + 8g .. +7 (zeros past N)
-  u32x4_t kf[S::KS], vf[S::KS];
-  {
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + head_off, head_bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + head_off, head_bytes);
-#pragma unroll
-    for (int ks = 0; ks < S::KS; ++ks) {
-      const uint32_t off = (uint32_t)my_key * D * 2 + (32 * ks + 8 * g) * 2;
-      kf[ks] = apply_sign(buffer_load16(rk, off, 0), ksign);
-      vf[ks] = buffer_load16(rv, off, 0);
-    }
-  }
-
-  // per-lane LDS offsets within a tile: operand rows (query 16b + kl, logical chunk 4ks + g) at
-  // row_base + 16*D*2*b + ((64*ks) ^ row_x); transposing reads (queries 4g + 16h + j/4, d
-  // columns 16blk + 4(j%4)) at tr_base[h] + ((32*blk) ^ tr_x[h])
+  // per-lane LDS offsets within a tile (and the resident K rows): operand rows (row 16b + kl,
+  // logical chunk 4ks + g) at row_base + 16*D*2*b + ((64*ks) ^ row_x); transposing reads
+  // (queries 4g + 16h + j/4, d columns 16blk + 4(j%4)) at tr_base[h] + ((32*blk) ^ tr_x[h])
   const int row_base = kl * D * 2;
   const int row_x = 16 * (g ^ swz16<D>(kl));
   int tr_base[2], tr_x[2];
@@ -856,8 +849,32 @@ fa2_bwd_dkdv16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     tr_x[h] = 16 * (((j & 3) >> 1) ^ swz16<D>(row));
   }
 
+  // V fragments (B operands of dP = dO V^T) of the wave's keys, and K's (of S = Q K^T) when they
+  // live in registers: lane holds row key_w0 + 16kp + kl, columns 32ks + 8g .. +7 (zeros past N)
+  u32x4_t kf[KP == 1 ? S::KS : 1], vf[KP][S::KS];
+  {
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + head_off, head_bytes);
+#pragma unroll
+    for (int kp = 0; kp < KP; ++kp)
+#pragma unroll
+      for (int ks = 0; ks < S::KS; ++ks)
+        vf[kp][ks] = buffer_load16(
+            rv, (uint32_t)(key_w0 + 16 * kp + kl) * D * 2 + (32 * ks + 8 * g) * 2, 0);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + head_off, head_bytes);
+    if constexpr (KP == 1) {
+#pragma unroll
+      for (int ks = 0; ks < S::KS; ++ks)
+        kf[ks] = apply_sign(
+            buffer_load16(rk, (uint32_t)(key_w0 + kl) * D * 2 + (32 * ks + 8 * g) * 2, 0), ksign);
+    } else {
+      // the workgroup's K rows into LDS (swz16 layout, rows = keys)
+      const TileLoader<D, S::THREADS, S::BK, true> kld(wave, lane);
+      kld.load(rk, smem + S::KRES0, (uint32_t)key_b0 * D * 2);
+    }
+  }
+
   const int n_qt = (N + S::BQ - 1) / S::BQ;
-  const int qt_begin = CAUSAL ? (tc.qb * S::BK) / S::BQ : 0;
+  const int qt_begin = CAUSAL ? key_b0 / S::BQ : 0;
   const int nt = n_qt - qt_begin;
   const long long n_all = (long long)group * nt;
   const int t_begin = (int)(n_all * sj / split);
@@ -893,16 +910,29 @@ fa2_bwd_dkdv16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     }
   };
 
-  f32x4_t dkacc[S::DB], dvacc[S::DB];
+  f32x4_t dkacc[KP][S::DB], dvacc[KP][S::DB];
 #pragma unroll
-  for (int b = 0; b < S::DB; ++b) {
-    dkacc[b] = f32x4_t{};
-    dvacc[b] = f32x4_t{};
-  }
+  for (int kp = 0; kp < KP; ++kp)
+#pragma unroll
+    for (int b = 0; b < S::DB; ++b) {
+      dkacc[kp][b] = f32x4_t{};
+      dvacc[kp][b] = f32x4_t{};
+    }
 
   if (n_steps > 0) load_stage(0);
   wait_vmem();
   __syncthreads();
+  if constexpr (KP > 1) {
+    if (ksign.and_mask != ~0u || ksign.xor_mask != 0u) {
+      // a scale <= 0: its sign goes into the resident K rows, once (see OperandSign)
+      for (int i = tid * 16; i < S::KRES; i += S::THREADS * 16)
+        *reinterpret_cast<u32x4_t*>(smem + S::KRES0 + i) =
+            apply_sign(*reinterpret_cast<const u32x4_t*>(smem + S::KRES0 + i), ksign);
+      __syncthreads();
+    }
+  }
+  // this wave's first K row in LDS (sub-block kp adds 16 rows)
+  const unsigned char* kres = smem + S::KRES0 + (size_t)wave * 16 * KP * D * 2;
 
   StepPos cur(t_begin, nt, qt_begin);  // the tile of the current step
   auto step = [&](auto stage_c, int t) {
@@ -922,55 +952,84 @@ fa2_bwd_dkdv16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       // LSE*log2(e) and -D of this lane's queries 16b + 4g + (0..3)
       const f32x4_t lsv[2] = {*reinterpret_cast<const f32x4_t*>(ts + 16 * g),
                               *reinterpret_cast<const f32x4_t*>(ts + 64 + 16 * g)};
+      const f32x4_t ndv[2] = {*reinterpret_cast<const f32x4_t*>(ts + S::BQ * 4 + 16 * g),
+                              *reinterpret_cast<const f32x4_t*>(ts + S::BQ * 4 + 64 + 16 * g)};
       // dP starts at -D, so the MFMAs leave dP - D
-      f32x4_t sacc[2] = {f32x4_t{}, f32x4_t{}};
-      f32x4_t dpacc[2] = {*reinterpret_cast<const f32x4_t*>(ts + S::BQ * 4 + 16 * g),
-                          *reinterpret_cast<const f32x4_t*>(ts + S::BQ * 4 + 64 + 16 * g)};
+      f32x4_t sacc[KP][2], dpacc[KP][2];
+#pragma unroll
+      for (int kp = 0; kp < KP; ++kp)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          sacc[kp][b] = f32x4_t{};
+          dpacc[kp][b] = ndv[b];
+        }
 #pragma unroll
       for (int ks = 0; ks < S::KS; ++ks) {
         const int off = row_base + ((64 * ks) ^ row_x);
+        u32x4_t kk[KP];
+        if constexpr (KP == 1) {
+          kk[0] = kf[ks];
+        } else {
+#pragma unroll
+          for (int kp = 0; kp < KP; ++kp)
+            kk[kp] = *reinterpret_cast<const u32x4_t*>(kres + off + kp * 16 * D * 2);
+        }
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
           const u32x4_t aq = *reinterpret_cast<const u32x4_t*>(tq + off + b * 16 * D * 2);
           const u32x4_t ad = *reinterpret_cast<const u32x4_t*>(tdo + off + b * 16 * D * 2);
-          sacc[b] = mfma16(aq, kf[ks], sacc[b]);
-          dpacc[b] = mfma16(ad, vf[ks], dpacc[b]);
+#pragma unroll
+          for (int kp = 0; kp < KP; ++kp) {
+            sacc[kp][b] = mfma16(aq, kk[kp], sacc[kp][b]);
+            dpacc[kp][b] = mfma16(ad, vf[kp][ks], dpacc[kp][b]);
+          }
         }
       }
       // hidden pairs (query past N, or causal query before the key) get S = -inf, so P = 0
-      const bool masked = (q0 + S::BQ > N) || (CAUSAL && q0 < key_w0 + 15);
+      const bool masked = (q0 + S::BQ > N) || (CAUSAL && q0 < key_w0 + 16 * KP - 1);
       if (masked) {
+#pragma unroll
+        for (int kp = 0; kp < KP; ++kp)
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int qq = q0 + 16 * b + 4 * g + r;
+              if (qq >= N || (CAUSAL && qq < key_w0 + 16 * kp + kl)) sacc[kp][b][r] = -INFINITY;
+            }
+      }
+      // P = exp2(S*c - LSE*log2(e)), dS = P * (dP - D), packed as the B operands (queries
+      // 8g .. 8g+7 of the MFMA's k range = block 0 registers, then block 1 registers)
+      u32x4_t bp[KP], bs[KP];
+#pragma unroll
+      for (int kp = 0; kp < KP; ++kp) {
+        float pv[8], dsv[8];
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int qq = q0 + 16 * b + 4 * g + r;
-            if (qq >= N || (CAUSAL && qq < my_key)) sacc[b][r] = -INFINITY;
+            const float p = fast_exp2(__builtin_fmaf(sacc[kp][b][r], scale_log2, -lsv[b][r]));
+            pv[4 * b + r] = p;
+            dsv[4 * b + r] = p * dpacc[kp][b][r];
           }
+        bp[kp] = u32x4_t{pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]), pack_bf16(pv[4], pv[5]),
+                         pack_bf16(pv[6], pv[7])};
+        bs[kp] = u32x4_t{pack_bf16(dsv[0], dsv[1]), pack_bf16(dsv[2], dsv[3]),
+                         pack_bf16(dsv[4], dsv[5]), pack_bf16(dsv[6], dsv[7])};
       }
-      // P = exp2(S*c - LSE*log2(e)), dS = P * (dP - D), packed as the B operands (queries
-      // 8g .. 8g+7 of the MFMA's k range = block 0 registers, then block 1 registers)
-      float pv[8], dsv[8];
-#pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float p = fast_exp2(__builtin_fmaf(sacc[b][r], scale_log2, -lsv[b][r]));
-          pv[4 * b + r] = p;
-          dsv[4 * b + r] = p * dpacc[b][r];
-        }
-      const u32x4_t bp = {pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]),
-                          pack_bf16(pv[4], pv[5]), pack_bf16(pv[6], pv[7])};
-      const u32x4_t bs = {pack_bf16(dsv[0], dsv[1]), pack_bf16(dsv[2], dsv[3]),
-                          pack_bf16(dsv[4], dsv[5]), pack_bf16(dsv[6], dsv[7])};
       // raised priority while the wave issues its dV/dK MFMAs
       __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int blk = 0; blk < S::DB; ++blk) {
         const int o0 = tr_base[0] + ((32 * blk) ^ tr_x[0]);
         const int o1 = tr_base[1] + ((32 * blk) ^ tr_x[1]);
-        dvacc[blk] = mfma16(tr_operand(tdo, o0, o1), bp, dvacc[blk]);
-        dkacc[blk] = mfma16(tr_operand(tq, o0, o1), bs, dkacc[blk]);
+        const u32x4_t ao = tr_operand(tdo, o0, o1);
+        const u32x4_t aq = tr_operand(tq, o0, o1);
+#pragma unroll
+        for (int kp = 0; kp < KP; ++kp) {
+          dvacc[kp][blk] = mfma16(ao, bp[kp], dvacc[kp][blk]);
+          dkacc[kp][blk] = mfma16(aq, bs[kp], dkacc[kp][blk]);
+        }
       }
       __builtin_amdgcn_s_setprio(0);
     }
@@ -983,28 +1042,35 @@ fa2_bwd_dkdv16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     if (t + 1 < n_steps) step(std::integral_constant<int, 1>{}, t + 1);
   }
 
-  // dK = scale * dK_acc, dV = dV_acc: lane holds key my_key, d columns 16blk + 4g + (0..3)
-  if (my_key >= N) return;
-  if (part == nullptr) {
-    uint16_t* dkrow = dk + head_off + (size_t)my_key * D + 4 * g;
-    uint16_t* dvrow = dv + head_off + (size_t)my_key * D + 4 * g;
+  // dK = scale * dK_acc, dV = dV_acc: lane holds key key_w0 + 16kp + kl, d columns
+  // 16blk + 4g + (0..3)
 #pragma unroll
-    for (int blk = 0; blk < S::DB; ++blk) {
-      *reinterpret_cast<u32x2_t*>(dkrow + 16 * blk) =
-          u32x2_t{pack_bf16(dkacc[blk][0] * scale, dkacc[blk][1] * scale),
-                  pack_bf16(dkacc[blk][2] * scale, dkacc[blk][3] * scale)};
-      *reinterpret_cast<u32x2_t*>(dvrow + 16 * blk) =
-          u32x2_t{pack_bf16(dvacc[blk][0], dvacc[blk][1]), pack_bf16(dvacc[blk][2], dvacc[blk][3])};
-    }
-  } else {
-    const size_t n_bhkv = (size_t)(bh_count / split);
-    float* pk = part + (size_t)sj * n_bhkv * N * D + (size_t)bhkv * N * D + (size_t)my_key * D + 4 * g;
-    float* pvv = part + ((size_t)split + sj) * n_bhkv * N * D + (size_t)bhkv * N * D +
-                 (size_t)my_key * D + 4 * g;
+  for (int kp = 0; kp < KP; ++kp) {
+    const int my_key = key_w0 + 16 * kp + kl;
+    if (my_key >= N) continue;
+    if (part == nullptr) {
+      uint16_t* dkrow = dk + head_off + (size_t)my_key * D + 4 * g;
+      uint16_t* dvrow = dv + head_off + (size_t)my_key * D + 4 * g;
 #pragma unroll
-    for (int blk = 0; blk < S::DB; ++blk) {
-      *reinterpret_cast<f32x4_t*>(pk + 16 * blk) = dkacc[blk] * scale;
-      *reinterpret_cast<f32x4_t*>(pvv + 16 * blk) = dvacc[blk];
+      for (int blk = 0; blk < S::DB; ++blk) {
+        *reinterpret_cast<u32x2_t*>(dkrow + 16 * blk) =
+            u32x2_t{pack_bf16(dkacc[kp][blk][0] * scale, dkacc[kp][blk][1] * scale),
+                    pack_bf16(dkacc[kp][blk][2] * scale, dkacc[kp][blk][3] * scale)};
+        *reinterpret_cast<u32x2_t*>(dvrow + 16 * blk) =
+            u32x2_t{pack_bf16(dvacc[kp][blk][0], dvacc[kp][blk][1]),
+                    pack_bf16(dvacc[kp][blk][2], dvacc[kp][blk][3])};
+      }
+    } else {
+      const size_t n_bhkv = (size_t)(bh_count / split);
+      float* pk = part + (size_t)sj * n_bhkv * N * D + (size_t)bhkv * N * D +
+                  (size_t)my_key * D + 4 * g;
+      float* pvv = part + ((size_t)split + sj) * n_bhkv * N * D + (size_t)bhkv * N * D +
+                   (size_t)my_key * D + 4 * g;
+#pragma unroll
+      for (int blk = 0; blk < S::DB; ++blk) {
+        *reinterpret_cast<f32x4_t*>(pk + 16 * blk) = dkacc[kp][blk] * scale;
+        *reinterpret_cast<f32x4_t*>(pvv + 16 * blk) = dvacc[kp][blk];
+      }
     }
   }
 }
@@ -1335,14 +1401,14 @@ hipError_t launch_dkdv256_t(const BwdArgs& a) {
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int KP = 1>
 hipError_t launch_dkdv16_t(const BwdArgs& a) {
-  using S = Kv16Shape<D>;
+  using S = Kv16Shape<D, KP>;
   const int n_kblocks = (a.N + S::BK - 1) / S::BK;
   const long long grid = (long long)n_kblocks * a.B * a.Hkv * a.kv_split;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const int bh_count = a.B * a.Hkv * a.kv_split;
-  hipLaunchKernelGGL((fa2_bwd_dkdv16_kernel<D, CAUSAL>), dim3((unsigned)grid), dim3(S::THREADS),
+  hipLaunchKernelGGL((fa2_bwd_dkdv16_kernel<D, CAUSAL, KP>), dim3((unsigned)grid), dim3(S::THREADS),
                      0, a.stream, static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                      static_cast<const uint16_t*>(a.dout), a.lse2, a.delta,
@@ -1359,13 +1425,16 @@ hipError_t launch_dkdv16_t(const BwdArgs& a) {
 template <bool DROP>
 hipError_t launch_bwd_dkdv_drop(const BwdArgs& a) {
   if constexpr (!DROP) {
-    // 16 keys per wave at d = 64 and 256 (fwd+bwd step at B2 H16 N4096 d256 +23-24%, at B8 H32
-    // N2048 d64 +2% non-causal); at d = 128 the 32-key kernel, which reads 30% fewer LDS bytes
-    // per MFMA, stays ahead (the 16-key kernel's step measured 5-7.5% slower there)
+    // 16-key MFMA blocks: at d = 256 one per wave (fwd+bwd step at B2 H16 N4096 +23-24% against
+    // the 32-key kernel); at d = 64 and 128 two per wave with K in LDS and V in registers (step at
+    // B4 H16 N2048 d128 +3.7% causal, +4.1% non-causal against the 32-key kernel, where one
+    // sub-block per wave was 5-7.5% slower for its LDS bytes per MFMA; at B8 H32 N2048 d64 +4.2%
+    // against one sub-block per wave)
     if (a.d == 256)
       return a.causal ? launch_dkdv16_t<256, true>(a) : launch_dkdv16_t<256, false>(a);
-    if (a.d == 64) return a.causal ? launch_dkdv16_t<64, true>(a) : launch_dkdv16_t<64, false>(a);
-    return a.causal ? launch_dkdv_t<128, true, false>(a) : launch_dkdv_t<128, false, false>(a);
+    if (a.d == 64)
+      return a.causal ? launch_dkdv16_t<64, true, 2>(a) : launch_dkdv16_t<64, false, 2>(a);
+    return a.causal ? launch_dkdv16_t<128, true, 2>(a) : launch_dkdv16_t<128, false, 2>(a);
   } else {
     // dropout: the 32-key kernels (their lane pairs share the keep bits of a key pair)
     if (a.d == 256)

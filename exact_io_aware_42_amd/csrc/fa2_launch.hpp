@@ -71,8 +71,8 @@ constexpr long long kDkdvMinWorkgroups = 512;
 constexpr int kDkdvMaxSplit = 8;
 inline int dkdv_split(int B, int H, int Hkv, int N, int d) {
   (void)H;
-  // key blocks of the dK/dV kernel without dropout: 128 keys at d = 128, 64 otherwise
-  const int bk = d == 128 ? 128 : 64;
+  // key blocks of the dK/dV kernel without dropout: 64 keys at d = 256, 128 otherwise
+  const int bk = d == 256 ? 64 : 128;
   const long long kblocks = (N + bk - 1) / bk;
   const long long base = kblocks * B * Hkv;
   if (base >= kDkdvMinWorkgroups) return 1;

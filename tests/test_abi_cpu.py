@@ -340,8 +340,8 @@ def test_dropout_validation():
 def _split_model(B, H, Hkv, N, d):
     """The rule the backward uses: split each (key block, K/V head) pair's steps only while
     those pairs number under 512, into the smallest count from 2 to 8 that reaches 512 (else
-    8); key blocks of 128 at d = 128, 64 otherwise."""
-    kb = -(-N // (128 if d == 128 else 64))
+    8); key blocks of 64 at d = 256, 128 otherwise."""
+    kb = -(-N // (64 if d == 256 else 128))
     base = kb * B * Hkv
     if base >= 512:
         return 1
