@@ -157,18 +157,24 @@ __device__ __forceinline__ u32x4_t apply_sign(u32x4_t x, const OperandSign& sg) 
 }
 
 // XOR swizzle of the query tiles of the 16-key dK/dV kernel, whose read patterns differ from the
-// ones above: (a) MFMA operand rows: 16 lanes read one logical chunk of 16 aligned consecutive
-// rows; (b) transposing reads: 32 lanes read 8 aligned consecutive rows, an even chunk and the
-// next in each. For D >= 128 (a row fills the 256-byte bank window; at D = 256 chunk bit 4 stays)
-// (a) needs swz bijective on row bits 0-3 and (b) needs swz bits 1-3 to differ across the 8 rows:
-// swz = (row & 7) << 1 | bit 3 of row. For D = 64 (two rows per window, the row parity picks the
-// half) (a) needs swz bijective on row bits 1-3 and (b) swz bits 1-2 to differ across the 4 rows
-// of one parity: swz = ((row >> 1) & 3) << 1 | bit 3 of row.
+// ones above: (a) MFMA operand rows: lane l reads logical chunk 4k + l/16 of row l%16; (b)
+// transposing reads: lanes 0-31 (then 32-63) read rows 8a .. 8a+7, an even chunk and the next in
+// each. gfx950's LDS, as measured by counter probes (two active lanes at a time, the bank-
+// conflict counter per pair): 64 banks of 4 bytes; a ds_read_b64 serves lanes 0-31, then
+// 32-63; a ds_read_b128 serves 16 lanes per cycle, lanes 0-3, 12-15, 20-27 together (the
+// 4-lane quads of a half-wave grouped by the parity of lane bits 2-4), then the other quads,
+// then the same for lanes 32-63. With row = l%16 in (a), one such group reads rows 0-3 and
+// 12-15 at chunk group g and rows 4-11 at g + 1, so swz must map rows 4-11 onto a set closed
+// under XOR 1 (the chunk-group step), and (b) needs swz bits 1-3 to differ across 8 aligned
+// rows. For D >= 128 (a row fills the 256-byte bank window; at D = 256 chunk bit 4 stays)
+// swz = (row & 7) << 1 does both; for D = 64 (two rows per window, the row parity picks the
+// half) swz = ((row >> 1) & 3) << 1. A swizzle bijective on 16 rows, (row & 7) << 1 | bit 3 of
+// row, measured 2-way conflicts on (a): 8 cycles and 4 conflict cycles per instruction.
 template <int D>
 __device__ __forceinline__ int swz16(int row) {
   static_assert(D == 64 || D == 128 || D == 256, "head dimension");
-  if constexpr (D >= 128) return ((row & 7) << 1) | ((row >> 3) & 1);
-  return (((row >> 1) & 3) << 1) | ((row >> 3) & 1);
+  if constexpr (D >= 128) return (row & 7) << 1;
+  return ((row >> 1) & 3) << 1;
 }
 
 // D(16x16) += A(16x32) * B(32x16), bf16 inputs, fp32 accumulate (v_mfma_f32_16x16x32_bf16).
