@@ -1247,6 +1247,16 @@ __global__ __launch_bounds__((DqShape<D>::THREADS), (DqShape<D>::OCC)) void fa2_
           }
           dsk[kb][i] = pack_bf16(p0 * dp0, p1 * dp1);
         }
+      if constexpr (D == 256) {
+        // d = 256: each exponential between two plain VALU ops instead of runs of eight (fwd+bwd
+        // step at B2 H16 N4096 +1.0-1.4%; at d = 64 and 128 within +-0.5%)
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+#pragma unroll
+        for (int i = 0; i < 16 * KB; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x400, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        }
+      }
       __builtin_amdgcn_s_setprio(1);  // as in the dK/dV kernel
       // dQ^T += K^T dS^T; MFMA u covers keys 16u .. 16u+15
 #pragma unroll
