@@ -186,7 +186,8 @@ size_t fa2_bwd_gqa_workspace_bytes(int B, int H, int Hkv, int N, int d) {
   bool empty;
   if (check_sizes(B, H, N, d, 1.0f, &empty) != FA2_OK || empty) return 0;
   if (Hkv <= 0 || H % Hkv != 0) return 0;
-  const int split = fa2::dkdv_split(B, H, Hkv, N, d);
+  // sized for the causal split, the larger of the two
+  const int split = fa2::dkdv_split(B, H, Hkv, N, d, true);
   const size_t part = split > 1 ? round256((size_t)2 * split * B * Hkv * N * d * sizeof(float)) : 0;
   return 2 * ws_part_bytes(B, H, N) + part;
 }
@@ -197,7 +198,7 @@ namespace {
 // the chip and the workspace holds the partial sums (fa2_bwd_gqa_workspace_bytes); with the
 // smaller workspace nothing is split.
 void set_kv_split(fa2::BwdArgs* a, void* workspace, size_t workspace_bytes) {
-  const int split = fa2::dkdv_split(a->B, a->H, a->Hkv, a->N, a->d);
+  const int split = fa2::dkdv_split(a->B, a->H, a->Hkv, a->N, a->d, a->causal);
   if (split > 1 &&
       workspace_bytes >= fa2_bwd_gqa_workspace_bytes(a->B, a->H, a->Hkv, a->N, a->d)) {
     a->kv_split = split;

@@ -134,9 +134,10 @@ fa2_status fa2_bwd_preprocess(const void* o, const void* dout, const float* lse,
  * (deterministic). kv_batch_stride must be a multiple of 8 and at least Hkv*N*d. Otherwise as
  * fa2_fwd / fa2_bwd (which are these calls with Hkv = H and kv_batch_stride = H*N*d).
  * Small problems: when the (key block of 128 keys, 64 at d = 256; K/V head) pairs are fewer
- * than 512 and the workspace holds fa2_bwd_gqa_workspace_bytes(...) bytes, fa2_bwd,
- * fa2_bwd_gqa and fa2_bwd_dropout cut each pair's (query head, query tile) steps into 2..8
- * equal ranges run by separate dK/dV workgroups, which write fp32 partial sums into the
+ * than 512 (1024 under the causal mask) and the workspace holds
+ * fa2_bwd_gqa_workspace_bytes(...) bytes, fa2_bwd, fa2_bwd_gqa and fa2_bwd_dropout cut each
+ * pair's (query head, query tile) steps into the smallest number of equal ranges, 2..8, that
+ * reaches that many workgroups, run by separate dK/dV workgroups, which write fp32 partial sums into the
  * workspace; a last pass adds them in a fixed order (deterministic; the order differs from the
  * unsplit path's, so results may differ from it in the last bits). With only
  * fa2_bwd_workspace_bytes(...) bytes nothing is split. */
@@ -145,9 +146,9 @@ fa2_status fa2_fwd_gqa(const void* q, const void* k, const void* v, void* o, flo
                        int causal, float softmax_scale, hipStream_t stream);
 
 /* Workspace bytes that let fa2_bwd (Hkv = H), fa2_bwd_gqa and fa2_bwd_dropout split the dK/dV
- * work of small problems (above): fa2_bwd_workspace_bytes plus, when they split into `parts`,
- * 2 * parts * B*Hkv*N*d fp32 partial sums (rounded up to 256 bytes). 0 for invalid or empty
- * sizes or Hkv not dividing H. */
+ * work of small problems (above): fa2_bwd_workspace_bytes plus, when the causal rule splits into
+ * `parts` (the larger of the two rules), 2 * parts * B*Hkv*N*d fp32 partial sums (rounded up to
+ * 256 bytes). 0 for invalid or empty sizes or Hkv not dividing H. */
 size_t fa2_bwd_gqa_workspace_bytes(int B, int H, int Hkv, int N, int d);
 
 fa2_status fa2_bwd_gqa(const void* q, const void* k, const void* v, const void* o,

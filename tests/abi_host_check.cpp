@@ -126,6 +126,14 @@ int main() {
   CHECK(fa2_bwd(P, P, P, P, P, F, P, P, P, wsbuf, ws_split, 2, 3, 100, 64, 1, sc, nullptr) ==
         FA2_OK);
   CHECK(g_bwd.kv_split > 1 && reinterpret_cast<unsigned char*>(g_bwd.kv_part) == wsbuf + ws);
+  // the split targets 1024 workgroups under the causal mask and 512 without: 200 (key block,
+  // head) pairs split into 6 and 3 parts; the workspace is sized for the causal split
+  const size_t ws200 = fa2_bwd_gqa_workspace_bytes(1, 200, 200, 1, 64);
+  CHECK(ws200 == 2 * 1024 + (size_t)2 * 6 * 200 * 64 * 4 && ws200 <= sizeof(wsbuf));
+  CHECK(fa2_bwd(P, P, P, P, P, F, P, P, P, wsbuf, ws200, 1, 200, 1, 64, 1, sc, nullptr) == FA2_OK);
+  CHECK(g_bwd.kv_split == 6);
+  CHECK(fa2_bwd(P, P, P, P, P, F, P, P, P, wsbuf, ws200, 1, 200, 1, 64, 0, sc, nullptr) == FA2_OK);
+  CHECK(g_bwd.kv_split == 3);
   CHECK(fa2_bwd_dropout(P, P, P, P, P, F, P, P, P, wsbuf, ws, 1, 4, 2, 16, 64, 2 * 16 * 64, 0,
                         sc, 0.5f, 3, 4, nullptr) == FA2_OK);
   CHECK(g_bwd.dropout && g_bwd.Hkv == 2 && g_bwd.drop_scale == 2.0f);

@@ -337,16 +337,18 @@ def test_dropout_validation():
                                2, None) == ops.FA2_OK
 
 
-def _split_model(B, H, Hkv, N, d):
+def _split_model(B, H, Hkv, N, d, causal=True):
     """The rule the backward uses: split each (key block, K/V head) pair's steps only while
-    those pairs number under 512, into the smallest count from 2 to 8 that reaches 512 (else
-    8); key blocks of 64 at d = 256, 128 otherwise."""
+    those pairs number under the target (1024 workgroups under the causal mask, 512 without),
+    into the smallest count from 2 to 8 that reaches it (else 8); key blocks of 64 at d = 256,
+    128 otherwise. The workspace size follows the causal rule (the larger split)."""
     kb = -(-N // (64 if d == 256 else 128))
     base = kb * B * Hkv
-    if base >= 512:
+    target = 1024 if causal else 512
+    if base >= target:
         return 1
     for s in range(2, 8):
-        if base * s >= 512:
+        if base * s >= target:
             return s
     return 8
 
