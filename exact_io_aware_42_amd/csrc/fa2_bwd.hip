@@ -785,7 +785,7 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
 // dO operand read, which halves the LDS reads per MFMA of those operands; the 128 keys' K rows
 // then stay in LDS (read per step) and only V's fragments live in registers, and 3 (d = 64) or
 // 2 (d = 128) workgroups of 4 waves share a CU, each SIMD interleaving independent workgroups.
-template <int D, int KP = 1>
+template <int D, int KP = 1, bool DROP = false>
 struct Kv16Shape {
   static constexpr int NW = 4, THREADS = 256, BQ = 32;
   static constexpr int BK = 64 * KP;                            // keys per workgroup
@@ -793,24 +793,26 @@ struct Kv16Shape {
   static constexpr int KS = D / 32;                             // k-steps of S and dP
   static constexpr int DB = D / 16;                             // 16-row blocks of dV^T, dK^T
   static constexpr int TILE = BQ * D * 2;
-  static constexpr int STATS = 2 * BQ * 4;  // LSE*log2(e) of the 32 queries, then -D
+  // LSE*log2(e) of the 32 queries, then -D, then (dropout) their row keys; 512 bytes with
+  // dropout, so that every tile starts on a 256-byte bank window
+  static constexpr int STATS = DROP ? 512 : 2 * BQ * 4;
   static constexpr int STAGE = 2 * TILE + STATS;
   static constexpr int KRES0 = 2 * STAGE;                // resident K rows (KP > 1)
   static constexpr int KRES = KP > 1 ? BK * D * 2 : 0;
   static constexpr int SMEM = KRES0 + KRES;
 };
 
-template <int D, bool CAUSAL, int KP>
-__global__ __launch_bounds__(256, (Kv16Shape<D, KP>::OCC))
-__attribute__((amdgpu_waves_per_eu(Kv16Shape<D, KP>::OCC, Kv16Shape<D, KP>::OCC))) void
+template <int D, bool CAUSAL, int KP, bool DROP>
+__global__ __launch_bounds__(256, (Kv16Shape<D, KP, DROP>::OCC))
+__attribute__((amdgpu_waves_per_eu(Kv16Shape<D, KP, DROP>::OCC, Kv16Shape<D, KP, DROP>::OCC))) void
 fa2_bwd_dkdv16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                       const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
                       const float* __restrict__ lse2, const float* __restrict__ delta,
                       uint16_t* __restrict__ dk, uint16_t* __restrict__ dv, int N, int n_kblocks,
                       int bh_count, int window, int n_qheads, int group, long long kv_bstride,
-                      float scale_log2, float scale, OperandSign ksign, float* __restrict__ part,
-                      int split) {
-  using S = Kv16Shape<D, KP>;
+                      float scale_log2, float scale, OperandSign ksign, DropParams drop,
+                      float* __restrict__ part, int split) {
+  using S = Kv16Shape<D, KP, DROP>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[S::SMEM];
 
   const int tid = threadIdx.x;
@@ -907,6 +909,8 @@ fa2_bwd_dkdv16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
     } else if (wave == 1) {
       if (lane < 8)
         buffer_load16_to_lds(rd, sst + S::BQ * 4, (uint32_t)lane * 16, (uint32_t)it * S::BQ * 4);
+    } else if (DROP && wave == 2) {
+      if (lane < S::BQ) store_row_key(sst + 2 * S::BQ * 4, drop, qh0 + gi, it * S::BQ, lane);
     }
   };
 
@@ -952,8 +956,12 @@ fa2_bwd_dkdv16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       // LSE*log2(e) and -D of this lane's queries 16b + 4g + (0..3)
       const f32x4_t lsv[2] = {*reinterpret_cast<const f32x4_t*>(ts + 16 * g),
                               *reinterpret_cast<const f32x4_t*>(ts + 64 + 16 * g)};
-      const f32x4_t ndv[2] = {*reinterpret_cast<const f32x4_t*>(ts + S::BQ * 4 + 16 * g),
-                              *reinterpret_cast<const f32x4_t*>(ts + S::BQ * 4 + 64 + 16 * g)};
+      // (with dropout -D is read after the score MFMAs, where it is used)
+      f32x4_t ndv[2] = {};
+      if constexpr (!DROP) {
+        ndv[0] = *reinterpret_cast<const f32x4_t*>(ts + S::BQ * 4 + 16 * g);
+        ndv[1] = *reinterpret_cast<const f32x4_t*>(ts + S::BQ * 4 + 64 + 16 * g);
+      }
       // dP starts at -D, so the MFMAs leave dP - D
       f32x4_t sacc[KP][2], dpacc[KP][2];
 #pragma unroll
@@ -961,7 +969,7 @@ fa2_bwd_dkdv16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
           sacc[kp][b] = f32x4_t{};
-          dpacc[kp][b] = ndv[b];
+          dpacc[kp][b] = DROP ? f32x4_t{} : ndv[b];
         }
 #pragma unroll
       for (int ks = 0; ks < S::KS; ++ks) {
@@ -1001,16 +1009,46 @@ fa2_bwd_dkdv16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
       // P = exp2(S*c - LSE*log2(e)), dS = P * (dP - D), packed as the B operands (queries
       // 8g .. 8g+7 of the MFMA's k range = block 0 registers, then block 1 registers)
       u32x4_t bp[KP], bs[KP];
+      // dropout: the words of this lane's 8 queries (registers of blocks 0, 1) and its key pair.
+      // The two lanes of a pair (kl even, odd: keys 2m, 2m+1) hold the same queries: the even
+      // lane hashes block 0's four, the odd lane block 1's, each takes the other four from its
+      // neighbour (DPP), and a byte permute moves the key's 16 bits to the top (low half for the
+      // even key, high half for the odd one), zeros below.
+      const int odd = kl & 1;
+      u32x4_t rkeys = {};
+      if constexpr (DROP) {
+        rkeys = *reinterpret_cast<const u32x4_t*>(ts + 2 * S::BQ * 4 + 64 * odd + 16 * g);
+        ndv[0] = *reinterpret_cast<const f32x4_t*>(ts + S::BQ * 4 + 16 * g);
+        ndv[1] = *reinterpret_cast<const f32x4_t*>(ts + S::BQ * 4 + 64 + 16 * g);
+      }
 #pragma unroll
       for (int kp = 0; kp < KP; ++kp) {
         float pv[8], dsv[8];
+        uint32_t dw[2][4];
+        if constexpr (DROP) {
+          const uint32_t pair = (uint32_t)((key_w0 + 16 * kp + kl) >> 1) * kDropKeyMul;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t w = pcg_hash(rkeys[r] ^ pair);
+            const uint32_t x = swap_adjacent_lanes(w);
+            dw[0][r] = __builtin_amdgcn_perm(x, w, odd ? 0x07060C0Cu : 0x01000C0Cu);
+            dw[1][r] = __builtin_amdgcn_perm(x, w, odd ? 0x03020C0Cu : 0x05040C0Cu);
+          }
+        }
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const float p = fast_exp2(__builtin_fmaf(sacc[kp][b][r], scale_log2, -lsv[b][r]));
-            pv[4 * b + r] = p;
-            dsv[4 * b + r] = p * dpacc[kp][b][r];
+            if constexpr (DROP) {
+              // kept with its 1/P(keep) scale, or 0: dV takes P*Z, dS = P*(Z*dP - D)
+              const float zs = dw[b][r] >= drop.thr ? drop.scale : 0.f;
+              pv[4 * b + r] = p * zs;
+              dsv[4 * b + r] = p * __builtin_fmaf(dpacc[kp][b][r], zs, ndv[b][r]);
+            } else {
+              pv[4 * b + r] = p;
+              dsv[4 * b + r] = p * dpacc[kp][b][r];
+            }
           }
         bp[kp] = u32x4_t{pack_bf16(pv[0], pv[1]), pack_bf16(pv[2], pv[3]), pack_bf16(pv[4], pv[5]),
                          pack_bf16(pv[6], pv[7])};
@@ -1411,14 +1449,14 @@ hipError_t launch_dkdv256_t(const BwdArgs& a) {
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, int KP = 1>
+template <int D, bool CAUSAL, int KP, bool DROP>
 hipError_t launch_dkdv16_t(const BwdArgs& a) {
-  using S = Kv16Shape<D, KP>;
+  using S = Kv16Shape<D, KP, DROP>;
   const int n_kblocks = (a.N + S::BK - 1) / S::BK;
   const long long grid = (long long)n_kblocks * a.B * a.Hkv * a.kv_split;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const int bh_count = a.B * a.Hkv * a.kv_split;
-  hipLaunchKernelGGL((fa2_bwd_dkdv16_kernel<D, CAUSAL, KP>), dim3((unsigned)grid), dim3(S::THREADS),
+  hipLaunchKernelGGL((fa2_bwd_dkdv16_kernel<D, CAUSAL, KP, DROP>), dim3((unsigned)grid), dim3(S::THREADS),
                      0, a.stream, static_cast<const uint16_t*>(a.q),
                      static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
                      static_cast<const uint16_t*>(a.dout), a.lse2, a.delta,
@@ -1427,8 +1465,9 @@ hipError_t launch_dkdv16_t(const BwdArgs& a) {
                      causal_window(bh_count, 4ll * a.N * D * (a.H / a.Hkv) / a.kv_split,
                                    n_kblocks, S::OCC, window_budget(D)),
                      a.H, a.H / a.Hkv, a.kv_bstride, a.scale_log2, a.scale,
-                     OperandSign{a.sgn_and, a.sgn_xor}, a.kv_split > 1 ? a.kv_part : nullptr,
-                     a.kv_split);
+                     OperandSign{a.sgn_and, a.sgn_xor},
+                     DropParams{a.drop_k0, a.drop_k1, a.drop_thr, a.drop_scale},
+                     a.kv_split > 1 ? a.kv_part : nullptr, a.kv_split);
   return hipGetLastError();
 }
 
@@ -1441,16 +1480,23 @@ hipError_t launch_bwd_dkdv_drop(const BwdArgs& a) {
     // sub-block per wave was 5-7.5% slower for its LDS bytes per MFMA; at B8 H32 N2048 d64 +4.2%
     // against one sub-block per wave)
     if (a.d == 256)
-      return a.causal ? launch_dkdv16_t<256, true>(a) : launch_dkdv16_t<256, false>(a);
+      return a.causal ? launch_dkdv16_t<256, true, 1, false>(a)
+                      : launch_dkdv16_t<256, false, 1, false>(a);
     if (a.d == 64)
-      return a.causal ? launch_dkdv16_t<64, true, 2>(a) : launch_dkdv16_t<64, false, 2>(a);
-    return a.causal ? launch_dkdv16_t<128, true, 2>(a) : launch_dkdv16_t<128, false, 2>(a);
+      return a.causal ? launch_dkdv16_t<64, true, 2, false>(a)
+                      : launch_dkdv16_t<64, false, 2, false>(a);
+    return a.causal ? launch_dkdv16_t<128, true, 2, false>(a)
+                    : launch_dkdv16_t<128, false, 2, false>(a);
   } else {
-    // dropout: the 32-key kernels (their lane pairs share the keep bits of a key pair)
+    // dropout: the 16x16x32 kernel at d = 64 (dropout step at B8 H32 N2048 +8.7% causal against
+    // the 32-key kernel); at d = 128 and 256 its dropout variant spills (160 and ~450 bytes per
+    // lane: the keep words and -D on top of 250-253 VGPRs) and measured 8-18% and 55% slower,
+    // so the 32-key kernels stay there (their lane pairs share the keep bits of a key pair)
+    if (a.d == 64)
+      return a.causal ? launch_dkdv16_t<64, true, 2, true>(a)
+                      : launch_dkdv16_t<64, false, 2, true>(a);
     if (a.d == 256)
       return a.causal ? launch_dkdv256_t<true, DROP>(a) : launch_dkdv256_t<false, DROP>(a);
-    if (a.d == 64)
-      return a.causal ? launch_dkdv_t<64, true, DROP>(a) : launch_dkdv_t<64, false, DROP>(a);
     return a.causal ? launch_dkdv_t<128, true, DROP>(a) : launch_dkdv_t<128, false, DROP>(a);
   }
 }
