@@ -7,7 +7,8 @@
         --out profiles/kernels_<workload>.txt --title "..." --cmd "rocprofv3 ..."
     # the same from run_kernel_trace.csv, one line per (kernel, grid size); --last N keeps
     # the last N dispatches of each line (the timed steps after the warm-up); --workgroups
-    # keeps only launches of the given grid sizes
+    # keeps only launches of the given grid sizes; --stop-at 'kernel|workgroups' adds a table
+    # of the dispatches before that launch (a benchmark's main loop, before its other cases)
     python -m exact_io_aware_42_amd.profiling trace --csv run_kernel_trace.csv \
         --out profiles/kernels_<workload>.txt --title "..." --cmd "rocprofv3 ..." [--last N]
     # effective clock per kernel: GRBM_GUI_ACTIVE (summed over the 8 XCDs) of each dispatch
@@ -145,20 +146,43 @@ def trace_main(a):
                 continue
             dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
             groups.setdefault(key, []).append((int(r["Start_Timestamp"]), dur))
-    total = sum(d for v in groups.values() for _, d in v)
-    rows = []
-    for (name, wgs), v in groups.items():
+    for v in groups.values():
         v.sort()
-        sel = [d for _, d in v][-a.last:] if a.last else [d for _, d in v]
-        rows.append((name, wgs, len(v), len(sel), statistics.mean(sel), min(sel), max(sel),
-                     100.0 * sum(d for _, d in v) / total))
-    rows.sort(key=lambda x: -x[7])
+    total = sum(d for v in groups.values() for _, d in v)
+
+    def table(sel_groups):
+        rows = []
+        for (name, wgs), v in sel_groups.items():
+            if not v:
+                continue
+            sel = [d for _, d in v][-a.last:] if a.last else [d for _, d in v]
+            rows.append((name, wgs, len(v), len(sel), statistics.mean(sel), min(sel), max(sel),
+                         100.0 * sum(d for _, d in v) / total))
+        rows.sort(key=lambda x: -x[7])
+        return rows
+
     with open(a.out, "w") as f:
         f.write(f"# rocprofv3 kernel trace: {a.title}\n")
         f.write(f"# command: {a.cmd}\n")
-        f.write("# kernel | workgroups | dispatches | dispatches averaged (last) | average us | "
+        head = ("# kernel | workgroups | dispatches | dispatches averaged (last) | average us | "
                 "min us | max us | share of GPU time\n")
-        for n, w, c, k, avg, mn, mx, pct in rows:
+        if a.stop_at:
+            # the leading segment: every dispatch before the first launch of the given
+            # (kernel, workgroup count), e.g. the first kernel after a benchmark's main loop
+            name, wgs = a.stop_at.rsplit("|", 1)
+            stops = [t for (n, w), v in groups.items() if n == name and w == int(wgs) for t, _ in v]
+            if not stops:
+                raise SystemExit(f"no launch of {a.stop_at!r} in {a.csv}")
+            t_stop = min(stops)
+            lead = {k: [x for x in v if x[0] < t_stop] for k, v in groups.items()}
+            f.write(f"# segment before the first launch of {name} on {wgs} workgroups; the last "
+                    f"{a.last} dispatches of each line in it are averaged\n")
+            f.write(head)
+            for n, w, c, k, avg, mn, mx, pct in table(lead):
+                f.write(f"{n} | {w} | {c} | {k} | {avg:.1f} | {mn:.1f} | {mx:.1f} | {pct:.1f}%\n")
+            f.write("# the whole run\n")
+        f.write(head)
+        for n, w, c, k, avg, mn, mx, pct in table(groups):
             f.write(f"{n} | {w} | {c} | {k} | {avg:.1f} | {mn:.1f} | {mx:.1f} | {pct:.1f}%\n")
     print(open(a.out).read())
 
@@ -282,6 +306,8 @@ def main(argv=None):
     tr.add_argument("--last", type=int, default=0)
     tr.add_argument("--workgroups", type=lambda x: [int(v) for v in x.split(",")], default=None,
                     help="keep only launches with these workgroup counts")
+    tr.add_argument("--stop-at", default=None,
+                    help="'kernel|workgroups': also summarise the dispatches before its first launch")
     ck = sub.add_parser("clock")
     ck.add_argument("--dir", required=True)
     ck.add_argument("--out", required=True)
