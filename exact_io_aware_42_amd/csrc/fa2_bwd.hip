@@ -17,10 +17,12 @@
 //                        dO and O rows it loads and stores -D and LSE*log2(e) of its queries
 //                        in the workspace; then it recomputes S^T and dP^T per key tile and
 //                        accumulates dQ^T = K^T dS^T.
-//   fa2_bwd_dkdv_kernel  grid over (key block of 128, head, batch): the block's K and V rows
-//                        stay in LDS, 64-query tiles of Q, dO, LSE*log2(e) and D stream
-//                        through LDS, and two waves per 32 keys (one per half of each query
-//                        tile) accumulate dK, dV in registers; the pair's sums meet in LDS.
+//   fa2_bwd_dkdv16_kernel grid over (key block, head, batch), 128 keys (64 at d = 256): 32-query
+//                        tiles of Q, dO, LSE*log2(e) and -D stream through LDS; each wave
+//                        forms S and dP of its 16 or 32 keys with 16x16x32 MFMAs (lane = key)
+//                        and accumulates its keys' dK, dV in registers. With dropout at d = 128
+//                        and 256 the 32-key kernels below (fa2_bwd_dkdv_kernel: K and V rows
+//                        resident in LDS, two waves per 32 keys; fa2_bwd_dkdv256_kernel).
 //   fa2_bwd_pre_kernel   D and LSE*log2(e) alone (HBM-bound), for callers that want dK/dV
 //                        without dQ.
 // dK/dV and dQ each recompute S and dP; dQ's two recompute GEMMs are the price of avoiding
@@ -770,11 +772,11 @@ __global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
 }
 
 // ---------------------------------------------------------------------------------------
-// dK, dV with 16 keys per wave (v_mfma_f32_16x16x32_bf16), without dropout. Workgroup = 4 waves
-// over 64 keys, one wave per SIMD, and several workgroups per CU (4 at d = 64, 3 at d = 128, 2
-// at d = 256), so each SIMD runs waves of independent workgroups. A wave keeps its 16 keys' K
-// and V fragments in registers (loaded once, the scale's sign applied to K) and its dK^T, dV^T
-// accumulators (d x 16 keys); 32-query tiles of Q and dO with their LSE*log2(e) and -D stream
+// dK, dV with 16-key MFMA blocks (v_mfma_f32_16x16x32_bf16). Workgroup = 4 waves over 64*KP
+// keys, one wave per SIMD, and several workgroups per CU (3 at d = 64, 2 at d = 128 and 256),
+// so each SIMD runs waves of independent workgroups. With KP = 1 (d = 256) a wave keeps its 16
+// keys' K and V fragments in registers (loaded once, the scale's sign applied to K) and its
+// dK^T, dV^T accumulators (d x 16 keys); 32-query tiles of Q and dO with their LSE*log2(e) and -D stream
 // through a 2-stage LDS ring (swz16 layout). Per tile, S = Q K^T and dP = dO V^T come out as two
 // 16-query blocks with lane = key (query order: block b, register r of lane group g is query
 // 16b + 4g + r), so the packed P and dS are directly the B operands of dV^T += dO^T P and

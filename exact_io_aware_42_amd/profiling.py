@@ -49,11 +49,36 @@ KERNEL_SOURCES = {
 }
 
 
+def strip_comments(src: str) -> str:
+    """C/C++ source without its comments, whitespace runs collapsed to one space (string
+    literals are kept as they are; the kernel sources hold none with comment markers)."""
+    out, i, n = [], 0, len(src)
+    while i < n:
+        if src.startswith("//", i):
+            j = src.find("\n", i)
+            i = n if j < 0 else j
+        elif src.startswith("/*", i):
+            j = src.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        elif src[i] == '"':
+            j = i + 1
+            while j < n and src[j] != '"':
+                j += 2 if src[j] == "\\" else 1
+            out.append(src[i:j + 1])
+            i = j + 1
+        else:
+            out.append(src[i])
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_digest(kernel: str) -> str:
+    """Digest of the code (comments and layout excluded) of the sources a kernel is built from."""
     h = hashlib.sha256()
     for n in KERNEL_SOURCES[kernel]:
-        with open(os.path.join(PKG_DIR, "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(PKG_DIR, "csrc", n)) as f:
+            h.update(strip_comments(f.read()).encode())
     return h.hexdigest()[:16]
 
 
