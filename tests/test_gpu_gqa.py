@@ -149,15 +149,17 @@ def test_split_groups_match_whole_groups(d):
 SPLIT_CASES = [((1, 8, 1, 77, 64), True), ((1, 16, 2, 257, 128), False),
                ((2, 16, 16, 130, 128), True), ((1, 6, 3, 1, 256), True),
                ((1, 4, 4, 600, 256), False), ((3, 8, 8, 65, 64), True),
-               ((1, 8, 8, 2048, 128), True), ((1, 8, 4, 2048, 64), False)]
+               ((1, 8, 8, 2048, 128), True), ((1, 8, 4, 2048, 64), False),
+               ((4, 8, 4, 2048, 128), True), ((4, 8, 4, 2048, 128), False)]
 
 
 @pytest.mark.parametrize("dims,causal", SPLIT_CASES,
                          ids=[f"{b}x{h}/{hk}x{n}x{d}-{'c' if c else 'f'}" for (b, h, hk, n, d), c in SPLIT_CASES])
 def test_split_steps_match_oracle(dims, causal):
     """Small problems split each (key block, K/V head) pair's steps into parts (here 2, 4 and
-    8, for one K/V head, many heads, a single query, ragged N, both masks): dQ, dK, dV against
-    the oracle."""
+    8, for one K/V head, many heads, a single query, ragged N, both masks; B4 H8 Hkv4 N2048
+    d128 splits into 4 parts under the causal mask and 2 without): dQ, dK, dV against the
+    oracle."""
     fa2 = _fa2()
     from exact_io_aware_42_amd import ops
     B, H, Hkv, N, d = dims
