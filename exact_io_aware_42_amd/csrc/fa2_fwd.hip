@@ -21,13 +21,16 @@
 //    query, so the rescale and the final 1/l are per-lane scalars;
 //  * K and V tiles move HBM -> LDS by buffer loads that write LDS directly (no VGPR staging,
 //    zero fill past the sequence end), into row-major tiles whose 16-byte chunks are XOR-
-//    swizzled so both LDS read patterns are free of bank conflicts, double-buffered
-//    (tile j+1 streams in while tile j is computed), one barrier per tile;
+//    swizzled so both LDS read patterns are free of bank conflicts, in a ring of four K and
+//    four V tiles at d >= 128 (two at d = 64): tiles are taken in groups of two (one at d = 64),
+//    the next group streams in while one is computed, and the workgroup meets at one barrier
+//    per group;
 //  * exp2 form: p = exp2(s * scale*log2(e) - m) is one FMA + one v_exp_f32. Masked tiles
 //    (causal diagonal, ragged tail) start their score accumulators at -inf instead of 0 for
 //    hidden keys. Two waves per SIMD (three at d = 64) let one wave's softmax VALU work
-//    overlap another wave's MFMAs. The key loop is unrolled by two so the LDS slot of a tile
-//    is a compile-time constant and every LDS address is a base register plus an immediate;
+//    overlap another wave's MFMAs. The key loop is unrolled over the ring so the LDS slot of
+//    a tile is a compile-time constant and every LDS address is a base register plus an
+//    immediate;
 //  * the LSE uses the fp32 sum of the unrounded p. O is normalised by the sum of the weights
 //    the PV MFMA actually used: on masked tiles (causal diagonal, ragged tail) a correction
 //    sum(bf16(p)) - sum(p) is added, so a row whose visible keys all lie in masked tiles (every
@@ -53,6 +56,14 @@ namespace {
 #ifndef FA2_FWD_OCC
 #define FA2_FWD_OCC 2  // waves per SIMD the forward kernel is compiled for
 #endif
+// Key tiles per workgroup barrier at d >= 128. The 8 waves of a workgroup drift apart within a
+// tile (two per SIMD take turns), and a per-wave timer probe put 12-15% of their time at the
+// per-tile barrier, also in the long non-causal forward; two tiles per barrier (a ring of 4+4
+// tiles, 128 KiB) measured +0.6-1.4% at d = 128 and +1.6-1.8% at d = 256 on every forward
+// workload.
+#ifndef FA2_FWD_TILES_PER_SYNC
+#define FA2_FWD_TILES_PER_SYNC 2
+#endif
 
 constexpr float kRescaleSum = 256.0f;  // a lane's partial sum of p per tile stays <= 2^8
 constexpr float kRescaleLog2 = 8.0f;   // so each p stays <= 2^8 (log2 units)
@@ -76,12 +87,20 @@ struct FwdShape {
   static constexpr int CB = D / 32;            // 32-row blocks of O^T
   static constexpr int TILE_BYTES = BC * D * 2;
   static constexpr int LOADS = TILE_BYTES / (THREADS * 16);  // 16-byte loads per lane per tile
+  // tiles per barrier: the LDS ring holds 2*TPB K tiles and as many V tiles (128 KiB at d >= 128,
+  // one workgroup per CU); d = 64 keeps 1 so that three workgroups fit a CU
+  static constexpr int TPB = D == 64 ? 1 : FA2_FWD_TILES_PER_SYNC;
+  static constexpr int SLOTS = 2 * TPB;
   static constexpr int K_SLOT0 = 0;
-  static constexpr int V_SLOT0 = 2 * TILE_BYTES;
-  static constexpr int SMEM = 4 * TILE_BYTES > NW * store_scratch_bytes(CB)
-                                 ? 4 * TILE_BYTES
-                                 : NW * store_scratch_bytes(CB);
+  static constexpr int V_SLOT0 = SLOTS * TILE_BYTES;
+  static constexpr int RING = 2 * SLOTS * TILE_BYTES;
+  static constexpr int SMEM =
+      RING > NW * store_scratch_bytes(CB) ? RING : NW * store_scratch_bytes(CB);
   static_assert(LOADS >= 1 && DCH >= 8, "tile shape");
+  static_assert(TPB == 1 || TPB == 2, "tiles per barrier");
+  // every LDS read is a base register plus a 16-bit immediate: the slot offsets within the K
+  // and within the V region stay below 64 KiB (the V region's base is in the registers)
+  static_assert(SLOTS * TILE_BYTES <= 65536, "ring immediates");
 };
 
 template <int D, bool CAUSAL, bool DROP>
@@ -173,7 +192,8 @@ __global__ __launch_bounds__(FwdShape<D>::THREADS, FA2_FWD_OCC) void fa2_fwd_ker
     for (int h = 0; h < 2; ++h) {
       const int row = 8 * g + 4 * h + jl / 4;
       const int col = 32 * cb + 16 * (grp & 1) + 4 * (jl & 3);
-      vbase[cb][h] = row * D * 2 + (((col >> 3) ^ swz<D>(row)) * 16) + (col & 7) * 2;
+      vbase[cb][h] =
+          S::V_SLOT0 + row * D * 2 + (((col >> 3) ^ swz<D>(row)) * 16) + (col & 7) * 2;
     }
   auto v_off = [&](int cb, int u, int h) {
     return vbase[cb % 4][h] + (cb / 4) * 256 + 16 * u * D * 2;
@@ -280,7 +300,7 @@ __global__ __launch_bounds__(FwdShape<D>::THREADS, FA2_FWD_OCC) void fa2_fwd_ker
   // O^T += V^T P^T from V slot `slot`; MFMA u covers keys 16u .. 16u+15 = score block u/2,
   // registers 8(u%2) .. 8(u%2)+7
   auto pv = [&](int slot, uint32_t (*pk)[8]) {
-    const unsigned char* vt = smem + S::V_SLOT0 + slot * S::TILE_BYTES;
+    const unsigned char* vt = smem + slot * S::TILE_BYTES;  // (V_SLOT0 is in vbase)
 #pragma unroll
     for (int u = 0; u < 2 * S::KB; ++u) {
       const u32x4_t b = {pk[u / 2][4 * (u % 2) + 0], pk[u / 2][4 * (u % 2) + 1],
@@ -305,22 +325,23 @@ __global__ __launch_bounds__(FwdShape<D>::THREADS, FA2_FWD_OCC) void fa2_fwd_ker
     for (int cb = 0; cb < S::CB; ++cb) oacc[cb] *= alpha;
   };
 
-  // ---- main loop: tile j+1 streams into the other LDS slot while tile j is computed
-  load_k(0, 0);
-  load_v(0, 0);
+  // ---- main loop over groups of TPB tiles: group g sits in ring half g % 2 (slots
+  // TPB*(g%2) + i) and the next group streams into the other half while it is computed; one
+  // barrier per group
+  constexpr int TPB = S::TPB;
+#pragma unroll
+  for (int i = 0; i < TPB; ++i)
+    if (i < n_tiles) {
+      load_k(i, i);
+      load_v(i, i);
+    }
   wait_vmem();
   __syncthreads();
   m_run = -INFINITY;
   bool first = true;
-  auto step = [&](auto slot_c, int j) {
+  // tile j from slot `slot` (nothing for a wave whose rows all precede the tile's keys)
+  auto tile = [&](auto slot_c, int j) {
     constexpr int slot = decltype(slot_c)::value;
-    // slot ^ 1 held tile j-1, whose readers all passed the barrier that ended step j-1
-    FA2_STAGE_SYNC();
-    if (j + 1 < n_tiles) {
-      load_k(j + 1, slot ^ 1);
-      load_v(j + 1, slot ^ 1);
-    }
-    FA2_STAGE_SYNC();
     if (j <= wave_last) {
       f32x16_t s[S::KB];
       const bool masked = tile_needs_mask(j);
@@ -361,13 +382,29 @@ __global__ __launch_bounds__(FwdShape<D>::THREADS, FA2_FWD_OCC) void fa2_fwd_ker
       __builtin_amdgcn_s_setprio(0);
       if (!DROP && masked) bf16_correction(pk, tile_sum);
     }
+  };
+  auto tile_group = [&](auto half_c, int j0) {
+    constexpr int half = decltype(half_c)::value;
+    // the other half held the previous group, whose readers all passed the barrier that ended it
+    FA2_STAGE_SYNC();
+#pragma unroll
+    for (int i = 0; i < TPB; ++i)
+      if (j0 + TPB + i < n_tiles) {
+        load_k(j0 + TPB + i, (half ^ 1) * TPB + i);
+        load_v(j0 + TPB + i, (half ^ 1) * TPB + i);
+      }
+    FA2_STAGE_SYNC();
+    tile(std::integral_constant<int, half * TPB>{}, j0);
+    if constexpr (TPB > 1) {
+      if (j0 + 1 < n_tiles) tile(std::integral_constant<int, half * TPB + 1>{}, j0 + 1);
+    }
     FA2_STAGE_SYNC();
     wait_vmem();
     __syncthreads();
   };
-  for (int j = 0; j < n_tiles; j += 2) {
-    step(std::integral_constant<int, 0>{}, j);
-    if (j + 1 < n_tiles) step(std::integral_constant<int, 1>{}, j + 1);
+  for (int j0 = 0; j0 < n_tiles; j0 += 2 * TPB) {
+    tile_group(std::integral_constant<int, 0>{}, j0);
+    if (j0 + TPB < n_tiles) tile_group(std::integral_constant<int, 1>{}, j0 + TPB);
   }
 
   // ---- epilogue: deferred normalisation, bf16 output, LSE
