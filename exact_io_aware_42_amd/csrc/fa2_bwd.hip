@@ -804,6 +804,44 @@ struct Kv16Shape {
   static constexpr int SMEM = KRES0 + KRES;
 };
 
+// The 16*KP x D tile of a wave's dK^T or dV^T accumulators (lane = key 16kp + l%16, columns
+// 16blk + 4(l/16) + (0..3)) times `mul`, as bf16 into rows row0 .. row0+16KP-1 of `out` (row
+// stride D; rows >= n_rows skipped) through `scratch` (LDS that only this wave uses,
+// rows16_scratch_bytes bytes, rows padded by 16 bytes: the 8-byte writes of 16 rows x 2 column
+// groups fall in distinct banks), so each global store writes whole row segments, 16 bytes per
+// lane, rather than 8 bytes in each of 16 rows. A wave's LDS accesses complete in order, so the
+// reads see the writes and the next call's writes follow this call's reads.
+template <int D, int KP>
+constexpr int rows16_scratch_bytes() { return 16 * KP * (D * 2 + 16); }
+template <int D, int KP>
+__device__ __forceinline__ void store_rows16_via_lds(unsigned char* scratch,
+                                                     const f32x4_t (*acc)[D / 16], float mul,
+                                                     uint16_t* out, int row0, int n_rows,
+                                                     int lane) {
+  constexpr int PITCH = D * 2 + 16;
+  constexpr int CH = D / 8, RPI = 64 / CH;  // 16-byte chunks per row, rows per store
+  const int kl = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int kp = 0; kp < KP; ++kp)
+#pragma unroll
+    for (int blk = 0; blk < D / 16; ++blk)
+      *reinterpret_cast<u32x2_t*>(scratch + (16 * kp + kl) * PITCH + (16 * blk + 4 * g) * 2) =
+          u32x2_t{pack_bf16(acc[kp][blk][0] * mul, acc[kp][blk][1] * mul),
+                  pack_bf16(acc[kp][blk][2] * mul, acc[kp][blk][3] * mul)};
+#pragma unroll
+  for (int i = 0; i < 16 * KP / RPI; ++i) {
+    const int rr = i * RPI + lane / CH, ch = lane % CH;
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(scratch + rr * PITCH + ch * 16);
+    if (row0 + rr < n_rows) *reinterpret_cast<u32x4_t*>(out + (size_t)(row0 + rr) * D + ch * 8) = v;
+  }
+}
+// At d = 128 the dK/dV kernel writes its rows through LDS (fwd+bwd step at B4 H16 N2048 +1.9%
+// causal, +1.3% non-causal); at d = 64 and 256 the same epilogue made the compiler spill 4 and 12
+// registers in the causal kernels (steps -2.7% and -7.9%), so they store directly.
+#ifndef FA2_DKDV16_LDS_EPILOGUE
+#define FA2_DKDV16_LDS_EPILOGUE 1
+#endif
+
 template <int D, bool CAUSAL, int KP, bool DROP>
 __global__ __launch_bounds__(256, (Kv16Shape<D, KP, DROP>::OCC))
 __attribute__((amdgpu_waves_per_eu(Kv16Shape<D, KP, DROP>::OCC, Kv16Shape<D, KP, DROP>::OCC))) void
@@ -816,6 +854,7 @@ fa2_bwd_dkdv16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
                       float* __restrict__ part, int split) {
   using S = Kv16Shape<D, KP, DROP>;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[S::SMEM];
+  static_assert(4 * rows16_scratch_bytes<D, KP>() <= S::SMEM, "output scratch");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -1084,6 +1123,13 @@ fa2_bwd_dkdv16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
 
   // dK = scale * dK_acc, dV = dV_acc: lane holds key key_w0 + 16kp + kl, d columns
   // 16blk + 4g + (0..3)
+  if (FA2_DKDV16_LDS_EPILOGUE && D == 128 && part == nullptr) {
+    // whole rows through LDS (the loop ended with a barrier: ring and resident K rows are free)
+    unsigned char* sc = smem + wave * rows16_scratch_bytes<D, KP>();
+    store_rows16_via_lds<D, KP>(sc, dkacc, scale, dk + head_off, key_w0, N, lane);
+    store_rows16_via_lds<D, KP>(sc, dvacc, 1.f, dv + head_off, key_w0, N, lane);
+    return;
+  }
 #pragma unroll
   for (int kp = 0; kp < KP; ++kp) {
     const int my_key = key_w0 + 16 * kp + kl;
