@@ -34,9 +34,14 @@ def run_fwd(bits_q, bits_k, bits_v, causal, scale):
     return o, lse
 
 
+# at d >= 128 the key tiles (64 keys, 32 at d = 256) go through a ring of four LDS slots in pairs:
+# N = 320, 327, 448 give 5, 6, 7 tiles (the last causal block too), 96 and 130 at d = 256 give 3
+# and 5, so every phase of the ring ends a key loop
 SMALL = [(1, 1, 1, 64), (1, 1, 1, 128), (1, 1, 5, 64), (2, 3, 77, 64), (1, 2, 200, 128),
          (1, 1, 129, 128), (2, 1, 383, 64), (1, 2, 1000, 128), (1, 1, 2049, 64),
-         (1, 1, 1, 256), (1, 2, 31, 256), (2, 1, 161, 256), (1, 2, 700, 256)]
+         (1, 2, 320, 128), (2, 1, 327, 128), (1, 1, 448, 128),
+         (1, 1, 1, 256), (1, 2, 31, 256), (1, 1, 96, 256), (1, 1, 130, 256), (2, 1, 161, 256),
+         (1, 2, 700, 256)]
 
 
 @pytest.mark.parametrize("causal", [False, True])
