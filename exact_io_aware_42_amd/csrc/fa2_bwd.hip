@@ -835,11 +835,15 @@ __device__ __forceinline__ void store_rows16_via_lds(unsigned char* scratch,
     if (row0 + rr < n_rows) *reinterpret_cast<u32x4_t*>(out + (size_t)(row0 + rr) * D + ch * 8) = v;
   }
 }
-// At d = 128 the dK/dV kernel writes its rows through LDS (fwd+bwd step at B4 H16 N2048 +1.9%
-// causal, +1.3% non-causal); at d = 64 and 256 the same epilogue made the compiler spill 4 and 12
-// registers in the causal kernels (steps -2.7% and -7.9%), so they store directly.
+// The dK/dV kernel writes its rows through LDS: fwd+bwd step at B4 H16 N2048 d128 +1.9% causal,
+// +1.3% non-causal; at d = 64 (B8 H32 N2048) +0.8-1.4% and d = 256 (B2 H16 N4096) +0.4-0.8%, once
+// the epilogue's addresses were kept from being computed before the key loop (held across it, they
+// had made the compiler spill 4 and 12 registers in the causal kernels: -2.7% and -7.9%).
 #ifndef FA2_DKDV16_LDS_EPILOGUE
 #define FA2_DKDV16_LDS_EPILOGUE 1
+#endif
+#ifndef FA2_DKDV16_LDS_EPILOGUE_MAX_D
+#define FA2_DKDV16_LDS_EPILOGUE_MAX_D 256
 #endif
 
 template <int D, bool CAUSAL, int KP, bool DROP>
@@ -1123,11 +1127,15 @@ fa2_bwd_dkdv16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
 
   // dK = scale * dK_acc, dV = dV_acc: lane holds key key_w0 + 16kp + kl, d columns
   // 16blk + 4g + (0..3)
-  if (FA2_DKDV16_LDS_EPILOGUE && D == 128 && part == nullptr) {
-    // whole rows through LDS (the loop ended with a barrier: ring and resident K rows are free)
+  if (FA2_DKDV16_LDS_EPILOGUE && D <= FA2_DKDV16_LDS_EPILOGUE_MAX_D && part == nullptr) {
+    // whole rows through LDS (the loop ended with a barrier: ring and resident K rows are free).
+    // The lane index passes through an empty asm statement so that the compiler cannot compute
+    // the epilogue's addresses before the loop and hold them across it
+    int lane_e = lane;
+    asm volatile("" : "+v"(lane_e));
     unsigned char* sc = smem + wave * rows16_scratch_bytes<D, KP>();
-    store_rows16_via_lds<D, KP>(sc, dkacc, scale, dk + head_off, key_w0, N, lane);
-    store_rows16_via_lds<D, KP>(sc, dvacc, 1.f, dv + head_off, key_w0, N, lane);
+    store_rows16_via_lds<D, KP>(sc, dkacc, scale, dk + head_off, key_w0, N, lane_e);
+    store_rows16_via_lds<D, KP>(sc, dvacc, 1.f, dv + head_off, key_w0, N, lane_e);
     return;
   }
 #pragma unroll
