@@ -4,16 +4,24 @@ through fwd/bwd (which split small problems' dK/dV work) against the CPU float64
 Bounds as in the other parity tests: without dropout (N(0, 1) inputs) max|dO| <= 1e-2,
 mean|dO| <= 1e-3 and max|dLSE| <= 1e-3; with dropout the bf16 rounding bound for O (the kept
 weights are scaled by 1/P(keep), so |O| leaves the range the fixed bound was set for) and
-1e-3 for LSE; 2e-2 * max|g| per gradient; single-key heads by their closed form."""
+1e-3 for LSE; 2e-2 * max|g| per gradient; single-key heads by their closed form. Shapes whose
+rows see so few keys that the exact output, merely rounded to bf16, already has a mean error above
+half the mean bound (small N, where |O| stays near |v|; under the causal mask also the first
+rows of somewhat larger N) are held to that rounding bound and max|dO| <= 1e-2 instead of the
+mean bound, which no bf16 output reliably meets there.
+The case count and seed can be overridden from the environment for a longer sweep."""
+import os
+
 import numpy as np
 import pytest
 import torch
 
-from exact_io_aware_42_amd.inputs import bf16_bits_to_f64, default_scale, normal_bf16
+from exact_io_aware_42_amd.inputs import (bf16_bits_to_f64, default_scale, f32_to_bf16_bits,
+                                          normal_bf16)
 from oracle import attention_backward_dropout, attention_forward_dropout
 
-from gpu_util import (assert_fwd_close, assert_fwd_within_rounding_bound, assert_grad_close,
-                      bf16_to_f64, to_dev)
+from gpu_util import (O_MAX, O_MEAN, assert_fwd_close, assert_fwd_within_rounding_bound,
+                      assert_grad_close, bf16_to_f64, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -34,7 +42,10 @@ def _cases(n=36, seed=20261202):
     return out
 
 
-CASES = _cases()
+# FA2_SWEEP_CASES / FA2_SWEEP_SEED widen or reseed the sweep for a longer run (defaults: 36 cases,
+# the fixed seed above)
+CASES = _cases(int(os.environ.get("FA2_SWEEP_CASES", "36")),
+               int(os.environ.get("FA2_SWEEP_SEED", "20261202")))
 
 
 @pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}x{c[1]}/{c[2]}x{c[3]}x{c[4]}-{'c' if c[5] else 'f'}-p{c[6]:.1f}" for c in CASES])
@@ -54,10 +65,15 @@ def test_sweep(case):
     kr, vr = np.repeat(k64, G, axis=1), np.repeat(v64, G, axis=1)
     okw = dict(causal=causal, scale=default_scale(d), p=p, seed=seed, offset=7)
     o_ref, lse_ref = attention_forward_dropout(q64, kr, vr, **okw)
-    if p:
+    # the exact output's own bf16 rounding: with rows of one to a few keys |O| stays near |v|,
+    # and rounding the exact result to bf16 alone averages ~1e-3 (the whole mean bound)
+    own = np.abs(bf16_bits_to_f64(f32_to_bf16_bits(o_ref.astype(np.float32))) - o_ref).mean()
+    if p or own > O_MEAN / 2:
         o_abs, _ = attention_forward_dropout(q64, kr, np.abs(vr), **okw)
         assert_fwd_within_rounding_bound(bf16_to_f64(o), lse.cpu().double().numpy(), o_ref,
                                          o_abs, lse_ref, str(case))
+        if not p:
+            assert np.abs(bf16_to_f64(o) - o_ref).max() <= O_MAX, case
     else:
         assert_fwd_close(bf16_to_f64(o), lse.cpu().double().numpy(), o_ref, lse_ref, str(case))
     gq, gk, gv = attention_backward_dropout(q64, kr, vr, do64, **okw)
