@@ -19,8 +19,9 @@ the same workload (whole heads) on the host cores. `forward_workloads` adds the 
 kernel's TFLOP/s on the forward-only workloads, `non_causal_step` the same fwd+bwd step
 without the causal mask, `d256_steps` the fwd+bwd step at head dimension 256, `gpt_layer_step` a GPT-style attention layer (bf16 projections + attention,
 forward and backward through torch.autograd), `gqa_step` the fwd+bwd step with 16 query
-heads sharing 4 K/V heads and `dropout_step` the fwd+bwd step with dropout p = 0.1 on the
-attention probabilities; none of them is part of `value`.
+heads sharing 4 K/V heads, `dropout_step` the fwd+bwd step with dropout p = 0.1 on the
+attention probabilities and `graph_step` the fwd+bwd step captured in a HIP graph and replayed;
+none of them is part of `value`.
 
 Prints ONE JSON line (rank 0).
 """
@@ -245,6 +246,58 @@ def dropout_step(fa2, torch, dev, p=0.1, steps=20, warmup=20):
     return {"shape": "B4 H16 N2048 d128 causal", "dropout_p": p, **r}
 
 
+def graph_step(fa2, torch, dev, steps=100, warmup=20, warm_ms=WARM_MS):
+    """The fwd+bwd step at the default workload's shape (B=4, H=16, N=2048, d=128, causal) with
+    caller-given outputs and workspace, captured once in a HIP graph and replayed: the launch
+    overhead floor of the step. Reported beside the same calls made eagerly on the same
+    inputs; not part of `value`."""
+    B, H, N, d = 4, 16, 2048, 128
+    g = torch.Generator(device="cpu").manual_seed(13)
+    mk = lambda: torch.randn(B, H, N, d, generator=g).to(torch.bfloat16).to(dev)
+    q, k, v, do = mk(), mk(), mk(), mk()
+    o, dq, dk, dv = (torch.empty_like(q) for _ in range(4))
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    ws = torch.empty(fa2.bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+
+    def step():
+        fa2.fwd(q, k, v, causal=True, out=o, lse=lse)
+        fa2.bwd(q, k, v, o, do, lse, causal=True, dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def timed(run):
+        # at least warm_ms of GPU time untimed (as for the main step), then `warmup` more runs
+        spent = 0.0
+        while spent < warm_ms:
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(10):
+                run()
+            e1.record()
+            torch.cuda.synchronize()
+            spent += e0.elapsed_time(e1)
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    eager_ms = timed(step)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    graph_ms = timed(graph.replay)
+    flop = 3.5 * fwd_flop(B, H, N, d, True)
+    return {"shape": "B4 H16 N2048 d128 causal", "ms_per_step": round(graph_ms, 4),
+            "tflops": round(flop / (graph_ms * 1e-3) / 1e12, 1),
+            "eager_ms_per_step": round(eager_ms, 4)}
+
+
 def measure_step(fa2, torch, dev, w, causal, with_bwd, steps, warmup, warm_ms=WARM_MS):
     """Run untimed steps (forward, then dQ and dK/dV) of workload `w` for at least `warm_ms` of
     GPU time (the clock needs a few hundred milliseconds of load to settle; a step count alone
@@ -410,6 +463,9 @@ def main():
         },
     }
     if not args.no_fwd_sweep:
+        if args.workload == 5 and with_bwd and causal:
+            # right after the main step, so that both run in the same state of the chip
+            out["graph_step"] = graph_step(fa2, torch, dev)
         out["forward_workloads"] = forward_sweep(fa2, torch, dev)
 
         def other_step(wo, co):
