@@ -20,9 +20,8 @@
 //   fa2_bwd_dkdv16_kernel grid over (key block, head, batch), 128 keys (64 at d = 256): 32-query
 //                        tiles of Q, dO, LSE*log2(e) and -D stream through LDS; each wave
 //                        forms S and dP of its 16 or 32 keys with 16x16x32 MFMAs (lane = key)
-//                        and accumulates its keys' dK, dV in registers. With dropout at d = 128
-//                        and 256 the 32-key kernels below (fa2_bwd_dkdv_kernel: K and V rows
-//                        resident in LDS, two waves per 32 keys; fa2_bwd_dkdv256_kernel).
+//                        and accumulates its keys' dK, dV in registers. With dropout at d = 256
+//                        the 32-key kernel fa2_bwd_dkdv256_kernel.
 //   fa2_bwd_pre_kernel   D and LSE*log2(e) alone (HBM-bound), for callers that want dK/dV
 //                        without dQ.
 // dK/dV and dQ each recompute S and dP; dQ's two recompute GEMMs are the price of avoiding
@@ -204,327 +203,6 @@ struct DropLanes {
     }
   }
 };
-
-// ---------------------------------------------------------------------------------------
-// dK, dV. Workgroup = 8 waves over 128 keys, whose K and V rows stay in LDS for the whole
-// kernel; query tiles of 64 stream through a second LDS ring. Waves w and w+4 share the 32 keys
-// 32(w%4) .. +31 and split each query tile: wave w takes queries 0..31, wave w+4 queries 32..63
-// (two waves per SIMD, each with one 32x32 S and dP block). S = Q K^T and dP = dO V^T come out
-// with lane = key and registers = queries (kmap order), so P and dS are directly the B operands
-// of dV^T = dO^T P and dK^T = Q^T dS; the dO^T and Q^T fragments come from the row-major tiles
-// through transposing reads. The two partial dK, dV of a key group are summed through LDS at the
-// end (each wave of the pair finishes one of the two).
-constexpr int kKvBK = 128;
-constexpr int kKvBQ = 64;
-constexpr int kKvThreads = 512;
-
-template <int D, bool CAUSAL, bool DROP>
-__global__ __launch_bounds__(kKvThreads) void fa2_bwd_dkdv_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-    const float* __restrict__ lse2, const float* __restrict__ delta, uint16_t* __restrict__ dk,
-    uint16_t* __restrict__ dv, int N, int n_kblocks, int bh_count, int window, int n_qheads,
-    int group, long long kv_bstride, float scale_log2, float scale, OperandSign ksign, DropParams drop,
-    float* __restrict__ part, int split) {
-  constexpr int KK = D / 16, CB = D / 32, DCH = D / 8;
-  // LDS: the two ring stages of Q and dO tiles at the bottom (every ds_read of them is a
-  // per-lane base plus a 16-bit immediate), then LSE*log2(e) and D of both stages, then the
-  // resident K and V rows (their per-lane bases carry the offset).
-  constexpr int TILE = kKvBQ * D * 2;
-  constexpr int KV_BYTES = kKvBK * D * 2;
-  constexpr int STAGE = 2 * TILE;               // Q, dO
-  constexpr int STATS0 = 2 * STAGE;             // per stage: LSE*log2(e), then D (256 B each)
-  constexpr int STATS_STAGE = (DROP ? 3 : 2) * kKvBQ * 4;  // + dropout row keys
-  constexpr int KV0 = STATS0 + 2 * STATS_STAGE;
-  constexpr int MAIN_BYTES = KV0 + 2 * KV_BYTES;
-  constexpr int ACC_BYTES = CB * 16 * 64 * 4;   // one wave's dK (or dV) accumulator
-  constexpr int XCH_BYTES = 8 * ACC_BYTES;      // combine area, reuses the main area
-  constexpr int SMEM = MAIN_BYTES > XCH_BYTES ? MAIN_BYTES : XCH_BYTES;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kw = wave & 3;   // key group
-  const int hq = wave >> 2;  // query half of each tile
-  const int l32 = lane & 31;
-  const int g = lane >> 5;
-
-  // causal: key block 0 sees every query tile, so ascending order is longest first
-  const TileCoord tc = schedule_tile<CAUSAL ? Order::kLongAscending : Order::kHeadMajor>(
-      blockIdx.x, n_kblocks, bh_count, window);
-  // tc.bh = (batch * Hkv + K/V head) * split + part. The query heads sharing this K/V head
-  // are qh0 .. qh0 + group - 1; their (head, query tile) steps are summed here in order, part
-  // sj taking the sj-th of `split` equal ranges of them (split > 1: into fp32 partial sums that
-  // fa2_bwd_kv_reduce_kernel adds).
-  const int sj = tc.bh % split;
-  const int bhkv = tc.bh / split;
-  const int n_kvheads = n_qheads / group;
-  const int b_idx = bhkv / n_kvheads;
-  const int kvh = bhkv - b_idx * n_kvheads;
-  const int qh0 = b_idx * n_qheads + kvh * group;
-  const size_t head_off =  // K, V, dK, dV
-      (size_t)b_idx * (size_t)kv_bstride + (size_t)kvh * (size_t)N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + head_off, head_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + head_off, head_bytes);
-
-  const int key_b0 = tc.qb * kKvBK;
-  const int key_w0 = key_b0 + kw * 32;
-  const int my_key = key_w0 + l32;
-  const DropLanes dl(lane, my_key);
-
-  // resident K and V rows of the block: 128 rows each, swz-swizzled; 1 KiB block i holds rows
-  // (64/DCH)*i ..
-  {
-    constexpr int LOADS = KV_BYTES / (kKvThreads * 16);
-    constexpr int RPB = 64 / DCH;
-#pragma unroll
-    for (int r = 0; r < LOADS; ++r) {
-      const int blk = 8 * r + wave;
-      const int row = blk * RPB + lane / DCH;
-      const uint32_t off = (uint32_t)(row * D * 2 + ((lane % DCH) ^ swz<D>(row)) * 16);
-      buffer_load16_to_lds(rk, smem + KV0 + blk * 1024, off, (uint32_t)key_b0 * D * 2);
-      buffer_load16_to_lds(rv, smem + KV0 + KV_BYTES + blk * 1024, off,
-                           (uint32_t)key_b0 * D * 2);
-    }
-  }
-  // per-lane offset of this wave's K/V fragment: row 32*kw + l32, logical chunk 2kk + g
-  const int kvrow = kw * 32 + l32;
-  int kvbase[KK];
-#pragma unroll
-  for (int kk = 0; kk < KK; ++kk)
-    kvbase[kk] = KV0 + kvrow * D * 2 + ((2 * kk + g) ^ swz<D>(kvrow)) * 16;
-  // LSE*log2(e) / D of this lane's queries 32hq + 16hf + 8g + (0..7) within a stage
-  const int statbase = STATS0 + (32 * hq + 8 * g) * 4;
-
-  const int n_qt = (N + kKvBQ - 1) / kKvBQ;
-  const int qt_begin = CAUSAL ? key_b0 / kKvBQ : 0;
-  // step T = 0 .. group*nt - 1 walks query tile qt_begin + T % nt of query head qh0 + T / nt;
-  // this part runs T = t_begin + t for t = 0 .. n_steps - 1
-  const int nt = n_qt - qt_begin;
-  const long long n_all = (long long)group * nt;
-  const int t_begin = (int)(n_all * sj / split);
-  const int n_steps = (int)(n_all * (sj + 1) / split) - t_begin;
-  const TileLoader<D, kKvThreads> ld(wave, lane);
-  // per-lane read offsets within a stage for this wave's query half: row-wise Q/dO fragments
-  // (rows 32hq + kmap(l32)) and transposing reads (k-steps t = 2hq + hf)
-  int qrow[KK], qtr[CB][2];
-  {
-    const TileReads<D> rd_off(lane);
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) qrow[kk] = rd_off.row_off(hq, kk);
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) qtr[cb][h] = rd_off.tr_off(cb, 2 * hq, h);
-  }
-
-  StepPos ldpos(t_begin, nt, qt_begin);  // the next tile to load (loads go in step order)
-  // buffer descriptors of the query head being loaded, rebuilt when the walk changes head
-  int ld_head = -1;
-  __amdgpu_buffer_rsrc_t rq, rdo, rl, rd;
-  auto load_stage = [&](int t, int stage) {
-    (void)t;
-    const int gi = ldpos.gi;
-    const int it = ldpos.it;
-    ldpos.next();
-    if (gi != ld_head) {
-      ld_head = gi;
-      const size_t qoff = (size_t)(qh0 + gi) * (size_t)N * D;
-      rq = make_rsrc(q + qoff, head_bytes);
-      rdo = make_rsrc(dout + qoff, head_bytes);
-      rl = make_rsrc(lse2 + (size_t)(qh0 + gi) * N, (uint32_t)N * 4);
-      rd = make_rsrc(delta + (size_t)(qh0 + gi) * N, (uint32_t)N * 4);
-    }
-    unsigned char* st = smem + stage * STAGE;
-    const uint32_t soff = (uint32_t)it * kKvBQ * D * 2;
-    ld.load(rq, st, soff);
-    ld.load(rdo, st + TILE, soff);
-    // LSE*log2(e) and D of the tile's 64 queries (256 bytes each): 16 lanes of waves 0 and 1
-    unsigned char* sst = smem + STATS0 + stage * STATS_STAGE;
-    if (wave == 0) {
-      if (lane < 16)
-        buffer_load16_to_lds(rl, sst, (uint32_t)lane * 16, (uint32_t)it * kKvBQ * 4);
-    } else if (wave == 1) {
-      if (lane < 16)
-        buffer_load16_to_lds(rd, sst + kKvBQ * 4, (uint32_t)lane * 16, (uint32_t)it * kKvBQ * 4);
-    } else if (DROP && wave == 2) {
-      store_row_key(sst + 2 * kKvBQ * 4, drop, qh0 + gi, it * kKvBQ, lane);
-    }
-  };
-
-  f32x16_t dkacc[CB], dvacc[CB];
-#pragma unroll
-  for (int cb = 0; cb < CB; ++cb) {
-    dkacc[cb] = f32x16_t{};
-    dvacc[cb] = f32x16_t{};
-  }
-
-  if (n_steps > 0) load_stage(0, 0);
-  wait_vmem();
-  __syncthreads();
-  if (ksign.and_mask != ~0u || ksign.xor_mask != 0u) {
-    // a scale <= 0: its sign goes into the resident K rows, once (see OperandSign)
-    for (int i = tid * 16; i < KV_BYTES; i += kKvThreads * 16)
-      *reinterpret_cast<u32x4_t*>(smem + KV0 + i) =
-          apply_sign(*reinterpret_cast<const u32x4_t*>(smem + KV0 + i), ksign);
-    __syncthreads();
-  }
-
-  // unrolled by two below, so the ring stage is a compile-time constant (LDS addresses are a
-  // base register plus an immediate)
-  StepPos cur(t_begin, nt, qt_begin);  // the tile of the current step
-  auto step = [&](auto stage_c, int t) {
-    constexpr int stage = decltype(stage_c)::value;
-    FA2_STAGE_SYNC();
-    if (t + 1 < n_steps) load_stage(t + 1, stage ^ 1);
-    FA2_STAGE_SYNC();
-    const int it = cur.it;
-    cur.next();
-    const int q0 = it * kKvBQ + 32 * hq;  // this wave's 32 queries
-    // every query of the half precedes every key of the wave: fully masked
-    const bool skip = CAUSAL && (q0 + 31 < key_w0);
-    if (!skip) {
-      const unsigned char* tq = smem + stage * STAGE;
-      const unsigned char* tdo = tq + TILE;
-      const unsigned char* ts = smem + statbase + stage * STATS_STAGE;
-      const bool masked = (q0 + 32 > N) || (CAUSAL && q0 < key_w0 + 31);
-
-      // dP starts at -D of each register's query (without dropout), so the MFMAs leave dP - D;
-      // register i is query q0 + 16(i/8) + 8g + i%8
-      f32x16_t s, dp;
-      if constexpr (DROP) {
-        dp = f32x16_t{};
-      } else {
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const unsigned char* sd = ts + 16 * hf * 4 + kKvBQ * 4;
-          const f32x4_t d0 = *reinterpret_cast<const f32x4_t*>(sd);
-          const f32x4_t d1 = *reinterpret_cast<const f32x4_t*>(sd + 16);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            dp[8 * hf + e] = d0[e];
-            dp[8 * hf + 4 + e] = d1[e];
-          }
-        }
-      }
-      if (masked) mask_queries<CAUSAL>(s, q0 + 8 * g, my_key, N, q0 + 32 > N);
-      else {
-        s = f32x16_t{};
-      }
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(smem + kvbase[kk]);
-        const u32x4_t vf = *reinterpret_cast<const u32x4_t*>(smem + kvbase[kk] + KV_BYTES);
-        const u32x4_t aq = *reinterpret_cast<const u32x4_t*>(tq + qrow[kk]);
-        const u32x4_t ad = *reinterpret_cast<const u32x4_t*>(tdo + qrow[kk]);
-        s = mfma32(aq, kf, s);
-        dp = mfma32(ad, vf, dp);
-      }
-      // P = exp2(s*c - LSE*log2e), dS = P * (dP - D)
-      uint32_t pk[8], dsk[8];
-      uint32_t dw[2][8];  // dropout: the 16 bits deciding (query of register 8hf + e, my_key)
-      if constexpr (DROP) dl.words(ts + 2 * kKvBQ * 4, dw);
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const unsigned char* sl = ts + 16 * hf * 4;  // queries 32hq + 16hf + 8g + (0..7)
-        const f32x4_t l0 = *reinterpret_cast<const f32x4_t*>(sl);
-        const f32x4_t l1 = *reinterpret_cast<const f32x4_t*>(sl + 16);
-        float p[8], ds[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float lv = e < 4 ? l0[e] : l1[e - 4];
-          const float pe = fast_exp2(__builtin_fmaf(s[8 * hf + e], scale_log2, -lv));
-          if constexpr (DROP) {
-            // kept with its 1/P(keep) scale, or 0; -D from the workspace
-            const f32x4_t d0 = *reinterpret_cast<const f32x4_t*>(sl + kKvBQ * 4);
-            const f32x4_t d1 = *reinterpret_cast<const f32x4_t*>(sl + kKvBQ * 4 + 16);
-            const float neg_d = e < 4 ? d0[e] : d1[e - 4];
-            const float zs = dw[hf][e] >= drop.thr ? drop.scale : 0.f;
-            p[e] = pe * zs;
-            ds[e] = pe * __builtin_fmaf(dp[8 * hf + e], zs, neg_d);
-          } else {
-            p[e] = pe;
-            ds[e] = pe * dp[8 * hf + e];
-          }
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pk[4 * hf + e] = pack_bf16(p[2 * e], p[2 * e + 1]);
-          dsk[4 * hf + e] = pack_bf16(ds[2 * e], ds[2 * e + 1]);
-        }
-      }
-      // raised priority while the wave issues its dV/dK MFMAs (the other wave on the SIMD runs
-      // its VALU work in between; measured +3.5%)
-      __builtin_amdgcn_s_setprio(1);
-      // dV^T += dO^T P and dK^T += Q^T dS over the wave's 32 queries (k-steps t = 2hq + hf,
-      // 16 rows = 16 * D * 2 bytes apart)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int hoff = hf * 16 * D * 2;
-        const u32x4_t bp = {pk[4 * hf + 0], pk[4 * hf + 1], pk[4 * hf + 2], pk[4 * hf + 3]};
-        const u32x4_t bs = {dsk[4 * hf + 0], dsk[4 * hf + 1], dsk[4 * hf + 2], dsk[4 * hf + 3]};
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          const u32x4_t ao = tr_operand(tdo + hoff, qtr[cb][0], qtr[cb][1]);
-          dvacc[cb] = mfma32(ao, bp, dvacc[cb]);
-          const u32x4_t aq = tr_operand(tq + hoff, qtr[cb][0], qtr[cb][1]);
-          dkacc[cb] = mfma32(aq, bs, dkacc[cb]);
-        }
-      }
-      __builtin_amdgcn_s_setprio(0);
-    }
-    FA2_STAGE_SYNC();
-    wait_vmem();
-    __syncthreads();
-  };
-  for (int t = 0; t < n_steps; t += 2) {
-    step(std::integral_constant<int, 0>{}, t);
-    if (t + 1 < n_steps) step(std::integral_constant<int, 1>{}, t + 1);
-  }
-
-  // Combine the pair's partial sums through LDS (the loop ended with a barrier, so the tiles are
-  // dead): wave (kw, 0) hands over dV and finishes dK, wave (kw, 1) hands over dK and finishes
-  // dV. Slot of wave w: ACC_BYTES at w * ACC_BYTES, register 4r..4r+3 of lane l at 16(64r + l).
-  {
-    f32x16_t* give = hq == 0 ? dvacc : dkacc;
-    unsigned char* mine = smem + wave * ACC_BYTES;
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        *reinterpret_cast<f32x4_t*>(mine + 16 * (64 * (4 * cb + r) + lane)) =
-            f32x4_t{give[cb][4 * r], give[cb][4 * r + 1], give[cb][4 * r + 2], give[cb][4 * r + 3]};
-  }
-  __syncthreads();
-  f32x16_t* keep = hq == 0 ? dkacc : dvacc;
-  {
-    const unsigned char* other = smem + (wave ^ 4) * ACC_BYTES;
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const f32x4_t x = *reinterpret_cast<const f32x4_t*>(other + 16 * (64 * (4 * cb + r) + lane));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) keep[cb][4 * r + e] += x[e];
-      }
-  }
-
-  // dK = scale * dK_acc (wave kw, 0), dV = dV_acc (wave kw, 1), keys key_w0 .. +31. The
-  // other wave's slot, which only this wave reads, is the transpose scratch.
-  static_assert(store_scratch_bytes(CB) <= ACC_BYTES, "transpose scratch");
-  const float mul = hq == 0 ? scale : 1.f;
-  if (part == nullptr) {
-    store_rows_via_lds<CB, D>(smem + (wave ^ 4) * ACC_BYTES, keep, mul,
-                              (hq == 0 ? dk : dv) + head_off, key_w0, N, lane);
-  } else {
-    const size_t n_bhkv = (size_t)(bh_count / split);
-    float* dst = part + ((hq == 0 ? 0 : (size_t)split) + sj) * n_bhkv * N * D +
-                 (size_t)bhkv * N * D;
-    store_rows_f32<CB, D>(keep, mul, dst, key_w0, N, lane);
-  }
-}
 
 // ---------------------------------------------------------------------------------------
 // dK, dV at d = 256. The fused form above would need 256 accumulator registers per wave, so here
@@ -791,7 +469,8 @@ template <int D, int KP = 1, bool DROP = false>
 struct Kv16Shape {
   static constexpr int NW = 4, THREADS = 256, BQ = 32;
   static constexpr int BK = 64 * KP;                            // keys per workgroup
-  static constexpr int OCC = KP > 1 ? (D == 64 ? 3 : 2) : (D == 64 ? 4 : (D == 128 ? 3 : 2));
+  static constexpr int OCC =
+      KP > 1 ? (D == 64 ? 3 : 2) : (D == 64 ? 4 : (D == 128 ? (DROP ? 2 : 3) : 2));
   static constexpr int KS = D / 32;                             // k-steps of S and dP
   static constexpr int DB = D / 16;                             // 16-row blocks of dV^T, dK^T
   static constexpr int TILE = BQ * D * 2;
@@ -1458,26 +1137,6 @@ hipError_t launch_pre_t(const BwdArgs& a) {
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL, bool DROP>
-hipError_t launch_dkdv_t(const BwdArgs& a) {
-  const int n_kblocks = (a.N + kKvBK - 1) / kKvBK;
-  const long long grid = (long long)n_kblocks * a.B * a.Hkv * a.kv_split;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fa2_bwd_dkdv_kernel<D, CAUSAL, DROP>), dim3((unsigned)grid), dim3(kKvThreads), 0,
-                     a.stream, static_cast<const uint16_t*>(a.q),
-                     static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
-                     static_cast<const uint16_t*>(a.dout), a.lse2, a.delta,
-                     static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), a.N, n_kblocks,
-                     a.B * a.Hkv * a.kv_split,
-                     causal_window(a.B * a.Hkv * a.kv_split,
-                                   4ll * a.N * D * (a.H / a.Hkv) / a.kv_split, n_kblocks, 1,
-                                   window_budget(D)),
-                     a.H, a.H / a.Hkv, a.kv_bstride, a.scale_log2,
-                     a.scale, OperandSign{a.sgn_and, a.sgn_xor},
-                     DropParams{a.drop_k0, a.drop_k1, a.drop_thr, a.drop_scale},
-                     a.kv_split > 1 ? a.kv_part : nullptr, a.kv_split);
-  return hipGetLastError();
-}
 
 template <int D, bool CAUSAL, bool DROP>
 hipError_t launch_dq_t(const BwdArgs& a) {
@@ -1565,15 +1224,19 @@ hipError_t launch_bwd_dkdv_drop(const BwdArgs& a) {
                     : launch_dkdv16_t<128, false, 2, false>(a);
   } else {
     // dropout: the 16x16x32 kernel at d = 64 (dropout step at B8 H32 N2048 +8.7% causal against
-    // the 32-key kernel); at d = 128 and 256 its dropout variant spills (160 and ~450 bytes per
-    // lane: the keep words and -D on top of 250-253 VGPRs) and measured 8-18% and 55% slower,
-    // so the 32-key kernels stay there (their lane pairs share the keep bits of a key pair)
+    // a 32-key kernel) and, with one sub-block per wave (K and V fragments in registers, 201-202
+    // VGPRs at two waves per SIMD), at d = 128 (dropout step at B4 H16 N2048 +1.5% causal, +1.2%
+    // non-causal against that 32-key kernel, since removed); with two sub-blocks its dropout
+    // variant spills at d = 128 and 256 (160 and ~450 bytes per lane: the keep words and -D on top
+    // of 250-253 VGPRs), so d = 256 keeps the 32-key kernel below, whose lane pairs share the keep
+    // bits of a key pair
     if (a.d == 64)
       return a.causal ? launch_dkdv16_t<64, true, 2, true>(a)
                       : launch_dkdv16_t<64, false, 2, true>(a);
     if (a.d == 256)
       return a.causal ? launch_dkdv256_t<true, DROP>(a) : launch_dkdv256_t<false, DROP>(a);
-    return a.causal ? launch_dkdv_t<128, true, DROP>(a) : launch_dkdv_t<128, false, DROP>(a);
+    return a.causal ? launch_dkdv16_t<128, true, 1, true>(a)
+                    : launch_dkdv16_t<128, false, 1, true>(a);
   }
 }
 

@@ -43,7 +43,6 @@ ROOT = os.path.dirname(PKG_DIR)
 KERNEL_SOURCES = {
     "fa2_fwd_kernel": ["fa2_device.hpp", "fa2_fwd.hip"],
     "fa2_bwd_dkdv16_kernel": ["fa2_device.hpp", "fa2_bwd.hip"],
-    "fa2_bwd_dkdv_kernel": ["fa2_device.hpp", "fa2_bwd.hip"],
     "fa2_bwd_dq_kernel": ["fa2_device.hpp", "fa2_bwd.hip"],
     "fa2_bwd_pre_kernel": ["fa2_device.hpp", "fa2_bwd.hip"],
 }
