@@ -32,6 +32,11 @@ fused kernels follow):
     dS = P * (dP - D)                        (row-softmax Jacobian applied to dP)
     dQ = scale * dS K,  dK = scale * dS^T Q
 
+A backward pass that takes O as an input (the fused one does; so does this function when
+given `o`) forms D from that O. At the exact O it is the gradient above; at an O rounded to
+the output format, D and so dS, dQ and dK move by the rounding's dot product with dO, which
+in rows of a few keys is not small against the gradient itself.
+
 Precision: float64 throughout; inputs are the exact bf16 values widened to float64.
 Query rows are processed in chunks: row i of the result depends only on q_i and the whole
 of K and V, so chunking changes nothing but memory use (pinned by a test).
@@ -111,13 +116,17 @@ def attention_forward(q, k, v, causal: bool = False, scale=None, rows=None,
     return o, lse
 
 
-def attention_backward(q, k, v, dout, causal: bool = False, scale=None, row_chunk: int = 512):
+def attention_backward(q, k, v, dout, causal: bool = False, scale=None, row_chunk: int = 512,
+                       o=None):
     """Exact gradients (dQ, dK, dV) of O = attention(Q, K, V) against the cotangent dO.
 
-    O and P are recomputed here in float64 from the definition; nothing from a GPU run is
-    used. Returns three float64 arrays of shape [B, H, N, d].
+    O and P are recomputed here in float64 from the definition. o: optional [B, H, N, d], the
+    output handed to a backward pass that takes O as an input; D_i is then formed from it
+    (with o = the exact O this is the exact gradient, as with o = None). Returns three
+    float64 arrays of shape [B, H, N, d].
     """
     q, k, v, dout = _as64(q), _as64(k), _as64(v), _as64(dout)
+    o_in = None if o is None else _as64(o)
     B, H, N, d = q.shape
     scale = resolve_scale(d, scale)
     dq = np.empty_like(q)
@@ -132,6 +141,8 @@ def attention_backward(q, k, v, dout, causal: bool = False, scale=None, row_chun
                 do_rows = dout[b, h, ri]
                 dv[b, h] += p.T @ do_rows
                 dp = do_rows @ v[b, h].T
+                if o_in is not None:
+                    o_rows = o_in[b, h, ri]
                 dvec = np.sum(do_rows * o_rows, axis=1, keepdims=True)
                 ds = p * (dp - dvec)
                 dq[b, h, ri] = scale * (ds @ k[b, h])

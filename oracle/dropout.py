@@ -136,9 +136,12 @@ def attention_forward_dropout(q, k, v, causal: bool = False, scale=None, p: floa
 
 def attention_backward_dropout(q, k, v, dout, causal: bool = False, scale=None, p: float = 0.0,
                                seed: int = 0, offset: int = 0, row_chunk: int = 512,
-                               bh_index=None):
-    """(dQ, dK, dV) of attention_forward_dropout against the cotangent dO."""
+                               bh_index=None, o=None):
+    """(dQ, dK, dV) of attention_forward_dropout against the cotangent dO. o: optional
+    [B, H, N, d], the output handed to a backward pass that takes O as an input; D_i is then
+    formed from it (None: the exact dropped O, giving the exact gradient)."""
     q, k, v, dout = _as64(q), _as64(k), _as64(v), _as64(dout)
+    o_in = None if o is None else _as64(o)
     B, H, N, d = q.shape
     scale = resolve_scale(d, scale)
     s_keep = keep_scale(p)
@@ -157,6 +160,8 @@ def attention_backward_dropout(q, k, v, dout, causal: bool = False, scale=None, 
                 do_rows = dout[b, h, ri]
                 dv[b, h] += pd.T @ do_rows
                 dp = zs * (do_rows @ v[b, h].T)
+                if o_in is not None:
+                    o_rows = o_in[b, h, ri]
                 dvec = np.sum(do_rows * o_rows, axis=1, keepdims=True)
                 ds = pr * (dp - dvec)
                 dq[b, h, ri] = scale * (ds @ k[b, h])

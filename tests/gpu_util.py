@@ -66,11 +66,16 @@ def assert_fwd_within_rounding_bound(o_gpu, lse_gpu, o_ref, o_abs_ref, lse_ref, 
     assert el <= LSE_MAX, info
 
 
-def assert_grad_close(got: np.ndarray, want: np.ndarray, what: str, bound: float = GRAD_REL):
+def assert_grad_close(got: np.ndarray, want: np.ndarray, what: str, bound: float = GRAD_REL,
+                      floor: float = 0.0):
+    """max|got - want| <= bound * max|want| + floor (floor: an absolute rounding bound for
+    gradients whose exact value can cancel to zero)."""
     assert np.isfinite(got).all(), f"{what}: non-finite gradient"
-    rel = np.abs(got - want).max() / max(np.abs(want).max(), 1e-30)
-    print(f"{what}: max|dg|/max|g| = {rel:.3e}", flush=True)
-    assert rel <= bound, f"{what}: relative error {rel:.3e} > {bound}"
+    err, top = np.abs(got - want).max(), np.abs(want).max()
+    rel = err / max(top, 1e-30)
+    print(f"{what}: max|dg|/max|g| = {rel:.3e} (max|dg| {err:.3e}, floor {floor:.3e})", flush=True)
+    assert err <= bound * top + floor, \
+        f"{what}: max|dg| {err:.3e} > {bound} * {top:.3e} + {floor:.3e} (relative {rel:.3e})"
 
 
 def compare_forward_all_heads(bq, bk, bv, o_bits, lse_gpu, causal, scale, what="",

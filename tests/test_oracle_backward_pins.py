@@ -106,3 +106,47 @@ def test_gradient_invariants(causal):
     kk = np.broadcast_to(k[:, :, :1], k.shape).copy()
     dq2, _, _ = attention_backward(q, kk, v, do, causal=causal)
     np.testing.assert_allclose(dq2, 0.0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_given_output_one_key_closed_form(causal):
+    # one key: P = 1 and the exact O is v, so dS = dO.v - dO.o' = -dO.(o' - v); the gradient
+    # at o' = v is zero, and a perturbed o' moves dQ by -scale (dO.delta) k, dK by the same
+    # with q, and leaves dV = dO
+    shape = (2, 3, 1, 16)
+    q, k, v, do = (_rand(shape, s) for s in (241, 242, 243, 244))
+    delta = 1e-3 * _rand(shape, 245)
+    scale = 0.37
+    dq0, dk0, dv0 = attention_backward(q, k, v, do, causal=causal, scale=scale, o=v)
+    # (zero up to float64 summation order: dO.v is taken once as a product, once as a sum)
+    assert np.abs(dq0).max() <= 1e-14 and np.abs(dk0).max() <= 1e-14
+    dq, dk, dv = attention_backward(q, k, v, do, causal=causal, scale=scale, o=v + delta)
+    proj = np.sum(do * delta, axis=-1, keepdims=True)
+    np.testing.assert_allclose(dq, -scale * proj * k, rtol=1e-9, atol=1e-14)
+    np.testing.assert_allclose(dk, -scale * proj * q, rtol=1e-9, atol=1e-14)
+    np.testing.assert_allclose(dv, do, rtol=0, atol=0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_given_output_shift_through_forward(causal):
+    # D_i moves by e_i = dO_i.(o'_i - O_i); dS_ij moves by -P_ij e_i, so dQ_i moves by
+    # -scale e_i sum_j P_ij k_j, which is row i of attention(Q, K, K), and dK_j by
+    # -scale sum_i P_ij e_i q_i; dV does not move
+    from oracle.attention import attention_probs
+    shape = (1, 2, 23, 8)
+    q, k, v, do = (_rand(shape, s) for s in (251, 252, 253, 254))
+    o, _ = attention_forward(q, k, v, causal=causal)
+    o2 = o + 0.05 * _rand(shape, 255)
+    g0 = attention_backward(q, k, v, do, causal=causal)
+    g1 = attention_backward(q, k, v, do, causal=causal, o=o)
+    for a, b in zip(g0, g1):
+        np.testing.assert_allclose(b, a, rtol=0, atol=1e-13)
+    dq, dk, dv = attention_backward(q, k, v, do, causal=causal, o=o2)
+    scale = 1.0 / math.sqrt(shape[-1])
+    e = np.sum(do * (o2 - o), axis=-1, keepdims=True)
+    pk, _ = attention_forward(q, k, k, causal=causal)
+    p = attention_probs(q, k, causal=causal)
+    np.testing.assert_allclose(dq - g0[0], -scale * e * pk, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk - g0[1], -scale * np.swapaxes(p, -1, -2) @ (e * q), rtol=0,
+                               atol=1e-12)
+    np.testing.assert_allclose(dv, g0[2], rtol=0, atol=0)

@@ -168,3 +168,28 @@ def test_sampled_heads_match_the_whole_batch():
         g1 = attention_backward_dropout(sl(q), sl(k), sl(v), sl(do), bh_index=ids, **kw)
         for a_, b_ in zip(g1, g):
             np.testing.assert_array_equal(a_[0, 0], b_[b, h])
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_given_output_shift_uses_undropped_p(causal):
+    # with dropout dS = P * (Z s dP - D) and P the undropped softmax, so a given O' moves dQ
+    # and dK exactly as without dropout: by -scale e_i (P K)_i and -scale P^T (e * Q), with
+    # e_i = dO_i.(O'_i - O_i) and O the dropped output; dV does not move
+    shape = (2, 2, 19, 8)
+    q, k, v, do = (_rand(shape, s) for s in (261, 262, 263, 264))
+    kw = dict(causal=causal, p=0.3, seed=11, offset=4)
+    o, _ = attention_forward_dropout(q, k, v, **kw)
+    o2 = o + 0.05 * _rand(shape, 265)
+    g0 = attention_backward_dropout(q, k, v, do, **kw)
+    g1 = attention_backward_dropout(q, k, v, do, o=o, **kw)
+    for a, b in zip(g0, g1):
+        np.testing.assert_allclose(b, a, rtol=0, atol=1e-13)
+    dq, dk, dv = attention_backward_dropout(q, k, v, do, o=o2, **kw)
+    scale = 1.0 / math.sqrt(shape[-1])
+    e = np.sum(do * (o2 - o), axis=-1, keepdims=True)
+    pk, _ = attention_forward(q, k, k, causal=causal)
+    p = attention_probs(q, k, causal=causal)
+    np.testing.assert_allclose(dq - g0[0], -scale * e * pk, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dk - g0[1], -scale * np.swapaxes(p, -1, -2) @ (e * q), rtol=0,
+                               atol=1e-12)
+    np.testing.assert_allclose(dv, g0[2], rtol=0, atol=0)
