@@ -17,11 +17,11 @@
 //                        dO and O rows it loads and stores -D and LSE*log2(e) of its queries
 //                        in the workspace; then it recomputes S^T and dP^T per key tile and
 //                        accumulates dQ^T = K^T dS^T.
-//   fa2_bwd_dkdv16_kernel grid over (key block, head, batch), 128 keys (64 at d = 256): 32-query
-//                        tiles of Q, dO, LSE*log2(e) and -D stream through LDS; each wave
-//                        forms S and dP of its 16 or 32 keys with 16x16x32 MFMAs (lane = key)
-//                        and accumulates its keys' dK, dV in registers. With dropout at d = 256
-//                        the 32-key kernel fa2_bwd_dkdv256_kernel.
+//   fa2_bwd_dkdv16_kernel grid over (key block, head, batch), 128 keys (64 at d = 256, and with
+//                        dropout at d = 128): 32-query tiles of Q, dO, LSE*log2(e) and -D
+//                        stream through LDS; each wave forms S and dP of its 16 or 32 keys
+//                        with 16x16x32 MFMAs (lane = key) and accumulates its keys' dK, dV in
+//                        registers.
 //   fa2_bwd_pre_kernel   D and LSE*log2(e) alone (HBM-bound), for callers that want dK/dV
 //                        without dQ.
 // dK/dV and dQ each recompute S and dP; dQ's two recompute GEMMs are the price of avoiding
@@ -172,295 +172,20 @@ __device__ __forceinline__ void store_row_key(unsigned char* rk, const DropParam
   reinterpret_cast<uint32_t*>(rk)[lane] = pcg_hash(a ^ (uint32_t)(row0 + lane));
 }
 
-struct DropLanes {
-  uint32_t pair;          // (my_key / 2) * kDropKeyMul
-  int own;                // byte offset of the 4 queries this lane hashes: 16 * (lane & 1)
-  uint32_t sel_lo, sel_hi;  // v_perm selectors: rows e = 0..3 and e = 4..7
-  __device__ __forceinline__ DropLanes(int lane, int my_key) {
-    const bool odd = lane & 1;  // my_key = 32-aligned base + lane % 32: same parity
-    pair = (uint32_t)(my_key >> 1) * kDropKeyMul;
-    own = odd ? 16 : 0;
-    // perm(x, w, sel) reads bytes 0-3 from w (this lane's word), 4-7 from x (the neighbour's);
-    // the key's 16 bits go to the top, zeros below. Even lane: rows 0-3 are its own words (low
-    // half), rows 4-7 its neighbour's (low half); odd lane: rows 0-3 the neighbour's (high
-    // half), rows 4-7 its own (high half).
-    sel_lo = odd ? 0x07060C0Cu : 0x01000C0Cu;
-    sel_hi = odd ? 0x03020C0Cu : 0x05040C0Cu;
-  }
-  // dw[hf][e]: the key's 16 bits (at the top of the word) for the query of register 8hf + e,
-  // i.e. the query at byte 4 * (16hf + e) of the row keys `rk` (the lane's query base applied).
-  __device__ __forceinline__ void words(const unsigned char* rk, uint32_t (&dw)[2][8]) const {
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const u32x4_t r = *reinterpret_cast<const u32x4_t*>(rk + 16 * hf * 4 + own);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t w = pcg_hash(r[k] ^ pair);
-        const uint32_t x = swap_adjacent_lanes(w);
-        dw[hf][k] = __builtin_amdgcn_perm(x, w, sel_lo);
-        dw[hf][4 + k] = __builtin_amdgcn_perm(x, w, sel_hi);
-      }
-    }
-  }
-};
-
-// ---------------------------------------------------------------------------------------
-// dK, dV at d = 256. The fused form above would need 256 accumulator registers per wave, so here
-// a wave accumulates one of them: workgroup = 4 waves over 64 keys, wave w serves the 32 keys
-// 32(w%2) .. +31; waves 0-1 accumulate dV (S, P, dV^T += dO^T P) and waves 2-3 dK (S, dP, dS,
-// dK^T += Q^T dS), 128 accumulator registers each (S is formed by both waves of a key group:
-// 1.25x the MFMAs of the fused form). The block's K and V rows stay in LDS (64 KiB); 32-query
-// tiles of Q, dO, LSE*log2(e) and D stream through a 2-stage ring at the bottom of LDS.
-constexpr int kKv256BK = 64;
-constexpr int kKv256BQ = 32;
-
-template <bool CAUSAL, bool DROP>
-__global__ __launch_bounds__(kThreads) void fa2_bwd_dkdv256_kernel(
-    const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const uint16_t* __restrict__ dout,
-    const float* __restrict__ lse2, const float* __restrict__ delta, uint16_t* __restrict__ dk,
-    uint16_t* __restrict__ dv, int N, int n_kblocks, int bh_count, int window, int n_qheads,
-    int group, long long kv_bstride, float scale_log2, float scale, OperandSign ksign, DropParams drop,
-    float* __restrict__ part, int split) {
-  constexpr int D = 256, KK = D / 16, CB = D / 32, DCH = D / 8;
-  constexpr int TILE = kKv256BQ * D * 2;          // 16 KiB
-  constexpr int KV_BYTES = kKv256BK * D * 2;      // 32 KiB
-  constexpr int STAGE = 2 * TILE;                 // Q, dO
-  constexpr int STATS0 = 2 * STAGE;               // per stage: LSE*log2(e), then D (128 B each)
-  constexpr int STATS_STAGE = (DROP ? 3 : 2) * kKv256BQ * 4;  // + dropout row keys
-  constexpr int KV0 = STATS0 + 2 * STATS_STAGE;
-  constexpr int SMEM = KV0 + 2 * KV_BYTES;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[SMEM];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int kw = wave & 1;      // key group
-  const bool dk_wave = wave >= 2;
-  const int l32 = lane & 31;
-  const int g = lane >> 5;
-
-  const TileCoord tc = schedule_tile<CAUSAL ? Order::kLongAscending : Order::kHeadMajor>(
-      blockIdx.x, n_kblocks, bh_count, window);
-  // tc.bh = (batch * Hkv + K/V head) * split + part, as in the d <= 128 kernel
-  const int sj = tc.bh % split;
-  const int bhkv = tc.bh / split;
-  const int n_kvheads = n_qheads / group;
-  const int b_idx = bhkv / n_kvheads;
-  const int kvh = bhkv - b_idx * n_kvheads;
-  const int qh0 = b_idx * n_qheads + kvh * group;
-  const size_t head_off =  // K, V, dK, dV
-      (size_t)b_idx * (size_t)kv_bstride + (size_t)kvh * (size_t)N * D;
-  const uint32_t head_bytes = (uint32_t)N * D * 2;
-  const __amdgpu_buffer_rsrc_t rk = make_rsrc(k + head_off, head_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_rsrc(v + head_off, head_bytes);
-
-  const int key_b0 = tc.qb * kKv256BK;
-  const int key_w0 = key_b0 + kw * 32;
-  const int my_key = key_w0 + l32;
-  const DropLanes dl(lane, my_key);
-
-  // resident K and V rows of the block (64 rows each, 2 rows per 1 KiB block)
-  {
-    constexpr int LOADS = KV_BYTES / (kThreads * 16);
-    constexpr int RPB = 64 / DCH;
-#pragma unroll
-    for (int r = 0; r < LOADS; ++r) {
-      const int blk = 4 * r + wave;
-      const int row = blk * RPB + lane / DCH;
-      const uint32_t off = (uint32_t)(row * D * 2 + ((lane % DCH) ^ swz<D>(row)) * 16);
-      buffer_load16_to_lds(rk, smem + KV0 + blk * 1024, off, (uint32_t)key_b0 * D * 2);
-      buffer_load16_to_lds(rv, smem + KV0 + KV_BYTES + blk * 1024, off,
-                           (uint32_t)key_b0 * D * 2);
-    }
-  }
-  // this wave's K/V fragment: row 32kw + l32, logical chunk 2kk + g (kk >= 8: +256 bytes)
-  const int kvrow = kw * 32 + l32;
-  int kvbase[8];
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk)
-    kvbase[kk] = KV0 + kvrow * D * 2 + ((2 * kk + g) ^ swz<D>(kvrow)) * 16;
-  auto kv_off = [&](int kk) { return kvbase[kk % 8] + (kk / 8) * 256; };
-  // LSE*log2(e) / D of this lane's queries 16hf + 8g + (0..7) within a stage
-  const int statbase = STATS0 + 8 * g * 4;
-
-  const int n_qt = (N + kKv256BQ - 1) / kKv256BQ;
-  const int qt_begin = CAUSAL ? key_b0 / kKv256BQ : 0;
-  // step T = 0 .. group*nt - 1 walks query tile qt_begin + T % nt of query head qh0 + T / nt;
-  // this part runs T = t_begin + t for t = 0 .. n_steps - 1
-  const int nt = n_qt - qt_begin;
-  const long long n_all = (long long)group * nt;
-  const int t_begin = (int)(n_all * sj / split);
-  const int n_steps = (int)(n_all * (sj + 1) / split) - t_begin;
-  const TileLoader<D, kThreads, kKv256BQ> ld(wave, lane);
-  const TileReads<D> rd_off(lane);
-
-  StepPos ldpos(t_begin, nt, qt_begin);  // the next tile to load (loads go in step order)
-  // buffer descriptors of the query head being loaded, rebuilt when the walk changes head
-  int ld_head = -1;
-  __amdgpu_buffer_rsrc_t rq, rdo, rl, rd;
-  auto load_stage = [&](int t, int stage) {
-    (void)t;
-    const int gi = ldpos.gi;
-    const int it = ldpos.it;
-    ldpos.next();
-    if (gi != ld_head) {
-      ld_head = gi;
-      const size_t qoff = (size_t)(qh0 + gi) * (size_t)N * D;
-      rq = make_rsrc(q + qoff, head_bytes);
-      rdo = make_rsrc(dout + qoff, head_bytes);
-      rl = make_rsrc(lse2 + (size_t)(qh0 + gi) * N, (uint32_t)N * 4);
-      rd = make_rsrc(delta + (size_t)(qh0 + gi) * N, (uint32_t)N * 4);
-    }
-    unsigned char* st = smem + stage * STAGE;
-    const uint32_t soff = (uint32_t)it * kKv256BQ * D * 2;
-    ld.load(rq, st, soff);
-    ld.load(rdo, st + TILE, soff);
-    // LSE*log2(e) and D of the tile's 32 queries (128 bytes each): 8 lanes of waves 0 and 1
-    unsigned char* sst = smem + STATS0 + stage * STATS_STAGE;
-    if (wave == 0) {
-      if (lane < 8)
-        buffer_load16_to_lds(rl, sst, (uint32_t)lane * 16, (uint32_t)it * kKv256BQ * 4);
-    } else if (wave == 1) {
-      if (lane < 8)
-        buffer_load16_to_lds(rd, sst + kKv256BQ * 4, (uint32_t)lane * 16,
-                             (uint32_t)it * kKv256BQ * 4);
-    } else if (DROP && wave == 2) {
-      if (lane < kKv256BQ) store_row_key(sst + 2 * kKv256BQ * 4, drop, qh0 + gi, it * kKv256BQ, lane);
-    }
-  };
-
-  f32x16_t acc[CB];  // dV^T (waves 0-1) or dK^T (waves 2-3) of the wave's 32 keys
-#pragma unroll
-  for (int cb = 0; cb < CB; ++cb) acc[cb] = f32x16_t{};
-
-  if (n_steps > 0) load_stage(0, 0);
-  wait_vmem();
-  __syncthreads();
-  if (ksign.and_mask != ~0u || ksign.xor_mask != 0u) {
-    // a scale <= 0: its sign goes into the resident K rows, once (see OperandSign)
-    for (int i = tid * 16; i < KV_BYTES; i += kThreads * 16)
-      *reinterpret_cast<u32x4_t*>(smem + KV0 + i) =
-          apply_sign(*reinterpret_cast<const u32x4_t*>(smem + KV0 + i), ksign);
-    __syncthreads();
-  }
-
-  StepPos cur(t_begin, nt, qt_begin);  // the tile of the current step
-  auto step = [&](auto stage_c, int t) {
-    constexpr int stage = decltype(stage_c)::value;
-    FA2_STAGE_SYNC();
-    if (t + 1 < n_steps) load_stage(t + 1, stage ^ 1);
-    FA2_STAGE_SYNC();
-    const int it = cur.it;
-    cur.next();
-    const int q0 = it * kKv256BQ;
-    // every query of the tile precedes every key of the wave: fully masked
-    const bool skip = CAUSAL && (q0 + kKv256BQ - 1 < key_w0);
-    if (!skip) {
-      const unsigned char* tq = smem + stage * STAGE;
-      const unsigned char* tdo = tq + TILE;
-      const unsigned char* ts = smem + statbase + stage * STATS_STAGE;
-      const bool masked = (q0 + kKv256BQ > N) || (CAUSAL && q0 < key_w0 + 31);
-      f32x16_t s, dp = f32x16_t{};
-      if (masked) mask_queries<CAUSAL>(s, q0 + 8 * g, my_key, N, q0 + 32 > N);
-      else {
-        s = f32x16_t{};
-      }
-      // S = Q K^T (both roles) and dP = dO V^T (dK waves), lane = key, registers = queries
-      if (dk_wave) {
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(smem + kv_off(kk));
-          const u32x4_t vf = *reinterpret_cast<const u32x4_t*>(smem + kv_off(kk) + KV_BYTES);
-          const u32x4_t aq = *reinterpret_cast<const u32x4_t*>(tq + rd_off.row_off(0, kk));
-          const u32x4_t ad = *reinterpret_cast<const u32x4_t*>(tdo + rd_off.row_off(0, kk));
-          s = mfma32(aq, kf, s);
-          dp = mfma32(ad, vf, dp);
-        }
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const u32x4_t kf = *reinterpret_cast<const u32x4_t*>(smem + kv_off(kk));
-          const u32x4_t aq = *reinterpret_cast<const u32x4_t*>(tq + rd_off.row_off(0, kk));
-          s = mfma32(aq, kf, s);
-        }
-      }
-      // P = exp2(s*c - LSE*log2e); dK waves: dS = P * (dP - D). Register i is query
-      // q0 + 16(i/8) + 8g + i%8.
-      uint32_t bk[8];
-      uint32_t dw[2][8];  // dropout: the 16 bits deciding (query of register 8hf + e, my_key)
-      if constexpr (DROP) dl.words(ts + 2 * kKv256BQ * 4, dw);
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const unsigned char* sl = ts + 16 * hf * 4;
-        const f32x4_t l0 = *reinterpret_cast<const f32x4_t*>(sl);
-        const f32x4_t l1 = *reinterpret_cast<const f32x4_t*>(sl + 16);
-        const f32x4_t d0 = *reinterpret_cast<const f32x4_t*>(sl + kKv256BQ * 4);
-        const f32x4_t d1 = *reinterpret_cast<const f32x4_t*>(sl + kKv256BQ * 4 + 16);
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float lv = e < 4 ? l0[e] : l1[e - 4];
-          const float neg_d = e < 4 ? d0[e] : d1[e - 4];  // -D
-          const float p = fast_exp2(__builtin_fmaf(s[8 * hf + e], scale_log2, -lv));
-          if constexpr (DROP) {
-            const float zs = dw[hf][e] >= drop.thr ? drop.scale : 0.f;
-            x[e] = dk_wave ? p * __builtin_fmaf(dp[8 * hf + e], zs, neg_d) : p * zs;
-          } else {
-            x[e] = dk_wave ? p * (dp[8 * hf + e] + neg_d) : p;
-          }
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) bk[4 * hf + e] = pack_bf16(x[2 * e], x[2 * e + 1]);
-      }
-      // dV^T += dO^T P or dK^T += Q^T dS over the tile's 32 queries (k-steps hf = 0, 1)
-      const unsigned char* ta = dk_wave ? tq : tdo;
-      __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const u32x4_t b = {bk[4 * hf + 0], bk[4 * hf + 1], bk[4 * hf + 2], bk[4 * hf + 3]};
-#pragma unroll
-        for (int cb = 0; cb < CB; ++cb) {
-          const u32x4_t a = tr_operand(ta, rd_off.tr_off(cb, hf, 0), rd_off.tr_off(cb, hf, 1));
-          acc[cb] = mfma32(a, b, acc[cb]);
-        }
-      }
-      __builtin_amdgcn_s_setprio(0);
-    }
-    FA2_STAGE_SYNC();
-    wait_vmem();
-    __syncthreads();
-  };
-  for (int t = 0; t < n_steps; t += 2) {
-    step(std::integral_constant<int, 0>{}, t);
-    if (t + 1 < n_steps) step(std::integral_constant<int, 1>{}, t + 1);
-  }
-
-  // dK = scale * dK_acc, dV = dV_acc, keys key_w0 .. +31 (the loop ended with a barrier: the
-  // ring is free for the transpose)
-  if (part == nullptr) {
-    store_rows_via_lds<CB, D>(smem + wave * store_scratch_bytes(CB), acc, dk_wave ? scale : 1.f,
-                              (dk_wave ? dk : dv) + head_off, key_w0, N, lane);
-  } else {
-    const size_t n_bhkv = (size_t)(bh_count / split);
-    float* dst = part + ((dk_wave ? 0 : (size_t)split) + sj) * n_bhkv * N * D +
-                 (size_t)bhkv * N * D;
-    store_rows_f32<CB, D>(acc, dk_wave ? scale : 1.f, dst, key_w0, N, lane);
-  }
-}
-
 // ---------------------------------------------------------------------------------------
 // dK, dV with 16-key MFMA blocks (v_mfma_f32_16x16x32_bf16). Workgroup = 4 waves over 64*KP
-// keys, one wave per SIMD, and several workgroups per CU (3 at d = 64, 2 at d = 128 and 256),
-// so each SIMD runs waves of independent workgroups. With KP = 1 (d = 256) a wave keeps its 16
+// keys, one wave per SIMD, and several workgroups per CU (3 at d = 64, 2 at d = 128 and 256;
+// with dropout 2 at d = 128 and 1 at d = 256, where the keep words and -D take the registers of a
+// second wave), so each SIMD runs waves of independent workgroups. With KP = 1 (d = 256, and
+// with dropout at d = 128) a wave keeps its 16
 // keys' K and V fragments in registers (loaded once, the scale's sign applied to K) and its
 // dK^T, dV^T accumulators (d x 16 keys); 32-query tiles of Q and dO with their LSE*log2(e) and -D stream
 // through a 2-stage LDS ring (swz16 layout). Per tile, S = Q K^T and dP = dO V^T come out as two
 // 16-query blocks with lane = key (query order: block b, register r of lane group g is query
 // 16b + 4g + r), so the packed P and dS are directly the B operands of dV^T += dO^T P and
 // dK^T += Q^T dS over the tile's 32 queries, whose A operands (dO^T, Q^T) come from transposing
-// reads of the same tiles. S is formed once per (key, query) pair and dK, dV share it, where the
-// 32-key d = 256 kernel forms it twice; the K/V operands come from registers instead of LDS.
+// reads of the same tiles. S is formed once per (key, query) pair and dK, dV share it (a split
+// into dK waves and dV waves would form it twice); the K/V operands come from registers.
 // KP = 2 (d = 64, 128): each wave takes two 16-key sub-blocks (32 keys) that share every Q and
 // dO operand read, which halves the LDS reads per MFMA of those operands; the 128 keys' K rows
 // then stay in LDS (read per step) and only V's fragments live in registers, and 3 (d = 64) or
@@ -470,7 +195,7 @@ struct Kv16Shape {
   static constexpr int NW = 4, THREADS = 256, BQ = 32;
   static constexpr int BK = 64 * KP;                            // keys per workgroup
   static constexpr int OCC =
-      KP > 1 ? (D == 64 ? 3 : 2) : (D == 64 ? 4 : (D == 128 ? (DROP ? 2 : 3) : 2));
+      KP > 1 ? (D == 64 ? 3 : 2) : (D == 64 ? 4 : (D == 128 ? (DROP ? 2 : 3) : (DROP ? 1 : 2)));
   static constexpr int KS = D / 32;                             // k-steps of S and dP
   static constexpr int DB = D / 16;                             // 16-row blocks of dV^T, dK^T
   static constexpr int TILE = BQ * D * 2;
@@ -548,7 +273,7 @@ fa2_bwd_dkdv16_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict
   // causal: key block 0 sees every query tile, so ascending order is longest first
   const TileCoord tc = schedule_tile<CAUSAL ? Order::kLongAscending : Order::kHeadMajor>(
       blockIdx.x, n_kblocks, bh_count, window);
-  // tc.bh = (batch * Hkv + K/V head) * split + part, as in the 32-key kernels
+  // tc.bh = (batch * Hkv + K/V head) * split + part
   const int sj = tc.bh % split;
   const int bhkv = tc.bh / split;
   const int n_kvheads = n_qheads / group;
@@ -1163,27 +888,6 @@ hipError_t launch_bwd_pre(const BwdArgs& a) {
   return a.d == 64 ? launch_pre_t<64>(a) : launch_pre_t<128>(a);
 }
 
-template <bool CAUSAL, bool DROP>
-hipError_t launch_dkdv256_t(const BwdArgs& a) {
-  const int n_kblocks = (a.N + kKv256BK - 1) / kKv256BK;
-  const long long grid = (long long)n_kblocks * a.B * a.Hkv * a.kv_split;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((fa2_bwd_dkdv256_kernel<CAUSAL, DROP>), dim3((unsigned)grid), dim3(kThreads), 0,
-                     a.stream, static_cast<const uint16_t*>(a.q),
-                     static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v),
-                     static_cast<const uint16_t*>(a.dout), a.lse2, a.delta,
-                     static_cast<uint16_t*>(a.dk), static_cast<uint16_t*>(a.dv), a.N, n_kblocks,
-                     a.B * a.Hkv * a.kv_split,
-                     causal_window(a.B * a.Hkv * a.kv_split,
-                                   4ll * a.N * 256 * (a.H / a.Hkv) / a.kv_split, n_kblocks, 1,
-                                   window_budget(256)),
-                     a.H, a.H / a.Hkv, a.kv_bstride, a.scale_log2,
-                     a.scale, OperandSign{a.sgn_and, a.sgn_xor},
-                     DropParams{a.drop_k0, a.drop_k1, a.drop_thr, a.drop_scale},
-                     a.kv_split > 1 ? a.kv_part : nullptr, a.kv_split);
-  return hipGetLastError();
-}
-
 template <int D, bool CAUSAL, int KP, bool DROP>
 hipError_t launch_dkdv16_t(const BwdArgs& a) {
   using S = Kv16Shape<D, KP, DROP>;
@@ -1228,13 +932,15 @@ hipError_t launch_bwd_dkdv_drop(const BwdArgs& a) {
     // VGPRs at two waves per SIMD), at d = 128 (dropout step at B4 H16 N2048 +1.5% causal, +1.2%
     // non-causal against that 32-key kernel, since removed); with two sub-blocks its dropout
     // variant spills at d = 128 and 256 (160 and ~450 bytes per lane: the keep words and -D on top
-    // of 250-253 VGPRs), so d = 256 keeps the 32-key kernel below, whose lane pairs share the keep
-    // bits of a key pair
+    // of 250-253 VGPRs). At d = 256 one sub-block per wave needs 370-372 VGPRs with dropout, so
+    // one workgroup per CU (dropout step at B2 H16 N4096 +19% causal, +20.6% non-causal against
+    // a 32-key kernel that split dK and dV over waves at two workgroups per CU, since removed)
     if (a.d == 64)
       return a.causal ? launch_dkdv16_t<64, true, 2, true>(a)
                       : launch_dkdv16_t<64, false, 2, true>(a);
     if (a.d == 256)
-      return a.causal ? launch_dkdv256_t<true, DROP>(a) : launch_dkdv256_t<false, DROP>(a);
+      return a.causal ? launch_dkdv16_t<256, true, 1, true>(a)
+                      : launch_dkdv16_t<256, false, 1, true>(a);
     return a.causal ? launch_dkdv16_t<128, true, 1, true>(a)
                     : launch_dkdv16_t<128, false, 1, true>(a);
   }

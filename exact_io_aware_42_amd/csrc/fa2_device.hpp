@@ -250,23 +250,6 @@ __device__ __forceinline__ void store_rows_via_lds(unsigned char* scratch, const
   }
 }
 
-// The same 32-row tile (layout as in store_rows_via_lds) times `mul` as fp32 into rows row0 ..
-// row0+31 of `out` (row stride LD floats; rows >= n_rows skipped), 16 bytes per lane.
-template <int NB, int LD>
-__device__ __forceinline__ void store_rows_f32(const f32x16_t* acc, float mul, float* out,
-                                               int row0, int n_rows, int lane) {
-  const int r = lane & 31, g = lane >> 5;
-  if (row0 + r >= n_rows) return;
-  float* row = out + (size_t)(row0 + r) * LD;
-#pragma unroll
-  for (int cb = 0; cb < NB; ++cb)
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-      *reinterpret_cast<f32x4_t*>(row + 32 * cb + 8 * t + 4 * g) =
-          f32x4_t{acc[cb][4 * t] * mul, acc[cb][4 * t + 1] * mul, acc[cb][4 * t + 2] * mul,
-                  acc[cb][4 * t + 3] * mul};
-}
-
 // Accumulator start values of a masked 32x32 score block: -inf for hidden entries, 0 otherwise.
 // Lane = query, registers = keys (the forward and dQ layout): register i holds key
 // base + 16(i/8) + 8g + i%8; mask_keys takes rel = (key of register 0) - key_lim, the lane's
@@ -276,26 +259,6 @@ __device__ __forceinline__ void mask_keys(f32x16_t& s, int rel) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) s[i] = rel > -(16 * (i / 8) + (i % 8)) ? -INFINITY : 0.f;
 }
-// Lane = key, registers = queries (the dK/dV layout): register i holds query
-// q_base + 16(i/8) + i%8 (q_base = the tile's first query + 8g). Hidden iff the query is past N
-// (only when the tile crosses N) or, causal, before the lane's key.
-template <bool CAUSAL>
-__device__ __forceinline__ void mask_queries(f32x16_t& s, int q_base, int my_key, int N,
-                                             bool tail) {
-  const int lo = q_base - my_key;  // query - key of register 0
-  const int hi = q_base - N;       // query - N of register 0
-  if (tail) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int c = 16 * (i / 8) + (i % 8);
-      s[i] = (hi >= -c || (CAUSAL && lo < -c)) ? -INFINITY : 0.f;
-    }
-  } else {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) s[i] = (CAUSAL && lo < -(16 * (i / 8) + (i % 8))) ? -INFINITY : 0.f;
-  }
-}
-
 // Workgroup id -> (block, batch*head) order. Workgroups are dealt to the 8 XCDs in turn
 // (id % 8), each XCD with its own L2; when the heads divide evenly, XCD x gets the heads
 // x, x+8, ... only.
