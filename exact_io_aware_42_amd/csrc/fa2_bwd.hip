@@ -12,11 +12,11 @@
 //   dV = P^T dO,  dK = scale dS^T Q,  dQ = scale dS K.
 //
 // Deterministic (no atomics); the backward runs two kernels, dQ first:
-//   fa2_bwd_dq_kernel    grid over (query block of 128, head, batch): the forward's layout
-//                        (lane = query). It first forms D_i = rowsum(dO_i * O_i) from the
-//                        dO and O rows it loads and stores -D and LSE*log2(e) of its queries
-//                        in the workspace; then it recomputes S^T and dP^T per key tile and
-//                        accumulates dQ^T = K^T dS^T.
+//   fa2_bwd_dq_kernel    grid over (query block, head, batch), 256 queries at d = 128 (128 at
+//                        d = 64 and 256): the forward's layout (lane = query). It first forms
+//                        D_i = rowsum(dO_i * O_i) from the dO and O rows it loads and stores -D
+//                        and LSE*log2(e) of its queries in the workspace; then it recomputes
+//                        S^T and dP^T per key tile and accumulates dQ^T = K^T dS^T.
 //   fa2_bwd_dkdv16_kernel grid over (key block, head, batch), 128 keys (64 at d = 256, and with
 //                        dropout at d = 128): 32-query tiles of Q, dO, LSE*log2(e) and -D
 //                        stream through LDS; each wave forms S and dP of its 16 or 32 keys

@@ -111,7 +111,7 @@ fa2_status fa2_bwd_dq(const void* q, const void* k, const void* v, const void* o
 
 /* fa2_bwd_dkdv: dk and dv [B,H,N,d] (bf16) from q, k, v, dout and a workspace filled by
  *   fa2_bwd_dq or fa2_bwd_preprocess (earlier on the same stream). Parallel over blocks of 128
- *   keys (64 at d = 256); recomputes P block by block. A scale <= 0 reaches this stage through
+ *   keys (64 at d = 256, and with dropout at d = 128); recomputes P block by block. A scale <= 0 reaches this stage through
  *   the resident K rows (negated, or zeroed for 0), dK = scale * dS^T Q as for any scale. */
 fa2_status fa2_bwd_dkdv(const void* q, const void* k, const void* v, const void* dout,
                         const void* workspace, size_t workspace_bytes, void* dk, void* dv,
