@@ -396,7 +396,7 @@ def measure_step(fa2, torch, dev, w, causal, with_bwd, steps, warmup, warm_ms=WA
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1 "
+        print(json.dumps({"error": "the benchmark runs on exactly one GPU; --gpus must be 1 "
                           "(the per-head work is independent, so more GPUs would shard "
                           "batch x heads without any exchange)"}))
         sys.exit(2)
