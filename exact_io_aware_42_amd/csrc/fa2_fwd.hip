@@ -258,7 +258,9 @@ __global__ __launch_bounds__(FwdShape<D>::THREADS, FA2_FWD_OCC) void fa2_fwd_ker
   // normaliser and the LSE stay those of the undropped p)
   auto probs = [&](const f32x16_t* s, uint32_t (*pk)[8], int j) {
     const float neg_m = -m_run;
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    // -0 is the identity of the fp32 add (-0 + x = x for every x), so the first add into each
+    // partial sum folds away; +0 is not (+0 + -0 = +0), and the compiler keeps those adds
+    float acc[4] = {-0.f, -0.f, -0.f, -0.f};
 #pragma unroll
     for (int kb = 0; kb < S::KB; ++kb)
 #pragma unroll
@@ -290,7 +292,7 @@ __global__ __launch_bounds__(FwdShape<D>::THREADS, FA2_FWD_OCC) void fa2_fwd_ker
   };
   // masked tiles: l_corr += sum of bf16(p) - sum of p (after the PV MFMAs, off their path)
   auto bf16_correction = [&](uint32_t (*pk)[8], float tile_sum) {
-    float b[2] = {0.f, 0.f};
+    float b[2] = {-0.f, -0.f};  // (-0: see probs)
 #pragma unroll
     for (int kb = 0; kb < S::KB; ++kb)
 #pragma unroll
