@@ -5,7 +5,8 @@ benchmark's CPU-baseline leg may import this package. The HIP library and its Py
 binding share no code with it and never call it.
 
 Modules:
-  attention   plain definition: forward (O, LSE), probabilities, analytic backward
+  attention   plain definition: forward (O, LSE), probabilities, analytic backward (whole,
+              or at sampled query rows and key rows)
   bruteforce  scalar loops for tiny shapes
   online      float64 model of the tiled online-softmax recurrence
   dropout     attention with dropout on P and its counter-based mask generator
@@ -14,7 +15,8 @@ Every function here is pinned by CPU tests to something other than itself (brute
 closed forms, invariants, finite differences, PyTorch's CPU scaled_dot_product_attention,
 hand-derived values under tests/golden/).
 """
-from .attention import attention_backward, attention_forward, attention_probs, resolve_scale
+from .attention import (attention_backward, attention_backward_sampled, attention_forward,
+                        attention_probs, resolve_scale)
 from .bruteforce import attention_bruteforce
 from .dropout import (attention_backward_dropout, attention_forward_dropout, keep_mask,
                       keep_scale, pcg_hash)
@@ -23,6 +25,7 @@ from .online import online_attention_forward
 __all__ = [
     "attention_forward",
     "attention_backward",
+    "attention_backward_sampled",
     "attention_probs",
     "resolve_scale",
     "attention_bruteforce",

@@ -47,7 +47,8 @@ import math
 
 import numpy as np
 
-__all__ = ["attention_forward", "attention_backward", "attention_probs", "resolve_scale"]
+__all__ = ["attention_forward", "attention_backward", "attention_backward_sampled",
+           "attention_probs", "resolve_scale"]
 
 
 def resolve_scale(d: int, scale) -> float:
@@ -147,4 +148,46 @@ def attention_backward(q, k, v, dout, causal: bool = False, scale=None, row_chun
                 ds = p * (dp - dvec)
                 dq[b, h, ri] = scale * (ds @ k[b, h])
                 dk[b, h] += scale * (ds.T @ q[b, h, ri])
+    return dq, dk, dv
+
+
+def attention_backward_sampled(q, k, v, dout, rows, keys, causal: bool = False, scale=None,
+                               row_chunk: int = 256):
+    """attention_backward restricted to some outputs, for problems too large for the whole
+    backward: dQ at the query rows `rows`, dK and dV at the key rows `keys`.
+
+    dQ_i depends on row i alone (its softmax over all keys). dK_j and dV_j sum over every query
+    row that sees key j; under the causal mask rows i < j have P_ij = 0 exactly, so only rows from
+    min(keys) on are visited. Each visited row's softmax is taken over all its keys, as in the
+    definition. Returns float64 [B, H, len(rows), d], [B, H, len(keys), d], [B, H, len(keys), d].
+    """
+    q, k, v, dout = _as64(q), _as64(k), _as64(v), _as64(dout)
+    B, H, N, d = q.shape
+    scale = resolve_scale(d, scale)
+    rows = np.asarray(rows, dtype=np.int64)
+    keys = np.asarray(keys, dtype=np.int64)
+    dq = np.empty((B, H, len(rows), d))
+    dk = np.zeros((B, H, len(keys), d))
+    dv = np.zeros((B, H, len(keys), d))
+    first = int(keys.min()) if causal and len(keys) else 0
+    for b in range(B):
+        for h in range(H):
+            for c0 in range(0, len(rows), row_chunk):
+                ri = rows[c0:c0 + row_chunk]
+                p, _ = _row_softmax(_masked_scores(q[b, h, ri], ri, k[b, h], causal, scale))
+                do_rows = dout[b, h, ri]
+                dvec = np.sum(do_rows * (p @ v[b, h]), axis=1, keepdims=True)
+                ds = p * (do_rows @ v[b, h].T - dvec)
+                dq[b, h, c0:c0 + len(ri)] = scale * (ds @ k[b, h])
+            if not len(keys):
+                continue
+            for c0 in range(first, N, row_chunk):
+                ri = np.arange(c0, min(N, c0 + row_chunk))
+                p, _ = _row_softmax(_masked_scores(q[b, h, ri], ri, k[b, h], causal, scale))
+                do_rows = dout[b, h, ri]
+                dvec = np.sum(do_rows * (p @ v[b, h]), axis=1, keepdims=True)
+                pk = p[:, keys]
+                dsk = pk * (do_rows @ v[b, h, keys].T - dvec)
+                dv[b, h] += pk.T @ do_rows
+                dk[b, h] += scale * (dsk.T @ q[b, h, ri])
     return dq, dk, dv

@@ -150,3 +150,20 @@ def test_given_output_shift_through_forward(causal):
     np.testing.assert_allclose(dk - g0[1], -scale * np.swapaxes(p, -1, -2) @ (e * q), rtol=0,
                                atol=1e-12)
     np.testing.assert_allclose(dv, g0[2], rtol=0, atol=0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_sampled_backward_is_the_whole_backward_at_those_rows(causal):
+    # the sampled form restricts the same definition: its dQ rows and dK, dV keys must be the
+    # whole backward's (which the finite-difference, autograd and hand-worked pins fix),
+    # including under the causal mask, where it visits only the rows from the first key on
+    from oracle import attention_backward_sampled
+    shape = (2, 2, 67, 16)
+    q, k, v, do = (_rand(shape, s) for s in (271, 272, 273, 274))
+    rows = [0, 1, 5, 33, 66]
+    keys = [3, 40, 41, 66]
+    dq, dk, dv = attention_backward(q, k, v, do, causal=causal)
+    sq, sk, sv = attention_backward_sampled(q, k, v, do, rows, keys, causal=causal, row_chunk=7)
+    np.testing.assert_allclose(sq, dq[:, :, rows], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(sk, dk[:, :, keys], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(sv, dv[:, :, keys], rtol=0, atol=1e-13)
