@@ -8,6 +8,7 @@ outputs the CPU oracle computes one by one.
     on see, so the oracle visits those rows alone.
   * N = 70001, d = 64, without the mask: O, LSE and dQ at sampled rows (dK and dV at any key
     would need every row's softmax: the whole O(N^2) backward).
+  * N = 70001, d = 256, causal: as the first case.
 
 Bounds as everywhere: max|dO| <= 1e-2, mean|dO| <= 1e-3, |dLSE| <= 1e-3 over the sampled rows,
 and max|dg| <= 2e-2 * max|g| over the sampled rows or keys.
@@ -23,7 +24,7 @@ from gpu_util import assert_fwd_close, assert_grad_close, bf16_to_f64, to_dev
 
 pytestmark = pytest.mark.gpu
 
-CASES = [(1, 1, 100003, 128, True), (1, 2, 70001, 64, False)]
+CASES = [(1, 1, 100003, 128, True), (1, 2, 70001, 64, False), (1, 1, 70001, 256, True)]
 
 
 @pytest.mark.parametrize("case", CASES, ids=[f"N{c[2]}-d{c[3]}-{'causal' if c[4] else 'full'}"
