@@ -203,21 +203,36 @@ def gpt_layer_step(torch, dev, steps=20, warmup=10):
             "attention_flop_share": round(fl["attention"] / total, 3)}
 
 
-def _timed_fwd_bwd(fa2, torch, dev, H, Hkv, steps, warmup, **kw):
-    """Mean wall time (ms) of fwd + bwd at B=4, N=2048, d=128, causal, with H query heads and
-    Hkv K/V heads; i.i.d. N(0,1) bf16 from a seeded torch generator. kw goes to fwd and bwd."""
+def _timed_fwd_bwd(fa2, torch, dev, H, Hkv, steps, warmup, warm_ms=WARM_MS, **kw):
+    """Mean time (ms) of fwd + bwd at B=4, N=2048, d=128, causal, with H query heads and Hkv K/V
+    heads; i.i.d. N(0,1) bf16 from a seeded torch generator. kw goes to fwd and bwd. As for the
+    main step: outputs and workspace given by the caller (the workspace sized for the split of
+    small problems), at least warm_ms of GPU time untimed, then `warmup` untimed steps."""
     B, N, d = 4, 2048, 128
     g = torch.Generator(device="cpu").manual_seed(11)
     mk = lambda h: torch.randn(B, h, N, d, generator=g).to(torch.bfloat16).to(dev)
     q, k, v, do = mk(H), mk(Hkv), mk(Hkv), mk(H)
+    o, dq = torch.empty_like(q), torch.empty_like(q)
+    dk, dv = torch.empty_like(k), torch.empty_like(v)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(1, fa2.bwd_workspace_bytes(B, H, N, d, Hkv)), dtype=torch.uint8,
+                     device=dev)
 
     def step():
-        o, lse = fa2.fwd(q, k, v, causal=True, **kw)
-        fa2.bwd(q, k, v, o, do, lse, causal=True, **kw)
+        fa2.fwd(q, k, v, causal=True, out=o, lse=lse, **kw)
+        fa2.bwd(q, k, v, o, do, lse, causal=True, dq=dq, dk=dk, dv=dv, workspace=ws, **kw)
 
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    spent = 0.0
+    while spent < warm_ms:
+        e0.record()
+        for _ in range(10):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        spent += e0.elapsed_time(e1)
     for _ in range(warmup):
         step()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     e0.record()
     for _ in range(steps):
