@@ -20,7 +20,8 @@ kernel's TFLOP/s on the forward-only workloads, `non_causal_step` the same fwd+b
 without the causal mask, `d256_steps` the fwd+bwd step at head dimension 256, `gpt_layer_step` a GPT-style attention layer (bf16 projections + attention,
 forward and backward through torch.autograd), `gqa_step` the fwd+bwd step with 16 query
 heads sharing 4 K/V heads, `dropout_step` the fwd+bwd step with dropout p = 0.1 on the
-attention probabilities and `graph_step` the fwd+bwd step captured in a HIP graph and replayed;
+attention probabilities, `graph_step` the fwd+bwd step captured in a HIP graph and replayed,
+and `gemm_yardstick` a library bf16 GEMM (8192^3, torch.matmul) on the same chip, for context;
 none of them is part of `value`.
 
 Prints ONE JSON line (rank 0).
@@ -259,6 +260,34 @@ def dropout_step(fa2, torch, dev, p=0.1, steps=20, warmup=20):
     r = _timed_fwd_bwd(fa2, torch, dev, 16, 16, steps, warmup, dropout_p=p, seed=1234,
                        offset=0)
     return {"shape": "B4 H16 N2048 d128 causal", "dropout_p": p, **r}
+
+
+def gemm_yardstick(torch, dev, n=8192, steps=20, warm_ms=WARM_MS):
+    """A library bf16 GEMM on the same chip, for context: C = A B with A, B [n, n] bf16 (fp32
+    accumulation) through torch.matmul (the ROCm BLAS libraries), after warm_ms of untimed GEMMs.
+    2 n^3 FLOP each. Not part of `value`."""
+    g = torch.Generator(device="cpu").manual_seed(17)
+    a = torch.randn(n, n, generator=g).to(torch.bfloat16).to(dev)
+    b = torch.randn(n, n, generator=g).to(torch.bfloat16).to(dev)
+    c = torch.empty(n, n, dtype=torch.bfloat16, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    spent = 0.0
+    while spent < warm_ms:
+        e0.record()
+        for _ in range(5):
+            torch.matmul(a, b, out=c)
+        e1.record()
+        torch.cuda.synchronize()
+        spent += e0.elapsed_time(e1)
+    e0.record()
+    for _ in range(steps):
+        torch.matmul(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    tflops = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    return {"shape": f"{n}x{n}x{n} bf16, torch.matmul", "ms": round(ms, 4),
+            "tflops": round(tflops, 1), "frac": round(tflops / PEAK_BF16_TFLOPS, 4)}
 
 
 def graph_step(fa2, torch, dev, steps=100, warmup=20, warm_ms=WARM_MS):
@@ -500,6 +529,7 @@ def main():
         out["gpt_layer_step"] = gpt_layer_step(torch, dev)
         out["gqa_step"] = gqa_step(fa2, torch, dev)
         out["dropout_step"] = dropout_step(fa2, torch, dev)
+        out["gemm_yardstick"] = gemm_yardstick(torch, dev)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, causal, with_bwd, args.cpu_seconds)
     print(json.dumps(out), flush=True)
