@@ -39,6 +39,9 @@ probability, so every output stays unbiased.
 Pinned by tests: p = 0 reduces to plain attention exactly; scalar-loop brute force; finite
 differences with the mask held fixed; keep rates and independence statistics of the mask;
 and that averaging O over many seeds approaches the undropped O (the 1/P(keep) scale).
+That h is bit for bit the published function is not pinned (no output values of it are at
+hand to compare against); the tests fix its statistics here and, on the GPU, that the kernels'
+mask equals this one bit for bit.
 """
 from __future__ import annotations
 
