@@ -9,6 +9,8 @@ outputs the CPU oracle computes one by one.
   * N = 70001, d = 64, without the mask: O, LSE and dQ at sampled rows (dK and dV at any key
     would need every row's softmax: the whole O(N^2) backward).
   * N = 70001, d = 256, causal: as the first case.
+  * N = 70001, d = 128, causal, dropout p = 0.2: O and LSE at sampled rows, whose keep bits hash
+    query and key-pair indices past 2^16 (O held to the rounding bound the dropout tests use).
 
 Bounds as everywhere: max|dO| <= 1e-2, mean|dO| <= 1e-3, |dLSE| <= 1e-3 over the sampled rows,
 and max|dg| <= 2e-2 * max|g| over the sampled rows or keys.
@@ -18,9 +20,10 @@ import pytest
 import torch
 
 from exact_io_aware_42_amd.inputs import bf16_bits_to_f64, default_scale, normal_bf16
-from oracle import attention_backward_sampled, attention_forward
+from oracle import attention_backward_sampled, attention_forward, attention_forward_dropout
 
-from gpu_util import assert_fwd_close, assert_grad_close, bf16_to_f64, to_dev
+from gpu_util import (assert_fwd_close, assert_fwd_within_rounding_bound, assert_grad_close,
+                      bf16_to_f64, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -61,3 +64,26 @@ def test_long_sequence_sampled(case):
         assert keys.min() > 65536
         assert_grad_close(bf16_to_f64(dk[:, :, keys]), gk, f"N={N} dk keys")
         assert_grad_close(bf16_to_f64(dv[:, :, keys]), gv, f"N={N} dv keys")
+
+
+def test_long_sequence_dropout_forward():
+    import exact_io_aware_42_amd as fa2
+    B, H, N, d = 1, 1, 70001, 128
+    p, seed, offset = float(np.float32(0.2)), 9400, 7
+    print(f"case B={B} H={H} N={N} d={d} causal=True p={p} seed={seed}", flush=True)
+    bq, bk, bv = (normal_bf16((B, H, N, d), seed + t) for t in range(3))
+    q, k, v = (to_dev(x) for x in (bq, bk, bv))
+    scale = default_scale(d)
+    o, lse = fa2.fwd(q, k, v, causal=True, scale=scale, dropout_p=p, seed=seed, offset=offset)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([[0, 1, 65535, 65536, 65537, N - 2, N - 1],
+                                     rng.integers(0, N, 40)]))
+    q64, k64, v64 = (bf16_bits_to_f64(x) for x in (bq, bk, bv))
+    kw = dict(causal=True, scale=scale, p=p, seed=seed, offset=offset, rows=rows)
+    o_ref, lse_ref = attention_forward_dropout(q64, k64, v64, **kw)
+    o_abs, _ = attention_forward_dropout(q64, k64, np.abs(v64), **kw)
+    assert_fwd_within_rounding_bound(bf16_to_f64(o[:, :, rows]),
+                                     lse[:, :, rows].cpu().double().numpy(), o_ref, o_abs, lse_ref,
+                                     f"N={N} dropout sampled rows")
+
