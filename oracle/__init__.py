@@ -18,8 +18,8 @@ hand-derived values under tests/golden/).
 from .attention import (attention_backward, attention_backward_sampled, attention_forward,
                         attention_probs, resolve_scale)
 from .bruteforce import attention_bruteforce
-from .dropout import (attention_backward_dropout, attention_forward_dropout, keep_mask,
-                      keep_scale, pcg_hash)
+from .dropout import (attention_backward_dropout, attention_backward_dropout_sampled,
+                      attention_forward_dropout, keep_mask, keep_scale, pcg_hash)
 from .online import online_attention_forward
 
 __all__ = [
@@ -31,6 +31,7 @@ __all__ = [
     "attention_bruteforce",
     "online_attention_forward",
     "attention_forward_dropout",
+    "attention_backward_dropout_sampled",
     "attention_backward_dropout",
     "keep_mask",
     "keep_scale",

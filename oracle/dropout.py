@@ -50,7 +50,8 @@ import numpy as np
 from .attention import _as64, _masked_scores, _row_softmax, resolve_scale
 
 __all__ = ["pcg_hash", "dropout_threshold", "keep_scale", "keep_mask",
-           "attention_forward_dropout", "attention_backward_dropout"]
+           "attention_forward_dropout", "attention_backward_dropout",
+           "attention_backward_dropout_sampled"]
 
 _M32 = np.uint64(0xFFFFFFFF)
 
@@ -170,3 +171,51 @@ def attention_backward_dropout(q, k, v, dout, causal: bool = False, scale=None, 
                 dq[b, h, ri] = scale * (ds @ k[b, h])
                 dk[b, h] += scale * (ds.T @ q[b, h, ri])
     return dq, dk, dv
+
+
+def attention_backward_dropout_sampled(q, k, v, dout, rows, keys, causal: bool = False,
+                                       scale=None, p: float = 0.0, seed: int = 0, offset: int = 0,
+                                       row_chunk: int = 256, bh_index=None):
+    """attention_backward_dropout restricted to some outputs, for problems too large for the
+    whole backward: dQ at the query rows `rows`, dK and dV at the key rows `keys`.
+
+    As the whole backward, row by row: each visited row's softmax and mask are taken over all
+    its keys. dQ_i needs row i alone; dK_j and dV_j sum over the query rows that see key j, and
+    under the causal mask rows i < j contribute exactly zero, so only rows from min(keys) on are
+    visited. Returns float64 [B, H, len(rows), d], [B, H, len(keys), d], [B, H, len(keys), d].
+    """
+    q, k, v, dout = _as64(q), _as64(k), _as64(v), _as64(dout)
+    B, H, N, d = q.shape
+    scale = resolve_scale(d, scale)
+    s_keep = keep_scale(p)
+    ids = _head_ids(B, H, bh_index)
+    rows = np.asarray(rows, dtype=np.int64)
+    keys = np.asarray(keys, dtype=np.int64)
+    dq = np.empty((B, H, len(rows), d))
+    dk = np.zeros((B, H, len(keys), d))
+    dv = np.zeros((B, H, len(keys), d))
+    first = int(keys.min()) if causal and len(keys) else 0
+    for b in range(B):
+        for h in range(H):
+            for c0 in range(0, len(rows), row_chunk):
+                ri = rows[c0:c0 + row_chunk]
+                pr, _ = _row_softmax(_masked_scores(q[b, h, ri], ri, k[b, h], causal, scale))
+                zs = keep_mask(seed, offset, ids[b, h], ri, N, p) * s_keep
+                do_rows = dout[b, h, ri]
+                dvec = np.sum(do_rows * ((pr * zs) @ v[b, h]), axis=1, keepdims=True)
+                ds = pr * (zs * (do_rows @ v[b, h].T) - dvec)
+                dq[b, h, c0:c0 + len(ri)] = scale * (ds @ k[b, h])
+            if not len(keys):
+                continue
+            for c0 in range(first, N, row_chunk):
+                ri = np.arange(c0, min(N, c0 + row_chunk))
+                pr, _ = _row_softmax(_masked_scores(q[b, h, ri], ri, k[b, h], causal, scale))
+                zs = keep_mask(seed, offset, ids[b, h], ri, N, p) * s_keep
+                do_rows = dout[b, h, ri]
+                dvec = np.sum(do_rows * ((pr * zs) @ v[b, h]), axis=1, keepdims=True)
+                pk, zk = pr[:, keys], zs[:, keys]
+                dsk = pk * (zk * (do_rows @ v[b, h, keys].T) - dvec)
+                dv[b, h] += (pk * zk).T @ do_rows
+                dk[b, h] += scale * (dsk.T @ q[b, h, ri])
+    return dq, dk, dv
+

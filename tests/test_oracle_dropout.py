@@ -193,3 +193,20 @@ def test_given_output_shift_uses_undropped_p(causal):
     np.testing.assert_allclose(dk - g0[1], -scale * np.swapaxes(p, -1, -2) @ (e * q), rtol=0,
                                atol=1e-12)
     np.testing.assert_allclose(dv, g0[2], rtol=0, atol=0)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_sampled_backward_is_the_whole_backward_at_those_rows(causal):
+    # the sampled form restricts the same definition (mask included): its dQ rows and dK, dV
+    # keys must be the whole dropout backward's, which the finite-difference pin fixes
+    from oracle import attention_backward_dropout_sampled
+    shape = (2, 2, 61, 8)
+    q, k, v, do = (_rand(shape, s) for s in (281, 282, 283, 284))
+    kw = dict(causal=causal, p=0.3, seed=21, offset=5)
+    rows = [0, 2, 17, 60]
+    keys = [1, 30, 31, 60]
+    dq, dk, dv = attention_backward_dropout(q, k, v, do, **kw)
+    sq, sk, sv = attention_backward_dropout_sampled(q, k, v, do, rows, keys, row_chunk=9, **kw)
+    np.testing.assert_allclose(sq, dq[:, :, rows], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(sk, dk[:, :, keys], rtol=0, atol=1e-13)
+    np.testing.assert_allclose(sv, dv[:, :, keys], rtol=0, atol=1e-13)
